@@ -1,0 +1,139 @@
+"""Host-side block bookkeeping that feeds the paged kernels.
+
+The library's kernels are stateless: they move bytes and attend.  Deciding which
+physical block holds which tokens is host work, done here:
+
+* a pool of ``num_blocks`` fixed-size blocks, handed out from a free list in
+  list order ("from anywhere free" -- [PA/paging], "PagedAttention" glossary,
+  section "Cách phân trang hoạt động");
+* one block table per sequence recording its blocks in logical order;
+* a new block only when the sequence's last block is full, so unused slots are
+  confined to the last block ([KVpag], "KV cache paginado e batching contínuo
+  para LLMs", section "Como funciona");
+* a reference count per block; forking a sequence shares every block
+  (count + 1, no data moves);
+* copy-on-write: a sequence about to write into a partly filled last block whose
+  count is above 1 takes a fresh block, records the (source, destination) pair
+  for ``copy_blocks``, drops the source's count by one and points its table at
+  the fresh block ([KVpag]; [PA/sharing], section "Chia sẻ block giữa các
+  chuỗi").  Sequences are served in the order the caller asks; the last holder
+  of a shared block writes in place because its count has dropped to 1.
+
+Running out of blocks raises ``OutOfBlocks``; no preemption is attempted here.
+"""
+
+from collections import deque
+
+import numpy as np
+
+
+class OutOfBlocks(RuntimeError):
+    pass
+
+
+class BlockManager:
+    def __init__(self, num_blocks, block_size, free_list=None):
+        if num_blocks <= 0 or block_size <= 0:
+            raise ValueError("num_blocks and block_size must be positive")
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+        order = range(num_blocks) if free_list is None else free_list
+        self._free = deque(int(b) for b in order)
+        if len(set(self._free)) != len(self._free) or any(not 0 <= b < num_blocks for b in self._free):
+            raise ValueError("free list must hold distinct ids in [0, num_blocks)")
+        self.refcount = np.zeros(self.num_blocks, dtype=np.int64)
+        self.tables = {}
+        self.lengths = {}
+
+    # -- allocation ---------------------------------------------------------
+    def _take(self):
+        if not self._free:
+            raise OutOfBlocks("no free physical block left")
+        b = self._free.popleft()
+        self.refcount[b] = 1
+        return b
+
+    def _release(self, b):
+        self.refcount[b] -= 1
+        if self.refcount[b] == 0:
+            self._free.append(b)
+
+    def num_free(self):
+        return len(self._free)
+
+    def add_sequence(self, seq, n_tokens=0):
+        """Register ``seq`` holding ``n_tokens`` tokens; returns the flat slots of those tokens."""
+        if seq in self.tables:
+            raise KeyError(f"sequence {seq} already exists")
+        self.tables[seq] = []
+        self.lengths[seq] = 0
+        return [self.append_slot(seq)[0] for _ in range(n_tokens)]
+
+    def append_slot(self, seq):
+        """Reserve the slot of ``seq``'s next token.
+
+        Returns ``(slot, cow_pair)``: ``slot`` is block * block_size + offset and
+        ``cow_pair`` is ``(src, dst)`` when the write needs a block copy first,
+        else ``None``.
+        """
+        table = self.tables[seq]
+        pos = self.lengths[seq]
+        bs = self.block_size
+        pair = None
+        if pos % bs == 0:                       # no block yet, or the last one is full
+            table.append(self._take())
+        else:
+            last = table[-1]
+            if self.refcount[last] > 1:         # shared partial block -> copy on write
+                fresh = self._take()
+                self.refcount[last] -= 1
+                table[-1] = fresh
+                pair = (last, fresh)
+        self.lengths[seq] = pos + 1
+        return table[pos // bs] * bs + pos % bs, pair
+
+    def fork(self, parent, child):
+        """``child`` shares every block of ``parent`` (reference counts + 1)."""
+        if child in self.tables:
+            raise KeyError(f"sequence {child} already exists")
+        self.tables[child] = list(self.tables[parent])
+        self.lengths[child] = self.lengths[parent]
+        for b in self.tables[child]:
+            self.refcount[b] += 1
+
+    def free_sequence(self, seq):
+        for b in self.tables.pop(seq):
+            self._release(b)
+        del self.lengths[seq]
+
+    # -- views for the kernels ---------------------------------------------
+    def block_table_array(self, seqs, max_blocks_per_seq):
+        """int32 ``[len(seqs), max_blocks_per_seq]``; unused entries are -1."""
+        out = np.full((len(seqs), max_blocks_per_seq), -1, dtype=np.int32)
+        for i, s in enumerate(seqs):
+            t = self.tables[s]
+            if len(t) > max_blocks_per_seq:
+                raise ValueError(f"sequence {s} holds {len(t)} blocks > {max_blocks_per_seq}")
+            out[i, :len(t)] = t
+        return out
+
+    def context_lens_array(self, seqs):
+        return np.array([self.lengths[s] for s in seqs], dtype=np.int32)
+
+    def slot(self, seq, pos):
+        t = self.tables[seq]
+        return t[pos // self.block_size] * self.block_size + pos % self.block_size
+
+    def utilisation(self):
+        """Tokens held / slots allocated over all distinct blocks in use."""
+        used = int(np.count_nonzero(self.refcount))
+        if used == 0:
+            return 1.0
+        # count each physical slot once even when shared
+        filled = {}
+        for s, t in self.tables.items():
+            n = self.lengths[s]
+            for j, b in enumerate(t):
+                k = min(self.block_size, n - j * self.block_size)
+                filled[b] = max(filled.get(b, 0), k)
+        return sum(filled.values()) / (used * self.block_size)

@@ -1,0 +1,230 @@
+"""Seeded synthetic inputs for the paged decode workloads.
+
+This module only draws random numbers and sizes buffers: it holds none of the
+method's arithmetic (no addressing, allocation, attention or encoding).  Both
+the GPU path's tests/bench and the CPU oracle consume what it produces.
+
+Draw order for a decode workload (one ``numpy.random.Generator`` seeded with the
+workload's seed, then one ``torch.Generator`` with the same seed for the
+tensors):  context lengths -> free-list permutation -> q -> K pool -> V pool ->
+new-token K -> new-token V.  Values are fp32 N(0, 1) cast to the storage dtype
+by round-to-nearest-even (torch's ``.to``).
+
+Length recipes:
+* ``("fixed", [..])``                     exact lengths;
+* ``("lognormal", median, sigma, lo, hi)`` ``clip(round(exp(N(ln median, sigma))), lo, hi)``;
+* ``("uniform", lo, hi)``                  integers uniform in [lo, hi].
+The lognormal sigma (0.6) is a reading: the workloads name only median and range.
+The pages measure on ShareGPT / Alpaca request traces; those are not used --
+these lognormal / uniform mixes of the stated sizes stand in for them.
+"""
+
+from dataclasses import dataclass, field, replace
+import math
+
+import numpy as np
+import torch
+
+DTYPES = {
+    "f32": torch.float32,
+    "f16": torch.float16,
+    "bf16": torch.bfloat16,
+    "fp8_e4m3": torch.uint8,   # stored codes; written by reshape_and_cache
+}
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    seed: int
+    num_seqs: int
+    num_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    q_dtype: str
+    kv_dtype: str
+    lengths: tuple
+    max_blocks_per_seq: int
+    num_blocks: int = 0          # 0 -> sized from the drawn lengths (pool_slack x need, upper bound)
+    pool_slack: float = 1.2
+    partition_size: int = 0      # 0 -> library's automatic choice
+    scale: float = 0.0           # 0 -> 1/sqrt(head_dim)
+
+    @property
+    def softmax_scale(self):
+        return self.scale if self.scale > 0 else 1.0 / math.sqrt(self.head_dim)
+
+
+@dataclass(frozen=True)
+class SharedPrefixWorkload:
+    """Parallel sampling over shared prompts, FP8 cache (copy-on-write workload)."""
+    name: str
+    seed: int
+    num_prompts: int
+    prompt_len: int
+    samples_per_prompt: int
+    cont_lo: int
+    cont_hi: int
+    num_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    max_blocks_per_seq: int
+    q_dtype: str = "f16"
+    src_dtype: str = "f16"
+    kv_dtype: str = "fp8_e4m3"
+
+    @property
+    def softmax_scale(self):
+        return 1.0 / math.sqrt(self.head_dim)
+
+
+# The five named workloads.
+TINY_F32 = DecodeWorkload(
+    name="tiny fp32 paged decode: 4 seqs ctx {40,17,1,64}, 8 heads MHA, d64, bs16, 64-block pool",
+    seed=25901, num_seqs=4, num_heads=8, num_kv_heads=8, head_dim=64, block_size=16,
+    q_dtype="f32", kv_dtype="f32", lengths=("fixed", (40, 17, 1, 64)),
+    max_blocks_per_seq=4, num_blocks=64, scale=1.0 / 8.0)
+
+LLAMA13B_F16 = DecodeWorkload(
+    name="LLaMA-13B-shaped decode, one layer: 64 seqs, 40/40 heads, d128, fp16, bs16, "
+         "lognormal ctx median 600 in [16,2048]",
+    seed=25902, num_seqs=64, num_heads=40, num_kv_heads=40, head_dim=128, block_size=16,
+    q_dtype="f16", kv_dtype="f16", lengths=("lognormal", 600, 0.6, 16, 2048),
+    max_blocks_per_seq=128)
+
+GQA_BF16 = DecodeWorkload(
+    name="GQA decode, one layer: 256 seqs, 64 q heads over 8 kv heads, d128, bf16, bs16, "
+         "lognormal ctx median 1000 in [32,4096]",
+    seed=25903, num_seqs=256, num_heads=64, num_kv_heads=8, head_dim=128, block_size=16,
+    q_dtype="bf16", kv_dtype="bf16", lengths=("lognormal", 1000, 0.6, 32, 4096),
+    max_blocks_per_seq=256)
+
+LONG_SPLITK_BF16 = DecodeWorkload(
+    name="long-context split-K decode: 8 seqs ctx uniform [32768,131072], 32 q / 8 kv heads, "
+         "d128, bf16, bs16, partitions of 512 tokens, 70000-block pool",
+    seed=25904, num_seqs=8, num_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+    q_dtype="bf16", kv_dtype="bf16", lengths=("uniform", 32768, 131072),
+    max_blocks_per_seq=8192, num_blocks=70000, partition_size=512)
+
+SHARED_PREFIX_FP8 = SharedPrefixWorkload(
+    name="shared-prefix parallel sampling with copy-on-write: 32 prompts x 1000 tokens, n=4, "
+         "continuations 0-512, 40 heads MHA, d128, fp16 q, fp8 e4m3 K/V with per-tensor scale",
+    seed=25905, num_prompts=32, prompt_len=1000, samples_per_prompt=4, cont_lo=0, cont_hi=512,
+    num_heads=40, head_dim=128, block_size=16, num_blocks=6400, max_blocks_per_seq=95)
+
+WORKLOADS = {
+    "tiny_f32": TINY_F32,
+    "llama13b_f16": LLAMA13B_F16,
+    "gqa_bf16": GQA_BF16,
+    "long_splitk_bf16": LONG_SPLITK_BF16,
+    "shared_prefix_fp8": SHARED_PREFIX_FP8,
+}
+
+
+def draw_lengths(rng, recipe, n):
+    kind = recipe[0]
+    if kind == "fixed":
+        vals = np.asarray(recipe[1], dtype=np.int64)
+        if len(vals) != n:
+            raise ValueError("fixed length list does not match num_seqs")
+        return vals
+    if kind == "lognormal":
+        _, median, sigma, lo, hi = recipe
+        x = np.exp(rng.normal(np.log(median), sigma, size=n))
+        return np.clip(np.rint(x), lo, hi).astype(np.int64)
+    if kind == "uniform":
+        _, lo, hi = recipe
+        return rng.integers(lo, hi + 1, size=n).astype(np.int64)
+    raise ValueError(f"unknown length recipe {kind}")
+
+
+def pool_blocks_upper_bound(lengths, block_size, slack):
+    """Pool size: slack x an upper bound on the blocks the lengths can occupy (sizing only)."""
+    bound = int(np.sum(lengths)) // block_size + len(lengths)
+    return int(math.ceil(slack * bound))
+
+
+def randn(gen, shape, dtype, device):
+    """fp32 N(0,1) drawn with ``gen`` on ``device``, cast by round-to-nearest-even."""
+    x = torch.randn(shape, generator=gen, dtype=torch.float32, device=device)
+    return x.to(dtype)
+
+
+def make_generator(seed, device):
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+@dataclass
+class DecodeInputs:
+    workload: DecodeWorkload
+    context_lens: np.ndarray       # int64 [S]
+    free_list: list                # seeded permutation of the pool's block ids
+    num_blocks: int
+    q: torch.Tensor                # [S, H, d]
+    k_cache: torch.Tensor          # [NB, KVH, bs, d]
+    v_cache: torch.Tensor
+    k_new: torch.Tensor            # [S, KVH, d]   the new token's key per sequence
+    v_new: torch.Tensor
+    extra: dict = field(default_factory=dict)
+
+
+def make_decode_inputs(w: DecodeWorkload, device="cpu", lengths=None):
+    """Draw every input of one decode step of workload ``w`` on ``device``."""
+    rng = np.random.default_rng(w.seed)
+    ctx = draw_lengths(rng, w.lengths, w.num_seqs) if lengths is None else np.asarray(lengths, np.int64)
+    nb = w.num_blocks or pool_blocks_upper_bound(ctx, w.block_size, w.pool_slack)
+    free_list = rng.permutation(nb).tolist()
+    gen = make_generator(w.seed, device)
+    qdt, kvdt = DTYPES[w.q_dtype], DTYPES[w.kv_dtype]
+    S, H, KVH, d, bs = w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size
+    q = randn(gen, (S, H, d), qdt, device)
+    k_cache = randn(gen, (nb, KVH, bs, d), kvdt, device)
+    v_cache = randn(gen, (nb, KVH, bs, d), kvdt, device)
+    k_new = randn(gen, (S, KVH, d), kvdt, device)
+    v_new = randn(gen, (S, KVH, d), kvdt, device)
+    return DecodeInputs(w, ctx, free_list, nb, q, k_cache, v_cache, k_new, v_new)
+
+
+def scaled(w: DecodeWorkload, **kw):
+    """A copy of workload ``w`` with some fields replaced (smaller parity-test variants)."""
+    return replace(w, **kw)
+
+
+@dataclass
+class SharedPrefixInputs:
+    workload: SharedPrefixWorkload
+    cont_lens: np.ndarray          # int64 [num_prompts * samples]
+    free_list: list
+    prompt_k: torch.Tensor         # [num_prompts, prompt_len, H, d] src dtype
+    prompt_v: torch.Tensor
+    gen: torch.Generator           # continues the stream: per-step K/V, then q
+
+
+def make_shared_prefix_inputs(w: SharedPrefixWorkload, device="cpu"):
+    rng = np.random.default_rng(w.seed)
+    n_seq = w.num_prompts * w.samples_per_prompt
+    cont = rng.integers(w.cont_lo, w.cont_hi + 1, size=n_seq).astype(np.int64)
+    free_list = rng.permutation(w.num_blocks).tolist()
+    gen = make_generator(w.seed, device)
+    sdt = DTYPES[w.src_dtype]
+    pk = randn(gen, (w.num_prompts, w.prompt_len, w.num_heads, w.head_dim), sdt, device)
+    pv = randn(gen, (w.num_prompts, w.prompt_len, w.num_heads, w.head_dim), sdt, device)
+    return SharedPrefixInputs(w, cont, free_list, pk, pv, gen)
+
+
+def draw_step_kv(inp: SharedPrefixInputs, n_tokens, device):
+    """Keys and values of the next ``n_tokens`` continuation tokens (draw order continues)."""
+    w = inp.workload
+    sdt = DTYPES[w.src_dtype]
+    k = randn(inp.gen, (n_tokens, w.num_heads, w.head_dim), sdt, device)
+    v = randn(inp.gen, (n_tokens, w.num_heads, w.head_dim), sdt, device)
+    return k, v
+
+
+def draw_query(inp: SharedPrefixInputs, n_seqs, device):
+    w = inp.workload
+    return randn(inp.gen, (n_seqs, w.num_heads, w.head_dim), DTYPES[w.q_dtype], device)

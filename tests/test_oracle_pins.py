@@ -1,0 +1,356 @@
+"""Pins of the CPU oracle to facts fixed outside the oracle itself (CPU only).
+
+Each test names what it pins and where the fact comes from: a value the pages
+print (fixtures under tests/golden/), a library routine that computes the same
+definition by another route, a closed form, or brute force on tiny inputs.
+"""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import e4m3_ref
+from oracle.paged_attention_ref import (
+    attend_one_ref, attend_ref, blocks_needed, copy_ref, gather_tokens,
+    merge_partials_ref, partial_state_ref, reshape_ref, slot_of, take_blocks,
+)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# Worked example of the glossary page (paging section): values it prints
+# ---------------------------------------------------------------------------
+
+def test_worked_example_table_gather_and_waste():
+    g = _golden("worked_example.json")
+    bs, d, nb, n = g["block_size"], g["head_dim"], g["pool_blocks"], g["request_tokens"]
+    free = list(g["free_blocks"])
+    keys = torch.randn(n, d, generator=torch.Generator().manual_seed(0)).numpy()
+    pool = np.zeros((nb, 1, bs, d), dtype=np.float32)          # one kv head
+    table = take_blocks(free, blocks_needed(n, bs))
+    assert table == g["expected_block_table"]
+    assert free == [2, 33]
+    slots = [slot_of(table, pos, bs) for pos in range(n)]
+    pool_k, _ = reshape_ref(keys[:, None, :], keys[:, None, :], pool, pool, np.array(slots), bs)
+    gathered = gather_tokens(pool_k, table, n, bs, 0)
+    assert np.array_equal(gathered, keys) == g["expected_keys_intact"]
+    assert len(table) * bs - n == g["expected_unused_slots_paged"]
+    assert g["reservation_tokens"] - n == g["expected_unused_slots_reserved"]
+    # the example's own gather form: pool[table] flattened, cut to the request length
+    flat = pool_k[table, 0].reshape(-1, d)[:n]
+    assert np.array_equal(flat, keys)
+
+
+def test_tiny_workload_block_count():
+    # 40, 17, 1 and 64 tokens at block size 16 take 3 + 2 + 1 + 4 blocks
+    assert [blocks_needed(c, 16) for c in (40, 17, 1, 64)] == [3, 2, 1, 4]
+    assert sum(blocks_needed(c, 16) for c in (40, 17, 1, 64)) == 10
+
+
+@pytest.mark.parametrize("bs", [1, 8, 16, 32])
+def test_waste_confined_to_last_block(bs):
+    for n in range(0, 300):
+        nb = blocks_needed(n, bs)
+        waste = nb * bs - n
+        assert 0 <= waste < bs                       # less than one block
+        assert waste == (-n) % bs
+        if nb:
+            assert (nb - 1) * bs < n <= nb * bs       # every block but the last is full
+
+
+def test_llama13b_bytes_per_sequence():
+    g = _golden("llama13b_kv_bytes.json")
+    s = g["model_shape_reading"]
+    per_token = 2 * s["layers"] * s["heads"] * s["head_dim"] * s["bytes_per_element"]
+    total = per_token * g["tokens"]
+    assert abs(total - g["approx_bytes_per_sequence"]) <= g["rounding"]
+
+
+def test_fp8_pool_is_half_of_fp16_pool():
+    shape = (10, 4, 16, 128)
+    assert np.zeros(shape, np.uint8).nbytes * 2 == np.zeros(shape, np.float16).nbytes
+
+
+# ---------------------------------------------------------------------------
+# Attention: library routine, closed forms, special cases, brute force
+# ---------------------------------------------------------------------------
+
+def _rand_case(seed, S, H, KVH, d, bs, lens, nb):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((S, H, d))
+    kp = rng.standard_normal((nb, KVH, bs, d))
+    vp = rng.standard_normal((nb, KVH, bs, d))
+    perm = rng.permutation(nb).tolist()
+    maxblk = max(blocks_needed(c, bs) for c in lens)
+    tables = np.full((S, maxblk), -1, np.int64)
+    for s, c in enumerate(lens):
+        t = take_blocks(perm, blocks_needed(c, bs))
+        tables[s, :len(t)] = t
+    return q, kp, vp, tables, np.array(lens)
+
+
+def _sdpa(q_vec, keys, values, scale):
+    """torch's scaled_dot_product_attention on CPU float64, one query row."""
+    qq = torch.from_numpy(np.asarray(q_vec, np.float64))[None, None, None, :]
+    kk = torch.from_numpy(np.asarray(keys, np.float64))[None, None]
+    vv = torch.from_numpy(np.asarray(values, np.float64))[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, scale=scale)[0, 0, 0].numpy()
+
+
+@pytest.mark.parametrize("seed,H,KVH,d,bs,lens", [
+    (1, 2, 2, 8, 4, [5, 1, 9]),
+    (2, 4, 1, 16, 16, [40, 17, 33]),
+    (3, 8, 2, 4, 2, [3, 7]),
+])
+def test_attend_matches_torch_sdpa(seed, H, KVH, d, bs, lens):
+    nb = sum(blocks_needed(c, bs) for c in lens) + 3
+    q, kp, vp, tables, ctx = _rand_case(seed, len(lens), H, KVH, d, bs, lens, nb)
+    scale = 1.0 / math.sqrt(d)
+    out = attend_ref(q, kp, vp, tables, ctx, scale, bs)
+    G = H // KVH
+    for s in range(len(lens)):
+        for h in range(H):
+            K = gather_tokens(kp, tables[s], ctx[s], bs, h // G)
+            V = gather_tokens(vp, tables[s], ctx[s], bs, h // G)
+            np.testing.assert_allclose(out[s, h], _sdpa(q[s, h], K, V, scale), rtol=1e-12, atol=1e-12)
+
+
+def test_gqa_equals_mha_with_repeated_kv_heads():
+    S, H, KVH, d, bs, lens = 3, 8, 2, 8, 4, [6, 11, 1]
+    nb = 12
+    q, kp, vp, tables, ctx = _rand_case(7, S, H, KVH, d, bs, lens, nb)
+    out_gqa = attend_ref(q, kp, vp, tables, ctx, 0.3, bs)
+    kp_rep = torch.from_numpy(kp).repeat_interleave(H // KVH, dim=1).numpy()
+    vp_rep = torch.from_numpy(vp).repeat_interleave(H // KVH, dim=1).numpy()
+    out_mha = attend_ref(q, kp_rep, vp_rep, tables, ctx, 0.3, bs)
+    np.testing.assert_array_equal(out_gqa, out_mha)
+
+
+def test_any_block_permutation_gives_the_same_output():
+    """Paged output equals contiguous attention for every placement of the blocks."""
+    bs, d, ctx, nb = 2, 3, 7, 5          # 4 blocks used out of a 5-block pool
+    rng = np.random.default_rng(11)
+    K = rng.standard_normal((ctx, d))
+    V = rng.standard_normal((ctx, d))
+    q = rng.standard_normal((1, 1, d))
+    ref = _sdpa(q[0, 0], K, V, 0.7)
+    outs = []
+    for perm in itertools.permutations(range(nb), blocks_needed(ctx, bs)):
+        kp = np.full((nb, 1, bs, d), np.nan)
+        vp = np.full((nb, 1, bs, d), np.nan)      # unused blocks and tail slots poisoned
+        table = list(perm)
+        for t in range(ctx):
+            kp[table[t // bs], 0, t % bs] = K[t]
+            vp[table[t // bs], 0, t % bs] = V[t]
+        out = attend_ref(q, kp, vp, np.array([table]), np.array([ctx]), 0.7, bs)
+        outs.append(out[0, 0])
+        np.testing.assert_allclose(out[0, 0], ref, rtol=1e-12, atol=1e-13)
+    assert len(outs) == 120
+    for o in outs[1:]:
+        np.testing.assert_array_equal(o, outs[0])
+
+
+def test_single_token_returns_its_value_exactly():
+    rng = np.random.default_rng(3)
+    K = rng.standard_normal((1, 8))
+    V = rng.standard_normal((1, 8))
+    np.testing.assert_array_equal(attend_one_ref(rng.standard_normal(8), K, V, 0.5), V[0])
+
+
+def test_zero_query_gives_mean_of_values():
+    rng = np.random.default_rng(4)
+    K = rng.standard_normal((13, 8))
+    V = rng.standard_normal((13, 8))
+    np.testing.assert_allclose(attend_one_ref(np.zeros(8), K, V, 0.5), V.mean(axis=0), rtol=1e-13, atol=1e-14)
+
+
+def test_one_hot_logit_selects_its_value_even_when_huge():
+    rng = np.random.default_rng(5)
+    d = 8
+    K = rng.standard_normal((9, d)) * 0.01
+    q = np.zeros(d); q[2] = 1000.0
+    K[6, 2] = 5.0                               # logit 5000 for token 6, |others| < ~30
+    V = rng.standard_normal((9, d))
+    out = attend_one_ref(q, K, V, 1.0)
+    assert np.all(np.isfinite(out))            # max subtraction keeps exp finite
+    np.testing.assert_allclose(out, V[6], rtol=0, atol=1e-12)
+
+
+def test_two_tokens_closed_form_logistic():
+    rng = np.random.default_rng(6)
+    for _ in range(20):
+        q = rng.standard_normal(4); K = rng.standard_normal((2, 4)); V = rng.standard_normal((2, 4))
+        sc = 0.37
+        a = sc * K[0] @ q; b = sc * K[1] @ q
+        w0 = 1.0 / (1.0 + math.exp(b - a))      # logistic form of a 2-way softmax
+        np.testing.assert_allclose(attend_one_ref(q, K, V, sc), w0 * V[0] + (1 - w0) * V[1], rtol=1e-12, atol=1e-13)
+
+
+def test_brute_force_tiny_with_fractions():
+    """ctx <= 3, d <= 2 with small integers: exact rational weights via math.exp of integers."""
+    K = np.array([[1.0, 0.0], [0.0, 1.0], [1.0, 1.0]])
+    V = np.array([[2.0, -1.0], [0.5, 4.0], [-3.0, 1.0]])
+    q = np.array([1.0, 2.0])
+    # logits 1, 2, 3 (scale 1): weights e^1 : e^2 : e^3
+    e = [math.e, math.e ** 2, math.e ** 3]
+    expect = sum(w * v for w, v in zip(e, V)) / sum(e)
+    np.testing.assert_allclose(attend_one_ref(q, K, V, 1.0), expect, rtol=1e-14)
+
+
+def test_zero_context_gives_zero_output():
+    q, kp, vp, tables, _ = _rand_case(8, 2, 2, 2, 4, 4, [4, 4], 4)
+    out = attend_ref(q, kp, vp, tables, np.array([0, 4]), 0.5, 4)
+    assert np.all(out[0] == 0.0)
+    assert np.any(out[1] != 0.0)
+
+
+@pytest.mark.parametrize("part", [1, 2, 3, 5, 16, 100])
+def test_partition_merge_equals_single_pass(part):
+    rng = np.random.default_rng(part)
+    n, d = 37, 6
+    q = rng.standard_normal(d) * 30.0           # logits ~ N(0, 30^2): needs the max shift
+    K = rng.standard_normal((n, d)); V = rng.standard_normal((n, d))
+    states = [partial_state_ref(q, K[a:a + part], V[a:a + part], 0.5) for a in range(0, n, part)]
+    states.append(partial_state_ref(q, K[:0], V[:0], 0.5))      # an empty slice merges as nothing
+    np.testing.assert_allclose(merge_partials_ref(states), _sdpa(q, K, V, 0.5), rtol=1e-11, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Cache writes and block copies: another formulation through torch indexing
+# ---------------------------------------------------------------------------
+
+def test_reshape_matches_flat_slot_indexing_and_touches_nothing_else():
+    rng = np.random.default_rng(9)
+    NB, KVH, bs, d, T = 7, 3, 4, 5, 9
+    kp = rng.integers(-1000, 1000, (NB, KVH, bs, d)).astype(np.int16)
+    vp = rng.integers(-1000, 1000, (NB, KVH, bs, d)).astype(np.int16)
+    key = rng.integers(-1000, 1000, (T, KVH, d)).astype(np.int16)
+    val = rng.integers(-1000, 1000, (T, KVH, d)).astype(np.int16)
+    slots = rng.choice(NB * bs, T, replace=False).astype(np.int64)
+    slots[[2, 5]] = -1                                       # padding tokens write nothing
+    k2, v2 = reshape_ref(key, val, kp, vp, slots, bs)
+    # same write via a [NB*bs, KVH, d] view of a [NB, bs, KVH, d] permutation
+    for pool, src, got in ((kp, key, k2), (vp, val, v2)):
+        t = torch.from_numpy(pool.copy()).permute(0, 2, 1, 3).contiguous().view(NB * bs, KVH, d)
+        keep = slots >= 0
+        t[torch.from_numpy(slots[keep])] = torch.from_numpy(src[keep])
+        expect = t.view(NB, bs, KVH, d).permute(0, 2, 1, 3).numpy()
+        np.testing.assert_array_equal(got, expect)
+        changed = np.argwhere(np.any(got != pool, axis=-1))
+        allowed = {(s // bs, h, s % bs) for s in slots[keep] for h in range(KVH)}
+        assert {tuple(c) for c in changed} <= allowed
+
+
+def test_copy_blocks_matches_index_copy():
+    rng = np.random.default_rng(10)
+    NB, KVH, bs, d = 9, 2, 4, 3
+    kp = rng.integers(0, 255, (NB, KVH, bs, d)).astype(np.uint8)
+    vp = rng.integers(0, 255, (NB, KVH, bs, d)).astype(np.uint8)
+    pairs = np.array([[1, 5], [1, 6], [3, 8]])
+    k2, v2 = copy_ref(kp, vp, pairs)
+    for pool, got in ((kp, k2), (vp, v2)):
+        t = torch.from_numpy(pool.copy())
+        t.index_copy_(0, torch.tensor(pairs[:, 1]), torch.from_numpy(pool)[torch.tensor(pairs[:, 0])])
+        np.testing.assert_array_equal(got, t.numpy())
+        for b in range(NB):
+            if b not in pairs[:, 1]:
+                np.testing.assert_array_equal(got[b], pool[b])
+
+
+# ---------------------------------------------------------------------------
+# E4M3 codec: OCP definition, torch's float8_e4m3fn cast, closed forms
+# ---------------------------------------------------------------------------
+
+def test_e4m3_decode_all_codes_match_torch_float8():
+    ours = e4m3_ref.decode_e4m3(np.arange(256))
+    lib = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(lib)
+    assert np.array_equal(np.isnan(ours), nan)
+    np.testing.assert_array_equal(ours[~nan], lib[~nan])
+    assert np.flatnonzero(nan).tolist() == [0x7F, 0xFF]
+
+
+def test_e4m3_closed_form_values():
+    dec = e4m3_ref.decode_e4m3
+    assert dec(0x7E) == 448.0                   # largest finite: 2^8 * 1.75
+    assert dec(0x01) == 2.0 ** -9               # smallest subnormal
+    assert dec(0x07) == 7 * 2.0 ** -9           # largest subnormal
+    assert dec(0x08) == 2.0 ** -6               # smallest normal
+    assert dec(0x38) == 1.0                     # exponent field = bias
+    assert dec(0xB8) == -1.0
+    assert dec(0x80) == 0.0 and np.signbit(dec(0x80))
+    assert np.isnan(dec(0x7F)) and np.isnan(dec(0xFF))
+
+
+@pytest.mark.parametrize("scale", [1.0, 2.0 ** -5, 3.7 / 448.0])
+def test_e4m3_encode_every_fp16_pattern_matches_torch_in_range(scale):
+    x = torch.arange(65536, dtype=torch.int32).to(torch.int16).view(torch.float16).to(torch.float32)
+    xs = x.numpy()
+    codes = e4m3_ref.encode_e4m3(xs, scale)
+    quot = torch.from_numpy((xs / np.float32(scale)).astype(np.float32))
+    lib = quot.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    in_range = np.abs(quot.numpy()) <= 448.0
+    assert in_range.sum() > 10000
+    np.testing.assert_array_equal(codes[in_range], lib[in_range])
+    big = np.isfinite(quot.numpy()) & ~in_range
+    assert np.all((codes[big] & 0x7F) == 0x7E)                  # saturate to +-448
+    assert np.array_equal(codes[big] >> 7, np.signbit(quot.numpy()[big]).astype(np.uint8))
+
+
+def test_e4m3_special_inputs():
+    enc = e4m3_ref.encode_e4m3
+    v = np.array([np.inf, -np.inf, np.nan, -np.nan, 0.0, -0.0, 1e30, -1e30], np.float32)
+    v[3] = -np.float32(np.nan)
+    got = enc(v, 1.0).tolist()
+    assert got[0] == 0x7E and got[1] == 0xFE
+    assert got[2] == 0x7F and got[3] == 0xFF
+    assert got[4] == 0x00 and got[5] == 0x80
+    assert got[6] == 0x7E and got[7] == 0xFE
+
+
+def test_e4m3_roundtrip_ties_and_error_bound():
+    enc, dec = e4m3_ref.encode_e4m3, e4m3_ref.decode_e4m3
+    finite = [c for c in range(256) if c not in (0x7F, 0xFF)]
+    vals = dec(np.array(finite))
+    assert enc(vals.astype(np.float32), 1.0).tolist() == finite        # exact values round-trip
+    pos = dec(np.arange(0x7F))
+    mids = (pos[:-1] + pos[1:]) / 2                                     # exact in float32
+    got = enc(mids.astype(np.float32), 1.0)
+    lo_codes = np.arange(0x7E)
+    expect = np.where(lo_codes % 2 == 0, lo_codes, lo_codes + 1)       # tie -> even mantissa
+    np.testing.assert_array_equal(got, expect)
+    rng = np.random.default_rng(12)
+    x = (rng.standard_normal(20000) * 50).astype(np.float32)
+    err = np.abs(dec(enc(x, 1.0)) - np.clip(x, -448, 448))
+    gap = np.diff(pos)
+    idx = np.clip(np.searchsorted(pos, np.minimum(np.abs(x), 448)) - 1, 0, len(gap) - 1)
+    assert np.all(err <= gap[idx] / 2 + 1e-12)                          # at most half a step
+
+
+# ---------------------------------------------------------------------------
+# Contiguous model
+# ---------------------------------------------------------------------------
+
+def test_contiguous_model_fork_is_independent():
+    m = oracle.ContiguousSequences()
+    m.new(0)
+    rows = np.arange(12, dtype=np.float32).reshape(3, 1, 4)
+    m.extend(0, rows, -rows)
+    m.fork(0, 1)
+    m.append(1, np.full((1, 4), 7, np.float32), np.full((1, 4), 8, np.float32))
+    assert m.length(0) == 3 and m.length(1) == 4
+    np.testing.assert_array_equal(m.keys(0), rows)
+    np.testing.assert_array_equal(m.keys(1)[:3], rows)
+    np.testing.assert_array_equal(m.values(1)[3], np.full((1, 4), 8))
