@@ -1,0 +1,284 @@
+"""Benchmark of one paged decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama13b_f16]
+
+A step is one pass of the hot path over one synthetic decode batch, inputs
+resident in HBM: reshape_and_cache writes every sequence's new key/value into
+the slot the block manager gave it, then paged_attention_decode attends over
+each sequence's paged context (the split-context reduce included when the plan
+uses one).  copy_blocks has no work in this workload (no block is shared); it is
+timed separately on the copy-on-write pairs of the shared-prefix workload and
+reported under "components".
+
+Prints one JSON line:
+* value      algorithmic KV bytes read per step / step time (GB/s), the step
+             being reshape_and_cache + attention;
+* roofline   the attention call (its kernels) against MI355X's 8 TB/s HBM;
+             achieved = algorithmic bytes per call / mean call time (HIP events
+             on the stream the kernels run on);
+* cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic.json")
+KERNEL_SOURCES = ["attn_vector.hip", "attn_mfma.hip", "attn_reduce.hip", "pkv_device.h", "pkv_api.hip"]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama13b_f16")
+    ap.add_argument("--partition", type=int, default=None, help="override the workload's partition size")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="bound on the oracle sample's CPU time")
+    ap.add_argument("--calibrate-copy", type=int, default=0,
+                    help="also run one copy_blocks of this many blocks (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_259_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per attention call from committed counter runs, if taken on the current kernels."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = t.get(workload)
+    if not entry or entry.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return entry.get("bytes_per_call")
+
+
+def algorithmic_bytes(w, ctx, elt_q, elt_kv):
+    """KV bytes each sequence's context reads, plus q, out, table entries and context lengths."""
+    kv = int(np.sum(ctx)) * w.num_kv_heads * w.head_dim * 2 * elt_kv
+    qo = 2 * w.num_seqs * w.num_heads * w.head_dim * elt_q
+    tables = int(np.sum(-(-ctx // w.block_size))) * 4 + 4 * w.num_seqs
+    return kv, kv + qo + tables
+
+
+class _BlockSubset:
+    """float64 host copy of some pool blocks, read as pool[block, kv_head] by the oracle."""
+
+    def __init__(self, pool, blocks):
+        import torch
+        ids = sorted(set(int(b) for b in blocks))
+        rows = pool.index_select(0, torch.tensor(ids, dtype=torch.int64, device=pool.device))
+        host = rows.cpu().to(torch.float64).numpy()
+        self._rows = {b: host[i] for i, b in enumerate(ids)}
+        self.shape = tuple(pool.shape)
+        self.dtype = np.float64
+
+    def __getitem__(self, key):
+        return self._rows[int(key[0])][key[1]]
+
+
+def cpu_baseline(w, inp, tables, ctx, budget_s):
+    """Time the oracle on whole sequences (all heads) until the wall-time budget is spent.
+
+    The oracle runs as it stands: numpy in float64, its BLAS calls free to use
+    the BLAS library's thread pool (the thread count is reported as ``cores``).
+    Host copies of the blocks each sequence uses are made outside the timing.
+    """
+    import oracle
+    import torch
+    from threadpoolctl import threadpool_info
+    q = inp["q"].cpu().to(torch.float64).numpy()
+    elt = inp["k"].element_size()
+    done, kv_bytes, spent = 0, 0, 0.0
+    for s in range(w.num_seqs):
+        n = int(ctx[s])
+        blocks = tables[s, : -(-n // w.block_size)]
+        kp = _BlockSubset(inp["k"], blocks)
+        vp = _BlockSubset(inp["v"], blocks)
+        t0 = time.perf_counter()
+        oracle.attend_ref(q[s:s + 1], kp, vp, tables[s:s + 1], ctx[s:s + 1], w.softmax_scale, w.block_size)
+        spent += time.perf_counter() - t0
+        done += 1
+        kv_bytes += n * w.num_kv_heads * w.head_dim * 2 * elt
+        if spent > budget_s:
+            break
+    blas_threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    return {
+        "value": round(kv_bytes / spent / 1e9, 6), "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
+        "seq_per_s": round(done / spent, 3),
+        "sample": f"first {done} of {w.num_seqs} sequences of the same decode step, all {w.num_heads} heads "
+                  f"({kv_bytes / 1e6:.1f} MB of KV), fp64 numpy oracle, {spent:.1f} s wall",
+        "host_cores_available": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the paged decode path has no "
+                                   "multi-GPU mode in this build (see the sharding notes in the design doc)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    from paged_kv_cache_259_amd import ops, synth
+    from paged_kv_cache_259_amd.block_manager import BlockManager
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[args.workload]
+    if not isinstance(w, synth.DecodeWorkload):
+        raise SystemExit("bench.py times decode workloads (llama13b_f16, gqa_bf16, long_splitk_bf16, tiny_f32)")
+    part = w.partition_size if args.partition is None else args.partition
+
+    # ---- inputs: seeded, generated on the device; tables from the host block manager
+    inp = synth.make_decode_inputs(w, device=dev)
+    bm = BlockManager(inp.num_blocks, w.block_size, inp.free_list)
+    seqs = list(range(w.num_seqs))
+    for s in seqs:
+        bm.add_sequence(s, int(inp.context_lens[s]) - 1)           # cached before this step
+    slots = torch.tensor([bm.append_slot(s)[0] for s in seqs], dtype=torch.int64, device=dev)
+    tables_np = bm.block_table_array(seqs, w.max_blocks_per_seq)
+    ctx_np = bm.context_lens_array(seqs)
+    tables = torch.from_numpy(tables_np).to(dev)
+    ctx = torch.from_numpy(ctx_np).to(dev)
+    max_ctx = int(ctx_np.max())
+    qd, kvd = ops.dtype_code(inp.q.dtype), ops.dtype_code(inp.k_cache.dtype)
+    plan = ops.attention_plan(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size, max_ctx, part,
+                              qd, kvd)
+    ws_bytes = ops.attention_workspace_bytes(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size,
+                                             max_ctx, part, qd, kvd)
+    workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(inp.q)
+    stream = torch.cuda.current_stream()
+
+    def reshape():
+        ops.reshape_and_cache(inp.k_new, inp.v_new, inp.k_cache, inp.v_cache, slots, stream=stream)
+
+    def attend():
+        ops.paged_attention_decode(out, inp.q, inp.k_cache, inp.v_cache, tables, ctx, w.softmax_scale, max_ctx,
+                                   partition_size=part, workspace=workspace, stream=stream)
+
+    for _ in range(args.warmup):
+        reshape()
+        attend()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        reshape()
+        ev[i][1].record(stream)
+        attend()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_reshape = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)])
+    t_attn = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)])
+    t_step = np.array([ev[i][0].elapsed_time(ev[i][2]) for i in range(K)])
+    step_ms = float(np.mean(t_step))
+
+    # ---- copy_blocks on copy-on-write pairs shaped like the shared-prefix workload (timed separately)
+    sp = synth.SHARED_PREFIX_FP8
+    n_pairs = 3 * sp.num_prompts
+    cb_pool_k = torch.zeros((2 * n_pairs + 8, sp.num_heads, sp.block_size, sp.head_dim), dtype=torch.uint8, device=dev)
+    cb_pool_v = torch.zeros_like(cb_pool_k)
+    perm = np.random.default_rng(sp.seed).permutation(2 * n_pairs)
+    pairs = torch.from_numpy(np.stack([perm[:n_pairs], perm[n_pairs:]], 1).astype(np.int64)).to(dev)
+    for _ in range(3):
+        ops.copy_blocks(cb_pool_k, cb_pool_v, pairs, stream=stream)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(20):
+        ops.copy_blocks(cb_pool_k, cb_pool_v, pairs, stream=stream)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_us = c0.elapsed_time(c1) / 20 * 1e3
+    block_bytes = sp.num_heads * sp.block_size * sp.head_dim
+
+    if args.calibrate_copy:
+        nb = args.calibrate_copy
+        big_k = torch.zeros((2 * nb, w.num_kv_heads, w.block_size, w.head_dim), dtype=inp.k_cache.dtype, device=dev)
+        big_v = torch.zeros_like(big_k)
+        cal = torch.from_numpy(np.stack([np.arange(nb), np.arange(nb, 2 * nb)], 1).astype(np.int64)).to(dev)
+        ops.copy_blocks(big_k, big_v, cal, stream=stream)
+        torch.cuda.synchronize()
+        del big_k, big_v
+
+    elt_q, elt_kv = inp.q.element_size(), inp.k_cache.element_size()
+    kv_bytes, alg_bytes = algorithmic_bytes(w, ctx_np.astype(np.int64), elt_q, elt_kv)
+    attn_ms = float(np.mean(t_attn))
+    achieved = alg_bytes / (attn_ms * 1e-3) / 1e9
+    traffic = measured_traffic(args.workload)
+    result = {
+        "metric": "paged decode KV-read GB/s (% of HBM peak) + sequences/sec per decode step",
+        "value": round(kv_bytes / (step_ms * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.kv_dtype,
+        "data": "synthetic (seeded N(0,1) q/K/V, lognormal context lengths, shuffled block tables)",
+        "config": {
+            "workload": w.name, "num_seqs": w.num_seqs, "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim, "block_size": w.block_size, "q_dtype": w.q_dtype, "kv_dtype": w.kv_dtype,
+            "sum_context": int(ctx_np.sum()), "max_context": max_ctx, "num_blocks": inp.num_blocks,
+            "plan": {"path": ["vector", "mfma"][plan[0]], "partition_tokens": plan[1], "num_partitions": plan[2]},
+        },
+        "pct_of_hbm_peak": round(100.0 * kv_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+        "seq_per_s": round(w.num_seqs / (step_ms * 1e-3), 1),
+        "kv_bytes_per_step": kv_bytes,
+        "components": {
+            "reshape_and_cache_us": round(float(np.mean(t_reshape)) * 1e3, 2),
+            "paged_attention_decode_us": round(attn_ms * 1e3, 2),
+            "paged_attention_decode_median_us": round(float(np.median(t_attn)) * 1e3, 2),
+            "attention_kv_gbps": round(kv_bytes / (attn_ms * 1e-3) / 1e9, 1),
+            "copy_blocks_us": round(copy_us, 2),
+            "copy_blocks_pairs": n_pairs,
+            "copy_blocks_gbps": round(2 * 2 * n_pairs * block_bytes / (copy_us * 1e-6) / 1e9, 1),
+            "wall_ms_per_step": round(wall / K * 1e3, 4),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "paged_attention_decode (attention kernel + split-context reduce when planned)",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_call": alg_bytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, {"q": inp.q, "k": inp.k_cache, "v": inp.v_cache}, tables_np,
+                                              ctx_np, args.cpu_seconds)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,196 @@
+/*
+ * pkv.h -- C ABI of the paged-KV decode library for AMD MI355X (gfx950).
+ *
+ * Three data-path calls and their helpers.  The library is stateless: the host
+ * owns the block bookkeeping (which physical block holds which tokens,
+ * reference counts, copy-on-write decisions); the library moves bytes and
+ * attends.  Sources cited (page title, then section):
+ *   [KVpag]      "KV cache paginado e batching contínuo para LLMs", "Como funciona"
+ *   [PA/paging]  "PagedAttention" (Ultralytics glossary), "Cách phân trang hoạt động"
+ *   [PA/sharing] same page, "Chia sẻ block giữa các chuỗi"
+ *   [PA/related] same page, "Các kỹ thuật liên quan"
+ *   [vLLM-rev]   "vLLM PagedAttention: uma revolução no throughput de inferência de LLMs"
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every pointer argument is a DEVICE pointer (HIP device memory) unless noted.
+ *   The caller allocates and owns every buffer, including the attention
+ *   workspace.  The library never allocates, frees or synchronises.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
+ *   call only enqueues work on it and returns; results are ready when the
+ *   stream reaches that point.
+ * - Pools (k_cache, v_cache): `[num_blocks][num_kv_heads][block_size][head_dim]`,
+ *   row-major, element type `kv_dtype`.  One (block, kv head) tile is the
+ *   contiguous `[block_size][head_dim]` block of [PA/paging]'s example.
+ *   A flat slot is `block * block_size + offset`.
+ * - Element types (`*_dtype`): PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3 (OCP
+ *   E4M3 "FN": bias 7, max +-448, no infinity, NaN = S.1111.111; the stored
+ *   value is code * scale with one fp32 scale per pool).
+ * - Return: PKV_OK (0) or a negative status (see pkv_status_string).  Every
+ *   argument check runs on the host before anything is enqueued, so an error
+ *   return means nothing was launched.  PKV_ERR_LAUNCH reports a HIP launch
+ *   failure (the stream's earlier work is unaffected).
+ * - Device-resident values (block ids, slots, context lengths) cannot be checked
+ *   on the host.  They are preconditions; the kernels clamp or skip values that
+ *   would address outside the buffers instead of faulting (each call says how),
+ *   so a broken table gives wrong numbers, never an out-of-bounds access.
+ */
+#ifndef PKV_H_
+#define PKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+#define PKV_F32 0
+#define PKV_F16 1
+#define PKV_BF16 2
+#define PKV_FP8_E4M3 3
+
+/* status codes */
+#define PKV_OK 0
+#define PKV_ERR_NULL_POINTER (-1)   /* a required pointer is NULL                          */
+#define PKV_ERR_BAD_SIZE (-2)       /* a size is negative / zero where it must be positive  */
+#define PKV_ERR_HEAD_GROUPING (-3)  /* num_heads is not a multiple of num_kv_heads          */
+#define PKV_ERR_UNSUPPORTED (-4)    /* head_dim / block_size / dtype combination not built  */
+#define PKV_ERR_PARTITION (-5)      /* partition_size not a positive multiple of block_size */
+#define PKV_ERR_WORKSPACE (-6)      /* workspace missing or smaller than required           */
+#define PKV_ERR_LAUNCH (-7)         /* HIP reported a launch error                          */
+#define PKV_ERR_SCALE (-8)          /* an FP8 scale is not a positive finite number         */
+
+/* attention kernel families reported by pkv_attention_plan */
+#define PKV_PATH_VECTOR 0  /* per-query-head vector kernel (wave shuffles, no MFMA)  */
+#define PKV_PATH_MFMA 1    /* grouped-query kernel: one kv head's group on MFMA      */
+
+/* Human-readable text of a status code (static string, never NULL). */
+const char* pkv_status_string(int status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int pkv_version(void);
+
+/*
+ * pkv_attention_plan -- how pkv_paged_attention_decode would run these shapes.
+ *
+ * Host-only; enqueues nothing.  Writes the kernel family (PKV_PATH_*), the
+ * partition size in tokens and the number of partitions per sequence
+ * (1 = single pass, no reduce kernel) through the three host pointers (any may
+ * be NULL).  `partition_size` 0 asks for the library's automatic choice.
+ * Returns the same status pkv_paged_attention_decode would return for these
+ * shapes (pointers aside).
+ */
+int pkv_attention_plan(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                       int block_size, int max_context_len, int partition_size,
+                       int q_dtype, int kv_dtype,
+                       int* path, int* partition_tokens, int* num_partitions);
+
+/*
+ * pkv_attention_workspace_bytes -- device workspace pkv_paged_attention_decode
+ * needs for these shapes (0 when it runs in a single pass).  The workspace holds
+ * fp32 per-partition summaries (running max, exp-sum and unnormalised output
+ * vector) for the split-context reduce.  Returns 0 also for invalid shapes.
+ */
+size_t pkv_attention_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                                     int block_size, int max_context_len, int partition_size,
+                                     int q_dtype, int kv_dtype);
+
+/*
+ * pkv_paged_attention_decode -- attention of each sequence's one new query token
+ * over its paged KV cache ([PA/paging]: the kernel walks the request's block
+ * table and gathers keys and values block by block; [KVpag]: decode consumes
+ * the cache of every token seen so far).
+ *
+ * For every sequence s and query head h, with G = num_heads / num_kv_heads and
+ * kv head g = h / G ([PA/related]: grouped-query heads share K/V heads):
+ *   K_t = k_cache[block_tables[s][t / bs]][g][t % bs][:]   (V likewise), t < ctx_s
+ *   logit_t = scale * <q[s][h][:], K_t>      (K_t, V_t times k_scale / v_scale for FP8)
+ *   out[s][h][:] = sum_t softmax(logit)_t * V_t
+ * computed in fp32 with an online (running max / running sum) softmax, so the
+ * score row is never written to memory ([PA/related], FlashAttention-style).
+ * ctx_s = context_lens[s] counts every cached token including the new one; a
+ * sequence with ctx_s == 0 gets a zero output row.
+ *
+ * out          [num_seqs][num_heads][head_dim], q_dtype (fp32/f16/bf16); written, must
+ *              not alias any input.  Rounded to nearest even from fp32.
+ * q            [num_seqs][num_heads][head_dim], q_dtype.
+ * k_cache, v_cache  pools as above, kv_dtype.  With PKV_FP8_E4M3 the values are
+ *              code * k_scale (resp. v_scale); k_scale / v_scale are ignored otherwise.
+ * block_tables [num_seqs][max_blocks_per_seq] int32; entries past ceil(ctx/bs) are never read.
+ * context_lens [num_seqs] int32.
+ * num_blocks   number of blocks in each pool.  A table entry outside
+ *              [0, num_blocks) makes the kernel skip that block's tokens.
+ * max_context_len  host-side upper bound of context_lens (sizes the partition grid).
+ *              Tokens past min(ctx_s, max_context_len rounded up to a partition,
+ *              max_blocks_per_seq * block_size) are ignored.
+ * partition_size   tokens per split-context partition (multiple of block_size),
+ *              or 0 for the automatic choice.  When more than one partition is
+ *              needed, each (sequence, head, partition) writes an fp32 summary to
+ *              `workspace` and a second kernel merges them:
+ *              M = max_p m_p; out = sum_p e^(m_p - M) o_p / sum_p e^(m_p - M) l_p.
+ * workspace    device buffer of at least pkv_attention_workspace_bytes(...) bytes
+ *              (may be NULL when that is 0).  Contents on entry are ignored.
+ * Supported: head_dim 64/128/256; block_size 8/16/32 (16 for the MFMA family);
+ *   (q, kv) dtypes (f32,f32), (f16,f16), (bf16,bf16), (f16,fp8), (bf16,fp8).
+ *   Grouped heads (G > 1) with 16-bit q run on MFMA; everything else on the
+ *   vector family.
+ */
+int pkv_paged_attention_decode(void* out, const void* q,
+                               const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, int max_blocks_per_seq,
+                               const int32_t* context_lens,
+                               int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                               int block_size, int num_blocks, int max_context_len,
+                               float scale, float k_scale, float v_scale,
+                               int q_dtype, int kv_dtype, int partition_size,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pkv_reshape_and_cache -- write each new token's key and value into the pool
+ * slot the host chose for it ([PA/paging] example: the token at position pos
+ * goes to block table[pos / bs], offset pos % bs).
+ *
+ * For token i with sigma = slot_mapping[i] >= 0, for every kv head h:
+ *   k_cache[sigma / bs][h][sigma % bs][:] = enc(key[i][h][:])   (value likewise)
+ * enc is a bit copy when src_dtype == kv_dtype, and for PKV_FP8_E4M3 the code of
+ * nearest_e4m3(clamp(fp32(x) / scale, -448, 448)) with IEEE fp32 division, ties
+ * to even mantissa, NaN -> 0x7F | sign.  sigma < 0 (padding) and
+ * sigma >= num_blocks * block_size are skipped.
+ *
+ * key, value   [num_tokens][num_kv_heads][head_dim], src_dtype (f32/f16/bf16).
+ * slot_mapping [num_tokens] int64.  Slots must be distinct within one call
+ *              (two tokens to one slot leave either value).
+ * k_scale, v_scale  FP8 encode scales (positive, finite); ignored otherwise.
+ * Supported: src_dtype == kv_dtype, or src f32/f16/bf16 -> kv PKV_FP8_E4M3;
+ *   head_dim a multiple of 16 up to 1024; any block_size >= 1.
+ * num_tokens == 0 is a no-op returning PKV_OK.
+ */
+int pkv_reshape_and_cache(const void* key, const void* value,
+                          void* k_cache, void* v_cache, const int64_t* slot_mapping,
+                          int num_tokens, int num_kv_heads, int head_dim, int block_size,
+                          int num_blocks, int src_dtype, int kv_dtype,
+                          float k_scale, float v_scale, void* stream);
+
+/*
+ * pkv_copy_blocks -- block-level copy-on-write ([KVpag]: before writing into a
+ * block still shared by other sequences, take a new block and copy the old
+ * one; [PA/sharing]).  The host decides the pairs; this call moves the bytes.
+ *
+ * For each pair p: k_cache[dst] = k_cache[src] and v_cache[dst] = v_cache[src],
+ * whole blocks (every kv head, every slot, raw bytes).
+ * block_mapping [num_pairs][2] int64 (src, dst).  Destination ids must be
+ *              distinct and disjoint from all source ids (then pair order does
+ *              not matter).  Pairs with an id outside [0, num_blocks) are skipped.
+ * num_pairs == 0 is a no-op returning PKV_OK.
+ */
+int pkv_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, int num_pairs,
+                    int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                    int kv_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H_ */

@@ -87,9 +87,10 @@ def encode_e4m3(x, scale):
     scale in float32 (IEEE single division, as numpy does it).
     """
     xf = np.asarray(x, dtype=np.float32)
-    q = (xf / np.float32(scale)).astype(np.float32)
-    neg = np.signbit(q)
-    isnan = np.isnan(q)
+    with np.errstate(over="ignore", invalid="ignore"):
+        q = (xf / np.float32(scale)).astype(np.float32)
+    neg = np.signbit(xf)             # scale > 0: the quotient has the input's sign
+    isnan = np.isnan(xf)
     mag = np.abs(q.astype(np.float64))
     mag = np.where(isnan, 0.0, np.minimum(mag, E4M3_MAX))
     code = _nearest_code_nonneg(mag)

@@ -1,0 +1,148 @@
+// attn_reduce.hip -- merge of the per-partition summaries of a split context.
+//
+// Each (sequence, head, partition p) left (m_p, l_p, o_p): running max (log2
+// domain), exp-sum and unnormalised output.  The merge is the identity of the
+// online softmax ("PagedAttention", Ultralytics glossary, section "Các kỹ thuật
+// liên quan": FlashAttention-style tiling never forms the score row):
+//   M = max_p m_p;  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p
+// Many partitions: one 256-thread workgroup per (sequence, head); threads read
+// the partition maxima and sums in parallel, then stripes of threads walk the
+// partitions with float4 loads of o_p and combine through LDS.  Few partitions:
+// one wave per (sequence, head), see attn_reduce_small_kernel.
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+template <class OT, int D>
+__global__ __launch_bounds__(256) void attn_reduce_kernel(ReduceParams p) {
+  constexpr int NT = 256;
+  constexpr int CH = D / 4;              // float4 chunks of one output row
+  constexpr int STRIPES = NT / CH;       // partitions walked side by side
+  const int sh = blockIdx.x;             // sequence * num_heads + head
+  const int seq = sh / p.num_heads;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+
+  int ctx = p.context_lens[seq];
+  ctx = ctx < 0 ? 0 : (ctx > p.ctx_cap ? p.ctx_cap : ctx);
+  const int np = (ctx + p.partition_tokens - 1) / p.partition_tokens;
+  const size_t base = (size_t)sh * p.num_partitions;
+
+  __shared__ float red[4];
+  __shared__ float sm[STRIPES][D];
+
+  float mx = -__builtin_inff();
+  for (int i = tid; i < np; i += NT) mx = fmaxf(mx, p.ws_m[base + i]);
+  mx = wave_max(mx);
+  if (lane == 0) red[w] = mx;
+  __syncthreads();
+  float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  M = (M == -__builtin_inff()) ? 0.f : M;   // no live partition: every weight below is 0
+  __syncthreads();
+
+  float ls = 0.f;
+  for (int i = tid; i < np; i += NT) ls += exp2_fast(p.ws_m[base + i] - M) * p.ws_l[base + i];
+  ls = wave_sum(ls);
+  if (lane == 0) red[w] = ls;
+  __syncthreads();
+  const float Lsum = (red[0] + red[1]) + (red[2] + red[3]);
+
+  const int c = tid % CH;
+  const int st = tid / CH;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+  for (int i = st; i < np; i += STRIPES) {
+    const float wt = exp2_fast(p.ws_m[base + i] - M);
+    const float4 o = *reinterpret_cast<const float4*>(p.ws_o + (base + i) * D + c * 4);
+    acc.x += wt * o.x; acc.y += wt * o.y; acc.z += wt * o.z; acc.w += wt * o.w;
+  }
+  sm[st][c * 4 + 0] = acc.x;
+  sm[st][c * 4 + 1] = acc.y;
+  sm[st][c * 4 + 2] = acc.z;
+  sm[st][c * 4 + 3] = acc.w;
+  __syncthreads();
+  const float inv = (np > 0 && Lsum > 0.f) ? 1.f / Lsum : 0.f;
+  for (int d = tid; d < D; d += NT) {
+    float o = 0.f;
+#pragma unroll
+    for (int s = 0; s < STRIPES; ++s) o += sm[s][d];
+    store_elem<OT>(p.out, (size_t)sh * D + d, o * inv);
+  }
+}
+
+// Few partitions (<= 64): one wave per (sequence, head), four per workgroup.
+// Lane p holds partition p's max and sum; lane l accumulates dims
+// [l*DV, l*DV+DV) over the partitions, reading each weight with a uniform
+// readlane.  No barriers, no LDS.
+template <class OT, int D>
+__global__ __launch_bounds__(256) void attn_reduce_small_kernel(ReduceParams p) {
+  constexpr int DV = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int sh = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (sh >= p.num_seqs * p.num_heads) return;          // whole wave exits together
+  const int seq = sh / p.num_heads;
+  int ctx = p.context_lens[seq];
+  ctx = ctx < 0 ? 0 : (ctx > p.ctx_cap ? p.ctx_cap : ctx);
+  const int np = (ctx + p.partition_tokens - 1) / p.partition_tokens;
+  const size_t base = (size_t)sh * p.num_partitions;
+  const float mp = lane < np ? p.ws_m[base + lane] : -__builtin_inff();
+  const float lp = lane < np ? p.ws_l[base + lane] : 0.f;
+  float M = wave_max(mp);
+  M = (M == -__builtin_inff()) ? 0.f : M;
+  const float wp = exp2_fast(mp - M);                  // 0 for lanes past np
+  const float L = wave_sum(wp * lp);
+  float acc[DV];
+#pragma unroll
+  for (int j = 0; j < DV; ++j) acc[j] = 0.f;
+  const float* o = p.ws_o + base * D + lane * DV;
+  for (int i0 = 0; i0 < np; i0 += 4) {                // four partitions' loads in flight at once
+    float v[4][DV];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < DV; ++j) v[u][j] = i0 + u < np ? o[(size_t)(i0 + u) * D + j] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float wi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wp), i0 + u));
+#pragma unroll
+      for (int j = 0; j < DV; ++j) acc[j] += wi * v[u][j];
+    }
+  }
+  const float inv = (np > 0 && L > 0.f) ? 1.f / L : 0.f;
+#pragma unroll
+  for (int j = 0; j < DV; ++j) store_elem<OT>(p.out, (size_t)sh * D + lane * DV + j, acc[j] * inv);
+}
+
+template <class OT>
+static hipError_t launch_reduce_d(const ReduceParams& p, int d, hipStream_t stream) {
+  const int units = p.num_seqs * p.num_heads;
+  if (p.num_partitions <= 64) {
+    const dim3 grid((unsigned)((units + 3) / 4));
+    switch (d) {
+      case 64: hipLaunchKernelGGL((attn_reduce_small_kernel<OT, 64>), grid, dim3(256), 0, stream, p); break;
+      case 128: hipLaunchKernelGGL((attn_reduce_small_kernel<OT, 128>), grid, dim3(256), 0, stream, p); break;
+      case 256: hipLaunchKernelGGL((attn_reduce_small_kernel<OT, 256>), grid, dim3(256), 0, stream, p); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
+  const dim3 grid((unsigned)units);
+  switch (d) {
+    case 64: hipLaunchKernelGGL((attn_reduce_kernel<OT, 64>), grid, dim3(256), 0, stream, p); break;
+    case 128: hipLaunchKernelGGL((attn_reduce_kernel<OT, 128>), grid, dim3(256), 0, stream, p); break;
+    case 256: hipLaunchKernelGGL((attn_reduce_kernel<OT, 256>), grid, dim3(256), 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_reduce(const ReduceParams& p, int out_dtype, int d, hipStream_t stream) {
+  if (out_dtype == 0) return launch_reduce_d<F32>(p, d, stream);
+  if (out_dtype == 1) return launch_reduce_d<F16>(p, d, stream);
+  if (out_dtype == 2) return launch_reduce_d<BF16>(p, d, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pkv

@@ -1,0 +1,161 @@
+// cache_ops.hip -- the two data-movement kernels of the paged cache.
+//
+// reshape_and_cache: scatter each new token's key/value rows into the slot the
+//   host chose ("PagedAttention", Ultralytics glossary, section "Cách phân trang
+//   hoạt động": token pos is stored in block table[pos / bs] at offset
+//   pos % bs; a flat slot is block * bs + offset).  One thread per 16 source
+//   bytes: a bit copy when the cache has the source's type, else the E4M3
+//   encode of value / scale (the FP8 cache of section "Các kỹ thuật liên quan").
+// copy_blocks: whole-block copies for copy-on-write ("KV cache paginado e
+//   batching contínuo para LLMs", section "Como funciona": a sequence writing
+//   into a shared block first gets a fresh block holding a copy).  A block of
+//   every kv head is one contiguous run of num_kv_heads * bs * head_dim
+//   elements, so a pair is two flat 16-byte-vector copies (K and V).
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+struct ReshapeParams {
+  const void* key;
+  const void* value;
+  void* k_cache;
+  void* v_cache;
+  const int64_t* slot_mapping;
+  int64_t num_slots;          // num_blocks * block_size
+  int num_tokens;
+  int num_kv_heads;
+  int head_dim;
+  int block_size;
+  float k_scale;
+  float v_scale;
+};
+
+// Bit copy: 16 bytes of source -> 16 bytes of cache.
+template <class T>
+__global__ __launch_bounds__(256) void reshape_copy_kernel(ReshapeParams p) {
+  constexpr int V = 16 / T::bytes;                       // elements per chunk
+  const int chunks_per_row = p.head_dim / V;
+  const int chunks_per_token = p.num_kv_heads * chunks_per_row;
+  const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t token = gid / chunks_per_token;
+  if (token >= (size_t)p.num_tokens) return;
+  const int r = (int)(gid - token * chunks_per_token);
+  const int h = r / chunks_per_row;
+  const int c = r - h * chunks_per_row;
+  const int64_t slot = p.slot_mapping[token];
+  if (slot < 0 || slot >= p.num_slots) return;           // padding / out of pool: skipped
+  const int64_t blk = slot / p.block_size;
+  const int64_t off = slot - blk * p.block_size;
+  const size_t src = (token * p.num_kv_heads + h) * (size_t)p.head_dim + (size_t)c * V;
+  const size_t dst = (((size_t)blk * p.num_kv_heads + h) * p.block_size + off) * (size_t)p.head_dim + (size_t)c * V;
+  const uint4 kv = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(p.key) + src * T::bytes);
+  const uint4 vv = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(p.value) + src * T::bytes);
+  *reinterpret_cast<uint4*>(reinterpret_cast<char*>(p.k_cache) + dst * T::bytes) = kv;
+  *reinterpret_cast<uint4*>(reinterpret_cast<char*>(p.v_cache) + dst * T::bytes) = vv;
+}
+
+// Encode: 16 bytes of source (4 fp32 or 8 16-bit values) -> 4 or 8 E4M3 codes.
+template <class S>
+__global__ __launch_bounds__(256) void reshape_fp8_kernel(ReshapeParams p) {
+  constexpr int V = 16 / S::bytes;
+  const int chunks_per_row = p.head_dim / V;
+  const int chunks_per_token = p.num_kv_heads * chunks_per_row;
+  const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t token = gid / chunks_per_token;
+  if (token >= (size_t)p.num_tokens) return;
+  const int r = (int)(gid - token * chunks_per_token);
+  const int h = r / chunks_per_row;
+  const int c = r - h * chunks_per_row;
+  const int64_t slot = p.slot_mapping[token];
+  if (slot < 0 || slot >= p.num_slots) return;
+  const int64_t blk = slot / p.block_size;
+  const int64_t off = slot - blk * p.block_size;
+  const size_t src = (token * p.num_kv_heads + h) * (size_t)p.head_dim + (size_t)c * V;
+  const size_t dst = (((size_t)blk * p.num_kv_heads + h) * p.block_size + off) * (size_t)p.head_dim + (size_t)c * V;
+  const uint4 kr = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(p.key) + src * S::bytes);
+  const uint4 vr = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(p.value) + src * S::bytes);
+  float kf[V], vf[V];
+  Unpack<S>::run(kr, kf);
+  Unpack<S>::run(vr, vf);
+  uint32_t kc[V / 4], vc[V / 4];
+#pragma unroll
+  for (int j = 0; j < V / 4; ++j) {
+    uint32_t a = 0, b = 0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      a |= e4m3_encode_scaled(kf[4 * j + t], p.k_scale) << (8 * t);
+      b |= e4m3_encode_scaled(vf[4 * j + t], p.v_scale) << (8 * t);
+    }
+    kc[j] = a;
+    vc[j] = b;
+  }
+  char* kd = reinterpret_cast<char*>(p.k_cache) + dst;
+  char* vd = reinterpret_cast<char*>(p.v_cache) + dst;
+  if constexpr (V == 8) {
+    *reinterpret_cast<uint2*>(kd) = make_uint2(kc[0], kc[1]);
+    *reinterpret_cast<uint2*>(vd) = make_uint2(vc[0], vc[1]);
+  } else {
+    *reinterpret_cast<uint32_t*>(kd) = kc[0];
+    *reinterpret_cast<uint32_t*>(vd) = vc[0];
+  }
+}
+
+hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                                    const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
+                                    int head_dim, int block_size, int num_blocks, int src_dtype, int kv_dtype,
+                                    float k_scale, float v_scale, hipStream_t stream) {
+  ReshapeParams p{key, value, k_cache, v_cache, slot_mapping, (int64_t)num_blocks * block_size,
+                  num_tokens, num_kv_heads, head_dim, block_size, k_scale, v_scale};
+  const int src_bytes = src_dtype == 0 ? 4 : 2;
+  const size_t chunks = (size_t)num_tokens * num_kv_heads * (head_dim * src_bytes / 16);
+  const dim3 grid((unsigned)((chunks + 255) / 256));
+  if (kv_dtype == src_dtype) {
+    if (src_bytes == 4) hipLaunchKernelGGL(reshape_copy_kernel<F32>, grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL(reshape_copy_kernel<F16>, grid, dim3(256), 0, stream, p);  // 16-bit: raw bits
+  } else if (kv_dtype == 3) {
+    if (src_dtype == 0) hipLaunchKernelGGL(reshape_fp8_kernel<F32>, grid, dim3(256), 0, stream, p);
+    else if (src_dtype == 1) hipLaunchKernelGGL(reshape_fp8_kernel<F16>, grid, dim3(256), 0, stream, p);
+    else if (src_dtype == 2) hipLaunchKernelGGL(reshape_fp8_kernel<BF16>, grid, dim3(256), 0, stream, p);
+    else return hipErrorInvalidValue;
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+struct CopyParams {
+  char* k_cache;
+  char* v_cache;
+  const int64_t* pairs;
+  int64_t block_bytes;
+  int num_blocks;
+  int wgs_per_block;
+};
+
+__global__ __launch_bounds__(256) void copy_blocks_kernel(CopyParams p) {
+  const int pair = blockIdx.x / p.wgs_per_block;
+  const int64_t chunk = (int64_t)(blockIdx.x - pair * p.wgs_per_block) * 256 + threadIdx.x;
+  if (chunk * 16 >= p.block_bytes) return;
+  const int64_t src = p.pairs[2 * pair];
+  const int64_t dst = p.pairs[2 * pair + 1];
+  if (src < 0 || src >= p.num_blocks || dst < 0 || dst >= p.num_blocks) return;
+  const int64_t so = src * p.block_bytes + chunk * 16;
+  const int64_t dof = dst * p.block_bytes + chunk * 16;
+  const uint4 k = *reinterpret_cast<const uint4*>(p.k_cache + so);
+  const uint4 v = *reinterpret_cast<const uint4*>(p.v_cache + so);
+  *reinterpret_cast<uint4*>(p.k_cache + dof) = k;
+  *reinterpret_cast<uint4*>(p.v_cache + dof) = v;
+}
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int num_pairs,
+                              int64_t block_bytes, int num_blocks, hipStream_t stream) {
+  const int64_t chunks = block_bytes / 16;
+  const int wgs = (int)((chunks + 255) / 256);
+  CopyParams p{reinterpret_cast<char*>(k_cache), reinterpret_cast<char*>(v_cache), pairs, block_bytes,
+               num_blocks, wgs};
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)((int64_t)num_pairs * wgs)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -1,0 +1,247 @@
+// pkv_api.hip -- the C ABI declared in include/pkv.h: host-side argument
+// checks, the choice of kernel family and context partitioning, and launches.
+// Nothing here allocates, frees or synchronises.
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "pkv.h"
+#include "pkv_internal.h"
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+#ifndef PKV_AUTO_PARTITION
+#define PKV_AUTO_PARTITION 512
+#endif
+constexpr int kAutoPartitionTokens = PKV_AUTO_PARTITION;
+
+struct Plan {
+  int path;            // PKV_PATH_*
+  int part_tokens;     // tokens per partition (multiple of block_size)
+  int num_parts;       // partitions per sequence
+  size_t ws_bytes;     // workspace needed (0 for a single pass)
+};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int dtype_bytes(int dt) {
+  switch (dt) {
+    case PKV_F32: return 4;
+    case PKV_F16: case PKV_BF16: return 2;
+    case PKV_FP8_E4M3: return 1;
+  }
+  return 0;
+}
+
+// PKV_ATTN_PATH=vector forces the vector family; =mfma asks for the MFMA family.
+int forced_path() {
+  const char* e = getenv("PKV_ATTN_PATH");
+  if (!e) return -1;
+  if (!strcmp(e, "vector")) return PKV_PATH_VECTOR;
+  if (!strcmp(e, "mfma")) return PKV_PATH_MFMA;
+  return -1;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int make_plan(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size, int max_context_len,
+              int partition_size, int q_dtype, int kv_dtype, Plan* out) {
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      max_context_len < 0)
+    return PKV_ERR_BAD_SIZE;
+  if (num_heads % num_kv_heads != 0) return PKV_ERR_HEAD_GROUPING;
+  if (dtype_bytes(q_dtype) == 0 || q_dtype == PKV_FP8_E4M3 || dtype_bytes(kv_dtype) == 0) return PKV_ERR_UNSUPPORTED;
+  if (partition_size < 0 || (partition_size > 0 && partition_size % block_size != 0)) return PKV_ERR_PARTITION;
+  const int group = num_heads / num_kv_heads;
+  const bool vec_ok = pkv::vector_supported(q_dtype, kv_dtype, head_dim, block_size);
+  const bool mfma_ok = pkv::mfma_supported(q_dtype, kv_dtype, head_dim, block_size, group);
+  int path;
+  const int forced = forced_path();
+  if (forced == PKV_PATH_VECTOR) path = PKV_PATH_VECTOR;
+  else if (forced == PKV_PATH_MFMA) path = PKV_PATH_MFMA;
+  else path = mfma_ok ? PKV_PATH_MFMA : PKV_PATH_VECTOR;
+  if ((path == PKV_PATH_MFMA && !mfma_ok) || (path == PKV_PATH_VECTOR && !vec_ok)) return PKV_ERR_UNSUPPORTED;
+
+  const int ptoks = partition_size > 0 ? partition_size : kAutoPartitionTokens / block_size * block_size;
+  int nparts = (max_context_len + ptoks - 1) / ptoks;
+  Plan pl;
+  pl.path = path;
+  if (nparts <= 1) {
+    // single pass: one partition covering the whole (rounded-up) context
+    const int toks = max_context_len > 0 ? (max_context_len + block_size - 1) / block_size * block_size : block_size;
+    pl.part_tokens = toks;
+    pl.num_parts = 1;
+    pl.ws_bytes = 0;
+  } else {
+    pl.part_tokens = ptoks;
+    pl.num_parts = nparts;
+    const size_t rows = (size_t)num_seqs * num_heads * nparts;
+    pl.ws_bytes = align_up(rows * head_dim * sizeof(float), 256) + 2 * align_up(rows * sizeof(float), 256);
+  }
+  const int units = path == PKV_PATH_MFMA ? num_kv_heads : num_heads;
+  if ((double)num_seqs * units * pl.num_parts > 2147483647.0) return PKV_ERR_BAD_SIZE;
+  *out = pl;
+  return PKV_OK;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH; }
+
+bool good_scale(float s) { return isfinite(s) && s > 0.f; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case PKV_ERR_BAD_SIZE: return "a size argument is out of range";
+    case PKV_ERR_HEAD_GROUPING: return "num_heads is not a multiple of num_kv_heads";
+    case PKV_ERR_UNSUPPORTED: return "unsupported head_dim / block_size / dtype combination or misaligned buffer";
+    case PKV_ERR_PARTITION: return "partition_size must be 0 or a positive multiple of block_size";
+    case PKV_ERR_WORKSPACE: return "workspace missing or smaller than pkv_attention_workspace_bytes()";
+    case PKV_ERR_LAUNCH: return "HIP kernel launch failed";
+    case PKV_ERR_SCALE: return "FP8 scale must be a positive finite number";
+  }
+  return "unknown status";
+}
+
+int pkv_version(void) { return 100; }
+
+int pkv_attention_plan(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+                       int max_context_len, int partition_size, int q_dtype, int kv_dtype, int* path,
+                       int* partition_tokens, int* num_partitions) {
+  Plan pl;
+  const int st = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len,
+                           partition_size, q_dtype, kv_dtype, &pl);
+  if (st != PKV_OK) return st;
+  if (path) *path = pl.path;
+  if (partition_tokens) *partition_tokens = pl.part_tokens;
+  if (num_partitions) *num_partitions = pl.num_parts;
+  return PKV_OK;
+}
+
+size_t pkv_attention_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+                                     int max_context_len, int partition_size, int q_dtype, int kv_dtype) {
+  Plan pl;
+  if (make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len, partition_size, q_dtype,
+                kv_dtype, &pl) != PKV_OK)
+    return 0;
+  return pl.ws_bytes;
+}
+
+int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+                               int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+                               int num_blocks, int max_context_len, float scale, float k_scale, float v_scale,
+                               int q_dtype, int kv_dtype, int partition_size, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  Plan pl;
+  int st = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len, partition_size,
+                     q_dtype, kv_dtype, &pl);
+  if (st != PKV_OK) return st;
+  if (max_blocks_per_seq <= 0 || num_blocks <= 0) return PKV_ERR_BAD_SIZE;
+  if (!isfinite(scale)) return PKV_ERR_BAD_SIZE;
+  if (kv_dtype == PKV_FP8_E4M3 && !(good_scale(k_scale) && good_scale(v_scale))) return PKV_ERR_SCALE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PKV_ERR_NULL_POINTER;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_UNSUPPORTED;
+  if (pl.num_parts > 1 && (!workspace || workspace_bytes < pl.ws_bytes || !aligned16(workspace)))
+    return PKV_ERR_WORKSPACE;
+
+  pkv::AttnParams p;
+  p.out = out;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  const size_t rows = (size_t)num_seqs * num_heads * pl.num_parts;
+  char* ws = reinterpret_cast<char*>(workspace);
+  p.ws_o = pl.num_parts > 1 ? reinterpret_cast<float*>(ws) : nullptr;
+  p.ws_m = pl.num_parts > 1 ? reinterpret_cast<float*>(ws + align_up(rows * head_dim * sizeof(float), 256)) : nullptr;
+  p.ws_l = pl.num_parts > 1 ? reinterpret_cast<float*>(ws + align_up(rows * head_dim * sizeof(float), 256) +
+                                                       align_up(rows * sizeof(float), 256))
+                            : nullptr;
+  p.num_seqs = num_seqs;
+  p.num_heads = num_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = num_heads / num_kv_heads;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.partition_blocks = pl.part_tokens / block_size;
+  p.num_partitions = pl.num_parts;
+  const long long cap_parts = (long long)pl.part_tokens * pl.num_parts;
+  const long long cap_table = (long long)max_blocks_per_seq * block_size;
+  long long cap = cap_parts < cap_table ? cap_parts : cap_table;
+  p.ctx_cap = (int)(cap < 2147483647LL ? cap : 2147483647LL);
+  const bool fp8 = kv_dtype == PKV_FP8_E4M3;
+  p.qk_scale = scale * kLog2e * (fp8 ? k_scale : 1.f);
+  p.v_scale = fp8 ? v_scale : 1.f;
+  const int units = pl.path == PKV_PATH_MFMA ? num_kv_heads : num_heads;
+  p.total_wgs = (uint32_t)((size_t)num_seqs * units * pl.num_parts);
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // start from a clean error state
+  hipError_t e = pl.path == PKV_PATH_MFMA ? pkv::launch_attention_mfma(p, q_dtype, head_dim, s)
+                                           : pkv::launch_attention_vector(p, q_dtype, kv_dtype, head_dim, block_size, s);
+  if (e != hipSuccess) return PKV_ERR_LAUNCH;
+  if (pl.num_parts > 1) {
+    pkv::ReduceParams r;
+    r.out = out;
+    r.context_lens = context_lens;
+    r.ws_m = p.ws_m;
+    r.ws_l = p.ws_l;
+    r.ws_o = p.ws_o;
+    r.num_seqs = num_seqs;
+    r.num_heads = num_heads;
+    r.num_partitions = pl.num_parts;
+    r.partition_tokens = pl.part_tokens;
+    r.ctx_cap = p.ctx_cap;
+    e = pkv::launch_attention_reduce(r, q_dtype, head_dim, s);
+  }
+  return launch_status(e);
+}
+
+int pkv_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                          const int64_t* slot_mapping, int num_tokens, int num_kv_heads, int head_dim,
+                          int block_size, int num_blocks, int src_dtype, int kv_dtype, float k_scale, float v_scale,
+                          void* stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return PKV_ERR_BAD_SIZE;
+  if (src_dtype != PKV_F32 && src_dtype != PKV_F16 && src_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  if (kv_dtype != src_dtype && kv_dtype != PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;
+  if (head_dim % 16 != 0 || head_dim > 1024) return PKV_ERR_UNSUPPORTED;
+  if (kv_dtype == PKV_FP8_E4M3 && !(good_scale(k_scale) && good_scale(v_scale))) return PKV_ERR_SCALE;
+  if ((double)num_tokens * num_kv_heads * head_dim / 4.0 > 2147483647.0 * 256.0) return PKV_ERR_BAD_SIZE;
+  if (num_tokens == 0) return PKV_OK;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PKV_ERR_NULL_POINTER;
+  if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  return launch_status(pkv::launch_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, num_tokens,
+                                                     num_kv_heads, head_dim, block_size, num_blocks, src_dtype,
+                                                     kv_dtype, k_scale, v_scale,
+                                                     reinterpret_cast<hipStream_t>(stream)));
+}
+
+int pkv_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, int num_pairs, int num_kv_heads,
+                    int head_dim, int block_size, int num_blocks, int kv_dtype, void* stream) {
+  if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return PKV_ERR_BAD_SIZE;
+  const int eb = dtype_bytes(kv_dtype);
+  if (eb == 0) return PKV_ERR_UNSUPPORTED;
+  const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * eb;
+  if (block_bytes % 16 != 0) return PKV_ERR_UNSUPPORTED;
+  const int64_t wgs = (block_bytes / 16 + 255) / 256;
+  if ((double)num_pairs * wgs > 2147483647.0) return PKV_ERR_BAD_SIZE;
+  if (num_pairs == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !block_mapping) return PKV_ERR_NULL_POINTER;
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  return launch_status(pkv::launch_copy_blocks(k_cache, v_cache, block_mapping, num_pairs, block_bytes, num_blocks,
+                                               reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,256 @@
+// pkv_device.h -- device-side helpers shared by the paged-KV kernels (gfx950 / CDNA4).
+//
+// Wave64 only.  Cross-lane work uses DPP inside 16-lane rows, ds_swizzle across
+// the two rows of a 32-lane half and ds_bpermute (__shfl_xor) across halves.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// ---------------------------------------------------------------------------
+// Element types.  `bytes` is the storage size; kId matches the PKV_* codes.
+// ---------------------------------------------------------------------------
+struct F32 { static constexpr int bytes = 4; static constexpr int kId = 0; };
+struct F16 { static constexpr int bytes = 2; static constexpr int kId = 1; };
+struct BF16 { static constexpr int bytes = 2; static constexpr int kId = 2; };
+struct FP8 { static constexpr int bytes = 1; static constexpr int kId = 3; };
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float u32_as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t f32_as_u32(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// Two packed 16-bit values (low half first) -> fp32.
+__device__ __forceinline__ void f16x2_to_f32(uint32_t u, float& lo, float& hi) {
+  half2_t h = __builtin_bit_cast(half2_t, u);
+  lo = (float)h.x;
+  hi = (float)h.y;
+}
+__device__ __forceinline__ void bf16x2_to_f32(uint32_t u, float& lo, float& hi) {
+  lo = u32_as_f32(u << 16);
+  hi = u32_as_f32(u & 0xffff0000u);
+}
+
+// 16 bytes of storage -> 16/bytes fp32 values.
+template <class T> struct Unpack;
+template <> struct Unpack<F32> {
+  static constexpr int N = 4;
+  __device__ __forceinline__ static void run(const uint4& r, float* f) {
+    f[0] = u32_as_f32(r.x); f[1] = u32_as_f32(r.y); f[2] = u32_as_f32(r.z); f[3] = u32_as_f32(r.w);
+  }
+};
+template <> struct Unpack<F16> {
+  static constexpr int N = 8;
+  __device__ __forceinline__ static void run(const uint4& r, float* f) {
+    f16x2_to_f32(r.x, f[0], f[1]); f16x2_to_f32(r.y, f[2], f[3]);
+    f16x2_to_f32(r.z, f[4], f[5]); f16x2_to_f32(r.w, f[6], f[7]);
+  }
+};
+template <> struct Unpack<BF16> {
+  static constexpr int N = 8;
+  __device__ __forceinline__ static void run(const uint4& r, float* f) {
+    bf16x2_to_f32(r.x, f[0], f[1]); bf16x2_to_f32(r.y, f[2], f[3]);
+    bf16x2_to_f32(r.z, f[4], f[5]); bf16x2_to_f32(r.w, f[6], f[7]);
+  }
+};
+// E4M3 decode uses the gfx950 convert, which implements the OCP E4M3 "FN"
+// decoding (all 256 codes were checked against the format's definition).
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t u, float* f) {
+  auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)u, false);
+  auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)u, true);
+  f[0] = lo[0]; f[1] = lo[1]; f[2] = hi[0]; f[3] = hi[1];
+}
+template <> struct Unpack<FP8> {
+  static constexpr int N = 16;
+  __device__ __forceinline__ static void run(const uint4& r, float* f) {
+    fp8x4_to_f32(r.x, f); fp8x4_to_f32(r.y, f + 4); fp8x4_to_f32(r.z, f + 8); fp8x4_to_f32(r.w, f + 12);
+  }
+};
+
+// One scalar element of storage type T at p[i] -> fp32.
+template <class T> __device__ __forceinline__ float load_elem(const void* p, size_t i);
+template <> __device__ __forceinline__ float load_elem<F32>(const void* p, size_t i) {
+  return reinterpret_cast<const float*>(p)[i];
+}
+template <> __device__ __forceinline__ float load_elem<F16>(const void* p, size_t i) {
+  return (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(p)[i]);
+}
+template <> __device__ __forceinline__ float load_elem<BF16>(const void* p, size_t i) {
+  return u32_as_f32((uint32_t)reinterpret_cast<const uint16_t*>(p)[i] << 16);
+}
+
+// fp32 -> storage, round to nearest even.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = f32_as_u32(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+template <class T> __device__ __forceinline__ void store_elem(void* p, size_t i, float v);
+template <> __device__ __forceinline__ void store_elem<F32>(void* p, size_t i, float v) {
+  reinterpret_cast<float*>(p)[i] = v;
+}
+template <> __device__ __forceinline__ void store_elem<F16>(void* p, size_t i, float v) {
+  reinterpret_cast<uint16_t*>(p)[i] = __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+template <> __device__ __forceinline__ void store_elem<BF16>(void* p, size_t i, float v) {
+  reinterpret_cast<uint16_t*>(p)[i] = f32_to_bf16_rne(v);
+}
+
+// ---------------------------------------------------------------------------
+// E4M3 encode (OCP "FN"): nearest code with ties to even mantissa, saturating
+// to +-448 (also for +-inf), NaN -> 0x7F | sign.  `v` is the already-scaled
+// fp32 value.  Pure integer/float bit work, independent of the hardware
+// convert (which does not saturate).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  const uint32_t u = f32_as_u32(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t ua = u & 0x7fffffffu;
+  if (ua > 0x7f800000u) return 0x7fu | sign;          // NaN
+  if (ua >= 0x43e00000u) return 0x7eu | sign;         // |v| >= 448 (and inf): saturate
+  if (ua < 0x3c800000u) {                              // |v| < 2^-6: subnormal step 2^-9
+    const float k = __builtin_rintf(u32_as_f32(ua) * 512.0f);  // exact scaling, RNE
+    return sign | (uint32_t)k;                         // k == 8 is the smallest normal
+  }
+  // normal: keep 3 mantissa bits of the fp32 pattern, round to nearest even
+  const uint32_t r = ua + 0x7ffffu + ((ua >> 20) & 1u);
+  const uint32_t e = (r >> 23) - 127u + 7u;            // E4M3 biased exponent (1..15)
+  const uint32_t m = (r >> 20) & 7u;
+  return sign | (e << 3) | m;
+}
+
+// Code of x / scale: the division is IEEE fp32 (correctly rounded; the library
+// is built without fast-math); a NaN input keeps its own sign bit.
+__device__ __forceinline__ uint32_t e4m3_encode_scaled(float x, float scale) {
+  const uint32_t u = f32_as_u32(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fu | ((u >> 24) & 0x80u);
+  return e4m3_encode(x / scale);
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane reductions.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float swz_xor16(float x) {  // lane ^ 16 within each 32-lane half
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401f));
+}
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+// Sum over each aligned group of N consecutive lanes (N = 1..64, power of two);
+// every lane of the group ends with the group's sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N >= 2) x += dpp_f32<0xb1>(x);    // quad_perm [1,0,3,2]: lane ^ 1
+  if constexpr (N >= 4) x += dpp_f32<0x4e>(x);    // quad_perm [2,3,0,1]: lane ^ 2
+  if constexpr (N >= 8) x += dpp_f32<0x141>(x);   // row_half_mirror: other quad of the 8
+  if constexpr (N >= 16) x += dpp_f32<0x140>(x);  // row_mirror: other half of the 16
+  if constexpr (N >= 32) x += swz_xor16(x);
+  if constexpr (N >= 64) x += xor32(x);
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+  for (int o = 1; o < 64; o <<= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  for (int o = 1; o < 64; o <<= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// Workgroup-id remap.  The dispatcher hands workgroup i to XCD i % 8 (each XCD
+// has its own L2).  Logical ids are regrouped in chunks of C consecutive ids:
+// a chunk runs on one XCD, back to back, and consecutive chunks go to
+// consecutive XCDs.  Consecutive sequences of one (head, partition) -- e.g. the
+// samples of one prompt that share its cached blocks -- then meet in one L2,
+// while every XCD still receives an even mix of partitions.  A bijection on
+// [0, n); ids past the last whole round of 8*C keep their order.
+// ---------------------------------------------------------------------------
+#ifndef PKV_XCD_CHUNK
+#define PKV_XCD_CHUNK 64
+#endif
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t i, uint32_t n) {
+  constexpr uint32_t X = 8, C = PKV_XCD_CHUNK;
+  if constexpr (C == 0) return i;
+  const uint32_t full = n / (X * C) * (X * C);
+  if (i >= full) return i;
+  const uint32_t x = i % X, k = i / X;
+  return ((k / C) * X + x) * C + (k % C);
+}
+
+// Logical work id -> (sequence, head unit, partition).  Partitions are the
+// slowest dimension.  With PKV_HEAD_FASTEST the head units of one sequence are
+// consecutive, so concurrent workgroups read the neighbouring per-head tiles of
+// the same physical blocks (one block of every kv head is one contiguous run).
+#ifndef PKV_HEAD_FASTEST
+#define PKV_HEAD_FASTEST 1
+#endif
+__device__ __forceinline__ void decode_work_id(uint32_t L, int num_seqs, int num_units, int& seq, int& unit,
+                                               int& part) {
+  if constexpr (PKV_HEAD_FASTEST) {
+    unit = (int)(L % (uint32_t)num_units);
+    const uint32_t rest = L / (uint32_t)num_units;
+    seq = (int)(rest % (uint32_t)num_seqs);
+    part = (int)(rest / (uint32_t)num_seqs);
+  } else {
+    seq = (int)(L % (uint32_t)num_seqs);
+    const uint32_t rest = L / (uint32_t)num_seqs;
+    unit = (int)(rest % (uint32_t)num_units);
+    part = (int)(rest / (uint32_t)num_units);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel parameter blocks (passed by value as kernel arguments).
+// ---------------------------------------------------------------------------
+struct AttnParams {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* ws_m;   // [S][H][NP]      running max of each partition (log2 domain)
+  float* ws_l;   // [S][H][NP]      exp-sum of each partition
+  float* ws_o;   // [S][H][NP][D]   unnormalised output of each partition (v_scale applied)
+  int num_seqs;
+  int num_heads;
+  int num_kv_heads;
+  int group;               // num_heads / num_kv_heads
+  int max_blocks_per_seq;
+  int num_blocks;
+  int partition_blocks;    // blocks per partition
+  int num_partitions;      // NP; 1 => the attention kernel writes `out` directly
+  int ctx_cap;             // contexts are clamped to this many tokens
+  float qk_scale;          // scale * log2(e) * k_scale
+  float v_scale;
+  uint32_t total_wgs;
+};
+
+struct ReduceParams {
+  void* out;
+  const int32_t* context_lens;
+  const float* ws_m;
+  const float* ws_l;
+  const float* ws_o;
+  int num_seqs;
+  int num_heads;
+  int num_partitions;
+  int partition_tokens;
+  int ctx_cap;
+};
+
+}  // namespace pkv

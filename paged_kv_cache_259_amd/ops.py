@@ -1,0 +1,179 @@
+"""Thin Python binding over ``libpkv.so`` (C ABI in include/pkv.h).
+
+Argument marshalling only: shapes and dtypes are read off torch tensors,
+``data_ptr()``s and torch's current HIP stream are passed to the C calls, and a
+negative status becomes a ``PkvError``.  Every step of the path runs in the HIP
+kernels; there is no CPU fallback -- importing this module raises ImportError
+when the library has not been built.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("PKV_LIB", os.path.join(_HERE, "libpkv.so"))
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"paged_kv_cache_259_amd: HIP library not found at {LIB_PATH}; "
+        "build it with `python -m paged_kv_cache_259_amd.build` (there is no CPU fallback)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+F32, F16, BF16, FP8_E4M3 = 0, 1, 2, 3
+PATH_VECTOR, PATH_MFMA = 0, 1
+
+_c_int, _c_float, _c_size, _vp = ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+
+_lib.pkv_status_string.restype = ctypes.c_char_p
+_lib.pkv_status_string.argtypes = [_c_int]
+_lib.pkv_version.restype = _c_int
+_lib.pkv_version.argtypes = []
+_lib.pkv_attention_plan.restype = _c_int
+_lib.pkv_attention_plan.argtypes = [_c_int] * 9 + [ctypes.POINTER(_c_int)] * 3
+_lib.pkv_attention_workspace_bytes.restype = _c_size
+_lib.pkv_attention_workspace_bytes.argtypes = [_c_int] * 9
+_lib.pkv_paged_attention_decode.restype = _c_int
+_lib.pkv_paged_attention_decode.argtypes = (
+    [_vp, _vp, _vp, _vp, _vp, _c_int, _vp]
+    + [_c_int] * 7
+    + [_c_float] * 3
+    + [_c_int] * 3
+    + [_vp, _c_size, _vp])
+_lib.pkv_reshape_and_cache.restype = _c_int
+_lib.pkv_reshape_and_cache.argtypes = [_vp] * 5 + [_c_int] * 7 + [_c_float] * 2 + [_vp]
+_lib.pkv_copy_blocks.restype = _c_int
+_lib.pkv_copy_blocks.argtypes = [_vp, _vp, _vp] + [_c_int] * 6 + [_vp]
+
+EXPORTED_SYMBOLS = (
+    "pkv_status_string", "pkv_version", "pkv_attention_plan", "pkv_attention_workspace_bytes",
+    "pkv_paged_attention_decode", "pkv_reshape_and_cache", "pkv_copy_blocks",
+)
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status, call):
+        self.status = status
+        super().__init__(f"{call}: {_lib.pkv_status_string(status).decode()} (status {status})")
+
+
+def _check(status, call):
+    if status != 0:
+        raise PkvError(status, call)
+
+
+def dtype_code(t: torch.dtype):
+    if t == torch.float32:
+        return F32
+    if t == torch.float16:
+        return F16
+    if t == torch.bfloat16:
+        return BF16
+    if t in (torch.uint8, torch.float8_e4m3fn):
+        return FP8_E4M3
+    raise TypeError(f"unsupported dtype {t}")
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def library_version():
+    return _lib.pkv_version()
+
+
+def attention_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len,
+                   partition_size=0, q_dtype=F16, kv_dtype=F16):
+    """(path, partition_tokens, num_partitions) the decode call would use."""
+    path, ptoks, nparts = _c_int(), _c_int(), _c_int()
+    _check(_lib.pkv_attention_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len,
+                                   partition_size, q_dtype, kv_dtype,
+                                   ctypes.byref(path), ctypes.byref(ptoks), ctypes.byref(nparts)),
+           "pkv_attention_plan")
+    return path.value, ptoks.value, nparts.value
+
+
+def attention_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len,
+                              partition_size=0, q_dtype=F16, kv_dtype=F16):
+    return _lib.pkv_attention_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                              max_context_len, partition_size, q_dtype, kv_dtype)
+
+
+def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+                           k_scale=1.0, v_scale=1.0, partition_size=0, workspace=None, num_blocks=None,
+                           stream=None):
+    """out[s, h] = softmax(scale * K_s q[s, h]) V_s over each sequence's paged context.
+
+    out, q: [S, H, d]; k_cache, v_cache: [NB, KVH, bs, d]; block_tables: int32
+    [S, maxblk]; context_lens: int32 [S].  ``workspace``: a device uint8 tensor
+    of at least ``attention_workspace_bytes(...)`` bytes (allocated here if None).
+    """
+    S, H, d = q.shape
+    NB, KVH, bs, d2 = k_cache.shape
+    if d2 != d or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch between q/out and the pools")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables must be [S, maxblk] and context_lens [S]")
+    for t in (out, q, k_cache, v_cache, block_tables, context_lens):
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    qd, kvd = dtype_code(q.dtype), dtype_code(k_cache.dtype)
+    if out.dtype != q.dtype:
+        raise TypeError("out must have q's dtype")
+    need = attention_workspace_bytes(S, H, KVH, d, bs, max_context_len, partition_size, qd, kvd)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _ptr(workspace) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.pkv_paged_attention_decode(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1],
+        _ptr(context_lens), S, H, KVH, d, bs, NB if num_blocks is None else num_blocks, max_context_len,
+        float(scale), float(k_scale), float(v_scale), qd, kvd, partition_size, ws_ptr, ws_bytes,
+        _stream(stream)), "pkv_paged_attention_decode")
+    return out
+
+
+def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, k_scale=1.0, v_scale=1.0, stream=None):
+    """k_cache[slot // bs, h, slot % bs] = enc(key[i, h]) for every token i (slot < 0 skipped)."""
+    T, KVH, d = key.shape
+    NB, KVH2, bs, d2 = k_cache.shape
+    if (KVH2, d2) != (KVH, d) or tuple(value.shape) != tuple(key.shape) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("shape mismatch between key/value and the pools")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (T,):
+        raise TypeError("slot_mapping must be int64 [num_tokens]")
+    for t in (key, value, k_cache, v_cache, slot_mapping):
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    _check(_lib.pkv_reshape_and_cache(
+        _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), T, KVH, d, bs, NB,
+        dtype_code(key.dtype), dtype_code(k_cache.dtype), float(k_scale), float(v_scale), _stream(stream)),
+        "pkv_reshape_and_cache")
+
+
+def copy_blocks(k_cache, v_cache, block_mapping, stream=None):
+    """Whole-block copies k_cache[dst] = k_cache[src] (and V) for each (src, dst) row of block_mapping."""
+    NB, KVH, bs, d = k_cache.shape
+    if tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache and v_cache differ in shape")
+    if block_mapping.dtype != torch.int64 or block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise TypeError("block_mapping must be int64 [num_pairs, 2]")
+    if not (k_cache.is_contiguous() and v_cache.is_contiguous() and block_mapping.is_contiguous()):
+        raise ValueError("all tensors must be contiguous")
+    _check(_lib.pkv_copy_blocks(
+        _ptr(k_cache), _ptr(v_cache), _ptr(block_mapping), block_mapping.shape[0], KVH, d, bs, NB,
+        dtype_code(k_cache.dtype), _stream(stream)), "pkv_copy_blocks")
+
+
+def raw_lib():
+    """The ctypes handle (tests call the C ABI directly through it)."""
+    return _lib

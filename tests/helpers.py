@@ -1,0 +1,145 @@
+"""Shared test helpers: decode cases built from the seeded generators, poisoning,
+host copies for the oracle, and the tolerance check.
+
+Tolerance (the workload's stated bound, read per element): |gpu - ref| <=
+2e-3 + 1e-2 |ref| for 16-bit or FP8 caches, 1e-5 + 1e-5 |ref| for fp32.
+"""
+
+import numpy as np
+import torch
+
+import oracle
+from paged_kv_cache_259_amd import synth
+from paged_kv_cache_259_amd.block_manager import BlockManager
+
+TOL = {"f32": (1e-5, 1e-5), "f16": (2e-3, 1e-2), "bf16": (2e-3, 1e-2), "fp8_e4m3": (2e-3, 1e-2)}
+NP_VIEW = {torch.float32: np.uint32, torch.float16: np.uint16, torch.bfloat16: np.uint16, torch.uint8: np.uint8}
+
+
+def bits(t):
+    """Raw bits of a tensor as a numpy integer array (bf16 has no numpy type)."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16 or t.dtype == torch.float16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float32:
+        return t.view(torch.int32).numpy().view(np.uint32)
+    return t.numpy()
+
+
+def as_f64(t):
+    return t.detach().cpu().to(torch.float64).numpy()
+
+
+def check_close(got, ref, tol, what=""):
+    atol, rtol = tol
+    got = np.asarray(got, np.float64)
+    err = np.abs(got - ref)
+    bound = atol + rtol * np.abs(ref)
+    bad = ~(err <= bound)
+    if bad.any():
+        idx = np.argwhere(bad)[:5].tolist()
+        raise AssertionError(f"{what}: {bad.sum()} elements out of tolerance; max err {np.nanmax(err):.3e}; first {idx}")
+    return float(err.max()) if err.size else 0.0
+
+
+class DecodeCase:
+    """Pools, tables and queries of one decode call; every context token already cached."""
+
+    def __init__(self, w, device, lengths=None, poison=True, fp8_scales=(0.02, 0.03)):
+        self.w = w
+        inp = synth.make_decode_inputs(w if w.kv_dtype != "fp8_e4m3" else _as_f16_kv(w), device="cpu",
+                                       lengths=lengths)
+        self.ctx = inp.context_lens.astype(np.int32)
+        self.bm = BlockManager(inp.num_blocks, w.block_size, inp.free_list)
+        self.seqs = list(range(w.num_seqs))
+        for s in self.seqs:
+            self.bm.add_sequence(s, int(self.ctx[s]))
+        self.tables = self.bm.block_table_array(self.seqs, w.max_blocks_per_seq)
+        self.num_blocks = inp.num_blocks
+        self.q = inp.q
+        self.k_scale, self.v_scale = 1.0, 1.0
+        if w.kv_dtype == "fp8_e4m3":
+            g = torch.Generator().manual_seed(w.seed + 1)
+            kc = torch.randint(0, 256, inp.k_cache.shape, generator=g, dtype=torch.int32).to(torch.uint8)
+            vc = torch.randint(0, 256, inp.k_cache.shape, generator=g, dtype=torch.int32).to(torch.uint8)
+            kc[(kc & 0x7F) == 0x7F] = 0x01          # no NaN codes in live slots
+            vc[(vc & 0x7F) == 0x7F] = 0x02
+            self.k_cache, self.v_cache = kc, vc
+            self.k_scale, self.v_scale = fp8_scales
+        else:
+            self.k_cache, self.v_cache = inp.k_cache, inp.v_cache
+        if poison:
+            self._poison()
+        self.device = device
+
+    def _poison(self):
+        bs = self.w.block_size
+        used = np.zeros(self.num_blocks, bool)
+        nan = 0x7F if self.k_cache.dtype == torch.uint8 else float("nan")
+        for s in self.seqs:
+            t = self.bm.tables[s]
+            used[t] = True
+            n = int(self.ctx[s])
+            if n % bs and t:
+                self.k_cache[t[-1], :, n % bs:] = nan
+                self.v_cache[t[-1], :, n % bs:] = nan
+        free = np.flatnonzero(~used)
+        if len(free):
+            self.k_cache[torch.from_numpy(free)] = nan
+            self.v_cache[torch.from_numpy(free)] = nan
+
+    def pools_f64(self):
+        if self.k_cache.dtype == torch.uint8:
+            return (oracle.dequant_e4m3(self.k_cache.numpy(), self.k_scale),
+                    oracle.dequant_e4m3(self.v_cache.numpy(), self.v_scale))
+        return as_f64(self.k_cache), as_f64(self.v_cache)
+
+    def reference(self):
+        kp, vp = self.pools_f64()
+        return oracle.attend_ref(as_f64(self.q), kp, vp, self.tables, self.ctx, self.w.softmax_scale,
+                                 self.w.block_size)
+
+    def run(self, partition_size=None, q=None, tables=None):
+        from paged_kv_cache_259_amd import ops
+        dev = self.device
+        q = (self.q if q is None else q).to(dev)
+        out = torch.empty_like(q)
+        ps = self.w.partition_size if partition_size is None else partition_size
+        ops.paged_attention_decode(
+            out, q, self.k_cache.to(dev), self.v_cache.to(dev),
+            torch.from_numpy(self.tables if tables is None else tables).to(dev),
+            torch.from_numpy(self.ctx).to(dev), self.w.softmax_scale, int(self.ctx.max()),
+            k_scale=self.k_scale, v_scale=self.v_scale, partition_size=ps)
+        torch.cuda.synchronize()
+        return out.cpu()
+
+
+def _as_f16_kv(w):
+    return synth.scaled(w, kv_dtype="f16")
+
+
+class SparsePool:
+    """Host copy of only the blocks some sequences use, indexed by their real ids.
+
+    The oracle's gather walks the real block table through ``pool[block, kv_head]``;
+    this object answers those reads for the copied blocks and refuses any other.
+    """
+
+    def __init__(self, pool_dev, block_ids, to_f64):
+        ids = sorted(set(int(b) for b in block_ids))
+        idx = torch.tensor(ids, dtype=torch.int64, device=pool_dev.device)
+        host = to_f64(pool_dev.index_select(0, idx))
+        self._rows = {b: host[i] for i, b in enumerate(ids)}
+        self.shape = pool_dev.shape
+        self.dtype = np.float64
+
+    def __getitem__(self, key):
+        b, h = key
+        return self._rows[int(b)][h]
+
+
+def sample_pairs(rng, S, H, n, always=()):
+    picks = {(int(s), int(rng.integers(0, H))) for s in rng.choice(S, size=min(n, S), replace=False)}
+    for s in always:
+        picks.add((int(s), int(rng.integers(0, H))))
+    return sorted(picks)

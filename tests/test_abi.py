@@ -1,0 +1,129 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol include/pkv.h declares,
+and its host-side argument checks return the documented status codes.  No call here
+reaches a kernel launch: each one fails a host check or is an empty no-op.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+LIB = os.path.join(ROOT, "paged_kv_cache_259_amd", "libpkv.so")
+
+FAKE = ctypes.c_void_p(0x10000)     # aligned, never dereferenced: every call below returns before a launch
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from paged_kv_cache_259_amd import build
+        build.build(verbose=False)
+    from paged_kv_cache_259_amd import ops
+    return ops.raw_lib()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(pkv_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_symbols()
+    assert len(names) == 7
+    for n in names:
+        assert hasattr(lib, n), n
+    nm = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (pkv_\w+)", nm))
+    assert set(names) <= exported
+
+
+def test_binding_declares_the_same_symbols(lib):
+    from paged_kv_cache_259_amd import ops
+    assert sorted(ops.EXPORTED_SYMBOLS) == declared_symbols()
+
+
+def test_status_strings(lib):
+    for st in range(0, -9, -1):
+        s = lib.pkv_status_string(st)
+        assert s and s != b"unknown status"
+    assert lib.pkv_status_string(-99) == b"unknown status"
+    assert lib.pkv_version() == 100
+
+
+def _plan(lib, *args):
+    path, pt, npart = ctypes.c_int(-1), ctypes.c_int(-1), ctypes.c_int(-1)
+    st = lib.pkv_attention_plan(*args, ctypes.byref(path), ctypes.byref(pt), ctypes.byref(npart))
+    return st, path.value, pt.value, npart.value
+
+
+def test_attention_plan_choices(lib):
+    # MHA -> vector family; GQA with 16-bit q -> MFMA family; fp32 GQA -> vector
+    assert _plan(lib, 64, 40, 40, 128, 16, 2048, 0, 1, 1) == (0, 0, 512, 4)
+    assert _plan(lib, 256, 64, 8, 128, 16, 4096, 0, 2, 2) == (0, 1, 512, 8)
+    assert _plan(lib, 8, 32, 8, 128, 16, 131072, 512, 2, 2) == (0, 1, 512, 256)
+    assert _plan(lib, 4, 8, 2, 128, 16, 100, 0, 0, 0)[:2] == (0, 0)
+    # short contexts: one pass, no workspace
+    assert _plan(lib, 4, 8, 8, 64, 16, 64, 0, 0, 0) == (0, 0, 64, 1)
+    assert lib.pkv_attention_workspace_bytes(4, 8, 8, 64, 16, 64, 0, 0, 0) == 0
+    assert lib.pkv_attention_workspace_bytes(2, 4, 4, 128, 16, 1000, 256, 1, 1) >= 2 * 4 * 4 * (128 + 2) * 4
+
+
+@pytest.mark.parametrize("args,status", [
+    ((4, 8, 3, 128, 16, 64, 0, 1, 1), -3),     # heads not a multiple of kv heads
+    ((4, 8, 8, 96, 16, 64, 0, 1, 1), -4),      # head_dim 96 not built
+    ((4, 8, 8, 128, 16, 64, 0, 3, 3), -4),     # fp8 queries
+    ((4, 8, 8, 128, 16, 64, 0, 1, 2), -4),     # f16 q with bf16 cache
+    ((4, 8, 8, 128, 16, 64, 24, 1, 1), -5),    # partition not a multiple of the block
+    ((-1, 8, 8, 128, 16, 64, 0, 1, 1), -2),
+    ((4, 8, 8, 128, 0, 64, 0, 1, 1), -2),
+])
+def test_attention_plan_rejects(lib, args, status):
+    assert _plan(lib, *args)[0] == status
+
+
+def _decode(lib, num_seqs=2, H=4, KVH=4, d=128, bs=16, NB=8, max_ctx=64, ks=1.0, vs=1.0, qd=1, kvd=1, part=0,
+            ws=None, ws_bytes=0, ptr=FAKE):
+    return lib.pkv_paged_attention_decode(ptr, FAKE, FAKE, FAKE, FAKE, 4, FAKE, num_seqs, H, KVH, d, bs, NB, max_ctx,
+                                          ctypes.c_float(0.1), ctypes.c_float(ks), ctypes.c_float(vs), qd, kvd, part,
+                                          ws, ws_bytes, None)
+
+
+def test_decode_host_checks(lib):
+    assert _decode(lib, num_seqs=0) == 0                       # empty batch: nothing to do
+    assert _decode(lib, H=6, KVH=4) == -3
+    assert _decode(lib, part=20) == -5
+    assert _decode(lib, max_ctx=1000, part=256) == -6           # needs a workspace
+    assert _decode(lib, max_ctx=1000, part=256, ws=FAKE, ws_bytes=16) == -6
+    assert _decode(lib, kvd=3, ks=0.0) == -8
+    assert _decode(lib, kvd=3, vs=float("inf")) == -8
+    assert _decode(lib, ptr=None) == -1
+    assert _decode(lib, ptr=ctypes.c_void_p(0x10004)) == -4    # misaligned output
+    assert _decode(lib, NB=0) == -2
+
+
+def test_reshape_and_copy_host_checks(lib):
+    f = ctypes.c_float
+    r = lib.pkv_reshape_and_cache
+    assert r(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 4, 128, 16, 8, 1, 1, f(1), f(1), None) == 0
+    assert r(FAKE, FAKE, FAKE, FAKE, FAKE, 5, 4, 128, 16, 8, 1, 2, f(1), f(1), None) == -4
+    assert r(FAKE, FAKE, FAKE, FAKE, FAKE, 5, 4, 120, 16, 8, 1, 1, f(1), f(1), None) == -4
+    assert r(FAKE, FAKE, FAKE, FAKE, FAKE, 5, 4, 128, 16, 8, 1, 3, f(-1), f(1), None) == -8
+    assert r(FAKE, None, FAKE, FAKE, FAKE, 5, 4, 128, 16, 8, 1, 1, f(1), f(1), None) == -1
+    assert r(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 4, 128, 16, 8, 1, 1, f(1), f(1), None) == -2
+    c = lib.pkv_copy_blocks
+    assert c(FAKE, FAKE, FAKE, 0, 4, 128, 16, 8, 1, None) == 0
+    assert c(FAKE, FAKE, FAKE, 3, 1, 4, 1, 8, 3, None) == -4      # 4-byte blocks: not 16-byte units
+    assert c(FAKE, FAKE, None, 3, 4, 128, 16, 8, 1, None) == -1
+    assert c(FAKE, FAKE, FAKE, 3, 4, 128, 16, 8, 7, None) == -4
+
+
+def test_missing_library_fails_loudly():
+    env = dict(os.environ, PKV_LIB="/nonexistent/libpkv.so")
+    r = subprocess.run([sys.executable, "-c", "import paged_kv_cache_259_amd.ops"], cwd=ROOT, env=env,
+                       capture_output=True, text=True)
+    assert r.returncode != 0 and "no CPU fallback" in r.stderr
