@@ -35,7 +35,7 @@ FLAGS = [
 
 def _compile(src, extra=()):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, *extra, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, f"-I{os.path.dirname(src)}", *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
@@ -43,14 +43,16 @@ def _compile(src, extra=()):
     return obj, msgs
 
 
-def build(verbose=True, defines=(), out=None, build_dir=None):
-    """Compile and link; ``defines`` are extra -D flags (tuning constants), ``out`` the .so path."""
+def build(verbose=True, defines=(), out=None, build_dir=None, csrc=None):
+    """Compile and link; ``defines`` are extra -D flags (tuning constants), ``out`` the .so path,
+    ``csrc`` another source directory with the same files (default: the package's csrc/)."""
     global BUILD
     lib = out or LIB
+    src_dir = csrc or CSRC
     BUILD = build_dir or os.path.join(PKG, "_build")
     os.makedirs(BUILD, exist_ok=True)
     extra = [f"-D{d}" for d in defines]
-    srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    srcs = sorted(os.path.join(src_dir, f) for f in os.listdir(src_dir) if f.endswith(".hip"))
     with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         results = list(ex.map(lambda f: _compile(f, extra), srcs))
     for obj, msgs in results:

@@ -115,8 +115,85 @@ __global__ __launch_bounds__(256) void attn_reduce_small_kernel(ReduceParams p) 
   for (int j = 0; j < DV; ++j) store_elem<OT>(p.out, (size_t)sh * D + lane * DV + j, acc[j] * inv);
 }
 
+// Balanced-slice mode: one wave per (sequence, head).  A sequence whose blocks
+// all fall in one slice was written by the attention kernel; an empty one gets
+// a zero row here; one that crosses slice boundaries k0..k1 has one summary
+// row per slice (row ((k*2 + which) * H + head), which = 1 only for the slice
+// where the sequence starts mid-slice) and is merged here.
+template <class OT, int D>
+__global__ __launch_bounds__(256) void attn_slice_finish_kernel(ReduceParams p) {
+  constexpr int DV = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int sh = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (sh >= p.num_seqs * p.num_heads) return;           // whole wave exits together
+  const int seq = sh / p.num_heads;
+  const int h = sh - seq * p.num_heads;
+  const int start = p.ws_prefix[seq], end = p.ws_prefix[seq + 1];
+  if (start == end) {
+#pragma unroll
+    for (int j = 0; j < DV; ++j) store_elem<OT>(p.out, (size_t)sh * D + lane * DV + j, 0.f);
+    return;
+  }
+  const int64_t T = p.ws_prefix[p.num_seqs];
+  const int NS = p.num_slices;
+  const int k0 = slice_of(start, T, NS), k1 = slice_of(end - 1, T, NS);
+  if (k0 == k1) return;
+  const int n = k1 - k0 + 1;
+  const bool starts_inside = start > slice_begin(k0, T, NS);
+  auto row_of = [&](int i) -> int64_t {
+    return ((int64_t)(k0 + i) * 2 + ((i == 0 && starts_inside) ? 1 : 0)) * p.num_heads + h;
+  };
+  // a slice with no items (more slices than items) wrote no row: skip it
+  auto live = [&](int i) -> bool { return slice_begin(k0 + i, T, NS) < slice_begin(k0 + i + 1, T, NS); };
+  float M = -__builtin_inff();
+  for (int i0 = 0; i0 < n; i0 += 64)
+    if (i0 + lane < n && live(i0 + lane)) M = fmaxf(M, p.ws_m[row_of(i0 + lane)]);
+  M = wave_max(M);
+  M = (M == -__builtin_inff()) ? 0.f : M;
+  float L = 0.f;
+  float acc[DV];
+#pragma unroll
+  for (int j = 0; j < DV; ++j) acc[j] = 0.f;
+  for (int i0 = 0; i0 < n; i0 += 64) {
+    const int cnt = n - i0 < 64 ? n - i0 : 64;
+    const bool mine = lane < cnt && live(i0 + lane);
+    const float wi = mine ? exp2_fast(p.ws_m[row_of(i0 + lane)] - M) : 0.f;
+    L += mine ? wi * p.ws_l[row_of(i0 + lane)] : 0.f;
+    const uint64_t live_mask = __ballot(mine);
+    for (int j0 = 0; j0 < cnt; j0 += 4) {               // four rows' loads in flight at once
+      float v[4][DV];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < DV; ++j)
+          v[u][j] = (j0 + u < cnt && ((live_mask >> (j0 + u)) & 1))
+                        ? p.ws_o[(size_t)row_of(i0 + j0 + u) * D + lane * DV + j] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wi), j0 + u));
+#pragma unroll
+        for (int j = 0; j < DV; ++j) acc[j] += wu * v[u][j];
+      }
+    }
+  }
+  L = wave_sum(L);
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+  for (int j = 0; j < DV; ++j) store_elem<OT>(p.out, (size_t)sh * D + lane * DV + j, acc[j] * inv);
+}
+
 template <class OT>
 static hipError_t launch_reduce_d(const ReduceParams& p, int d, hipStream_t stream) {
+  if (p.num_slices > 0) {
+    const dim3 grid((unsigned)((p.num_seqs * p.num_heads + 3) / 4));
+    switch (d) {
+      case 64: hipLaunchKernelGGL((attn_slice_finish_kernel<OT, 64>), grid, dim3(256), 0, stream, p); break;
+      case 128: hipLaunchKernelGGL((attn_slice_finish_kernel<OT, 128>), grid, dim3(256), 0, stream, p); break;
+      case 256: hipLaunchKernelGGL((attn_slice_finish_kernel<OT, 256>), grid, dim3(256), 0, stream, p); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   const int units = p.num_seqs * p.num_heads;
   if (p.num_partitions <= 64) {
     const dim3 grid((unsigned)((units + 3) / 4));

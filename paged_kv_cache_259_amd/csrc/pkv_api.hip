@@ -16,10 +16,28 @@ constexpr float kLog2e = 1.4426950408889634f;
 #endif
 constexpr int kAutoPartitionTokens = PKV_AUTO_PARTITION;
 
+#ifndef PKV_SLICE_WGS_VEC
+#define PKV_SLICE_WGS_VEC 1280   // resident 4-wave workgroups of the vector kernel on 256 CUs
+#endif
+#ifndef PKV_SLICE_WGS_MFMA
+#define PKV_SLICE_WGS_MFMA 1024  // resident 4-wave workgroups of the MFMA kernel on 256 CUs
+#endif
+constexpr int kSingleMaxTokens = 256;    // contexts this short: one pass, no split
+#ifndef PKV_LONGEST_FIRST
+#define PKV_LONGEST_FIRST 1
+#endif
+
+enum Mode { kSingle = 0, kPartitions = 1, kSlices = 2 };
+
 struct Plan {
   int path;            // PKV_PATH_*
-  int part_tokens;     // tokens per partition (multiple of block_size)
-  int num_parts;       // partitions per sequence
+  int mode;            // Mode
+  int part_tokens;     // tokens per partition (partitions / single pass), 0 for slices
+  int num_parts;       // partitions per sequence, or number of slices
+  int units;           // head units per sequence: query heads (vector) or kv heads (MFMA)
+  bool longest_first;  // one pass in decreasing context order
+  size_t rows;         // fp32 summary rows in the workspace
+  size_t off_m, off_l, off_prefix;
   size_t ws_bytes;     // workspace needed (0 for a single pass)
 };
 
@@ -63,24 +81,58 @@ int make_plan(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int b
   else path = mfma_ok ? PKV_PATH_MFMA : PKV_PATH_VECTOR;
   if ((path == PKV_PATH_MFMA && !mfma_ok) || (path == PKV_PATH_VECTOR && !vec_ok)) return PKV_ERR_UNSUPPORTED;
 
-  const int ptoks = partition_size > 0 ? partition_size : kAutoPartitionTokens / block_size * block_size;
-  int nparts = (max_context_len + ptoks - 1) / ptoks;
-  Plan pl;
+  Plan pl{};
   pl.path = path;
-  if (nparts <= 1) {
-    // single pass: one partition covering the whole (rounded-up) context
-    const int toks = max_context_len > 0 ? (max_context_len + block_size - 1) / block_size * block_size : block_size;
-    pl.part_tokens = toks;
-    pl.num_parts = 1;
-    pl.ws_bytes = 0;
+  pl.units = path == PKV_PATH_MFMA ? num_kv_heads : num_heads;
+  const int max_blocks = (max_context_len + block_size - 1) / block_size;
+  if (partition_size > 0 || num_seqs > pkv::kMaxSliceSeqs) {
+    // fixed partitions (the caller's size, or 512 tokens for very large batches)
+    const int ptoks = partition_size > 0 ? partition_size : kAutoPartitionTokens / block_size * block_size;
+    const int nparts = (max_context_len + ptoks - 1) / ptoks;
+    if (nparts > 1) {
+      pl.mode = kPartitions;
+      pl.part_tokens = ptoks;
+      pl.num_parts = nparts;
+      pl.rows = (size_t)num_seqs * num_heads * nparts;
+    } else {
+      pl.mode = kSingle;
+    }
+  } else if (max_context_len > kSingleMaxTokens &&
+             (long long)num_seqs * pl.units < 2LL * (path == PKV_PATH_MFMA ? PKV_SLICE_WGS_MFMA : PKV_SLICE_WGS_VEC)) {
+    // few (sequence, head) units for the resident workgroups: balanced slices,
+    // about one round of resident workgroups, at least two blocks per slice
+    const int target = path == PKV_PATH_MFMA ? PKV_SLICE_WGS_MFMA : PKV_SLICE_WGS_VEC;
+    long long ns = (target + pl.units - 1) / pl.units;
+    const long long items = (long long)num_seqs * max_blocks;
+    if (ns > items / 2) ns = items / 2;
+    if (ns > 1) {
+      pl.mode = kSlices;
+      pl.num_parts = (int)ns;
+      pl.rows = (size_t)ns * 2 * num_heads;
+    } else {
+      pl.mode = kSingle;
+    }
   } else {
-    pl.part_tokens = ptoks;
-    pl.num_parts = nparts;
-    const size_t rows = (size_t)num_seqs * num_heads * nparts;
-    pl.ws_bytes = align_up(rows * head_dim * sizeof(float), 256) + 2 * align_up(rows * sizeof(float), 256);
+    pl.mode = kSingle;
   }
-  const int units = path == PKV_PATH_MFMA ? num_kv_heads : num_heads;
-  if ((double)num_seqs * units * pl.num_parts > 2147483647.0) return PKV_ERR_BAD_SIZE;
+  if (pl.mode == kSingle) {
+    // one pass: one partition covering the whole (rounded-up) context; with
+    // enough units, workgroups take sequences longest first
+    pl.part_tokens = max_blocks > 0 ? max_blocks * block_size : block_size;
+    pl.num_parts = 1;
+    // (measured: helps the vector family; the MFMA family's ordering cost outweighs it)
+    pl.longest_first = PKV_LONGEST_FIRST && path == PKV_PATH_VECTOR && num_seqs > 1 &&
+                       num_seqs <= pkv::kMaxSliceSeqs;
+  }
+  if (pl.mode != kSingle) {
+    pl.off_m = align_up(pl.rows * head_dim * sizeof(float), 256);
+    pl.off_l = pl.off_m + align_up(pl.rows * sizeof(float), 256);
+    pl.off_prefix = pl.off_l + align_up(pl.rows * sizeof(float), 256);
+    pl.ws_bytes = pl.off_prefix + (pl.mode == kSlices ? align_up((size_t)(num_seqs + 1) * sizeof(int), 256) : 0);
+  }
+  const long long wgs = pl.mode == kSlices ? (long long)pl.num_parts * pl.units
+                                           : (long long)num_seqs * pl.units * pl.num_parts;
+  if (wgs > 2147483647LL) return PKV_ERR_BAD_SIZE;
   *out = pl;
   return PKV_OK;
 }
@@ -118,7 +170,7 @@ int pkv_attention_plan(int num_seqs, int num_heads, int num_kv_heads, int head_d
                            partition_size, q_dtype, kv_dtype, &pl);
   if (st != PKV_OK) return st;
   if (path) *path = pl.path;
-  if (partition_tokens) *partition_tokens = pl.part_tokens;
+  if (partition_tokens) *partition_tokens = pl.mode == kSlices ? 0 : pl.part_tokens;
   if (num_partitions) *num_partitions = pl.num_parts;
   return PKV_OK;
 }
@@ -148,57 +200,70 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
   if (num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PKV_ERR_NULL_POINTER;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_UNSUPPORTED;
-  if (pl.num_parts > 1 && (!workspace || workspace_bytes < pl.ws_bytes || !aligned16(workspace)))
+  if (pl.mode != kSingle && (!workspace || workspace_bytes < pl.ws_bytes || !aligned16(workspace)))
     return PKV_ERR_WORKSPACE;
 
-  pkv::AttnParams p;
+  pkv::AttnParams p{};
   p.out = out;
   p.q = q;
   p.k_cache = k_cache;
   p.v_cache = v_cache;
   p.block_tables = block_tables;
   p.context_lens = context_lens;
-  const size_t rows = (size_t)num_seqs * num_heads * pl.num_parts;
   char* ws = reinterpret_cast<char*>(workspace);
-  p.ws_o = pl.num_parts > 1 ? reinterpret_cast<float*>(ws) : nullptr;
-  p.ws_m = pl.num_parts > 1 ? reinterpret_cast<float*>(ws + align_up(rows * head_dim * sizeof(float), 256)) : nullptr;
-  p.ws_l = pl.num_parts > 1 ? reinterpret_cast<float*>(ws + align_up(rows * head_dim * sizeof(float), 256) +
-                                                       align_up(rows * sizeof(float), 256))
-                            : nullptr;
+  if (pl.mode != kSingle) {
+    p.ws_o = reinterpret_cast<float*>(ws);
+    p.ws_m = reinterpret_cast<float*>(ws + pl.off_m);
+    p.ws_l = reinterpret_cast<float*>(ws + pl.off_l);
+    p.ws_prefix = pl.mode == kSlices ? reinterpret_cast<int*>(ws + pl.off_prefix) : nullptr;
+  }
   p.num_seqs = num_seqs;
   p.num_heads = num_heads;
   p.num_kv_heads = num_kv_heads;
   p.group = num_heads / num_kv_heads;
   p.max_blocks_per_seq = max_blocks_per_seq;
   p.num_blocks = num_blocks;
-  p.partition_blocks = pl.part_tokens / block_size;
-  p.num_partitions = pl.num_parts;
-  const long long cap_parts = (long long)pl.part_tokens * pl.num_parts;
-  const long long cap_table = (long long)max_blocks_per_seq * block_size;
-  long long cap = cap_parts < cap_table ? cap_parts : cap_table;
+  long long cap_table = (long long)max_blocks_per_seq * block_size;
+  long long cap;
+  if (pl.mode == kSlices) {
+    p.num_slices = pl.num_parts;
+    p.longest_first = 0;
+    p.partition_blocks = 0;
+    p.num_partitions = 0;
+    cap = ((long long)max_context_len + block_size - 1) / block_size * block_size;
+  } else {
+    p.num_slices = 0;
+    p.longest_first = pl.longest_first ? 1 : 0;
+    p.partition_blocks = pl.part_tokens / block_size;
+    p.num_partitions = pl.num_parts;
+    cap = (long long)pl.part_tokens * pl.num_parts;
+  }
+  if (cap > cap_table) cap = cap_table;
   p.ctx_cap = (int)(cap < 2147483647LL ? cap : 2147483647LL);
   const bool fp8 = kv_dtype == PKV_FP8_E4M3;
   p.qk_scale = scale * kLog2e * (fp8 ? k_scale : 1.f);
   p.v_scale = fp8 ? v_scale : 1.f;
-  const int units = pl.path == PKV_PATH_MFMA ? num_kv_heads : num_heads;
-  p.total_wgs = (uint32_t)((size_t)num_seqs * units * pl.num_parts);
+  p.total_wgs = (uint32_t)(pl.mode == kSlices ? (size_t)pl.num_parts * pl.units
+                                              : (size_t)num_seqs * pl.units * pl.num_parts);
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // start from a clean error state
   hipError_t e = pl.path == PKV_PATH_MFMA ? pkv::launch_attention_mfma(p, q_dtype, head_dim, s)
                                            : pkv::launch_attention_vector(p, q_dtype, kv_dtype, head_dim, block_size, s);
   if (e != hipSuccess) return PKV_ERR_LAUNCH;
-  if (pl.num_parts > 1) {
-    pkv::ReduceParams r;
+  if (pl.mode != kSingle) {
+    pkv::ReduceParams r{};
     r.out = out;
     r.context_lens = context_lens;
     r.ws_m = p.ws_m;
     r.ws_l = p.ws_l;
     r.ws_o = p.ws_o;
+    r.ws_prefix = p.ws_prefix;
     r.num_seqs = num_seqs;
     r.num_heads = num_heads;
-    r.num_partitions = pl.num_parts;
+    r.num_partitions = p.num_partitions;
     r.partition_tokens = pl.part_tokens;
+    r.num_slices = p.num_slices;
     r.ctx_cap = p.ctx_cap;
     e = pkv::launch_attention_reduce(r, q_dtype, head_dim, s);
   }

@@ -216,6 +216,91 @@ __device__ __forceinline__ void decode_work_id(uint32_t L, int num_seqs, int num
 // ---------------------------------------------------------------------------
 // Kernel parameter blocks (passed by value as kernel arguments).
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// Balanced slices of the context.  For one head unit, the work items are the
+// (sequence, block) pairs of every sequence laid end to end: sequence s owns
+// items [prefix[s], prefix[s+1]) with prefix[s+1] - prefix[s] = ceil(ctx_s/bs).
+// Slice k of NS covers items [k*T/NS, (k+1)*T/NS), T = prefix[S], so every
+// workgroup gets the same amount of KV to read whatever the length mix.
+// ---------------------------------------------------------------------------
+constexpr int kMaxSliceSeqs = 1024;   // prefix kept in LDS; more sequences use fixed partitions
+
+__device__ __forceinline__ int64_t slice_begin(int k, int64_t T, int ns) { return (int64_t)k * T / ns; }
+
+// Slice holding item x (0 <= x < T).
+__device__ __forceinline__ int slice_of(int64_t x, int64_t T, int ns) {
+  int k = (int)(x * ns / T);
+  while (k + 1 < ns && slice_begin(k + 1, T, ns) <= x) ++k;
+  while (k > 0 && slice_begin(k, T, ns) > x) --k;
+  return k;
+}
+
+// Exclusive block prefix of the (clamped) context lengths into LDS:
+// s_prefix[s] for s = 0..S (s_prefix[S] = T).  Every thread of the workgroup
+// calls it; NT threads, S <= kMaxSliceSeqs.  Ends with a barrier.
+template <int NT>
+__device__ void block_prefix(const int32_t* context_lens, int S, int ctx_cap, int bs, int* s_prefix, int* s_wsum) {
+  constexpr int PER = (kMaxSliceSeqs + NT - 1) / NT;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int v[PER];
+  int local = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int idx = tid * PER + i;
+    int c = idx < S ? context_lens[idx] : 0;
+    c = c < 0 ? 0 : (c > ctx_cap ? ctx_cap : c);
+    v[i] = (c + bs - 1) / bs;
+    local += v[i];
+  }
+  int x = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) s_wsum[w] = x;
+  __syncthreads();
+  int run = x - local;
+  for (int i = 0; i < w; ++i) run += s_wsum[i];
+  if (tid == 0) s_prefix[0] = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int idx = tid * PER + i;
+    run += v[i];
+    if (idx < S) s_prefix[idx + 1] = run;
+  }
+  __syncthreads();
+}
+
+// Longest-first order for one-pass decoding: the sequence whose clamped
+// context is the r-th longest (ties by index).  Every thread of the workgroup
+// calls it (S <= kMaxSliceSeqs); s_ctx is an LDS scratch of kMaxSliceSeqs ints.
+// Dispatching workgroups in this order is greedy longest-processing-time list
+// scheduling: long sequences start first and short ones fill the tail.
+template <int NT>
+__device__ int seq_of_rank(const int32_t* context_lens, int S, int ctx_cap, int r, int* s_ctx, int* s_pick) {
+  const int tid = threadIdx.x;
+  for (int t = tid; t < S; t += NT) {
+    int c = context_lens[t];
+    s_ctx[t] = c < 0 ? 0 : (c > ctx_cap ? ctx_cap : c);
+  }
+  __syncthreads();
+  for (int t = tid; t < S; t += NT) {
+    const int c = s_ctx[t];
+    int rank = 0;
+    int u = 0;
+    for (; u + 4 <= S; u += 4) {
+      const int4 cu = *reinterpret_cast<const int4*>(s_ctx + u);
+      rank += (cu.x > c || (cu.x == c && u < t)) + (cu.y > c || (cu.y == c && u + 1 < t)) +
+              (cu.z > c || (cu.z == c && u + 2 < t)) + (cu.w > c || (cu.w == c && u + 3 < t));
+    }
+    for (; u < S; ++u) rank += s_ctx[u] > c || (s_ctx[u] == c && u < t);
+    if (rank == r) *s_pick = t;
+  }
+  __syncthreads();
+  return *s_pick;
+}
+
 struct AttnParams {
   void* out;
   const void* q;
@@ -235,6 +320,9 @@ struct AttnParams {
   int partition_blocks;    // blocks per partition
   int num_partitions;      // NP; 1 => the attention kernel writes `out` directly
   int ctx_cap;             // contexts are clamped to this many tokens
+  int num_slices;          // > 0: balanced slices (partition fields unused)
+  int longest_first;       // one pass: workgroup r takes the r-th longest sequence
+  int* ws_prefix;          // [S+1] block prefix, written by workgroup 0 in slice mode
   float qk_scale;          // scale * log2(e) * k_scale
   float v_scale;
   uint32_t total_wgs;
@@ -246,10 +334,12 @@ struct ReduceParams {
   const float* ws_m;
   const float* ws_l;
   const float* ws_o;
+  const int* ws_prefix;    // slice mode
   int num_seqs;
   int num_heads;
-  int num_partitions;
+  int num_partitions;      // partition mode
   int partition_tokens;
+  int num_slices;          // slice mode when > 0
   int ctx_cap;
 };
 

@@ -62,15 +62,25 @@ def _plan(lib, *args):
 
 
 def test_attention_plan_choices(lib):
-    # MHA -> vector family; GQA with 16-bit q -> MFMA family; fp32 GQA -> vector
-    assert _plan(lib, 64, 40, 40, 128, 16, 2048, 0, 1, 1) == (0, 0, 512, 4)
-    assert _plan(lib, 256, 64, 8, 128, 16, 4096, 0, 2, 2) == (0, 1, 512, 8)
+    # MHA -> vector family; GQA with 16-bit q -> MFMA family; fp32 GQA -> vector.
+    # partition_size 0 with many (sequence, head) units -> one pass, longest sequences first
+    assert _plan(lib, 64, 40, 40, 128, 16, 2048, 0, 1, 1) == (0, 0, 2048, 1)
+    assert _plan(lib, 256, 64, 8, 128, 16, 4096, 0, 2, 2) == (0, 1, 4096, 1)
+    # few units and long contexts -> balanced slices (partition_tokens reported as 0, num_partitions = slices)
+    st, path, pt, ns = _plan(lib, 8, 32, 8, 128, 16, 131072, 0, 2, 2)
+    assert (st, path, pt) == (0, 1, 0) and ns > 1
+    # an explicit partition size -> fixed partitions
     assert _plan(lib, 8, 32, 8, 128, 16, 131072, 512, 2, 2) == (0, 1, 512, 256)
     assert _plan(lib, 4, 8, 2, 128, 16, 100, 0, 0, 0)[:2] == (0, 0)
     # short contexts: one pass, no workspace
     assert _plan(lib, 4, 8, 8, 64, 16, 64, 0, 0, 0) == (0, 0, 64, 1)
     assert lib.pkv_attention_workspace_bytes(4, 8, 8, 64, 16, 64, 0, 0, 0) == 0
     assert lib.pkv_attention_workspace_bytes(2, 4, 4, 128, 16, 1000, 256, 1, 1) >= 2 * 4 * 4 * (128 + 2) * 4
+    # slices: summary rows for two segments per slice and head, plus the block prefix
+    ns = _plan(lib, 3, 4, 4, 128, 16, 1000, 0, 1, 1)[3]
+    assert lib.pkv_attention_workspace_bytes(3, 4, 4, 128, 16, 1000, 0, 1, 1) >= ns * 2 * 4 * (128 + 2) * 4 + 4 * 4
+    # more sequences than the slice prefix holds -> fixed 512-token partitions
+    assert _plan(lib, 1025, 4, 4, 128, 16, 2000, 0, 1, 1) == (0, 0, 512, 4)
 
 
 @pytest.mark.parametrize("args,status", [

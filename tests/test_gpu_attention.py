@@ -218,3 +218,38 @@ def test_bad_arguments_raise(ops):
     with pytest.raises(ops.PkvError) as e:
         ops.paged_attention_decode(out, q, k8, k8, bt, cl, 0.1, 64, k_scale=0.0)
     assert e.value.status == -8
+
+
+@pytest.mark.parametrize("kind", ["mha", "gqa"])
+def test_slices_with_empty_contexts_and_more_slices_than_blocks(ops, kind):
+    """Balanced slices when most slices are empty and several contexts are 0."""
+    H, KVH, dt = (4, 4, "f16") if kind == "mha" else (16, 2, "bf16")
+    w = W(S=6, H=H, KVH=KVH, d=128, q=dt, kv=dt, lens=(300, 0, 0, 1, 0, 17), seed=13, maxblk=19)
+    case = DecodeCase(w, DEV)
+    path, ptoks, nslices = ops.attention_plan(6, H, KVH, 128, 16, 300, 0, ops.dtype_code(case.q.dtype),
+                                              ops.dtype_code(case.k_cache.dtype))
+    assert ptoks == 0 and nslices > 21                  # more slices than the 21 blocks in use
+    out = case.run(partition_size=0)
+    for s in (1, 2, 4):
+        assert torch.all(out[s] == 0)
+    _check(case, out, f"slices {kind}")
+
+
+@pytest.mark.parametrize("kind", ["mha", "gqa"])
+def test_slices_one_long_sequence_among_short_ones(ops, kind):
+    """One sequence spanning many slices next to many one-block ones."""
+    H, KVH, dt = (2, 2, "bf16") if kind == "mha" else (8, 1, "f16")
+    lens = (3000,) + tuple(1 + 7 * i for i in range(40))
+    w = W(S=len(lens), H=H, KVH=KVH, d=128, q=dt, kv=dt, lens=lens, seed=14)
+    case = DecodeCase(w, DEV)
+    out = case.run(partition_size=0)
+    _check(case, out, f"long+short slices {kind}")
+
+
+def test_many_sequences_use_fixed_partitions(ops):
+    lens = tuple(int(x) for x in np.random.default_rng(15).integers(1, 600, size=1100))
+    w = W(S=len(lens), H=2, KVH=2, d=64, q="f16", kv="f16", lens=lens, seed=15)
+    case = DecodeCase(w, DEV)
+    assert ops.attention_plan(len(lens), 2, 2, 64, 16, max(lens), 0, ops.F16, ops.F16)[1] == 512
+    out = case.run(partition_size=0)
+    _check(case, out, "1100 sequences")
