@@ -78,7 +78,8 @@ int pkv_version(void);
  * Host-only; enqueues nothing.  Writes the kernel family (PKV_PATH_*), the
  * partition size in tokens and the number of partitions per sequence
  * (1 = single pass, no reduce kernel) through the three host pointers (any may
- * be NULL).  `partition_size` 0 asks for the library's automatic choice.
+ * be NULL); balanced slices report partition size 0 and the number of slices.
+ * `partition_size` 0 asks for the library's automatic choice.
  * Returns the same status pkv_paged_attention_decode would return for these
  * shapes (pointers aside).
  */
@@ -89,9 +90,10 @@ int pkv_attention_plan(int num_seqs, int num_heads, int num_kv_heads, int head_d
 
 /*
  * pkv_attention_workspace_bytes -- device workspace pkv_paged_attention_decode
- * needs for these shapes (0 when it runs in a single pass).  The workspace holds
- * fp32 per-partition summaries (running max, exp-sum and unnormalised output
- * vector) for the split-context reduce.  Returns 0 also for invalid shapes.
+ * needs for these shapes.  It holds the longest-first sequence order of a
+ * one-pass launch (4 bytes per sequence), or the fp32 per-partition / per-slice
+ * summaries (running max, exp-sum and unnormalised output vector) of a split
+ * context.  0 for a one-pass launch of one sequence, and for invalid shapes.
  */
 size_t pkv_attention_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
                                      int block_size, int max_context_len, int partition_size,
@@ -126,10 +128,15 @@ size_t pkv_attention_workspace_bytes(int num_seqs, int num_heads, int num_kv_hea
  *              Tokens past min(ctx_s, max_context_len rounded up to a partition,
  *              max_blocks_per_seq * block_size) are ignored.
  * partition_size   tokens per split-context partition (multiple of block_size),
- *              or 0 for the automatic choice.  When more than one partition is
- *              needed, each (sequence, head, partition) writes an fp32 summary to
- *              `workspace` and a second kernel merges them:
+ *              or 0 for the automatic choice.  With partitions, each (sequence,
+ *              head, partition) of a context longer than one partition writes an
+ *              fp32 summary to `workspace` and a second kernel merges them:
  *              M = max_p m_p; out = sum_p e^(m_p - M) o_p / sum_p e^(m_p - M) l_p.
+ *              The automatic choice is one pass when there are enough (sequence,
+ *              head) units to fill the GPU (sequences dispatched longest first,
+ *              ordered by a small sort kernel into the workspace), else balanced
+ *              slices: every workgroup gets the same number of blocks, contexts
+ *              crossing a slice boundary are merged by the second kernel.
  * workspace    device buffer of at least pkv_attention_workspace_bytes(...) bytes
  *              (may be NULL when that is 0).  Contents on entry are ignored.
  * Supported: head_dim 64/128/256; block_size 8/16/32 (16 for the MFMA family);

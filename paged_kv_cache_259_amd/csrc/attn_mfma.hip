@@ -315,14 +315,14 @@ void attn_mfma_kernel(AttnParams p) {
 
   int seq, kvh, part;
   decode_work_id(L, p.num_seqs, p.num_kv_heads, seq, kvh, part);
-  if (p.longest_first)                                      // one pass only (part == 0)
-    seq = seq_of_rank<NW * 64>(p.context_lens, p.num_seqs, p.ctx_cap, seq, sm.prefix, sm.wsum);
+  if (p.seq_order) seq = p.seq_order[seq];                // one pass only: longest first
   int ctx = p.context_lens[seq];
   ctx = ctx < 0 ? 0 : (ctx > p.ctx_cap ? p.ctx_cap : ctx);
   const int nblk = (ctx + A::BS - 1) / A::BS;
   const int b_begin = part * p.partition_blocks;
-  const bool direct = p.num_partitions == 1;
-  if (!direct && b_begin >= nblk) return;
+  // a context that fits in one partition is finished here; the reduce skips it
+  const bool direct = p.num_partitions == 1 || nblk <= p.partition_blocks;
+  if (b_begin >= nblk && (part > 0 || !direct)) return;     // empty partition
   int b_end = b_begin + p.partition_blocks;
   b_end = b_end < nblk ? b_end : nblk;
   st.init();

@@ -180,7 +180,7 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // [0, n); ids past the last whole round of 8*C keep their order.
 // ---------------------------------------------------------------------------
 #ifndef PKV_XCD_CHUNK
-#define PKV_XCD_CHUNK 64
+#define PKV_XCD_CHUNK 0
 #endif
 __device__ __forceinline__ uint32_t xcd_remap(uint32_t i, uint32_t n) {
   constexpr uint32_t X = 8, C = PKV_XCD_CHUNK;
@@ -272,35 +272,6 @@ __device__ void block_prefix(const int32_t* context_lens, int S, int ctx_cap, in
   __syncthreads();
 }
 
-// Longest-first order for one-pass decoding: the sequence whose clamped
-// context is the r-th longest (ties by index).  Every thread of the workgroup
-// calls it (S <= kMaxSliceSeqs); s_ctx is an LDS scratch of kMaxSliceSeqs ints.
-// Dispatching workgroups in this order is greedy longest-processing-time list
-// scheduling: long sequences start first and short ones fill the tail.
-template <int NT>
-__device__ int seq_of_rank(const int32_t* context_lens, int S, int ctx_cap, int r, int* s_ctx, int* s_pick) {
-  const int tid = threadIdx.x;
-  for (int t = tid; t < S; t += NT) {
-    int c = context_lens[t];
-    s_ctx[t] = c < 0 ? 0 : (c > ctx_cap ? ctx_cap : c);
-  }
-  __syncthreads();
-  for (int t = tid; t < S; t += NT) {
-    const int c = s_ctx[t];
-    int rank = 0;
-    int u = 0;
-    for (; u + 4 <= S; u += 4) {
-      const int4 cu = *reinterpret_cast<const int4*>(s_ctx + u);
-      rank += (cu.x > c || (cu.x == c && u < t)) + (cu.y > c || (cu.y == c && u + 1 < t)) +
-              (cu.z > c || (cu.z == c && u + 2 < t)) + (cu.w > c || (cu.w == c && u + 3 < t));
-    }
-    for (; u < S; ++u) rank += s_ctx[u] > c || (s_ctx[u] == c && u < t);
-    if (rank == r) *s_pick = t;
-  }
-  __syncthreads();
-  return *s_pick;
-}
-
 struct AttnParams {
   void* out;
   const void* q;
@@ -321,7 +292,7 @@ struct AttnParams {
   int num_partitions;      // NP; 1 => the attention kernel writes `out` directly
   int ctx_cap;             // contexts are clamped to this many tokens
   int num_slices;          // > 0: balanced slices (partition fields unused)
-  int longest_first;       // one pass: workgroup r takes the r-th longest sequence
+  const int* seq_order;    // one pass: workgroup r takes sequence seq_order[r] (longest first), or r if null
   int* ws_prefix;          // [S+1] block prefix, written by workgroup 0 in slice mode
   float qk_scale;          // scale * log2(e) * k_scale
   float v_scale;
