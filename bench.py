@@ -6,7 +6,8 @@ A step is one pass of the hot path over one synthetic decode batch, inputs
 resident in HBM: reshape_and_cache writes every sequence's new key/value into
 the slot the block manager gave it, then paged_attention_decode attends over
 each sequence's paged context (the split-context reduce included when the plan
-uses one).  copy_blocks has no work in this workload (no block is shared); it is
+uses one).  The block manager's host bookkeeping (tables, slots, the
+longest-first sequence order) is built before the timed region.  copy_blocks has no work in this workload (no block is shared); it is
 timed separately on the copy-on-write pairs of the shared-prefix workload and
 reported under "components".
 
@@ -160,6 +161,7 @@ def main():
     ctx_np = bm.context_lens_array(seqs)
     tables = torch.from_numpy(tables_np).to(dev)
     ctx = torch.from_numpy(ctx_np).to(dev)
+    order = torch.from_numpy(bm.longest_first(seqs)).to(dev)      # host bookkeeping, like the tables
     max_ctx = int(ctx_np.max())
     qd, kvd = ops.dtype_code(inp.q.dtype), ops.dtype_code(inp.k_cache.dtype)
     plan = ops.attention_plan(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size, max_ctx, part,
@@ -175,7 +177,7 @@ def main():
 
     def attend():
         ops.paged_attention_decode(out, inp.q, inp.k_cache, inp.v_cache, tables, ctx, w.softmax_scale, max_ctx,
-                                   partition_size=part, workspace=workspace, stream=stream)
+                                   partition_size=part, workspace=workspace, seq_order=order, stream=stream)
 
     for _ in range(args.warmup):
         reshape()

@@ -90,10 +90,10 @@ int pkv_attention_plan(int num_seqs, int num_heads, int num_kv_heads, int head_d
 
 /*
  * pkv_attention_workspace_bytes -- device workspace pkv_paged_attention_decode
- * needs for these shapes.  It holds the longest-first sequence order of a
- * one-pass launch (4 bytes per sequence), or the fp32 per-partition / per-slice
- * summaries (running max, exp-sum and unnormalised output vector) of a split
- * context.  0 for a one-pass launch of one sequence, and for invalid shapes.
+ * needs for these shapes: the fp32 per-partition / per-slice summaries (running
+ * max, exp-sum and unnormalised output vector) of a split context, plus the
+ * block prefix of the sequences for balanced slices.  0 for a one-pass launch
+ * and for invalid shapes.
  */
 size_t pkv_attention_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
                                      int block_size, int max_context_len, int partition_size,
@@ -122,6 +122,14 @@ size_t pkv_attention_workspace_bytes(int num_seqs, int num_heads, int num_kv_hea
  *              code * k_scale (resp. v_scale); k_scale / v_scale are ignored otherwise.
  * block_tables [num_seqs][max_blocks_per_seq] int32; entries past ceil(ctx/bs) are never read.
  * context_lens [num_seqs] int32.
+ * seq_order    optional [num_seqs] int32 device array: the sequences longest
+ *              context first (a permutation of 0..num_seqs-1).  It only decides
+ *              which sequences start first in a one-pass launch -- any
+ *              permutation gives the same results; the host that builds the
+ *              block tables knows the lengths and can sort them for free.  NULL:
+ *              every workgroup derives the order itself from context_lens.
+ *              Entries are clamped to [0, num_seqs); a non-permutation leaves
+ *              some output rows unwritten.
  * num_blocks   number of blocks in each pool.  A table entry outside
  *              [0, num_blocks) makes the kernel skip that block's tokens.
  * max_context_len  host-side upper bound of context_lens (sizes the partition grid).
@@ -133,8 +141,8 @@ size_t pkv_attention_workspace_bytes(int num_seqs, int num_heads, int num_kv_hea
  *              fp32 summary to `workspace` and a second kernel merges them:
  *              M = max_p m_p; out = sum_p e^(m_p - M) o_p / sum_p e^(m_p - M) l_p.
  *              The automatic choice is one pass when there are enough (sequence,
- *              head) units to fill the GPU (sequences dispatched longest first,
- *              ordered by a small sort kernel into the workspace), else balanced
+ *              head) units to fill the GPU (sequences dispatched longest first),
+ *              else balanced
  *              slices: every workgroup gets the same number of blocks, contexts
  *              crossing a slice boundary are merged by the second kernel.
  * workspace    device buffer of at least pkv_attention_workspace_bytes(...) bytes
@@ -147,7 +155,7 @@ size_t pkv_attention_workspace_bytes(int num_seqs, int num_heads, int num_kv_hea
 int pkv_paged_attention_decode(void* out, const void* q,
                                const void* k_cache, const void* v_cache,
                                const int32_t* block_tables, int max_blocks_per_seq,
-                               const int32_t* context_lens,
+                               const int32_t* context_lens, const int32_t* seq_order,
                                int num_seqs, int num_heads, int num_kv_heads, int head_dim,
                                int block_size, int num_blocks, int max_context_len,
                                float scale, float k_scale, float v_scale,

@@ -120,6 +120,15 @@ class BlockManager:
     def context_lens_array(self, seqs):
         return np.array([self.lengths[s] for s in seqs], dtype=np.int32)
 
+    def longest_first(self, seqs):
+        """Positions 0..len(seqs)-1 ordered by decreasing context length (ties by position).
+
+        A scheduling hint for the one-pass attention launch: long contexts start
+        first.  Any permutation gives the same attention results.
+        """
+        lens = self.context_lens_array(seqs)
+        return np.argsort(-lens, kind="stable").astype(np.int32)
+
     def slot(self, seq, pos):
         t = self.tables[seq]
         return t[pos // self.block_size] * self.block_size + pos % self.block_size

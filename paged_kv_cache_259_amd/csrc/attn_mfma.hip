@@ -315,7 +315,14 @@ void attn_mfma_kernel(AttnParams p) {
 
   int seq, kvh, part;
   decode_work_id(L, p.num_seqs, p.num_kv_heads, seq, kvh, part);
-  if (p.seq_order) seq = p.seq_order[seq];                // one pass only: longest first
+  if (p.longest_first) {                                    // one pass only
+    if (p.seq_order) {
+      const int o = p.seq_order[seq];
+      seq = o < 0 ? 0 : (o >= p.num_seqs ? p.num_seqs - 1 : o);
+    } else {
+      seq = seq_of_rank<NW * 64>(p.context_lens, p.num_seqs, p.ctx_cap, A::BS, seq, sm.prefix, sm.wsum);
+    }
+  }
   int ctx = p.context_lens[seq];
   ctx = ctx < 0 ? 0 : (ctx > p.ctx_cap ? p.ctx_cap : ctx);
   const int nblk = (ctx + A::BS - 1) / A::BS;

@@ -184,63 +184,6 @@ __global__ __launch_bounds__(256) void attn_slice_finish_kernel(ReduceParams p) 
   for (int j = 0; j < DV; ++j) store_elem<OT>(p.out, (size_t)sh * D + lane * DV + j, acc[j] * inv);
 }
 
-// Longest-first order of the sequences for a one-pass launch: a counting sort
-// of the block counts (descending; counts above kOrderBins-1 share the top bin)
-// written to order[0..S).  Sequences of equal count may come out in any order:
-// that changes which workgroup takes them, never their results.  One
-// workgroup; dispatching attention workgroups in this order is greedy
-// longest-processing-time list scheduling on each XCD.
-constexpr int kOrderBins = 2048;
-__global__ __launch_bounds__(256) void attn_order_kernel(const int32_t* context_lens, int S, int ctx_cap, int bs,
-                                                          int* order) {
-  __shared__ int hist[kOrderBins];
-  __shared__ int wsum[4];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  for (int i = tid; i < kOrderBins; i += 256) hist[i] = 0;
-  __syncthreads();
-  for (int t = tid; t < S; t += 256) {
-    int c = context_lens[t];
-    c = c < 0 ? 0 : (c > ctx_cap ? ctx_cap : c);
-    int nb = (c + bs - 1) / bs;
-    nb = nb < kOrderBins - 1 ? nb : kOrderBins - 1;
-    atomicAdd(&hist[kOrderBins - 1 - nb], 1);              // bin 0 = longest
-  }
-  __syncthreads();
-  // exclusive scan of the bins: thread tid owns bins [tid*8, tid*8+8)
-  constexpr int PER = kOrderBins / 256;
-  int v[PER], local = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) { v[i] = hist[tid * PER + i]; local += v[i]; }
-  int x = local;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  if (lane == 63) wsum[w] = x;
-  __syncthreads();
-  int run = x - local;
-  for (int i = 0; i < w; ++i) run += wsum[i];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) { hist[tid * PER + i] = run; run += v[i]; }
-  __syncthreads();
-  for (int t = tid; t < S; t += 256) {
-    int c = context_lens[t];
-    c = c < 0 ? 0 : (c > ctx_cap ? ctx_cap : c);
-    int nb = (c + bs - 1) / bs;
-    nb = nb < kOrderBins - 1 ? nb : kOrderBins - 1;
-    const int pos = atomicAdd(&hist[kOrderBins - 1 - nb], 1);
-    order[pos] = t;
-  }
-}
-
-hipError_t launch_attention_order(const int32_t* context_lens, int num_seqs, int ctx_cap, int block_size, int* order,
-                                  hipStream_t stream) {
-  hipLaunchKernelGGL(attn_order_kernel, dim3(1), dim3(256), 0, stream, context_lens, num_seqs, ctx_cap, block_size,
-                     order);
-  return hipGetLastError();
-}
-
 template <class OT>
 static hipError_t launch_reduce_d(const ReduceParams& p, int d, hipStream_t stream) {
   if (p.num_slices > 0) {

@@ -342,7 +342,14 @@ void attn_vector_kernel(AttnParams p) {
   // fixed partitions of partition_blocks blocks (one pass when num_partitions == 1)
   int seq, head, part;
   decode_work_id(L, p.num_seqs, p.num_heads, seq, head, part);
-  if (p.seq_order) seq = p.seq_order[seq];                // one pass only: longest first
+  if (p.longest_first) {                                    // one pass only
+    if (p.seq_order) {
+      const int o = p.seq_order[seq];
+      seq = o < 0 ? 0 : (o >= p.num_seqs ? p.num_seqs - 1 : o);
+    } else {
+      seq = seq_of_rank<NW * 64>(p.context_lens, p.num_seqs, p.ctx_cap, BS, seq, sm.prefix, sm.wsum);
+    }
+  }
   int ctx = p.context_lens[seq];
   ctx = ctx < 0 ? 0 : (ctx > p.ctx_cap ? p.ctx_cap : ctx);
   const int nblk = (ctx + BS - 1) / BS;

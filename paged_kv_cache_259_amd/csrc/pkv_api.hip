@@ -120,16 +120,13 @@ int make_plan(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int b
     // enough units, workgroups take sequences longest first
     pl.part_tokens = max_blocks > 0 ? max_blocks * block_size : block_size;
     pl.num_parts = 1;
-    pl.longest_first = PKV_LONGEST_FIRST && num_seqs > 1;
+    pl.longest_first = PKV_LONGEST_FIRST && num_seqs > 1 && num_seqs <= pkv::kMaxSliceSeqs;
   }
   if (pl.mode != kSingle) {
     pl.off_m = align_up(pl.rows * head_dim * sizeof(float), 256);
     pl.off_l = pl.off_m + align_up(pl.rows * sizeof(float), 256);
     pl.off_prefix = pl.off_l + align_up(pl.rows * sizeof(float), 256);
     pl.ws_bytes = pl.off_prefix + (pl.mode == kSlices ? align_up((size_t)(num_seqs + 1) * sizeof(int), 256) : 0);
-  } else if (pl.longest_first) {
-    pl.off_prefix = 0;                                   // the sequence order
-    pl.ws_bytes = align_up((size_t)num_seqs * sizeof(int), 256);
   }
   const long long wgs = pl.mode == kSlices ? (long long)pl.num_parts * pl.units
                                            : (long long)num_seqs * pl.units * pl.num_parts;
@@ -187,6 +184,7 @@ size_t pkv_attention_workspace_bytes(int num_seqs, int num_heads, int num_kv_hea
 
 int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                                const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+                               const int32_t* seq_order,
                                int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
                                int num_blocks, int max_context_len, float scale, float k_scale, float v_scale,
                                int q_dtype, int kv_dtype, int partition_size, void* workspace,
@@ -228,13 +226,14 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
   long long cap;
   if (pl.mode == kSlices) {
     p.num_slices = pl.num_parts;
-    p.seq_order = nullptr;
+    p.longest_first = 0;
     p.partition_blocks = 0;
     p.num_partitions = 0;
     cap = ((long long)max_context_len + block_size - 1) / block_size * block_size;
   } else {
     p.num_slices = 0;
-    p.seq_order = pl.longest_first ? reinterpret_cast<int*>(ws + pl.off_prefix) : nullptr;
+    p.longest_first = pl.longest_first ? 1 : 0;
+    p.seq_order = pl.longest_first ? seq_order : nullptr;
     p.partition_blocks = pl.part_tokens / block_size;
     p.num_partitions = pl.num_parts;
     cap = (long long)pl.part_tokens * pl.num_parts;
@@ -249,11 +248,6 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // start from a clean error state
-  if (p.seq_order) {
-    if (pkv::launch_attention_order(context_lens, num_seqs, p.ctx_cap, block_size, const_cast<int*>(p.seq_order), s) !=
-        hipSuccess)
-      return PKV_ERR_LAUNCH;
-  }
   hipError_t e = pl.path == PKV_PATH_MFMA ? pkv::launch_attention_mfma(p, q_dtype, head_dim, s)
                                            : pkv::launch_attention_vector(p, q_dtype, kv_dtype, head_dim, block_size, s);
   if (e != hipSuccess) return PKV_ERR_LAUNCH;

@@ -272,6 +272,84 @@ __device__ void block_prefix(const int32_t* context_lens, int S, int ctx_cap, in
   __syncthreads();
 }
 
+// ---------------------------------------------------------------------------
+// Longest-first order for one-pass launches, computed inside every workgroup.
+// Sequences are keyed by their block count in half-octave buckets (key 0 for
+// an empty context, then 2 keys per power of two), counted with wave ballots;
+// rank r is the r-th sequence in decreasing key order, ties in index order.
+// Dispatching workgroups in this order is greedy longest-processing-time list
+// scheduling up to a factor sqrt(2) in the sort key; which workgroup takes a
+// sequence never changes its result.  All threads call it; S <= kMaxSliceSeqs.
+// ---------------------------------------------------------------------------
+constexpr int kOrderKeys = 32;
+
+__device__ __forceinline__ int order_key(int nblk) {
+  if (nblk <= 0) return 0;
+  const int msb = 31 - __builtin_clz((unsigned)nblk);
+  const int half = msb > 0 ? (nblk >> (msb - 1)) & 1 : 0;
+  const int k = 1 + 2 * msb + half;
+  return k < kOrderKeys ? k : kOrderKeys - 1;
+}
+
+template <int NT>
+__device__ int seq_of_rank(const int32_t* context_lens, int S, int ctx_cap, int bs, int r, int* s_cnt, int* s_pick) {
+  constexpr int NWV = NT / 64;
+  constexpr int CHUNKS = (kMaxSliceSeqs + NT - 1) / NT;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int key[CHUNKS];
+#pragma unroll
+  for (int c = 0; c < CHUNKS; ++c) {
+    const int t = c * NT + tid;
+    int ctx = t < S ? context_lens[t] : 0;
+    ctx = ctx < 0 ? 0 : (ctx > ctx_cap ? ctx_cap : ctx);
+    key[c] = t < S ? order_key((ctx + bs - 1) / bs) : -1;
+  }
+  // s_cnt[(c * NWV + w) * kOrderKeys + k]: sequences with key k in wave w of chunk c
+#pragma unroll
+  for (int c = 0; c < CHUNKS; ++c) {
+    if (c * NT >= S) break;                                  // uniform
+    int mine = 0;
+#pragma unroll
+    for (int k = 0; k < kOrderKeys; ++k) {
+      const int n = __builtin_popcountll(__ballot(key[c] == k));
+      if (lane == k) mine = n;
+    }
+    if (lane < kOrderKeys) s_cnt[(c * NWV + w) * kOrderKeys + lane] = mine;
+  }
+  __syncthreads();
+  // the bucket holding rank r (keys in decreasing order), and r's position in
+  // it: lane k sums bucket k, a suffix scan over lanes gives each bucket's first
+  // rank, a ballot finds the bucket containing r
+  const int groups = ((S + NT - 1) / NT) * NWV;
+  int tot = 0;
+  if (lane < kOrderKeys)
+    for (int g = 0; g < groups; ++g) tot += s_cnt[g * kOrderKeys + lane];
+  int suffix = tot;                                          // sum of buckets lane .. kOrderKeys-1
+#pragma unroll
+  for (int off = 1; off < kOrderKeys; off <<= 1) {
+    const int y = __shfl_down(suffix, off, 64);
+    if (lane + off < kOrderKeys) suffix += y;
+  }
+  const int first_rank = suffix - tot;                       // ranks of longer buckets come first
+  const bool hit = lane < kOrderKeys && tot > 0 && r >= first_rank && r < first_rank + tot;
+  const int K = __builtin_ffsll((long long)__ballot(hit)) - 1;
+  int before = r - __shfl(first_rank, K, 64);                // members of bucket K before the target
+#pragma unroll
+  for (int c = 0; c < CHUNKS; ++c) {
+    if (c * NT >= S) break;
+    int prior = 0;                                           // bucket-K members in earlier waves of this chunk
+    for (int g = 0; g < w; ++g) prior += s_cnt[(c * NWV + g) * kOrderKeys + K];
+    const uint64_t m = __ballot(key[c] == K);
+    const int below = __builtin_popcountll(m & ((1ull << lane) - 1ull));
+    if (key[c] == K && prior + below == before) *s_pick = c * NT + tid;
+    int chunk_total = 0;
+    for (int g = 0; g < NWV; ++g) chunk_total += s_cnt[(c * NWV + g) * kOrderKeys + K];
+    before -= chunk_total;
+  }
+  __syncthreads();
+  return *s_pick;
+}
+
 struct AttnParams {
   void* out;
   const void* q;
@@ -292,7 +370,8 @@ struct AttnParams {
   int num_partitions;      // NP; 1 => the attention kernel writes `out` directly
   int ctx_cap;             // contexts are clamped to this many tokens
   int num_slices;          // > 0: balanced slices (partition fields unused)
-  const int* seq_order;    // one pass: workgroup r takes sequence seq_order[r] (longest first), or r if null
+  int longest_first;       // one pass: workgroup r takes the r-th longest sequence
+  const int32_t* seq_order;  // one pass: the caller's longest-first order (else derived in-workgroup)
   int* ws_prefix;          // [S+1] block prefix, written by workgroup 0 in slice mode
   float qk_scale;          // scale * log2(e) * k_scale
   float v_scale;

@@ -15,8 +15,6 @@ hipError_t launch_attention_vector(const AttnParams& p, int q_dtype, int kv_dtyp
                                    hipStream_t stream);
 hipError_t launch_attention_mfma(const AttnParams& p, int q_dtype, int head_dim, hipStream_t stream);
 hipError_t launch_attention_reduce(const ReduceParams& p, int out_dtype, int head_dim, hipStream_t stream);
-hipError_t launch_attention_order(const int32_t* context_lens, int num_seqs, int ctx_cap, int block_size, int* order,
-                                  hipStream_t stream);
 
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
                                     const int64_t* slot_mapping, int num_tokens, int num_kv_heads,

@@ -37,7 +37,7 @@ _lib.pkv_attention_workspace_bytes.restype = _c_size
 _lib.pkv_attention_workspace_bytes.argtypes = [_c_int] * 9
 _lib.pkv_paged_attention_decode.restype = _c_int
 _lib.pkv_paged_attention_decode.argtypes = (
-    [_vp, _vp, _vp, _vp, _vp, _c_int, _vp]
+    [_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp]
     + [_c_int] * 7
     + [_c_float] * 3
     + [_c_int] * 3
@@ -109,12 +109,14 @@ def attention_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, block
 
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
                            k_scale=1.0, v_scale=1.0, partition_size=0, workspace=None, num_blocks=None,
-                           stream=None):
+                           seq_order=None, stream=None):
     """out[s, h] = softmax(scale * K_s q[s, h]) V_s over each sequence's paged context.
 
     out, q: [S, H, d]; k_cache, v_cache: [NB, KVH, bs, d]; block_tables: int32
     [S, maxblk]; context_lens: int32 [S].  ``workspace``: a device uint8 tensor
     of at least ``attention_workspace_bytes(...)`` bytes (allocated here if None).
+    ``seq_order``: optional int32 [S] device tensor, the sequences longest first
+    (scheduling only; see ``BlockManager.longest_first``).
     """
     S, H, d = q.shape
     NB, KVH, bs, d2 = k_cache.shape
@@ -135,9 +137,12 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _ptr(workspace) if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if seq_order is not None and (seq_order.dtype != torch.int32 or seq_order.shape != (S,)
+                                  or not seq_order.is_contiguous()):
+        raise ValueError("seq_order must be a contiguous int32 [S] tensor")
     _check(_lib.pkv_paged_attention_decode(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1],
-        _ptr(context_lens), S, H, KVH, d, bs, NB if num_blocks is None else num_blocks, max_context_len,
+        _ptr(context_lens), _ptr(seq_order), S, H, KVH, d, bs, NB if num_blocks is None else num_blocks, max_context_len,
         float(scale), float(k_scale), float(v_scale), qd, kvd, partition_size, ws_ptr, ws_bytes,
         _stream(stream)), "pkv_paged_attention_decode")
     return out

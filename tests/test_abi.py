@@ -72,10 +72,9 @@ def test_attention_plan_choices(lib):
     # an explicit partition size -> fixed partitions
     assert _plan(lib, 8, 32, 8, 128, 16, 131072, 512, 2, 2) == (0, 1, 512, 256)
     assert _plan(lib, 4, 8, 2, 128, 16, 100, 0, 0, 0)[:2] == (0, 0)
-    # short contexts: one pass; the workspace only holds the longest-first sequence order
+    # short contexts: one pass, no workspace
     assert _plan(lib, 4, 8, 8, 64, 16, 64, 0, 0, 0) == (0, 0, 64, 1)
-    assert lib.pkv_attention_workspace_bytes(4, 8, 8, 64, 16, 64, 0, 0, 0) == 256
-    assert lib.pkv_attention_workspace_bytes(1, 8, 8, 64, 16, 64, 0, 0, 0) == 0
+    assert lib.pkv_attention_workspace_bytes(4, 8, 8, 64, 16, 64, 0, 0, 0) == 0
     assert lib.pkv_attention_workspace_bytes(2, 4, 4, 128, 16, 1000, 256, 1, 1) >= 2 * 4 * 4 * (128 + 2) * 4
     # slices: summary rows for two segments per slice and head, plus the block prefix
     ns = _plan(lib, 3, 4, 4, 128, 16, 1000, 0, 1, 1)[3]
@@ -99,14 +98,13 @@ def test_attention_plan_rejects(lib, args, status):
 
 def _decode(lib, num_seqs=2, H=4, KVH=4, d=128, bs=16, NB=8, max_ctx=64, ks=1.0, vs=1.0, qd=1, kvd=1, part=0,
             ws=None, ws_bytes=0, ptr=FAKE):
-    return lib.pkv_paged_attention_decode(ptr, FAKE, FAKE, FAKE, FAKE, 4, FAKE, num_seqs, H, KVH, d, bs, NB, max_ctx,
+    return lib.pkv_paged_attention_decode(ptr, FAKE, FAKE, FAKE, FAKE, 4, FAKE, None, num_seqs, H, KVH, d, bs, NB, max_ctx,
                                           ctypes.c_float(0.1), ctypes.c_float(ks), ctypes.c_float(vs), qd, kvd, part,
                                           ws, ws_bytes, None)
 
 
 def test_decode_host_checks(lib):
     assert _decode(lib, num_seqs=0) == 0                       # empty batch: nothing to do
-    assert _decode(lib) == -6                                  # one pass still needs the order workspace
     assert _decode(lib, H=6, KVH=4) == -3
     assert _decode(lib, part=20) == -5
     assert _decode(lib, max_ctx=1000, part=256) == -6           # needs a workspace

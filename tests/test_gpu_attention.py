@@ -253,3 +253,17 @@ def test_many_sequences_use_fixed_partitions(ops):
     assert ops.attention_plan(len(lens), 2, 2, 64, 16, max(lens), 0, ops.F16, ops.F16)[1] == 512
     out = case.run(partition_size=0)
     _check(case, out, "1100 sequences")
+
+
+@pytest.mark.parametrize("kind", ["mha", "gqa"])
+def test_sequence_order_only_schedules(ops, kind):
+    """Kernel-derived, host longest-first and an arbitrary permutation give identical bits."""
+    H, KVH, dt = (4, 4, "f16") if kind == "mha" else (16, 2, "bf16")
+    lens = tuple(int(x) for x in np.random.default_rng(16).integers(1, 1500, size=23))
+    w = W(S=len(lens), H=H, KVH=KVH, d=128, q=dt, kv=dt, lens=lens, seed=16)
+    case = DecodeCase(w, DEV)
+    base = case.run(partition_size=0)
+    _check(case, base, f"order {kind}")
+    for order in ("host", np.random.default_rng(17).permutation(len(lens)).astype(np.int32)):
+        out = case.run(partition_size=0, seq_order=order)
+        assert torch.equal(out.view(torch.int16), base.view(torch.int16))

@@ -39,9 +39,10 @@ def _decode_step(ops, w):
     slot_t = torch.tensor(slots, dtype=torch.int64, device=DEV)
     ops.reshape_and_cache(inp.k_new, inp.v_new, inp.k_cache, inp.v_cache, slot_t)
     out = torch.empty_like(inp.q)
+    order = torch.from_numpy(bm.longest_first(seqs)).to(DEV)       # as bench.py launches it
     ops.paged_attention_decode(out, inp.q, inp.k_cache, inp.v_cache, torch.from_numpy(tables).to(DEV),
                                torch.from_numpy(ctx).to(DEV), w.softmax_scale, int(ctx.max()),
-                               partition_size=w.partition_size)
+                               partition_size=w.partition_size, seq_order=order)
     torch.cuda.synchronize()
     return inp, tables, ctx, slots, k_before, v_before, out
 
