@@ -299,7 +299,7 @@ void attn_vector_kernel(AttnParams p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int row = lane / A::LPR;
   const int col = lane % A::LPR;
-  const uint32_t L = xcd_remap(blockIdx.x, p.total_wgs);
+  const uint32_t L = xcd_remap(blockIdx.x, p.total_wgs, p.xcd_chunk);
   typename A::State st;
 
   if (p.num_slices > 0) {

@@ -26,6 +26,9 @@ constexpr int kSingleMaxTokens = 256;    // contexts this short: one pass, no sp
 #ifndef PKV_LONGEST_FIRST
 #define PKV_LONGEST_FIRST 1
 #endif
+#ifndef PKV_PARTITION_XCD_CHUNK
+#define PKV_PARTITION_XCD_CHUNK 64   // fixed partitions: runs of 64 work ids per XCD
+#endif
 
 enum Mode { kSingle = 0, kPartitions = 1, kSlices = 2 };
 
@@ -59,6 +62,16 @@ int forced_path() {
   if (!strcmp(e, "vector")) return PKV_PATH_VECTOR;
   if (!strcmp(e, "mfma")) return PKV_PATH_MFMA;
   return -1;
+}
+
+// PKV_XCD_CHUNK=<n> overrides the XCD run length of every launch (tuning).
+int xcd_chunk_for(int mode) {
+  const char* e = getenv("PKV_XCD_CHUNK");
+  if (e && *e) {
+    const int v = atoi(e);
+    if (v >= 0 && v <= 4096) return v;
+  }
+  return mode == kPartitions ? PKV_PARTITION_XCD_CHUNK : 0;
 }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -245,6 +258,7 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
   p.v_scale = fp8 ? v_scale : 1.f;
   p.total_wgs = (uint32_t)(pl.mode == kSlices ? (size_t)pl.num_parts * pl.units
                                               : (size_t)num_seqs * pl.units * pl.num_parts);
+  p.xcd_chunk = (uint32_t)xcd_chunk_for(pl.mode);
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // start from a clean error state

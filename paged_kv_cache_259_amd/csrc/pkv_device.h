@@ -179,16 +179,17 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // while every XCD still receives an even mix of partitions.  A bijection on
 // [0, n); ids past the last whole round of 8*C keep their order.
 // ---------------------------------------------------------------------------
-#ifndef PKV_XCD_CHUNK
-#define PKV_XCD_CHUNK 0
-#endif
-__device__ __forceinline__ uint32_t xcd_remap(uint32_t i, uint32_t n) {
-  constexpr uint32_t X = 8, C = PKV_XCD_CHUNK;
-  if constexpr (C == 0) return i;
-  const uint32_t full = n / (X * C) * (X * C);
+// Workgroup -> logical work id.  The hardware deals consecutive workgroup ids
+// round-robin to the 8 XCDs (each with its own L2).  chunk == 0 keeps that
+// order; chunk C > 0 gives each XCD runs of C consecutive logical ids instead
+// (the tail that does not fill 8 * C ids keeps the hardware order).
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t i, uint32_t n, uint32_t chunk) {
+  constexpr uint32_t X = 8;
+  if (chunk == 0) return i;
+  const uint32_t full = n / (X * chunk) * (X * chunk);
   if (i >= full) return i;
   const uint32_t x = i % X, k = i / X;
-  return ((k / C) * X + x) * C + (k % C);
+  return ((k / chunk) * X + x) * chunk + (k % chunk);
 }
 
 // Logical work id -> (sequence, head unit, partition).  Partitions are the
@@ -376,6 +377,7 @@ struct AttnParams {
   float qk_scale;          // scale * log2(e) * k_scale
   float v_scale;
   uint32_t total_wgs;
+  uint32_t xcd_chunk;       // see xcd_remap
 };
 
 struct ReduceParams {

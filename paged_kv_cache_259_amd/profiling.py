@@ -1,0 +1,120 @@
+"""Summaries of rocprofv3 runs of bench.py (reads the result databases; no GPU).
+
+    python -m paged_kv_cache_259_amd.profiling trace DIR
+        per-kernel call count and durations from a ``--kernel-trace`` run.
+    python -m paged_kv_cache_259_amd.profiling counters FETCH_DIR WRITE_DIR --workload W --calibrate-copy N
+        HBM bytes per attention call from a ``--pmc FETCH_SIZE`` run and a
+        ``--pmc WRITE_SIZE`` run of ``bench.py --calibrate-copy N``.  The runs'
+        one copy_blocks call over N block pairs is a plain copy of known size
+        (N blocks read and N written in each pool); the counters' reading on it
+        gives the factor that turns each counter into bytes.  Writes the entry
+        for W into profiles/attention_traffic.json, keyed by the hash of the
+        attention kernels' sources, so bench.py reports it only while the
+        kernels are unchanged.
+"""
+
+import argparse
+import collections
+import glob
+import json
+import os
+import sqlite3
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _db(d):
+    found = glob.glob(os.path.join(d, "**", "*.db"), recursive=True)
+    if not found:
+        raise SystemExit(f"no rocprofv3 database under {d}")
+    return sqlite3.connect(found[0])
+
+
+def _short(name):
+    s = name.split("(")[0]
+    for p in ("void ", "pkv::"):
+        s = s.replace(p, "")
+    return s
+
+
+def trace(d, out=sys.stdout):
+    c = _db(d)
+    rows = c.execute("select name, count(*), avg(duration), min(duration), max(duration), sum(duration) "
+                     "from kernels group by name order by sum(duration) desc").fetchall()
+    tot = sum(r[5] for r in rows) or 1
+    print(f"{'kernel':64s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'total%':>7s}", file=out)
+    for name, n, avg, mn, mx, s in rows[:12]:
+        print(f"{_short(name)[:64]:64s} {n:6d} {avg / 1e3:9.2f} {mn / 1e3:9.2f} {mx / 1e3:9.2f} "
+              f"{100 * s / tot:7.2f}", file=out)
+
+
+def _counter(d, counter):
+    c = _db(d)
+    rows = c.execute("select kernel_name, grid_size, counter_name, value from counters_collection").fetchall()
+    agg = collections.defaultdict(list)
+    for k, g, n, v in rows:
+        if n == counter and "pkv" in k:
+            agg[(_short(k), g)].append(v)
+    return {k: sum(v) / len(v) for k, v in agg.items()}
+
+
+def counters(fetch_dir, write_dir, workload, n_pairs, out=sys.stdout):
+    sys.path.insert(0, ROOT)
+    import bench
+    from paged_kv_cache_259_amd import synth
+    w = synth.WORKLOADS[workload]
+    elt = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}[w.kv_dtype]
+    block_bytes = w.num_kv_heads * w.block_size * w.head_dim * elt
+    f = _counter(fetch_dir, "FETCH_SIZE")
+    wr = _counter(write_dir, "WRITE_SIZE")
+    copies = sorted((k for k in f if k[0] == "copy_blocks_kernel"), key=lambda k: -f[k])
+    if not copies:
+        raise SystemExit("no copy_blocks calibration dispatch in the FETCH_SIZE run")
+    cal = copies[0]
+    copy_bytes = 2 * n_pairs * block_bytes          # K and V pools, each read once and written once
+    fs, ws = copy_bytes / (f[cal] * 1024), copy_bytes / (wr[cal] * 1024)
+    print(f"calibration: copy_blocks of {n_pairs} block pairs ({copy_bytes / 1e9:.3f} GB read, same written): "
+          f"FETCH_SIZE {f[cal]:.1f} KiB (scale {fs:.4f}), WRITE_SIZE {wr[cal]:.1f} KiB (scale {ws:.4f})", file=out)
+    total_r = total_w = 0.0
+    for k in sorted(k for k in f if k[0].startswith("attn_")):
+        rb, wb = f[k] * 1024 * fs, wr.get(k, 0.0) * 1024 * ws
+        total_r += rb
+        total_w += wb
+        print(f"{k[0][:58]:58s} grid {k[1]:8d}  FETCH_SIZE {f[k]:12.1f} KiB -> {rb / 1e6:9.2f} MB read;  "
+              f"WRITE_SIZE {wr.get(k, 0.0):10.1f} KiB -> {wb / 1e6:7.2f} MB written", file=out)
+    print(f"attention call total: {total_r / 1e6:.2f} MB read + {total_w / 1e6:.2f} MB written = "
+          f"{(total_r + total_w) / 1e6:.2f} MB", file=out)
+    path = os.path.join(ROOT, "profiles", "attention_traffic.json")
+    table = {}
+    if os.path.exists(path):
+        with open(path) as fh:
+            table = json.load(fh)
+    table[workload] = {"kernel_source_hash": bench.kernel_source_hash(), "bytes_per_call": int(total_r + total_w),
+                       "read_bytes": int(total_r), "write_bytes": int(total_w),
+                       "fetch_scale": round(fs, 5), "write_scale": round(ws, 5),
+                       "summary": f"profiles/attention_traffic_{workload}.md"}
+    with open(path, "w") as fh:
+        json.dump(table, fh, indent=1)
+        fh.write("\n")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("dir")
+    c = sub.add_parser("counters")
+    c.add_argument("fetch_dir")
+    c.add_argument("write_dir")
+    c.add_argument("--workload", required=True)
+    c.add_argument("--calibrate-copy", type=int, required=True)
+    a = ap.parse_args()
+    if a.cmd == "trace":
+        trace(a.dir)
+    else:
+        counters(a.fetch_dir, a.write_dir, a.workload, a.calibrate_copy)
+
+
+if __name__ == "__main__":
+    main()
