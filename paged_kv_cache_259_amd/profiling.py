@@ -93,7 +93,7 @@ def counters(fetch_dir, write_dir, workload, n_pairs, out=sys.stdout):
     table[workload] = {"kernel_source_hash": bench.kernel_source_hash(), "bytes_per_call": int(total_r + total_w),
                        "read_bytes": int(total_r), "write_bytes": int(total_w),
                        "fetch_scale": round(fs, 5), "write_scale": round(ws, 5),
-                       "summary": f"profiles/attention_traffic_{workload}.md"}
+                       "summary": f"profiles/paged_attention_decode_{workload}.md"}
     with open(path, "w") as fh:
         json.dump(table, fh, indent=1)
         fh.write("\n")
