@@ -7,9 +7,13 @@ resident in HBM: reshape_and_cache writes every sequence's new key/value into
 the slot the block manager gave it, then paged_attention_decode attends over
 each sequence's paged context (the split-context reduce included when the plan
 uses one).  The block manager's host bookkeeping (tables, slots, the
-longest-first sequence order) is built before the timed region.  copy_blocks has no work in this workload (no block is shared); it is
-timed separately on the copy-on-write pairs of the shared-prefix workload and
-reported under "components".
+longest-first sequence order) is built before the timed region.
+
+Reported separately under "components" (not part of the step):
+* copy_blocks on copy-on-write pairs shaped like the shared-prefix workload
+  (this workload shares no block);
+* swap_blocks: every block of the 16 most recent sequences swapped out to a
+  pinned host pool and back in (the preemption path), GB/s over the host link.
 
 Prints one JSON line:
 * value      algorithmic KV bytes read per step / step time (GB/s), the step
@@ -219,6 +223,30 @@ def main():
     copy_us = c0.elapsed_time(c1) / 20 * 1e3
     block_bytes = sp.num_heads * sp.block_size * sp.head_dim
 
+    # ---- swap_blocks: the 16 most recent sequences preempted whole (device -> pinned host) and back
+    n_sw = min(16, w.num_seqs)
+    sw_blocks = np.unique(np.concatenate([tables_np[s, : -(-int(ctx_np[s]) // w.block_size)]
+                                          for s in seqs[-n_sw:]])).astype(np.int64)
+    host_k = torch.empty((len(sw_blocks),) + tuple(inp.k_cache.shape[1:]), dtype=inp.k_cache.dtype, pin_memory=True)
+    host_v = torch.empty((len(sw_blocks),) + tuple(inp.k_cache.shape[1:]), dtype=inp.k_cache.dtype, pin_memory=True)
+    out_map = torch.from_numpy(np.stack([sw_blocks, np.arange(len(sw_blocks))], 1)).to(dev)
+    in_map = torch.from_numpy(np.stack([np.arange(len(sw_blocks)), sw_blocks], 1)).to(dev)   # back in place
+    sw_bytes = 2 * len(sw_blocks) * inp.k_cache[0].numel() * inp.k_cache.element_size()
+    ops.swap_blocks(inp.k_cache, inp.v_cache, host_k, host_v, out_map, stream=stream)
+    ops.swap_blocks(host_k, host_v, inp.k_cache, inp.v_cache, in_map, stream=stream)
+    sw_ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    t_out, t_in = [], []
+    for _ in range(5):
+        sw_ev[0].record(stream)
+        ops.swap_blocks(inp.k_cache, inp.v_cache, host_k, host_v, out_map, stream=stream)
+        sw_ev[1].record(stream)
+        ops.swap_blocks(host_k, host_v, inp.k_cache, inp.v_cache, in_map, stream=stream)
+        sw_ev[2].record(stream)
+        torch.cuda.synchronize()
+        t_out.append(sw_ev[0].elapsed_time(sw_ev[1]))
+        t_in.append(sw_ev[1].elapsed_time(sw_ev[2]))
+    swap_out_ms, swap_in_ms = float(np.median(t_out)), float(np.median(t_in))
+
     if args.calibrate_copy:
         nb = args.calibrate_copy
         big_k = torch.zeros((2 * nb, w.num_kv_heads, w.block_size, w.head_dim), dtype=inp.k_cache.dtype, device=dev)
@@ -264,6 +292,10 @@ def main():
             "copy_blocks_pairs": n_pairs,
             "copy_blocks_gbps": round(2 * 2 * n_pairs * block_bytes / (copy_us * 1e-6) / 1e9, 1),
             "wall_ms_per_step": round(wall / K * 1e3, 4),
+            "swap_blocks": {"blocks": int(len(sw_blocks)), "sequences": n_sw, "bytes": int(sw_bytes),
+                            "out_us": round(swap_out_ms * 1e3, 1), "in_us": round(swap_in_ms * 1e3, 1),
+                            "out_gbps": round(sw_bytes / (swap_out_ms * 1e-3) / 1e9, 1),
+                            "in_gbps": round(sw_bytes / (swap_in_ms * 1e-3) / 1e9, 1)},
         },
         "roofline": {
             "bound": "hbm",

@@ -1,7 +1,7 @@
 /*
  * pkv.h -- C ABI of the paged-KV decode library for AMD MI355X (gfx950).
  *
- * Three data-path calls and their helpers.  The library is stateless: the host
+ * Four data-path calls and their helpers.  The library is stateless: the host
  * owns the block bookkeeping (which physical block holds which tokens,
  * reference counts, copy-on-write decisions); the library moves bytes and
  * attends.  Sources cited (page title, then section):
@@ -61,6 +61,8 @@ extern "C" {
 #define PKV_ERR_WORKSPACE (-6)      /* workspace missing or smaller than required           */
 #define PKV_ERR_LAUNCH (-7)         /* HIP reported a launch error                          */
 #define PKV_ERR_SCALE (-8)          /* an FP8 scale is not a positive finite number         */
+#define PKV_ERR_MEMORY_KIND (-9)    /* a buffer is neither device memory nor pinned host     */
+                                    /* memory the device can address                         */
 
 /* attention kernel families reported by pkv_attention_plan */
 #define PKV_PATH_VECTOR 0  /* per-query-head vector kernel (wave shuffles, no MFMA)  */
@@ -203,6 +205,37 @@ int pkv_reshape_and_cache(const void* key, const void* value,
 int pkv_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, int num_pairs,
                     int num_kv_heads, int head_dim, int block_size, int num_blocks,
                     int kv_dtype, void* stream);
+
+/*
+ * pkv_swap_blocks -- whole-block copies between two pools, for preemption by
+ * swapping ([KVpag]: when physical blocks run out, the most recent requests are
+ * preempted, all or nothing, and their blocks are recovered by swapping them to
+ * CPU memory and back).  The host decides the pairs (which GPU block goes to
+ * which host block, and back); this call moves the bytes in one launch.
+ *
+ * For each pair p = (src, dst):
+ *   dst_k[dst] = src_k[src] and dst_v[dst] = src_v[src]
+ * whole blocks (every kv head, every slot, raw bytes), the two pools having the
+ * same block shape [num_kv_heads][block_size][head_dim] of kv_dtype.
+ *
+ * src_k, src_v   source pools, [src_num_blocks] blocks each.
+ * dst_k, dst_v   destination pools, [dst_num_blocks] blocks each; must not
+ *                overlap the source pools.
+ * Each pool, and block_mapping, is either device memory or pinned host memory
+ * (hipHostMalloc, e.g. torch's pin_memory=True) that the device addresses over
+ * the host link; the library looks each pointer up with the HIP runtime and
+ * returns PKV_ERR_MEMORY_KIND, launching nothing, for any other memory
+ * (pageable host memory).  A swap-out is device -> host, a swap-in host -> device.
+ * block_mapping  [num_pairs][2] int64 (src, dst).  Destination ids must be
+ *                distinct.  Pairs with src outside [0, src_num_blocks) or dst
+ *                outside [0, dst_num_blocks) are skipped.
+ * num_pairs == 0 is a no-op returning PKV_OK.
+ * The host must not touch a host pool until the stream has passed this call.
+ */
+int pkv_swap_blocks(const void* src_k, const void* src_v, int src_num_blocks,
+                    void* dst_k, void* dst_v, int dst_num_blocks,
+                    const int64_t* block_mapping, int num_pairs,
+                    int num_kv_heads, int head_dim, int block_size, int kv_dtype, void* stream);
 
 #ifdef __cplusplus
 }

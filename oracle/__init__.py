@@ -44,6 +44,7 @@ from .paged_attention_ref import (  # noqa: F401
     attend_one_ref,
     reshape_ref,
     copy_ref,
+    swap_ref,
     partial_state_ref,
     merge_partials_ref,
 )

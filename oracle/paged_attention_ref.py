@@ -205,3 +205,20 @@ def copy_ref(k_pool, v_pool, pairs):
         k_new[dst] = k_pool[src]
         v_new[dst] = v_pool[src]
     return k_new, v_new
+
+
+def swap_ref(src_k, src_v, dst_k, dst_v, pairs):
+    """Block copies between two pools (swap-out to host memory, swap-in back).
+
+    [KVpag]: when physical blocks run out, the most recent requests are
+    preempted whole and their blocks are recovered by swapping them to CPU
+    memory (and later back).  For each (src, dst): destination block dst becomes
+    a copy of source block src (all kv heads, all slots); the source pools are
+    not changed.  Returns the new destination pools.
+    """
+    k_new = np.array(dst_k, copy=True)
+    v_new = np.array(dst_v, copy=True)
+    for src, dst in np.asarray(pairs).reshape(-1, 2).tolist():
+        k_new[dst] = src_k[src]
+        v_new[dst] = src_v[src]
+    return k_new, v_new

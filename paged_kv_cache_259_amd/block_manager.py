@@ -19,7 +19,12 @@ physical block holds which tokens is host work, done here:
   chuỗi").  Sequences are served in the order the caller asks; the last holder
   of a shared block writes in place because its count has dropped to 1.
 
-Running out of blocks raises ``OutOfBlocks``; no preemption is attempted here.
+Running out of blocks raises ``OutOfBlocks``.  Preemption is the caller's
+decision; ``preemption_victims`` gives the order the pages describe (requests
+served first come, first served; the most recent ones are preempted first, all
+or nothing -- [KVpag]), and ``swap_out`` / ``swap_in`` move a preempted group's
+blocks to a second, host-side pool and back, returning the (src, dst) pairs for
+``swap_blocks``.
 """
 
 from collections import deque
@@ -32,8 +37,8 @@ class OutOfBlocks(RuntimeError):
 
 
 class BlockManager:
-    def __init__(self, num_blocks, block_size, free_list=None):
-        if num_blocks <= 0 or block_size <= 0:
+    def __init__(self, num_blocks, block_size, free_list=None, num_host_blocks=0):
+        if num_blocks <= 0 or block_size <= 0 or num_host_blocks < 0:
             raise ValueError("num_blocks and block_size must be positive")
         self.num_blocks = int(num_blocks)
         self.block_size = int(block_size)
@@ -44,6 +49,11 @@ class BlockManager:
         self.refcount = np.zeros(self.num_blocks, dtype=np.int64)
         self.tables = {}
         self.lengths = {}
+        # host-side pool for swapped-out sequences
+        self.num_host_blocks = int(num_host_blocks)
+        self._host_free = deque(range(self.num_host_blocks))
+        self.host_refcount = np.zeros(self.num_host_blocks, dtype=np.int64)
+        self.swapped = {}          # seq -> host block table (lengths stay in self.lengths)
 
     # -- allocation ---------------------------------------------------------
     def _take(self):
@@ -102,9 +112,95 @@ class BlockManager:
             self.refcount[b] += 1
 
     def free_sequence(self, seq):
-        for b in self.tables.pop(seq):
-            self._release(b)
+        if seq in self.swapped:
+            for h in self.swapped.pop(seq):
+                self.host_refcount[h] -= 1
+                if self.host_refcount[h] == 0:
+                    self._host_free.append(h)
+        else:
+            for b in self.tables.pop(seq):
+                self._release(b)
         del self.lengths[seq]
+
+    # -- preemption by swapping -----------------------------------------------
+    @staticmethod
+    def preemption_victims(groups_by_arrival, blocks_needed, blocks_held, num_free):
+        """Groups to preempt, most recent arrival first, until ``blocks_needed`` blocks are free.
+
+        ``groups_by_arrival``: running groups in arrival order (each a tuple of
+        sequences that share blocks, e.g. the samples of one prompt);
+        ``blocks_held(group)``: GPU blocks freed by preempting that group.  A
+        group is preempted whole or not at all.  Raises ``OutOfBlocks`` when even
+        preempting every group would not free enough.
+        """
+        victims, free = [], num_free
+        for g in reversed(list(groups_by_arrival)):
+            if free >= blocks_needed:
+                break
+            victims.append(g)
+            free += blocks_held(g)
+        if free < blocks_needed:
+            raise OutOfBlocks(f"{blocks_needed} blocks needed, at most {free} can be freed")
+        return victims
+
+    def group_blocks(self, seqs):
+        """Distinct GPU blocks held by ``seqs``; raises if one is shared with a sequence outside."""
+        seqs = list(seqs)
+        holders = {}
+        for s in seqs:
+            for b in self.tables[s]:
+                holders[b] = holders.get(b, 0) + 1
+        for b, n in holders.items():
+            if self.refcount[b] != n:
+                raise ValueError(f"block {b} is shared with a sequence outside the group")
+        return holders
+
+    def swap_out(self, seqs):
+        """Move every block of the group ``seqs`` to the host pool.
+
+        Returns ``(gpu_block, host_block)`` pairs, one per distinct block (a block
+        shared inside the group is copied once and stays shared on the host).
+        The GPU blocks return to the free list.
+        """
+        seqs = list(seqs)
+        holders = self.group_blocks(seqs)
+        if len(holders) > len(self._host_free):
+            raise OutOfBlocks("no room in the host pool")
+        to_host = {}
+        for b in holders:                       # first-use order of the group's tables
+            h = self._host_free.popleft()
+            to_host[b] = h
+            self.host_refcount[h] = holders[b]
+        for s in seqs:
+            self.swapped[s] = [to_host[b] for b in self.tables.pop(s)]
+        for b in holders:
+            self.refcount[b] = 0
+            self._free.append(b)
+        return list(to_host.items())
+
+    def swap_in(self, seqs):
+        """Bring the swapped-out group ``seqs`` back; returns ``(host_block, gpu_block)`` pairs."""
+        seqs = list(seqs)
+        holders = {}
+        for s in seqs:
+            for h in self.swapped[s]:
+                holders[h] = holders.get(h, 0) + 1
+        for h, n in holders.items():
+            if self.host_refcount[h] != n:
+                raise ValueError(f"host block {h} is shared with a sequence outside the group")
+        if len(holders) > len(self._free):
+            raise OutOfBlocks("not enough free GPU blocks to swap in")
+        to_gpu = {}
+        for h in holders:
+            b = self._take()
+            self.refcount[b] = holders[h]
+            to_gpu[h] = b
+        for s in seqs:
+            self.tables[s] = [to_gpu[h] for h in self.swapped.pop(s)]
+        for h in holders:
+            self.host_refcount[h] = 0
+            self._host_free.append(h)
+        return list(to_gpu.items())
 
     # -- views for the kernels ---------------------------------------------
     def block_table_array(self, seqs, max_blocks_per_seq):

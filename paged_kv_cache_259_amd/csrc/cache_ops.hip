@@ -1,4 +1,5 @@
-// cache_ops.hip -- the two data-movement kernels of the paged cache.
+// cache_ops.hip -- the data-movement kernels of the paged cache and their C entry points
+// (pkv_reshape_and_cache, pkv_copy_blocks, pkv_swap_blocks; include/pkv.h).
 //
 // reshape_and_cache: scatter each new token's key/value rows into the slot the
 //   host chose ("PagedAttention", Ultralytics glossary, section "Cách phân trang
@@ -11,6 +12,9 @@
 //   into a shared block first gets a fresh block holding a copy).  A block of
 //   every kv head is one contiguous run of num_kv_heads * bs * head_dim
 //   elements, so a pair is two flat 16-byte-vector copies (K and V).
+// swap_blocks: the same copy between a device pool and a pinned host pool
+//   (same page and section: preempted requests' blocks are swapped out to CPU
+//   memory and back in).
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -125,37 +129,152 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
 }
 
 struct CopyParams {
-  char* k_cache;
-  char* v_cache;
+  const char* src_k;
+  const char* src_v;
+  char* dst_k;
+  char* dst_v;
   const int64_t* pairs;
   int64_t block_bytes;
-  int num_blocks;
+  int src_blocks;
+  int dst_blocks;
   int wgs_per_block;
 };
 
+// Whole blocks, K and V, 16 bytes per thread.  Serves copy_blocks (one pool) and
+// swap_blocks (a device pool and a pinned host pool, either way round).
 __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyParams p) {
   const int pair = blockIdx.x / p.wgs_per_block;
   const int64_t chunk = (int64_t)(blockIdx.x - pair * p.wgs_per_block) * 256 + threadIdx.x;
   if (chunk * 16 >= p.block_bytes) return;
   const int64_t src = p.pairs[2 * pair];
   const int64_t dst = p.pairs[2 * pair + 1];
-  if (src < 0 || src >= p.num_blocks || dst < 0 || dst >= p.num_blocks) return;
+  if (src < 0 || src >= p.src_blocks || dst < 0 || dst >= p.dst_blocks) return;
   const int64_t so = src * p.block_bytes + chunk * 16;
   const int64_t dof = dst * p.block_bytes + chunk * 16;
-  const uint4 k = *reinterpret_cast<const uint4*>(p.k_cache + so);
-  const uint4 v = *reinterpret_cast<const uint4*>(p.v_cache + so);
-  *reinterpret_cast<uint4*>(p.k_cache + dof) = k;
-  *reinterpret_cast<uint4*>(p.v_cache + dof) = v;
+  const uint4 k = *reinterpret_cast<const uint4*>(p.src_k + so);
+  const uint4 v = *reinterpret_cast<const uint4*>(p.src_v + so);
+  *reinterpret_cast<uint4*>(p.dst_k + dof) = k;
+  *reinterpret_cast<uint4*>(p.dst_v + dof) = v;
 }
 
-hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int num_pairs,
-                              int64_t block_bytes, int num_blocks, hipStream_t stream) {
+hipError_t launch_copy_blocks(const void* src_k, const void* src_v, int src_blocks, void* dst_k, void* dst_v,
+                              int dst_blocks, const int64_t* pairs, int num_pairs, int64_t block_bytes,
+                              hipStream_t stream) {
   const int64_t chunks = block_bytes / 16;
   const int wgs = (int)((chunks + 255) / 256);
-  CopyParams p{reinterpret_cast<char*>(k_cache), reinterpret_cast<char*>(v_cache), pairs, block_bytes,
-               num_blocks, wgs};
+  CopyParams p{reinterpret_cast<const char*>(src_k), reinterpret_cast<const char*>(src_v),
+               reinterpret_cast<char*>(dst_k), reinterpret_cast<char*>(dst_v), pairs, block_bytes,
+               src_blocks, dst_blocks, wgs};
   hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)((int64_t)num_pairs * wgs)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace pkv
+
+using namespace pkv;
+
+namespace {
+
+// The address a kernel uses for p: p itself for device memory, the runtime's
+// device-side address for pinned host memory, NULL for anything else (pageable
+// host memory, unknown pointers).  Clears the error the query leaves behind.
+static void* device_address(void* p) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (attr.type == hipMemoryTypeDevice) return p;
+  if (attr.type == hipMemoryTypeHost) {
+    void* d = nullptr;
+    if (hipHostGetDevicePointer(&d, p, 0) != hipSuccess || d == nullptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    return d;
+  }
+  return nullptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                          const int64_t* slot_mapping, int num_tokens, int num_kv_heads, int head_dim,
+                          int block_size, int num_blocks, int src_dtype, int kv_dtype, float k_scale, float v_scale,
+                          void* stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return PKV_ERR_BAD_SIZE;
+  if (src_dtype != PKV_F32 && src_dtype != PKV_F16 && src_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  if (kv_dtype != src_dtype && kv_dtype != PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;
+  if (head_dim % 16 != 0 || head_dim > 1024) return PKV_ERR_UNSUPPORTED;
+  if (kv_dtype == PKV_FP8_E4M3 && !(good_scale(k_scale) && good_scale(v_scale))) return PKV_ERR_SCALE;
+  if ((double)num_tokens * num_kv_heads * head_dim / 4.0 > 2147483647.0 * 256.0) return PKV_ERR_BAD_SIZE;
+  if (num_tokens == 0) return PKV_OK;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PKV_ERR_NULL_POINTER;
+  if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  return launch_status(launch_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, num_tokens,
+                                                     num_kv_heads, head_dim, block_size, num_blocks, src_dtype,
+                                                     kv_dtype, k_scale, v_scale,
+                                                     reinterpret_cast<hipStream_t>(stream)));
+}
+
+int pkv_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, int num_pairs, int num_kv_heads,
+                    int head_dim, int block_size, int num_blocks, int kv_dtype, void* stream) {
+  if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return PKV_ERR_BAD_SIZE;
+  const int eb = dtype_bytes(kv_dtype);
+  if (eb == 0) return PKV_ERR_UNSUPPORTED;
+  const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * eb;
+  if (block_bytes % 16 != 0) return PKV_ERR_UNSUPPORTED;
+  const int64_t wgs = (block_bytes / 16 + 255) / 256;
+  if ((double)num_pairs * wgs > 2147483647.0) return PKV_ERR_BAD_SIZE;
+  if (num_pairs == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !block_mapping) return PKV_ERR_NULL_POINTER;
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  return launch_status(launch_copy_blocks(k_cache, v_cache, num_blocks, k_cache, v_cache, num_blocks,
+                                               block_mapping, num_pairs, block_bytes,
+                                               reinterpret_cast<hipStream_t>(stream)));
+}
+
+int pkv_swap_blocks(const void* src_k, const void* src_v, int src_num_blocks, void* dst_k, void* dst_v,
+                    int dst_num_blocks, const int64_t* block_mapping, int num_pairs, int num_kv_heads,
+                    int head_dim, int block_size, int kv_dtype, void* stream) {
+  if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || src_num_blocks <= 0 ||
+      dst_num_blocks <= 0)
+    return PKV_ERR_BAD_SIZE;
+  const int eb = dtype_bytes(kv_dtype);
+  if (eb == 0) return PKV_ERR_UNSUPPORTED;
+  const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * eb;
+  if (block_bytes % 16 != 0) return PKV_ERR_UNSUPPORTED;
+  const int64_t wgs = (block_bytes / 16 + 255) / 256;
+  if ((double)num_pairs * wgs > 2147483647.0) return PKV_ERR_BAD_SIZE;
+  if (num_pairs == 0) return PKV_OK;
+  if (!src_k || !src_v || !dst_k || !dst_v || !block_mapping) return PKV_ERR_NULL_POINTER;
+  const char* sk = static_cast<const char*>(src_k);
+  const char* sv = static_cast<const char*>(src_v);
+  const char* dk = static_cast<const char*>(dst_k);
+  const char* dv = static_cast<const char*>(dst_v);
+  const int64_t sbytes = src_num_blocks * block_bytes, dbytes = dst_num_blocks * block_bytes;
+  auto overlap = [](const char* a, int64_t na, const char* b, int64_t nb) { return a < b + nb && b < a + na; };
+  if (overlap(sk, sbytes, dk, dbytes) || overlap(sk, sbytes, dv, dbytes) || overlap(sv, sbytes, dk, dbytes) ||
+      overlap(sv, sbytes, dv, dbytes))
+    return PKV_ERR_BAD_SIZE;
+  void* a[5] = {const_cast<void*>(src_k), const_cast<void*>(src_v), dst_k, dst_v,
+                const_cast<int64_t*>(block_mapping)};
+  for (void*& x : a) {
+    x = device_address(x);
+    if (!x) return PKV_ERR_MEMORY_KIND;
+  }
+  for (int i = 0; i < 4; ++i)
+    if (!aligned16(a[i])) return PKV_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  return launch_status(launch_copy_blocks(a[0], a[1], src_num_blocks, a[2], a[3], dst_num_blocks,
+                                               static_cast<const int64_t*>(a[4]), num_pairs, block_bytes,
+                                               reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

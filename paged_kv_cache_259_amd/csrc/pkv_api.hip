@@ -1,5 +1,6 @@
-// pkv_api.hip -- the C ABI declared in include/pkv.h: host-side argument
-// checks, the choice of kernel family and context partitioning, and launches.
+// pkv_api.hip -- the attention half of the C ABI declared in include/pkv.h:
+// host-side argument checks, the choice of kernel family and launch shape, and
+// launches; plus the status strings and version.
 // Nothing here allocates, frees or synchronises.
 #include <math.h>
 #include <stdlib.h>
@@ -44,17 +45,6 @@ struct Plan {
   size_t ws_bytes;     // workspace needed (0 for a single pass)
 };
 
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
-int dtype_bytes(int dt) {
-  switch (dt) {
-    case PKV_F32: return 4;
-    case PKV_F16: case PKV_BF16: return 2;
-    case PKV_FP8_E4M3: return 1;
-  }
-  return 0;
-}
-
 // PKV_ATTN_PATH=vector forces the vector family; =mfma asks for the MFMA family.
 int forced_path() {
   const char* e = getenv("PKV_ATTN_PATH");
@@ -82,7 +72,7 @@ int make_plan(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int b
       max_context_len < 0)
     return PKV_ERR_BAD_SIZE;
   if (num_heads % num_kv_heads != 0) return PKV_ERR_HEAD_GROUPING;
-  if (dtype_bytes(q_dtype) == 0 || q_dtype == PKV_FP8_E4M3 || dtype_bytes(kv_dtype) == 0) return PKV_ERR_UNSUPPORTED;
+  if (pkv::dtype_bytes(q_dtype) == 0 || q_dtype == PKV_FP8_E4M3 || pkv::dtype_bytes(kv_dtype) == 0) return PKV_ERR_UNSUPPORTED;
   if (partition_size < 0 || (partition_size > 0 && partition_size % block_size != 0)) return PKV_ERR_PARTITION;
   const int group = num_heads / num_kv_heads;
   const bool vec_ok = pkv::vector_supported(q_dtype, kv_dtype, head_dim, block_size);
@@ -148,10 +138,6 @@ int make_plan(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int b
   return PKV_OK;
 }
 
-int launch_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH; }
-
-bool good_scale(float s) { return isfinite(s) && s > 0.f; }
-
 }  // namespace
 
 extern "C" {
@@ -167,6 +153,7 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_WORKSPACE: return "workspace missing or smaller than pkv_attention_workspace_bytes()";
     case PKV_ERR_LAUNCH: return "HIP kernel launch failed";
     case PKV_ERR_SCALE: return "FP8 scale must be a positive finite number";
+    case PKV_ERR_MEMORY_KIND: return "buffer is neither device memory nor pinned host memory";
   }
   return "unknown status";
 }
@@ -208,11 +195,11 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
   if (st != PKV_OK) return st;
   if (max_blocks_per_seq <= 0 || num_blocks <= 0) return PKV_ERR_BAD_SIZE;
   if (!isfinite(scale)) return PKV_ERR_BAD_SIZE;
-  if (kv_dtype == PKV_FP8_E4M3 && !(good_scale(k_scale) && good_scale(v_scale))) return PKV_ERR_SCALE;
+  if (kv_dtype == PKV_FP8_E4M3 && !(pkv::good_scale(k_scale) && pkv::good_scale(v_scale))) return PKV_ERR_SCALE;
   if (num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PKV_ERR_NULL_POINTER;
-  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_UNSUPPORTED;
-  if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes || !aligned16(workspace)))
+  if (!pkv::aligned16(out) || !pkv::aligned16(q) || !pkv::aligned16(k_cache) || !pkv::aligned16(v_cache)) return PKV_ERR_UNSUPPORTED;
+  if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes || !pkv::aligned16(workspace)))
     return PKV_ERR_WORKSPACE;
 
   pkv::AttnParams p{};
@@ -281,46 +268,7 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
     r.ctx_cap = p.ctx_cap;
     e = pkv::launch_attention_reduce(r, q_dtype, head_dim, s);
   }
-  return launch_status(e);
-}
-
-int pkv_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
-                          const int64_t* slot_mapping, int num_tokens, int num_kv_heads, int head_dim,
-                          int block_size, int num_blocks, int src_dtype, int kv_dtype, float k_scale, float v_scale,
-                          void* stream) {
-  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
-    return PKV_ERR_BAD_SIZE;
-  if (src_dtype != PKV_F32 && src_dtype != PKV_F16 && src_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
-  if (kv_dtype != src_dtype && kv_dtype != PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;
-  if (head_dim % 16 != 0 || head_dim > 1024) return PKV_ERR_UNSUPPORTED;
-  if (kv_dtype == PKV_FP8_E4M3 && !(good_scale(k_scale) && good_scale(v_scale))) return PKV_ERR_SCALE;
-  if ((double)num_tokens * num_kv_heads * head_dim / 4.0 > 2147483647.0 * 256.0) return PKV_ERR_BAD_SIZE;
-  if (num_tokens == 0) return PKV_OK;
-  if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PKV_ERR_NULL_POINTER;
-  if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_UNSUPPORTED;
-  (void)hipGetLastError();
-  return launch_status(pkv::launch_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, num_tokens,
-                                                     num_kv_heads, head_dim, block_size, num_blocks, src_dtype,
-                                                     kv_dtype, k_scale, v_scale,
-                                                     reinterpret_cast<hipStream_t>(stream)));
-}
-
-int pkv_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, int num_pairs, int num_kv_heads,
-                    int head_dim, int block_size, int num_blocks, int kv_dtype, void* stream) {
-  if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
-    return PKV_ERR_BAD_SIZE;
-  const int eb = dtype_bytes(kv_dtype);
-  if (eb == 0) return PKV_ERR_UNSUPPORTED;
-  const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * eb;
-  if (block_bytes % 16 != 0) return PKV_ERR_UNSUPPORTED;
-  const int64_t wgs = (block_bytes / 16 + 255) / 256;
-  if ((double)num_pairs * wgs > 2147483647.0) return PKV_ERR_BAD_SIZE;
-  if (num_pairs == 0) return PKV_OK;
-  if (!k_cache || !v_cache || !block_mapping) return PKV_ERR_NULL_POINTER;
-  if (!aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_UNSUPPORTED;
-  (void)hipGetLastError();
-  return launch_status(pkv::launch_copy_blocks(k_cache, v_cache, block_mapping, num_pairs, block_bytes, num_blocks,
-                                               reinterpret_cast<hipStream_t>(stream)));
+  return pkv::launch_status(e);
 }
 
 }  // extern "C"

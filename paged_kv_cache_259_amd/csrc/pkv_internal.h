@@ -2,11 +2,26 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
+#include "pkv.h"
 #include "pkv_device.h"
 
 namespace pkv {
+
+// Host-side helpers of the C-ABI layer.
+inline int dtype_bytes(int dt) {
+  switch (dt) {
+    case PKV_F32: return 4;
+    case PKV_F16: case PKV_BF16: return 2;
+    case PKV_FP8_E4M3: return 1;
+  }
+  return 0;
+}
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool good_scale(float s) { return isfinite(s) && s > 0.f; }
+inline int launch_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH; }
 
 bool vector_supported(int q_dtype, int kv_dtype, int head_dim, int block_size);
 bool mfma_supported(int q_dtype, int kv_dtype, int head_dim, int block_size, int group);
@@ -20,7 +35,8 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
                                     const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
                                     int head_dim, int block_size, int num_blocks, int src_dtype, int kv_dtype,
                                     float k_scale, float v_scale, hipStream_t stream);
-hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int num_pairs,
-                              int64_t block_bytes, int num_blocks, hipStream_t stream);
+hipError_t launch_copy_blocks(const void* src_k, const void* src_v, int src_blocks, void* dst_k, void* dst_v,
+                              int dst_blocks, const int64_t* pairs, int num_pairs, int64_t block_bytes,
+                              hipStream_t stream);
 
 }  // namespace pkv

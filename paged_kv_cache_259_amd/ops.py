@@ -46,10 +46,12 @@ _lib.pkv_reshape_and_cache.restype = _c_int
 _lib.pkv_reshape_and_cache.argtypes = [_vp] * 5 + [_c_int] * 7 + [_c_float] * 2 + [_vp]
 _lib.pkv_copy_blocks.restype = _c_int
 _lib.pkv_copy_blocks.argtypes = [_vp, _vp, _vp] + [_c_int] * 6 + [_vp]
+_lib.pkv_swap_blocks.restype = _c_int
+_lib.pkv_swap_blocks.argtypes = [_vp, _vp, _c_int, _vp, _vp, _c_int, _vp] + [_c_int] * 5 + [_vp]
 
 EXPORTED_SYMBOLS = (
     "pkv_status_string", "pkv_version", "pkv_attention_plan", "pkv_attention_workspace_bytes",
-    "pkv_paged_attention_decode", "pkv_reshape_and_cache", "pkv_copy_blocks",
+    "pkv_paged_attention_decode", "pkv_reshape_and_cache", "pkv_copy_blocks", "pkv_swap_blocks",
 )
 
 
@@ -177,6 +179,34 @@ def copy_blocks(k_cache, v_cache, block_mapping, stream=None):
     _check(_lib.pkv_copy_blocks(
         _ptr(k_cache), _ptr(v_cache), _ptr(block_mapping), block_mapping.shape[0], KVH, d, bs, NB,
         dtype_code(k_cache.dtype), _stream(stream)), "pkv_copy_blocks")
+
+
+def swap_blocks(src_k, src_v, dst_k, dst_v, block_mapping, stream=None):
+    """dst_k[dst] = src_k[src] (and V) for each (src, dst) row of block_mapping, between two pools.
+
+    One pool is typically on the GPU and the other a pinned CPU tensor
+    (``pin_memory=True``): swap-out is GPU -> CPU, swap-in CPU -> GPU.
+    ``block_mapping`` (int64 [num_pairs, 2]) may be on the GPU or pinned.  The
+    copy is enqueued on the stream: keep pinned tensors alive, and do not read a
+    CPU pool, until the stream has passed the call.
+    """
+    NB_s, KVH, bs, d = src_k.shape
+    NB_d = dst_k.shape[0]
+    if tuple(src_v.shape) != tuple(src_k.shape) or tuple(dst_v.shape) != tuple(dst_k.shape) \
+            or tuple(dst_k.shape[1:]) != (KVH, bs, d):
+        raise ValueError("pools differ in block shape")
+    if not (src_k.dtype == src_v.dtype == dst_k.dtype == dst_v.dtype):
+        raise TypeError("pools differ in dtype")
+    if block_mapping.dtype != torch.int64 or block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise TypeError("block_mapping must be int64 [num_pairs, 2]")
+    for t in (src_k, src_v, dst_k, dst_v, block_mapping):
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+        if t.device.type == "cpu" and not t.is_pinned():
+            raise ValueError("CPU tensors must be pinned (pin_memory=True)")
+    _check(_lib.pkv_swap_blocks(
+        _ptr(src_k), _ptr(src_v), NB_s, _ptr(dst_k), _ptr(dst_v), NB_d, _ptr(block_mapping),
+        block_mapping.shape[0], KVH, d, bs, dtype_code(src_k.dtype), _stream(stream)), "pkv_swap_blocks")
 
 
 def raw_lib():

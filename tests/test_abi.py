@@ -34,7 +34,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_symbols()
-    assert len(names) == 7
+    assert len(names) == 8
     for n in names:
         assert hasattr(lib, n), n
     nm = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
@@ -48,7 +48,7 @@ def test_binding_declares_the_same_symbols(lib):
 
 
 def test_status_strings(lib):
-    for st in range(0, -9, -1):
+    for st in range(0, -10, -1):
         s = lib.pkv_status_string(st)
         assert s and s != b"unknown status"
     assert lib.pkv_status_string(-99) == b"unknown status"
@@ -130,6 +130,21 @@ def test_reshape_and_copy_host_checks(lib):
     assert c(FAKE, FAKE, FAKE, 3, 1, 4, 1, 8, 3, None) == -4      # 4-byte blocks: not 16-byte units
     assert c(FAKE, FAKE, None, 3, 4, 128, 16, 8, 1, None) == -1
     assert c(FAKE, FAKE, FAKE, 3, 4, 128, 16, 8, 7, None) == -4
+
+
+def test_swap_host_checks(lib):
+    s = lib.pkv_swap_blocks
+    A, B, M = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x900000), ctypes.c_void_p(0x2000000)
+    assert s(A, A, 8, B, B, 4, M, 0, 4, 128, 16, 1, None) == 0          # no pairs: nothing to do
+    assert s(A, A, 8, B, B, 4, M, -1, 4, 128, 16, 1, None) == -2
+    assert s(A, A, 0, B, B, 4, M, 3, 4, 128, 16, 1, None) == -2          # empty source pool
+    assert s(A, A, 8, B, B, 0, M, 3, 4, 128, 16, 1, None) == -2
+    assert s(A, A, 8, B, B, 4, M, 3, 4, 128, 16, 7, None) == -4          # unknown dtype
+    assert s(A, A, 8, B, B, 4, M, 3, 1, 4, 1, 3, None) == -4             # 4-byte blocks
+    assert s(A, A, 8, B, None, 4, M, 3, 4, 128, 16, 1, None) == -1
+    assert s(A, A, 8, B, B, 4, None, 3, 4, 128, 16, 1, None) == -1
+    # 1000 source blocks of 16 KiB from 0x10000 run past 0x900000: the pools overlap
+    assert s(A, A, 1000, B, B, 4, M, 3, 4, 128, 16, 1, None) == -2
 
 
 def test_missing_library_fails_loudly():

@@ -17,6 +17,7 @@ import torch
 import oracle
 from oracle import e4m3_ref
 from oracle.paged_attention_ref import (
+    swap_ref,
     attend_one_ref, attend_ref, blocks_needed, copy_ref, gather_tokens,
     merge_partials_ref, partial_state_ref, reshape_ref, slot_of, take_blocks,
 )
@@ -267,6 +268,45 @@ def test_copy_blocks_matches_index_copy():
         for b in range(NB):
             if b not in pairs[:, 1]:
                 np.testing.assert_array_equal(got[b], pool[b])
+
+
+def test_swap_matches_index_copy_across_pools_and_leaves_source():
+    rng = np.random.default_rng(11)
+    KVH, bs, d = 2, 4, 3
+    gk = rng.integers(0, 255, (9, KVH, bs, d)).astype(np.uint8)
+    gv = rng.integers(0, 255, (9, KVH, bs, d)).astype(np.uint8)
+    hk = rng.integers(0, 255, (5, KVH, bs, d)).astype(np.uint8)       # a smaller host pool
+    hv = rng.integers(0, 255, (5, KVH, bs, d)).astype(np.uint8)
+    pairs = np.array([[7, 0], [2, 4], [8, 1]])
+    gk0, gv0 = gk.copy(), gv.copy()
+    k2, v2 = swap_ref(gk, gv, hk, hv, pairs)
+    np.testing.assert_array_equal(gk, gk0)
+    np.testing.assert_array_equal(gv, gv0)
+    for src, dst, got in ((gk, hk, k2), (gv, hv, v2)):
+        t = torch.from_numpy(dst.copy())
+        t.index_copy_(0, torch.tensor(pairs[:, 1]), torch.from_numpy(src)[torch.tensor(pairs[:, 0])])
+        np.testing.assert_array_equal(got, t.numpy())
+        assert got.shape == dst.shape
+        for b in range(5):
+            if b not in pairs[:, 1]:
+                np.testing.assert_array_equal(got[b], dst[b])
+
+
+def test_swap_out_then_in_restores_every_sequence_through_new_tables():
+    """A round trip through a host pool into different GPU blocks gathers the same tokens."""
+    rng = np.random.default_rng(12)
+    NB, KVH, bs, d = 12, 2, 4, 3
+    gk = rng.standard_normal((NB, KVH, bs, d))
+    gv = rng.standard_normal((NB, KVH, bs, d))
+    table, n = [3, 9, 5], 10
+    before = [oracle.gather_tokens(p, table, n, bs, h) for p in (gk, gv) for h in range(KVH)]
+    hk, hv = swap_ref(gk, gv, np.zeros((4, KVH, bs, d)), np.zeros((4, KVH, bs, d)), [[3, 2], [9, 0], [5, 3]])
+    gk2, gv2 = gk.copy(), gv.copy()
+    gk2[[3, 9, 5]] = np.nan                                   # the freed blocks are reused by others
+    gk2, gv2 = swap_ref(hk, hv, gk2, gv2, [[2, 7], [0, 1], [3, 11]])
+    after = [oracle.gather_tokens(p, [7, 1, 11], n, bs, h) for p in (gk2, gv2) for h in range(KVH)]
+    for a, b in zip(before, after):
+        np.testing.assert_array_equal(a, b)
 
 
 # ---------------------------------------------------------------------------
