@@ -28,6 +28,9 @@ Sources cited in this package (page title, then section):
 * [PA/related]  same page, section "Các kỹ thuật liên quan" (related
   techniques): FlashAttention-style tiling never writes the score matrix; GQA
   shares K/V heads between query heads; FP8 cache stores 8-bit keys/values.
+* [vLLM-rev]  "vLLM PagedAttention: uma revolução no throughput de inferência
+  de LLMs", feature list: chunked prefill (a long prompt's prefill split into
+  chunks), prefix caching, prefill compute-bound vs decode bandwidth-bound.
 * [OFP8]  the OCP 8-bit floating point specification (E4M3 "FN" encoding) --
   not on the pages; the pages only say "8-bit".  It fixes the codec.
 
@@ -45,6 +48,7 @@ from .paged_attention_ref import (  # noqa: F401
     reshape_ref,
     copy_ref,
     swap_ref,
+    prefill_ref,
     partial_state_ref,
     merge_partials_ref,
 )

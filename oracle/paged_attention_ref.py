@@ -222,3 +222,41 @@ def swap_ref(src_k, src_v, dst_k, dst_v, pairs):
         k_new[dst] = src_k[src]
         v_new[dst] = src_v[src]
     return k_new, v_new
+
+
+def prefill_ref(q, k_pool, v_pool, block_tables, context_lens, query_start_loc, scale, block_size):
+    """Chunked prefill attention over paged K/V, float64.
+
+    [vLLM-rev] (feature list): the prefill of a long prompt is split into chunks,
+    so each chunk's queries attend to the context cached by earlier chunks as
+    well as to the chunk itself.  Reading taken: sequence s contributes
+    ``n = query_start_loc[s+1] - query_start_loc[s]`` query tokens (rows
+    ``query_start_loc[s] ..`` of ``q``), which are its last n positions;
+    ``context_lens[s]`` counts every cached token including the chunk (whose K/V
+    were written into the pool first).  Query i sits at position
+    ``p = context_lens[s] - n + i`` and attends to positions 0..p (causal); a
+    negative p (more queries than tokens) gives a zero row.  Grouped heads as in
+    ``attend_ref``.  ``q``: ``[T, H, d]``; returns ``[T, H, d]``.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    T, H, d = q.shape
+    KVH = k_pool.shape[1]
+    if H % KVH != 0:
+        raise ValueError("num_heads must be a multiple of num_kv_heads")
+    group = H // KVH
+    qsl = np.asarray(query_start_loc)
+    out = np.zeros((T, H, d), dtype=np.float64)
+    for s in range(len(context_lens)):
+        ctx = int(context_lens[s])
+        first, last = int(qsl[s]), int(qsl[s + 1])
+        n = last - first
+        for g in range(KVH):
+            keys = gather_tokens(k_pool, block_tables[s], ctx, block_size, g)
+            values = gather_tokens(v_pool, block_tables[s], ctx, block_size, g)
+            for i in range(n):
+                pos = ctx - n + i
+                if pos < 0:
+                    continue
+                for h in range(g * group, (g + 1) * group):
+                    out[first + i, h] = attend_one_ref(q[first + i, h], keys[:pos + 1], values[:pos + 1], scale)
+    return out

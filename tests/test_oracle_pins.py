@@ -17,7 +17,7 @@ import torch
 import oracle
 from oracle import e4m3_ref
 from oracle.paged_attention_ref import (
-    swap_ref,
+    swap_ref, prefill_ref,
     attend_one_ref, attend_ref, blocks_needed, copy_ref, gather_tokens,
     merge_partials_ref, partial_state_ref, reshape_ref, slot_of, take_blocks,
 )
@@ -307,6 +307,89 @@ def test_swap_out_then_in_restores_every_sequence_through_new_tables():
     after = [oracle.gather_tokens(p, [7, 1, 11], n, bs, h) for p in (gk2, gv2) for h in range(KVH)]
     for a, b in zip(before, after):
         np.testing.assert_array_equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# Chunked prefill: decode, causal SDPA, chunking, causality, GQA
+# ---------------------------------------------------------------------------
+
+def _paged_problem(rng, lens, H, KVH, d, bs, extra_blocks=3):
+    nblk = [-(-n // bs) for n in lens]
+    NB = sum(nblk) + extra_blocks
+    perm = rng.permutation(NB)
+    tables = np.full((len(lens), max(nblk)), -1, dtype=np.int64)
+    k = 0
+    for s, m in enumerate(nblk):
+        tables[s, :m] = perm[k:k + m]
+        k += m
+    kp = np.full((NB, KVH, bs, d), np.nan)
+    vp = np.full((NB, KVH, bs, d), np.nan)
+    for s, n in enumerate(lens):
+        for t in range(n):
+            kp[tables[s, t // bs], :, t % bs] = rng.standard_normal((KVH, d))
+            vp[tables[s, t // bs], :, t % bs] = rng.standard_normal((KVH, d))
+    return kp, vp, tables
+
+
+def test_prefill_chunk_of_one_is_decode():
+    rng = np.random.default_rng(30)
+    lens, H, KVH, d, bs = [5, 17, 1, 33], 4, 2, 8, 4
+    kp, vp, tables = _paged_problem(rng, lens, H, KVH, d, bs)
+    q = rng.standard_normal((len(lens), H, d))
+    got = prefill_ref(q, kp, vp, tables, lens, np.arange(len(lens) + 1), 0.3, bs)
+    np.testing.assert_array_equal(got, attend_ref(q, kp, vp, tables, lens, 0.3, bs))
+
+
+def test_prefill_whole_prompt_is_causal_sdpa():
+    rng = np.random.default_rng(31)
+    lens, H, KVH, d, bs = [13, 7, 20], 6, 3, 8, 4
+    kp, vp, tables = _paged_problem(rng, lens, H, KVH, d, bs)
+    qsl = np.concatenate([[0], np.cumsum(lens)])
+    q = rng.standard_normal((int(qsl[-1]), H, d))
+    got = prefill_ref(q, kp, vp, tables, lens, qsl, 0.25, bs)
+    for s, n in enumerate(lens):
+        K = np.stack([gather_tokens(kp, tables[s], n, bs, g) for g in range(KVH)])      # [KVH, n, d]
+        V = np.stack([gather_tokens(vp, tables[s], n, bs, g) for g in range(KVH)])
+        K = torch.from_numpy(np.repeat(K, H // KVH, axis=0))
+        V = torch.from_numpy(np.repeat(V, H // KVH, axis=0))
+        Q = torch.from_numpy(q[qsl[s]:qsl[s + 1]].transpose(1, 0, 2).copy())            # [H, n, d]
+        ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, is_causal=True, scale=0.25)
+        np.testing.assert_allclose(got[qsl[s]:qsl[s + 1]], ref.numpy().transpose(1, 0, 2), rtol=1e-12, atol=1e-12)
+
+
+def test_prefill_in_chunks_equals_one_chunk():
+    """Chunks [0,4), [4,11), [11,19) of one prompt, each with the context cached so far."""
+    rng = np.random.default_rng(32)
+    n, H, KVH, d, bs = 19, 2, 1, 8, 4
+    kp, vp, tables = _paged_problem(rng, [n], H, KVH, d, bs)
+    q = rng.standard_normal((n, H, d))
+    whole = prefill_ref(q, kp, vp, tables, [n], [0, n], 0.5, bs)
+    parts = [prefill_ref(q[a:b], kp, vp, tables, [b], [0, b - a], 0.5, bs) for a, b in ((0, 4), (4, 11), (11, 19))]
+    np.testing.assert_array_equal(np.concatenate(parts), whole)
+    # two sequences' chunks packed in one call: rows land at their query offsets
+    both = prefill_ref(np.concatenate([q[4:11], q[11:19]]), kp, vp, np.concatenate([tables, tables]), [11, 19],
+                       [0, 7, 15], 0.5, bs)
+    np.testing.assert_array_equal(both, whole[4:19])
+
+
+def test_prefill_is_causal_and_short_contexts_give_zero_rows():
+    rng = np.random.default_rng(33)
+    n, H, KVH, d, bs = 9, 2, 2, 4, 4
+    kp, vp, tables = _paged_problem(rng, [n], H, KVH, d, bs)
+    q = rng.standard_normal((n, H, d))
+    base = prefill_ref(q, kp, vp, tables, [n], [0, n], 1.0, bs)
+    kp2, vp2 = kp.copy(), vp.copy()
+    t = 6                                             # change the token at position 6
+    kp2[tables[0, t // bs], :, t % bs] += 5.0
+    vp2[tables[0, t // bs], :, t % bs] -= 3.0
+    moved = prefill_ref(q, kp2, vp2, tables, [n], [0, n], 1.0, bs)
+    np.testing.assert_array_equal(moved[:t], base[:t])
+    assert np.all(np.abs(moved[t:] - base[t:]).max(axis=(1, 2)) > 0)
+    np.testing.assert_array_equal(base[0], np.stack([vp[tables[0, 0], h // (H // KVH), 0] for h in range(H)]))
+    # 3 queries over a 2-token context: the first has no position and stays zero
+    short = prefill_ref(q[:3], kp, vp, tables, [2], [0, 3], 1.0, bs)
+    assert not short[0].any()
+    np.testing.assert_array_equal(short[1:], prefill_ref(q[1:3], kp, vp, tables, [2], [0, 2], 1.0, bs))
 
 
 # ---------------------------------------------------------------------------
