@@ -2,6 +2,10 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama13b_f16]
 
+With a prefill workload (prefill_llama13b_f16, prefill_gqa_bf16) the step is
+reshape_and_cache of the chunks' K/V followed by paged_prefill_attention, and
+the roofline is the dense MFMA peak instead of HBM.
+
 A step is one pass of the hot path over one synthetic decode batch, inputs
 resident in HBM: reshape_and_cache writes every sequence's new key/value into
 the slot the block manager gave it, then paged_attention_decode attends over
@@ -136,6 +140,120 @@ def cpu_baseline(w, inp, tables, ctx, budget_s):
     }
 
 
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}     # dense MFMA, MI355X
+
+
+def prefill_flops(w, ctx, chunk):
+    """QK and PV flops of the visible (query, key) pairs: 4 * d * H per pair."""
+    pairs = 0
+    for c, n in zip(ctx.tolist(), chunk.tolist()):
+        first = c - n + 1                          # keys visible to the chunk's first query
+        pairs += n * first + n * (n - 1) // 2
+    return 4 * w.head_dim * w.num_heads * pairs
+
+
+def cpu_baseline_prefill(w, inp, tables, ctx, budget_s):
+    """The oracle's prefill_ref, one whole sequence (all rows, all heads) at a time, until the budget is spent."""
+    import oracle
+    import torch
+    from threadpoolctl import threadpool_info
+    qsl = inp.query_start_loc
+    done, flops, spent = 0, 0, 0.0
+    for s in range(w.num_seqs):
+        n, c = int(inp.chunk_lens[s]), int(ctx[s])
+        blocks = tables[s, : -(-c // w.block_size)]
+        kp = _BlockSubset(inp.k_cache, blocks)
+        vp = _BlockSubset(inp.v_cache, blocks)
+        q = inp.q[int(qsl[s]):int(qsl[s + 1])].cpu().to(torch.float64).numpy()
+        t0 = time.perf_counter()
+        oracle.prefill_ref(q, kp, vp, tables[s:s + 1], ctx[s:s + 1], np.array([0, n]), w.softmax_scale, w.block_size)
+        spent += time.perf_counter() - t0
+        done += 1
+        flops += prefill_flops(w, ctx[s:s + 1].astype(np.int64), inp.chunk_lens[s:s + 1].astype(np.int64))
+        if spent > budget_s:
+            break
+    blas_threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"first {done} of {w.num_seqs} sequences of the same prefill step, all rows and heads, "
+                      f"fp64 numpy oracle, {spent:.1f} s wall",
+            "host_cores_available": len(os.sched_getaffinity(0))}
+
+
+def main_prefill(args, w):
+    """One chunked-prefill step: reshape_and_cache of the chunk's K/V, then prefill attention."""
+    import torch
+    from paged_kv_cache_259_amd import ops, synth
+    from paged_kv_cache_259_amd.block_manager import BlockManager
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = synth.make_prefill_inputs(w, device=dev)
+    bm = BlockManager(inp.num_blocks, w.block_size, inp.free_list)
+    seqs = list(range(w.num_seqs))
+    slots = []
+    for s in seqs:
+        bm.add_sequence(s, int(inp.context_lens[s] - inp.chunk_lens[s]))
+        slots += [bm.append_slot(s)[0] for _ in range(int(inp.chunk_lens[s]))]
+    slots = torch.tensor(slots, dtype=torch.int64, device=dev)
+    tables_np = bm.block_table_array(seqs, w.max_blocks_per_seq)
+    tables = torch.from_numpy(tables_np).to(dev)
+    ctx_np = bm.context_lens_array(seqs)
+    ctx = torch.from_numpy(ctx_np).to(dev)
+    qsl = torch.from_numpy(inp.query_start_loc.astype(np.int32)).to(dev)
+    max_q, max_ctx = int(inp.chunk_lens.max()), int(ctx_np.max())
+    out = torch.empty_like(inp.q)
+    stream = torch.cuda.current_stream()
+
+    def reshape():
+        ops.reshape_and_cache(inp.k_new, inp.v_new, inp.k_cache, inp.v_cache, slots, stream=stream)
+
+    def attend():
+        ops.paged_prefill_attention(out, inp.q, inp.k_cache, inp.v_cache, tables, ctx, qsl, w.softmax_scale, max_q,
+                                    max_ctx, stream=stream)
+
+    for _ in range(args.warmup):
+        reshape()
+        attend()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        ev[i][0].record(stream)
+        reshape()
+        ev[i][1].record(stream)
+        attend()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    t_attn = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)])
+    t_step = np.array([ev[i][0].elapsed_time(ev[i][2]) for i in range(K)])
+    flops = prefill_flops(w, ctx_np.astype(np.int64), inp.chunk_lens.astype(np.int64))
+    attn_ms, step_ms = float(np.mean(t_attn)), float(np.mean(t_step))
+    tokens = int(inp.chunk_lens.sum())
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS[w.dtype]
+    result = {
+        "metric": "paged chunked-prefill attention TFLOP/s (% of dense MFMA peak) + prefill tokens/s per layer step",
+        "value": round(flops / (step_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) q/K/V, uniform prior context lengths, shuffled block tables)",
+        "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_heads": w.num_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
+                   "query_tokens": tokens, "sum_context": int(ctx_np.sum()), "max_context": max_ctx},
+        "tokens_per_s": round(tokens / (step_ms * 1e-3), 1),
+        "components": {"reshape_and_cache_us": round(float(np.mean(t_step - t_attn)) * 1e3, 2),
+                       "paged_prefill_attention_us": round(attn_ms * 1e3, 2),
+                       "paged_prefill_attention_median_us": round(float(np.median(t_attn)) * 1e3, 2)},
+        "roofline": {"bound": "mfma", "kernel": "paged_prefill_attention", "achieved": round(achieved, 2),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "algorithmic_flops_per_call": int(flops)},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_prefill(w, inp, tables_np, ctx_np, args.cpu_seconds)
+    print(json.dumps(result))
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -150,6 +268,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = synth.WORKLOADS[args.workload]
+    if isinstance(w, synth.PrefillWorkload):
+        return main_prefill(args, w)
     if not isinstance(w, synth.DecodeWorkload):
         raise SystemExit("bench.py times decode workloads (llama13b_f16, gqa_bf16, long_splitk_bf16, tiny_f32)")
     part = w.partition_size if args.partition is None else args.partition

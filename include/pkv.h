@@ -1,7 +1,7 @@
 /*
  * pkv.h -- C ABI of the paged-KV decode library for AMD MI355X (gfx950).
  *
- * Four data-path calls and their helpers.  The library is stateless: the host
+ * Five data-path calls and their helpers.  The library is stateless: the host
  * owns the block bookkeeping (which physical block holds which tokens,
  * reference counts, copy-on-write decisions); the library moves bytes and
  * attends.  Sources cited (page title, then section):
@@ -205,6 +205,42 @@ int pkv_reshape_and_cache(const void* key, const void* value,
 int pkv_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, int num_pairs,
                     int num_kv_heads, int head_dim, int block_size, int num_blocks,
                     int kv_dtype, void* stream);
+
+/*
+ * pkv_paged_prefill_attention -- chunked prefill over the paged cache
+ * ([vLLM-rev] feature list: a long prompt's prefill is split into chunks;
+ * [PA/paging]: keys and values are gathered block by block through the table).
+ *
+ * Sequence s contributes n_s = query_start_loc[s+1] - query_start_loc[s] query
+ * tokens, rows query_start_loc[s] .. of q and out.  They are the sequence's
+ * last n_s positions: ctx_s = context_lens[s] counts every cached token
+ * including the chunk, whose K/V the caller wrote into the pool first
+ * (pkv_reshape_and_cache).  Query i sits at position p = ctx_s - n_s + i and
+ * attends causally to positions 0..p; for each query head h (kv head g = h / G):
+ *   out[row][h][:] = sum_{t<=p} softmax_t(scale * <q[row][h], K_t>) V_t
+ * in fp32 with an online softmax; the probabilities enter the PV product
+ * rounded to the q dtype.  A row with p < 0 (more queries than context) is zero.
+ *
+ * out, q       [num_tokens][num_heads][head_dim], q_dtype.
+ * query_start_loc  [num_seqs + 1] int32, non-decreasing, from 0 to num_tokens;
+ *              entries are clamped to [0, num_tokens] (a broken array gives wrong
+ *              rows, never an access outside q / out).
+ * k_cache, v_cache, block_tables, num_blocks  as for pkv_paged_attention_decode
+ *              (blocks the table maps outside [0, num_blocks) are skipped).
+ * context_lens [num_seqs] int32.
+ * max_query_len    host bound on every n_s (sizes the grid); rows past it are
+ *              not written.  max_context_len: host bound on context_lens (larger
+ *              values are clamped, giving wrong positions but no stray access).
+ * Supported: q_dtype == kv_dtype in {PKV_F16, PKV_BF16}, head_dim 64 or 128,
+ *   block_size 16.  Needs no workspace.  max_query_len, num_seqs or num_tokens
+ *   == 0 is a no-op returning PKV_OK.
+ */
+int pkv_paged_prefill_attention(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables, int max_blocks_per_seq,
+                                const int32_t* context_lens, const int32_t* query_start_loc,
+                                int num_seqs, int num_tokens, int num_heads, int num_kv_heads, int head_dim,
+                                int block_size, int num_blocks, int max_query_len, int max_context_len,
+                                float scale, int q_dtype, int kv_dtype, void* stream);
 
 /*
  * pkv_swap_blocks -- whole-block copies between two pools, for preemption by

@@ -271,4 +271,55 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
   return pkv::launch_status(e);
 }
 
+int pkv_paged_prefill_attention(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+                                const int32_t* query_start_loc, int num_seqs, int num_tokens, int num_heads,
+                                int num_kv_heads,
+                                int head_dim, int block_size, int num_blocks, int max_query_len,
+                                int max_context_len, float scale, int q_dtype, int kv_dtype, void* stream) {
+  if (num_seqs < 0 || num_tokens < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      max_query_len < 0 || max_context_len < 0 || max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return PKV_ERR_BAD_SIZE;
+  if (num_heads % num_kv_heads != 0) return PKV_ERR_HEAD_GROUPING;
+  if (!pkv::prefill_supported(q_dtype, kv_dtype, head_dim, block_size)) return PKV_ERR_UNSUPPORTED;
+  if (!isfinite(scale)) return PKV_ERR_BAD_SIZE;
+  const int bm = pkv::prefill_tile_rows();
+  const long long tiles = ((long long)max_query_len + bm - 1) / bm;
+  const long long wgs = (long long)num_seqs * num_heads * tiles;
+  if (wgs > 2147483647LL) return PKV_ERR_BAD_SIZE;
+  if (wgs == 0 || num_tokens == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start_loc)
+    return PKV_ERR_NULL_POINTER;
+  if (!pkv::aligned16(out) || !pkv::aligned16(q) || !pkv::aligned16(k_cache) || !pkv::aligned16(v_cache))
+    return PKV_ERR_UNSUPPORTED;
+  pkv::PrefillParams p{};
+  p.out = out;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.query_start_loc = query_start_loc;
+  p.num_seqs = num_seqs;
+  p.num_tokens = num_tokens;
+  p.num_heads = num_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = num_heads / num_kv_heads;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.max_query_len = max_query_len;
+  p.q_tiles = (int)tiles;
+  const long long cap_table = (long long)max_blocks_per_seq * block_size;
+  p.ctx_cap = (int)(max_context_len < cap_table ? max_context_len : cap_table);
+  p.qk_scale = scale * kLog2e;
+  p.total_wgs = (uint32_t)wgs;
+  // the query tiles and heads that read one kv head's K/V run on one XCD (shared L2)
+  const char* e = getenv("PKV_PREFILL_XCD_CHUNK");
+  long long chunk = (long long)tiles * p.group;
+  if (e && *e) chunk = atoi(e);
+  p.xcd_chunk = (uint32_t)(chunk < 0 ? 0 : (chunk > 4096 ? 4096 : chunk));
+  (void)hipGetLastError();
+  return pkv::launch_status(pkv::launch_prefill(p, q_dtype, head_dim, reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -395,4 +395,28 @@ struct ReduceParams {
   int ctx_cap;
 };
 
+// Chunked prefill over the paged cache (see prefill_mfma.hip).
+struct PrefillParams {
+  void* out;                       // [num_tokens][num_heads][D]
+  const void* q;                   // [num_tokens][num_heads][D]
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* query_start_loc;  // [num_seqs + 1]
+  int num_seqs;
+  int num_tokens;                  // rows of q / out
+  int num_heads;
+  int num_kv_heads;
+  int group;
+  int max_blocks_per_seq;
+  int num_blocks;
+  int max_query_len;
+  int q_tiles;                     // query tiles per sequence in the grid
+  int ctx_cap;
+  float qk_scale;                  // scale * log2(e)
+  uint32_t total_wgs;
+  uint32_t xcd_chunk;
+};
+
 }  // namespace pkv

@@ -46,12 +46,15 @@ _lib.pkv_reshape_and_cache.restype = _c_int
 _lib.pkv_reshape_and_cache.argtypes = [_vp] * 5 + [_c_int] * 7 + [_c_float] * 2 + [_vp]
 _lib.pkv_copy_blocks.restype = _c_int
 _lib.pkv_copy_blocks.argtypes = [_vp, _vp, _vp] + [_c_int] * 6 + [_vp]
+_lib.pkv_paged_prefill_attention.restype = _c_int
+_lib.pkv_paged_prefill_attention.argtypes = [_vp] * 5 + [_c_int] + [_vp, _vp] + [_c_int] * 9 + [_c_float] + [_c_int] * 2 + [_vp]
 _lib.pkv_swap_blocks.restype = _c_int
 _lib.pkv_swap_blocks.argtypes = [_vp, _vp, _c_int, _vp, _vp, _c_int, _vp] + [_c_int] * 5 + [_vp]
 
 EXPORTED_SYMBOLS = (
     "pkv_status_string", "pkv_version", "pkv_attention_plan", "pkv_attention_workspace_bytes",
     "pkv_paged_attention_decode", "pkv_reshape_and_cache", "pkv_copy_blocks", "pkv_swap_blocks",
+    "pkv_paged_prefill_attention",
 )
 
 
@@ -147,6 +150,36 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         _ptr(context_lens), _ptr(seq_order), S, H, KVH, d, bs, NB if num_blocks is None else num_blocks, max_context_len,
         float(scale), float(k_scale), float(v_scale), qd, kvd, partition_size, ws_ptr, ws_bytes,
         _stream(stream)), "pkv_paged_attention_decode")
+    return out
+
+
+def paged_prefill_attention(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale,
+                            max_query_len, max_context_len, num_blocks=None, stream=None):
+    """Chunked prefill: query row i of sequence s (rows query_start_loc[s]..) sits at
+    position context_lens[s] - n_s + i and attends causally over the paged cache.
+
+    out, q: [num_tokens, H, d]; pools [NB, KVH, bs, d]; block_tables int32
+    [S, maxblk]; context_lens int32 [S]; query_start_loc int32 [S + 1].
+    """
+    T, H, d = q.shape
+    NB, KVH, bs, d2 = k_cache.shape
+    S = context_lens.shape[0]
+    if d2 != d or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch between q/out and the pools")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32 or query_start_loc.dtype != torch.int32:
+        raise TypeError("block_tables, context_lens and query_start_loc must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or query_start_loc.shape != (S + 1,):
+        raise ValueError("block_tables must be [S, maxblk] and query_start_loc [S + 1]")
+    for t in (out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc):
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    if out.dtype != q.dtype:
+        raise TypeError("out must have q's dtype")
+    _check(_lib.pkv_paged_prefill_attention(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1],
+        _ptr(context_lens), _ptr(query_start_loc), S, T, H, KVH, d, bs, NB if num_blocks is None else num_blocks,
+        int(max_query_len), int(max_context_len), float(scale), dtype_code(q.dtype), dtype_code(k_cache.dtype),
+        _stream(stream)), "pkv_paged_prefill_attention")
     return out
 
 

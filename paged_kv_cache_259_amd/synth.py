@@ -80,6 +80,27 @@ class SharedPrefixWorkload:
         return 1.0 / math.sqrt(self.head_dim)
 
 
+@dataclass(frozen=True)
+class PrefillWorkload:
+    """Chunked prefill: each sequence has ``prior`` cached tokens and a chunk of new query tokens."""
+    name: str
+    seed: int
+    num_seqs: int
+    num_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    dtype: str
+    chunk: tuple                 # length recipe of the chunks (query tokens per sequence)
+    prior: tuple                 # length recipe of the context cached before the chunk
+    max_blocks_per_seq: int
+    pool_slack: float = 1.2
+
+    @property
+    def softmax_scale(self):
+        return 1.0 / math.sqrt(self.head_dim)
+
+
 # The five named workloads.
 TINY_F32 = DecodeWorkload(
     name="tiny fp32 paged decode: 4 seqs ctx {40,17,1,64}, 8 heads MHA, d64, bs16, 64-block pool",
@@ -114,12 +135,27 @@ SHARED_PREFIX_FP8 = SharedPrefixWorkload(
     seed=25905, num_prompts=32, prompt_len=1000, samples_per_prompt=4, cont_lo=0, cont_hi=512,
     num_heads=40, head_dim=128, block_size=16, num_blocks=6400, max_blocks_per_seq=95)
 
+# Chunked prefill (the next workload after decode: compute-bound, MFMA-dense).
+PREFILL_LLAMA13B_F16 = PrefillWorkload(
+    name="chunked prefill, LLaMA-13B-shaped layer: 8 seqs x 512-token chunks over 0-3584 cached tokens, "
+         "40/40 heads, d128, fp16, bs16",
+    seed=25906, num_seqs=8, num_heads=40, num_kv_heads=40, head_dim=128, block_size=16, dtype="f16",
+    chunk=("fixed", (512,) * 8), prior=("uniform", 0, 3584), max_blocks_per_seq=256)
+
+PREFILL_GQA_BF16 = PrefillWorkload(
+    name="chunked prefill, GQA layer: 16 seqs x 512-token chunks over 0-7680 cached tokens, "
+         "64 q / 8 kv heads, d128, bf16, bs16",
+    seed=25907, num_seqs=16, num_heads=64, num_kv_heads=8, head_dim=128, block_size=16, dtype="bf16",
+    chunk=("fixed", (512,) * 16), prior=("uniform", 0, 7680), max_blocks_per_seq=512)
+
 WORKLOADS = {
     "tiny_f32": TINY_F32,
     "llama13b_f16": LLAMA13B_F16,
     "gqa_bf16": GQA_BF16,
     "long_splitk_bf16": LONG_SPLITK_BF16,
     "shared_prefix_fp8": SHARED_PREFIX_FP8,
+    "prefill_llama13b_f16": PREFILL_LLAMA13B_F16,
+    "prefill_gqa_bf16": PREFILL_GQA_BF16,
 }
 
 
@@ -228,3 +264,40 @@ def draw_step_kv(inp: SharedPrefixInputs, n_tokens, device):
 def draw_query(inp: SharedPrefixInputs, n_seqs, device):
     w = inp.workload
     return randn(inp.gen, (n_seqs, w.num_heads, w.head_dim), DTYPES[w.q_dtype], device)
+
+
+@dataclass
+class PrefillInputs:
+    workload: PrefillWorkload
+    chunk_lens: np.ndarray         # int64 [S] query tokens per sequence
+    context_lens: np.ndarray       # int64 [S] prior + chunk
+    query_start_loc: np.ndarray    # int64 [S + 1]
+    free_list: list
+    num_blocks: int
+    q: torch.Tensor                # [T, H, d]
+    k_cache: torch.Tensor          # [NB, KVH, bs, d]
+    v_cache: torch.Tensor
+    k_new: torch.Tensor            # [T, KVH, d] the chunk's keys, in query order
+    v_new: torch.Tensor
+
+
+def make_prefill_inputs(w: PrefillWorkload, device="cpu", chunk=None, prior=None):
+    """Draw one chunked-prefill step: chunk lengths -> prior lengths -> free-list permutation
+    -> q -> K pool -> V pool -> chunk K -> chunk V."""
+    rng = np.random.default_rng(w.seed)
+    n = draw_lengths(rng, w.chunk, w.num_seqs) if chunk is None else np.asarray(chunk, np.int64)
+    pre = draw_lengths(rng, w.prior, w.num_seqs) if prior is None else np.asarray(prior, np.int64)
+    ctx = pre + n
+    nb = pool_blocks_upper_bound(ctx, w.block_size, w.pool_slack)
+    free_list = rng.permutation(nb).tolist()
+    qsl = np.concatenate([[0], np.cumsum(n)]).astype(np.int64)
+    T = int(qsl[-1])
+    gen = make_generator(w.seed, device)
+    dt = DTYPES[w.dtype]
+    H, KVH, d, bs = w.num_heads, w.num_kv_heads, w.head_dim, w.block_size
+    q = randn(gen, (T, H, d), dt, device)
+    k_cache = randn(gen, (nb, KVH, bs, d), dt, device)
+    v_cache = randn(gen, (nb, KVH, bs, d), dt, device)
+    k_new = randn(gen, (T, KVH, d), dt, device)
+    v_new = randn(gen, (T, KVH, d), dt, device)
+    return PrefillInputs(w, n, ctx, qsl, free_list, nb, q, k_cache, v_cache, k_new, v_new)

@@ -34,7 +34,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_symbols()
-    assert len(names) == 8
+    assert len(names) == 9
     for n in names:
         assert hasattr(lib, n), n
     nm = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
@@ -145,6 +145,24 @@ def test_swap_host_checks(lib):
     assert s(A, A, 8, B, B, 4, None, 3, 4, 128, 16, 1, None) == -1
     # 1000 source blocks of 16 KiB from 0x10000 run past 0x900000: the pools overlap
     assert s(A, A, 1000, B, B, 4, M, 3, 4, 128, 16, 1, None) == -2
+
+
+def test_prefill_host_checks(lib):
+    f = lib.pkv_paged_prefill_attention
+    sc = ctypes.c_float(0.1)
+
+    def call(S=2, T=100, H=4, KVH=4, d=128, bs=16, NB=8, mq=64, mc=128, qd=1, kvd=1, out=FAKE, tables=FAKE,
+             maxblk=8):
+        return f(out, FAKE, FAKE, FAKE, tables, maxblk, FAKE, FAKE, S, T, H, KVH, d, bs, NB, mq, mc, sc, qd, kvd, None)
+
+    assert call(S=0) == 0 and call(mq=0) == 0 and call(T=0) == 0   # nothing to do
+    assert call(T=-1) == -2
+    assert call(H=6, KVH=4) == -3
+    assert call(d=256) == -4 and call(bs=8) == -4 and call(qd=0, kvd=0) == -4 and call(kvd=3) == -4
+    assert call(qd=1, kvd=2) == -4
+    assert call(NB=0) == -2 and call(mq=-1) == -2 and call(maxblk=0) == -2
+    assert call(out=None) == -1 and call(tables=None) == -1
+    assert call(out=ctypes.c_void_p(0x10008)) == -4             # misaligned output
 
 
 def test_missing_library_fails_loudly():
