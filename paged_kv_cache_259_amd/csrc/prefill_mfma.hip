@@ -4,53 +4,47 @@
 // feature list: chunked prefill); each chunk's queries are the sequence's last
 // n positions and attend causally to every token cached so far, the chunk's own
 // K/V included (written to the pool by reshape_and_cache first).  Unlike decode
-// this is a dense contraction: a 64-query tile reuses every K/V tile 64 times.
+// this is a dense contraction: a 128-query tile reuses every K/V tile 128 times.
 //
-// One workgroup of 4 waves per (sequence, 64-query tile, query head); wave w
-// owns query rows 16w .. 16w+15 of the tile.  Per step of 32 tokens (two
-// 16-token blocks):
+// One workgroup of 4 waves per (sequence, 128-query tile, query head); wave w
+// owns query rows 32w .. 32w+31 of the tile as two 16-row groups.  Per step of
+// 32 tokens (two 16-token blocks):
 //   staging  256 threads load the step's K and V rows (16-byte loads through
 //            the block table) into registers one step ahead, then store them to
-//            LDS: K row-major [token][dim], V transposed [dim][token].
+//            LDS: K row-major [token][dim]; V transposed [dim][token] with the
+//            tokens of a step in the order the QK result holds them (below).
 //   QK       S^T[token][query] = sum_k K[token][k] Q[query][k]
-//            v_mfma_f32_16x16x32 (f16/bf16), A = K rows from LDS, B = Q^T held
-//            in registers; lane l gets tokens 4(l/16)+r of query l%16.
-//   softmax  causal / context mask, running max over the 32 tokens (the lane's
-//            8 values, then lanes l^16 and l^32), exp2 in the log2 domain.
+//            v_mfma_f32_16x16x32 (f16/bf16), A = K rows from LDS (read once,
+//            used by both row groups), B = Q^T held in registers; lane l gets
+//            tokens 4(l/16)+r and 16+4(l/16)+r (r = 0..3) of query l%16.
+//   softmax  causal / context mask (only on steps that straddle a boundary),
+//            running max over the 32 tokens (the lane's 8 values, then lanes
+//            l^16 and l^32), exp2 in the log2 domain.
 //   PV       O^T[dim][query] += sum_k V^T[dim][token_k] P^T[token_k][query]
-//            v_mfma_f32_16x16x16 (f16/bf16), A = V^T rows from LDS (4 tokens =
-//            8 bytes), B = P^T, which is exactly the lane's own 4 softmax
-//            weights of the QK result rounded to the input type.
+//            v_mfma_f32_16x16x32 again: the contraction index k of lane group
+//            l/16 is its 8 tokens above, so B = P^T is exactly the lane's own
+//            8 softmax weights rounded to the input type, and A = V^T is one
+//            16-byte LDS read of a row of the reordered V^T tile.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
 namespace pkv {
 
-typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-
 template <class T> struct PrefillOp;
 template <> struct PrefillOp<BF16> {
-  __device__ __forceinline__ static f32x4_t qk(const uint4& a, const uint4& b, f32x4_t c) {
+  __device__ __forceinline__ static f32x4_t mma(const uint4& a, const uint4& b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
                                                    c, 0, 0, 0);
   }
-  __device__ __forceinline__ static f32x4_t pv(const uint2& a, const uint2& b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, a), __builtin_bit_cast(bf16x4_t, b),
-                                                     c, 0, 0, 0);
-  }
-  __device__ __forceinline__ static uint32_t pack(float x, float y) {
-    return (uint32_t)f32_to_bf16_rne(x) | ((uint32_t)f32_to_bf16_rne(y) << 16);
+  __device__ __forceinline__ static uint32_t pack(float x, float y) {      // round to nearest even
+    const bf162_t h = {(__bf16)x, (__bf16)y};
+    return __builtin_bit_cast(uint32_t, h);
   }
 };
 template <> struct PrefillOp<F16> {
-  __device__ __forceinline__ static f32x4_t qk(const uint4& a, const uint4& b, f32x4_t c) {
+  __device__ __forceinline__ static f32x4_t mma(const uint4& a, const uint4& b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
                                                   0, 0, 0);
-  }
-  __device__ __forceinline__ static f32x4_t pv(const uint2& a, const uint2& b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a), __builtin_bit_cast(f16x4_t, b), c,
-                                                 0, 0, 0);
   }
   __device__ __forceinline__ static uint32_t pack(float x, float y) {
     const half2_t h = {(_Float16)x, (_Float16)y};
@@ -58,19 +52,23 @@ template <> struct PrefillOp<F16> {
   }
 };
 
-template <class T, int D>
+template <class T, int D, int RW>
 struct Prefill {
   static constexpr int BS = 16;                 // tokens per block
   static constexpr int STEP = 32;               // tokens per step (two blocks)
   static constexpr int NW = 4;
-  static constexpr int BM = NW * 16;            // query rows per workgroup
+  static constexpr int BM = NW * 16 * RW;       // query rows per workgroup
   static constexpr int NC = D / 32;             // QK k-steps of 32 dims
   static constexpr int ND = D / 16;             // PV output tiles of 16 dims
   static constexpr int CPR = D / 8;             // 16-byte chunks per token row
   static constexpr int CH = STEP * CPR / (NW * 64);   // chunks per thread per tensor per step
   static constexpr int KSTR = D + 8;            // LDS row stride of K (elements)
   static constexpr int VSTR = STEP + 8;         // LDS row stride of V^T (elements)
-  static_assert(CH >= 1 && STEP * CPR == CH * NW * 64, "staging must cover the step exactly");
+  static_assert(CH == 1 || CH == 2, "staging covers a step with one or two chunks per thread");
+
+  // column of token t (0..31) of a step in the V^T tile: lane group g = (t%16)/4
+  // reads columns 8g .. 8g+7 = tokens 4g..4g+3, then 16+4g..16+4g+3
+  __device__ __forceinline__ static int vcol(int t) { return 8 * ((t & 15) >> 2) + 4 * (t >> 4) + (t & 3); }
 
   struct Smem {
     alignas(16) uint16_t k[2][STEP * KSTR];
@@ -78,9 +76,9 @@ struct Prefill {
   };
 };
 
-template <class T, int D>
+template <class T, int D, int RW>
 __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
-  using P = Prefill<T, D>;
+  using P = Prefill<T, D, RW>;
   using Op = PrefillOp<T>;
   constexpr int STEP = P::STEP, BS = P::BS, NC = P::NC, ND = P::ND, CPR = P::CPR, CH = P::CH;
   __shared__ typename P::Smem sm;
@@ -114,37 +112,52 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
   int nkeys = base + row0 + rows_here;                      // keys 0 .. nkeys-1 serve this tile
   nkeys = nkeys > ctx ? ctx : (nkeys < 0 ? 0 : nkeys);
   const int nsteps = (nkeys + STEP - 1) / STEP;
-  const int wave_last_pos = base + row0 + 16 * w + 15;      // causal limit of the wave's rows
+  const int wrow0 = row0 + 16 * RW * w;                     // the wave's first row
+  const int wave_first_pos = base + wrow0;
+  const int wave_last_pos = wave_first_pos + 16 * RW - 1;   // causal limit of the wave's rows
+  const bool wave_rows_real = wrow0 + 16 * RW <= n;
 
-  // B operand of QK: Q^T, lane l holds query row 16w + c16, dims 32c + 8 g4 .. +8
-  const int qrow = row0 + 16 * w + c16;
-  const bool qreal = qrow < n;
-  const int qpos = base + qrow;
-  uint4 qf[NC];
-  {
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) + ((size_t)(q0 + (qreal ? qrow : 0)) * p.num_heads + h) * D;
+  // B operand of QK: Q^T, lane l holds query row wrow0 + 16 g + c16, dims 32c + 8 g4 .. +8
+  uint4 qf[RW][NC];
+  int qpos[RW];
+  bool qreal[RW];
+#pragma unroll
+  for (int g = 0; g < RW; ++g) {
+    const int qrow = wrow0 + 16 * g + c16;
+    qreal[g] = qrow < n;
+    qpos[g] = base + qrow;
+    const uint16_t* qp =
+        reinterpret_cast<const uint16_t*>(p.q) + ((size_t)(q0 + (qreal[g] ? qrow : 0)) * p.num_heads + h) * D;
 #pragma unroll
     for (int c = 0; c < NC; ++c)
-      qf[c] = qreal ? *reinterpret_cast<const uint4*>(qp + c * 32 + g4 * 8) : make_uint4(0u, 0u, 0u, 0u);
+      qf[g][c] = qreal[g] ? *reinterpret_cast<const uint4*>(qp + c * 32 + g4 * 8) : make_uint4(0u, 0u, 0u, 0u);
   }
 
-  float m = -__builtin_inff(), lsum = 0.f;
-  f32x4_t O[ND];
+  float m[RW], lsum[RW];
+  f32x4_t O[RW][ND];
 #pragma unroll
-  for (int dt = 0; dt < ND; ++dt) O[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int g = 0; g < RW; ++g) {
+    m[g] = -__builtin_inff();
+    lsum[g] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) O[g][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
 
   const int32_t* table = p.block_tables + (size_t)seq * p.max_blocks_per_seq;
   const size_t block_stride = (size_t)p.num_kv_heads * BS * D;             // elements
   const uint16_t* kpool = reinterpret_cast<const uint16_t*>(p.k_cache) + (size_t)kvh * BS * D;
   const uint16_t* vpool = reinterpret_cast<const uint16_t*>(p.v_cache) + (size_t)kvh * BS * D;
 
+  // staging assignment: chunk column `col` of token stok + j (j < CH); with two
+  // chunks a thread holds the same columns of two adjacent tokens, which sit in
+  // adjacent V^T columns, so their V values go to LDS as 32-bit pairs
+  const int col = tid % CPR;
+  const int stok = (tid / CPR) * CH;
   uint4 kreg[CH], vreg[CH];
   auto load_step = [&](int i) {
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-      const int c = tid + j * P::NW * 64;
-      const int tok = c / CPR, col = c - tok * CPR;
-      const int pos = i * STEP + tok;
+      const int pos = i * STEP + stok + j;
       const int blk = pos < nkeys ? table[pos / BS] : -1;
       const bool ok = blk >= 0 && blk < p.num_blocks;
       const size_t off = (size_t)blk * block_stride + (size_t)(pos % BS) * D + col * 8;
@@ -154,14 +167,22 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
   };
   auto store_step = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      const int c = tid + j * P::NW * 64;
-      const int tok = c / CPR, col = c - tok * CPR;
-      *reinterpret_cast<uint4*>(&sm.k[buf][tok * P::KSTR + col * 8]) = kreg[j];
-      const uint32_t u[4] = {vreg[j].x, vreg[j].y, vreg[j].z, vreg[j].w};
+    for (int j = 0; j < CH; ++j)
+      *reinterpret_cast<uint4*>(&sm.k[buf][(stok + j) * P::KSTR + col * 8]) = kreg[j];
+    uint16_t* vt = &sm.vt[buf][(col * 8) * P::VSTR + P::vcol(stok)];
+    if constexpr (CH == 2) {
+      const uint32_t a[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
+      const uint32_t b[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        sm.vt[buf][(col * 8 + e) * P::VSTR + tok] = (uint16_t)(u[e >> 1] >> (16 * (e & 1)));
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t lo = (a[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+        const uint32_t hi = (b[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+        *reinterpret_cast<uint32_t*>(vt + e * P::VSTR) = lo | (hi << 16);
+      }
+    } else {
+      const uint32_t a[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vt[e * P::VSTR] = (uint16_t)(a[e >> 1] >> (16 * (e & 1)));
     }
   };
 
@@ -173,103 +194,121 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
   for (int i = 0; i < nsteps; ++i) {
     const int buf = i & 1;
     if (i + 1 < nsteps) load_step(i + 1);
-    if (i * STEP <= wave_last_pos) {                        // wave-uniform: some key of the step is visible
+    const int k0 = i * STEP;
+    if (k0 <= wave_last_pos) {                              // wave-uniform: some key of the step is visible
       // blocks of this step that the table maps outside the pool are skipped
       bool blk_ok[2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        const int pos = i * STEP + kt * BS;
+        const int pos = k0 + kt * BS;
         const int b = pos < nkeys ? table[pos / BS] : -1;
         blk_ok[kt] = b >= 0 && b < p.num_blocks;
       }
-      f32x4_t S[2];
+      // every key of the step visible to every row of the wave: no per-element mask
+      const bool interior = k0 + STEP - 1 <= wave_first_pos && k0 + STEP <= nkeys && blk_ok[0] && blk_ok[1] &&
+                            wave_rows_real;
+      f32x4_t S[RW][2];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        S[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int g = 0; g < RW; ++g)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) S[g][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           const uint4 kf = *reinterpret_cast<const uint4*>(&sm.k[buf][(kt * 16 + c16) * P::KSTR + c * 32 + g4 * 8]);
-          S[kt] = Op::qk(kf, qf[c], S[kt]);
+#pragma unroll
+          for (int g = 0; g < RW; ++g) S[g][kt] = Op::mma(kf, qf[g][c], S[g][kt]);
         }
+      uint4 pk[RW];
+#pragma unroll
+      for (int g = 0; g < RW; ++g) {
+        float s[2][4];
+        float mx = -__builtin_inff();
+        if (interior) {
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              s[kt][r] = S[g][kt][r] * p.qk_scale;
+              mx = fmaxf(mx, s[kt][r]);
+            }
+        } else {
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int kpos = k0 + kt * BS + g4 * 4 + r;
+              const bool vis = blk_ok[kt] && kpos < nkeys && kpos <= qpos[g] && qreal[g];
+              s[kt][r] = vis ? S[g][kt][r] * p.qk_scale : -__builtin_inff();
+              mx = fmaxf(mx, s[kt][r]);
+            }
+        }
+        mx = fmaxf(mx, swz_xor16(mx));
+        mx = fmaxf(mx, xor32(mx));
+        const float mn = fmaxf(m[g], mx);
+        const float mref = mn == -__builtin_inff() ? 0.f : mn;   // a row with nothing visible yet stays empty
+        const float alpha = exp2_fast(m[g] - mref);
+        float pr[2][4];
+        float ps = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            pr[kt][r] = exp2_fast(s[kt][r] - mref);
+            ps += pr[kt][r];
+          }
+        lsum[g] = lsum[g] * alpha + ps;
+        m[g] = mn;
+        pk[g] = make_uint4(Op::pack(pr[0][0], pr[0][1]), Op::pack(pr[0][2], pr[0][3]), Op::pack(pr[1][0], pr[1][1]),
+                           Op::pack(pr[1][2], pr[1][3]));
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) O[g][dt] *= alpha;
       }
-      float s[2][4];
-      float mx = -__builtin_inff();
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int kpos = i * STEP + kt * BS + g4 * 4 + r;
-          const bool vis = blk_ok[kt] && kpos < nkeys && kpos <= qpos && qreal;
-          s[kt][r] = vis ? S[kt][r] * p.qk_scale : -__builtin_inff();
-          mx = fmaxf(mx, s[kt][r]);
-        }
-      mx = fmaxf(mx, swz_xor16(mx));
-      mx = fmaxf(mx, xor32(mx));
-      const float mn = fmaxf(m, mx);
-      const float mref = mn == -__builtin_inff() ? 0.f : mn;   // a row with nothing visible yet stays empty
-      const float alpha = exp2_fast(m - mref);
-      float pr[2][4];
-      float ps = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pr[kt][r] = exp2_fast(s[kt][r] - mref);
-          ps += pr[kt][r];
-        }
-      lsum = lsum * alpha + ps;
-      m = mn;
-      uint2 pk[2];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-        pk[kt] = make_uint2(Op::pack(pr[kt][0], pr[kt][1]), Op::pack(pr[kt][2], pr[kt][3]));
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt) {
-        O[dt] *= alpha;
+        const uint4 vf = *reinterpret_cast<const uint4*>(&sm.vt[buf][(dt * 16 + c16) * P::VSTR + g4 * 8]);
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          const uint2 vf =
-              *reinterpret_cast<const uint2*>(&sm.vt[buf][(dt * 16 + c16) * P::VSTR + kt * 16 + g4 * 4]);
-          O[dt] = Op::pv(vf, pk[kt], O[dt]);
-        }
+        for (int g = 0; g < RW; ++g) O[g][dt] = Op::mma(vf, pk[g], O[g][dt]);
       }
     }
     if (i + 1 < nsteps) store_step((i + 1) & 1);
     __syncthreads();
   }
 
-  // normalise and write: lane l holds out[query 16w + c16][dims 16 dt + 4 g4 + r]
-  lsum += swz_xor16(lsum);
-  lsum += xor32(lsum);
-  if (qreal) {
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    const size_t orow = ((size_t)(q0 + qrow) * p.num_heads + h) * D;
+  // normalise and write: lane l holds out[row wrow0 + 16 g + c16][dims 16 dt + 4 g4 + r]
 #pragma unroll
-    for (int dt = 0; dt < ND; ++dt) {
-      const size_t e = orow + dt * 16 + g4 * 4;
-      uint2 v;
-      if constexpr (T::kId == BF16::kId) {
-        v = make_uint2((uint32_t)f32_to_bf16_rne(O[dt][0] * inv) | ((uint32_t)f32_to_bf16_rne(O[dt][1] * inv) << 16),
-                       (uint32_t)f32_to_bf16_rne(O[dt][2] * inv) | ((uint32_t)f32_to_bf16_rne(O[dt][3] * inv) << 16));
-      } else {
-        v = make_uint2(PrefillOp<F16>::pack(O[dt][0] * inv, O[dt][1] * inv),
-                       PrefillOp<F16>::pack(O[dt][2] * inv, O[dt][3] * inv));
+  for (int g = 0; g < RW; ++g) {
+    float ls = lsum[g];
+    ls += swz_xor16(ls);
+    ls += xor32(ls);
+    if (qreal[g]) {
+      const float inv = ls > 0.f ? 1.f / ls : 0.f;
+      const size_t orow = ((size_t)(q0 + wrow0 + 16 * g + c16) * p.num_heads + h) * D;
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) {
+        const uint2 v = make_uint2(Op::pack(O[g][dt][0] * inv, O[g][dt][1] * inv),
+                                   Op::pack(O[g][dt][2] * inv, O[g][dt][3] * inv));
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + orow + dt * 16 + g4 * 4) = v;
       }
-      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + e) = v;
     }
   }
 }
+
+#ifndef PKV_PREFILL_RW
+#define PKV_PREFILL_RW 2
+#endif
 
 bool prefill_supported(int q_dtype, int kv_dtype, int head_dim, int block_size) {
   return q_dtype == kv_dtype && (q_dtype == F16::kId || q_dtype == BF16::kId) && (head_dim == 64 || head_dim == 128) &&
          block_size == 16;
 }
 
-int prefill_tile_rows() { return Prefill<F16, 128>::BM; }
+int prefill_tile_rows() { return Prefill<F16, 128, PKV_PREFILL_RW>::BM; }
 
 template <class T, int D>
 static hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((prefill_mfma_kernel<T, D>), dim3(p.total_wgs), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((prefill_mfma_kernel<T, D, PKV_PREFILL_RW>), dim3(p.total_wgs), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
