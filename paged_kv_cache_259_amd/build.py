@@ -32,10 +32,18 @@ FLAGS = [
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 
+# Per-file code generation options.  The prefill kernel rescales its MFMA
+# accumulators only on some steps; kept in AGPRs, the compiler copies all of
+# them to VGPRs on every step to serve that branch, so its MFMAs use VGPRs.
+FILE_FLAGS = {
+    "prefill_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
 
 def _compile(src, extra=()):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, f"-I{os.path.dirname(src)}", *extra, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), f"-I{os.path.dirname(src)}", *extra,
+           "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:

@@ -11,20 +11,24 @@
 // 32 tokens (two 16-token blocks):
 //   staging  256 threads load the step's K and V rows (16-byte loads through
 //            the block table) into registers one step ahead, then store them to
-//            LDS: K row-major [token][dim]; V transposed [dim][token] with the
-//            tokens of a step in the order the QK result holds them (below).
+//            LDS row-major [token][dim] with 16-byte stores.
 //   QK       S^T[token][query] = sum_k K[token][k] Q[query][k]
 //            v_mfma_f32_16x16x32 (f16/bf16), A = K rows from LDS (read once,
 //            used by both row groups), B = Q^T held in registers; lane l gets
 //            tokens 4(l/16)+r and 16+4(l/16)+r (r = 0..3) of query l%16.
 //   softmax  causal / context mask (only on steps that straddle a boundary),
-//            running max over the 32 tokens (the lane's 8 values, then lanes
-//            l^16 and l^32), exp2 in the log2 domain.
+//            max over the 32 tokens (the lane's 8 values, then lanes l^16 and
+//            l^32), exp2 in the log2 domain against a reference max that moves
+//            only when a row's max grows by more than 2^8.
 //   PV       O^T[dim][query] += sum_k V^T[dim][token_k] P^T[token_k][query]
 //            v_mfma_f32_16x16x32 again: the contraction index k of lane group
 //            l/16 is its 8 tokens above, so B = P^T is exactly the lane's own
-//            8 softmax weights rounded to the input type, and A = V^T is one
-//            16-byte LDS read of a row of the reordered V^T tile.
+//            8 softmax weights rounded to the input type.  A = V^T comes from
+//            the row-major V tile through the transposing LDS read
+//            ds_read_b64_tr_b16: within a 16-lane group, output lane j gets
+//            element j%4 of the 4 values at lane 4m + j/4's address, for
+//            m = 0..3; lane (c16, g4) points at token 4 g4 + c16/4, dims
+//            d0 + 4 (c16%4) .. +3, so it receives V[4 g4 + m][d0 + c16].
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -52,6 +56,17 @@ template <> struct PrefillOp<F16> {
   }
 };
 
+constexpr float kRescale = 8.f;
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// ds_read_b64_tr_b16 on an LDS address (8-byte aligned)
+__device__ __forceinline__ uint2 read_tr16(const uint16_t* lds) {
+  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(lds));
+  return __builtin_bit_cast(uint2, v);
+}
+
 template <class T, int D, int RW>
 struct Prefill {
   static constexpr int BS = 16;                 // tokens per block
@@ -63,16 +78,12 @@ struct Prefill {
   static constexpr int CPR = D / 8;             // 16-byte chunks per token row
   static constexpr int CH = STEP * CPR / (NW * 64);   // chunks per thread per tensor per step
   static constexpr int KSTR = D + 8;            // LDS row stride of K (elements)
-  static constexpr int VSTR = STEP + 8;         // LDS row stride of V^T (elements)
+  static constexpr int VSTR = D + 16;           // LDS row stride of V: 4 rows of a transposing read hit distinct banks
   static_assert(CH == 1 || CH == 2, "staging covers a step with one or two chunks per thread");
-
-  // column of token t (0..31) of a step in the V^T tile: lane group g = (t%16)/4
-  // reads columns 8g .. 8g+7 = tokens 4g..4g+3, then 16+4g..16+4g+3
-  __device__ __forceinline__ static int vcol(int t) { return 8 * ((t & 15) >> 2) + 4 * (t >> 4) + (t & 3); }
 
   struct Smem {
     alignas(16) uint16_t k[2][STEP * KSTR];
-    alignas(16) uint16_t vt[2][D * VSTR];
+    alignas(16) uint16_t v[2][STEP * VSTR];
   };
 };
 
@@ -148,9 +159,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
   const uint16_t* kpool = reinterpret_cast<const uint16_t*>(p.k_cache) + (size_t)kvh * BS * D;
   const uint16_t* vpool = reinterpret_cast<const uint16_t*>(p.v_cache) + (size_t)kvh * BS * D;
 
-  // staging assignment: chunk column `col` of token stok + j (j < CH); with two
-  // chunks a thread holds the same columns of two adjacent tokens, which sit in
-  // adjacent V^T columns, so their V values go to LDS as 32-bit pairs
+  // staging assignment: 16-byte chunk column `col` of tokens stok .. stok + CH - 1
   const int col = tid % CPR;
   const int stok = (tid / CPR) * CH;
   uint4 kreg[CH], vreg[CH];
@@ -167,24 +176,13 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
   };
   auto store_step = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < CH; ++j)
+    for (int j = 0; j < CH; ++j) {
       *reinterpret_cast<uint4*>(&sm.k[buf][(stok + j) * P::KSTR + col * 8]) = kreg[j];
-    uint16_t* vt = &sm.vt[buf][(col * 8) * P::VSTR + P::vcol(stok)];
-    if constexpr (CH == 2) {
-      const uint32_t a[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
-      const uint32_t b[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t lo = (a[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-        const uint32_t hi = (b[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-        *reinterpret_cast<uint32_t*>(vt + e * P::VSTR) = lo | (hi << 16);
-      }
-    } else {
-      const uint32_t a[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vt[e * P::VSTR] = (uint16_t)(a[e >> 1] >> (16 * (e & 1)));
+      *reinterpret_cast<uint4*>(&sm.v[buf][(stok + j) * P::VSTR + col * 8]) = vreg[j];
     }
   };
+  // transposing-read address of this lane inside a V tile: token 4 g4 + c16/4, dims 4 (c16%4) ..
+  const int vrd = (g4 * 4 + (c16 >> 2)) * P::VSTR + 4 * (c16 & 3);
 
   if (nsteps > 0) {
     load_step(0);
@@ -246,9 +244,20 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
         }
         mx = fmaxf(mx, swz_xor16(mx));
         mx = fmaxf(mx, xor32(mx));
-        const float mn = fmaxf(m[g], mx);
-        const float mref = mn == -__builtin_inff() ? 0.f : mn;   // a row with nothing visible yet stays empty
-        const float alpha = exp2_fast(m[g] - mref);
+        // The reference max only moves when a row's max grows by more than
+        // kRescale (log2 domain): softmax does not depend on the reference, the
+        // weights stay <= 2^kRescale, and the accumulators are rescaled on few
+        // steps (a wave-uniform branch) instead of every step.
+        const bool grow = mx > m[g] + kRescale;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+          const float mn = grow ? mx : m[g];
+          const float alpha = m[g] == -__builtin_inff() ? 0.f : exp2_fast(m[g] - mn);
+          lsum[g] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < ND; ++dt) O[g][dt] *= alpha;
+          m[g] = mn;
+        }
+        const float mref = m[g] == -__builtin_inff() ? 0.f : m[g];   // nothing visible yet: weights are 0
         float pr[2][4];
         float ps = 0.f;
 #pragma unroll
@@ -258,16 +267,15 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
             pr[kt][r] = exp2_fast(s[kt][r] - mref);
             ps += pr[kt][r];
           }
-        lsum[g] = lsum[g] * alpha + ps;
-        m[g] = mn;
+        lsum[g] += ps;
         pk[g] = make_uint4(Op::pack(pr[0][0], pr[0][1]), Op::pack(pr[0][2], pr[0][3]), Op::pack(pr[1][0], pr[1][1]),
                            Op::pack(pr[1][2], pr[1][3]));
-#pragma unroll
-        for (int dt = 0; dt < ND; ++dt) O[g][dt] *= alpha;
       }
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt) {
-        const uint4 vf = *reinterpret_cast<const uint4*>(&sm.vt[buf][(dt * 16 + c16) * P::VSTR + g4 * 8]);
+        const uint2 lo = read_tr16(&sm.v[buf][vrd + dt * 16]);                 // tokens 4 g4 + m
+        const uint2 hi = read_tr16(&sm.v[buf][vrd + 16 * P::VSTR + dt * 16]);  // tokens 16 + 4 g4 + m
+        const uint4 vf = make_uint4(lo.x, lo.y, hi.x, hi.y);
 #pragma unroll
         for (int g = 0; g < RW; ++g) O[g][dt] = Op::mma(vf, pk[g], O[g][dt]);
       }
