@@ -162,46 +162,37 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
   // staging assignment: 16-byte chunk column `col` of tokens stok .. stok + CH - 1
   const int col = tid % CPR;
   const int stok = (tid / CPR) * CH;
-  uint4 kreg[CH], vreg[CH];
-  auto load_step = [&](int i) {
+  const int nkblk = (nkeys + BS - 1) / BS;
+  // block ids of step st's two blocks (-1 past the keys); uniform, so scalar loads
+  auto ids_of = [&](int st) -> int2 {
+    return make_int2(2 * st < nkblk ? table[2 * st] : -1, 2 * st + 1 < nkblk ? table[2 * st + 1] : -1);
+  };
+  auto load_step = [&](int i, int2 ids, uint4 (&kr)[CH], uint4 (&vr)[CH]) {
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
       const int pos = i * STEP + stok + j;
-      const int blk = pos < nkeys ? table[pos / BS] : -1;
+      const int blk = pos < nkeys ? (stok + j < BS ? ids.x : ids.y) : -1;
       const bool ok = blk >= 0 && blk < p.num_blocks;
       const size_t off = (size_t)blk * block_stride + (size_t)(pos % BS) * D + col * 8;
-      kreg[j] = ok ? *reinterpret_cast<const uint4*>(kpool + off) : make_uint4(0u, 0u, 0u, 0u);
-      vreg[j] = ok ? *reinterpret_cast<const uint4*>(vpool + off) : make_uint4(0u, 0u, 0u, 0u);
+      kr[j] = ok ? *reinterpret_cast<const uint4*>(kpool + off) : make_uint4(0u, 0u, 0u, 0u);
+      vr[j] = ok ? *reinterpret_cast<const uint4*>(vpool + off) : make_uint4(0u, 0u, 0u, 0u);
     }
   };
-  auto store_step = [&](int buf) {
+  auto store_step = [&](int buf, const uint4 (&kr)[CH], const uint4 (&vr)[CH]) {
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-      *reinterpret_cast<uint4*>(&sm.k[buf][(stok + j) * P::KSTR + col * 8]) = kreg[j];
-      *reinterpret_cast<uint4*>(&sm.v[buf][(stok + j) * P::VSTR + col * 8]) = vreg[j];
+      *reinterpret_cast<uint4*>(&sm.k[buf][(stok + j) * P::KSTR + col * 8]) = kr[j];
+      *reinterpret_cast<uint4*>(&sm.v[buf][(stok + j) * P::VSTR + col * 8]) = vr[j];
     }
   };
   // transposing-read address of this lane inside a V tile: token 4 g4 + c16/4, dims 4 (c16%4) ..
   const int vrd = (g4 * 4 + (c16 >> 2)) * P::VSTR + 4 * (c16 & 3);
 
-  if (nsteps > 0) {
-    load_step(0);
-    store_step(0);
-  }
-  __syncthreads();
-  for (int i = 0; i < nsteps; ++i) {
-    const int buf = i & 1;
-    if (i + 1 < nsteps) load_step(i + 1);
+  auto compute = [&](int i, int buf, int2 ids) {
     const int k0 = i * STEP;
     if (k0 <= wave_last_pos) {                              // wave-uniform: some key of the step is visible
       // blocks of this step that the table maps outside the pool are skipped
-      bool blk_ok[2];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const int pos = k0 + kt * BS;
-        const int b = pos < nkeys ? table[pos / BS] : -1;
-        blk_ok[kt] = b >= 0 && b < p.num_blocks;
-      }
+      const bool blk_ok[2] = {ids.x >= 0 && ids.x < p.num_blocks, ids.y >= 0 && ids.y < p.num_blocks};
       // every key of the step visible to every row of the wave: no per-element mask
       const bool interior = k0 + STEP - 1 <= wave_first_pos && k0 + STEP <= nkeys && blk_ok[0] && blk_ok[1] &&
                             wave_rows_real;
@@ -280,8 +271,33 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
         for (int g = 0; g < RW; ++g) O[g][dt] = Op::mma(vf, pk[g], O[g][dt]);
       }
     }
-    if (i + 1 < nsteps) store_step((i + 1) & 1);
+  };
+
+  // Pipeline: K/V rows of step i+2 are loaded into one register set while step i
+  // is computed from LDS and step i+1 (loaded a step earlier into the other set)
+  // waits to be stored; block ids come three steps ahead.  Unrolled by two so
+  // both register sets are named statically.
+  uint4 kA[CH], vA[CH], kB[CH], vB[CH];
+  int2 id0 = ids_of(0), id1 = ids_of(1), id2 = ids_of(2);
+  if (nsteps > 0) load_step(0, id0, kA, vA);
+  if (nsteps > 1) load_step(1, id1, kB, vB);
+  if (nsteps > 0) store_step(0, kA, vA);
+  __syncthreads();
+  for (int i = 0; i < nsteps; i += 2) {
+    const int2 id3 = ids_of(i + 3);
+    if (i + 2 < nsteps) load_step(i + 2, id2, kA, vA);
+    compute(i, 0, id0);
+    if (i + 1 < nsteps) store_step(1, kB, vB);
     __syncthreads();
+    if (i + 1 >= nsteps) break;                             // workgroup-uniform
+    const int2 id4 = ids_of(i + 4);
+    if (i + 3 < nsteps) load_step(i + 3, id3, kB, vB);
+    compute(i + 1, 1, id1);
+    if (i + 2 < nsteps) store_step(0, kA, vA);
+    __syncthreads();
+    id0 = id2;
+    id1 = id3;
+    id2 = id4;
   }
 
   // normalise and write: lane l holds out[row wrow0 + 16 g + c16][dims 16 dt + 4 g4 + r]
