@@ -312,6 +312,7 @@ int pkv_paged_prefill_attention(void* out, const void* q, const void* k_cache, c
   const long long cap_table = (long long)max_blocks_per_seq * block_size;
   p.ctx_cap = (int)(max_context_len < cap_table ? max_context_len : cap_table);
   p.qk_scale = scale * kLog2e;
+  p.longest_first = PKV_LONGEST_FIRST && num_seqs > 1 && num_seqs <= pkv::kMaxSliceSeqs;
   p.total_wgs = (uint32_t)wgs;
   // the query tiles and heads that read one kv head's K/V run on one XCD (shared L2)
   const char* e = getenv("PKV_PREFILL_XCD_CHUNK");

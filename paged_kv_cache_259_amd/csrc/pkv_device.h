@@ -414,6 +414,7 @@ struct PrefillParams {
   int max_query_len;
   int q_tiles;                     // query tiles per sequence in the grid
   int ctx_cap;
+  int longest_first;               // sequences dispatched in decreasing context length
   float qk_scale;                  // scale * log2(e)
   uint32_t total_wgs;
   uint32_t xcd_chunk;

@@ -58,6 +58,13 @@ template <> struct PrefillOp<F16> {
 
 constexpr float kRescale = 8.f;
 
+#ifndef PKV_PREFILL_RW
+#define PKV_PREFILL_RW 2      // 16-row query groups per wave
+#endif
+#ifndef PKV_PREFILL_NS
+#define PKV_PREFILL_NS 2      // 32-token PV k-steps per pipeline step
+#endif
+
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
@@ -70,7 +77,9 @@ __device__ __forceinline__ uint2 read_tr16(const uint16_t* lds) {
 template <class T, int D, int RW>
 struct Prefill {
   static constexpr int BS = 16;                 // tokens per block
-  static constexpr int STEP = 32;               // tokens per step (two blocks)
+  static constexpr int NS = PKV_PREFILL_NS;     // PV k-steps (32 tokens each) per step
+  static constexpr int STEP = 32 * NS;          // tokens per step
+  static constexpr int KT = STEP / 16;          // blocks per step
   static constexpr int NW = 4;
   static constexpr int BM = NW * 16 * RW;       // query rows per workgroup
   static constexpr int NC = D / 32;             // QK k-steps of 32 dims
@@ -79,7 +88,7 @@ struct Prefill {
   static constexpr int CH = STEP * CPR / (NW * 64);   // chunks per thread per tensor per step
   static constexpr int KSTR = D + 8;            // LDS row stride of K (elements)
   static constexpr int VSTR = D + 16;           // LDS row stride of V: 4 rows of a transposing read hit distinct banks
-  static_assert(CH == 1 || CH == 2, "staging covers a step with one or two chunks per thread");
+  static_assert(CH == 1 || CH == 2 || CH == 4, "staging: 1, 2 or 4 chunks per thread per step");
 
   struct Smem {
     alignas(16) uint16_t k[2][STEP * KSTR];
@@ -91,7 +100,9 @@ template <class T, int D, int RW>
 __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
   using P = Prefill<T, D, RW>;
   using Op = PrefillOp<T>;
-  constexpr int STEP = P::STEP, BS = P::BS, NC = P::NC, ND = P::ND, CPR = P::CPR, CH = P::CH;
+  constexpr int STEP = P::STEP, BS = P::BS, NC = P::NC, ND = P::ND, CPR = P::CPR, CH = P::CH, KT = P::KT,
+                NS = P::NS;
+  struct StepIds { int b[KT]; };                            // block ids of one step (-1 past the keys)
   __shared__ typename P::Smem sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -99,12 +110,16 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
   const int c16 = lane & 15;
   const int g4 = lane >> 4;
 
-  // work id: query tiles fastest (longest first), then head, then sequence
+  // work id: query tiles fastest (last tile first), then head, then sequence;
+  // sequences in decreasing context length (longest first) when asked
   const uint32_t L = xcd_remap(blockIdx.x, p.total_wgs, p.xcd_chunk);
   const int tile = p.q_tiles - 1 - (int)(L % (uint32_t)p.q_tiles);
   const uint32_t rest = L / (uint32_t)p.q_tiles;
   const int h = (int)(rest % (uint32_t)p.num_heads);
-  const int seq = (int)(rest / (uint32_t)p.num_heads);
+  int seq = (int)(rest / (uint32_t)p.num_heads);
+  if (p.longest_first)   // LDS scratch borrowed from the K tiles, which are first written after its last barrier
+    seq = seq_of_rank<P::NW * 64>(p.context_lens, p.num_seqs, p.ctx_cap, BS, seq, reinterpret_cast<int*>(&sm.k[0][0]),
+                                  reinterpret_cast<int*>(&sm.k[1][0]));
   const int kvh = h / p.group;
 
   // rows [q0, q1) of q / out; offsets are clamped to the num_tokens rows that exist
@@ -163,15 +178,21 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
   const int col = tid % CPR;
   const int stok = (tid / CPR) * CH;
   const int nkblk = (nkeys + BS - 1) / BS;
-  // block ids of step st's two blocks (-1 past the keys); uniform, so scalar loads
-  auto ids_of = [&](int st) -> int2 {
-    return make_int2(2 * st < nkblk ? table[2 * st] : -1, 2 * st + 1 < nkblk ? table[2 * st + 1] : -1);
+  // block ids of step st; uniform, so scalar loads
+  auto ids_of = [&](int st) -> StepIds {
+    StepIds r;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) r.b[kt] = KT * st + kt < nkblk ? table[KT * st + kt] : -1;
+    return r;
   };
-  auto load_step = [&](int i, int2 ids, uint4 (&kr)[CH], uint4 (&vr)[CH]) {
+  auto load_step = [&](int i, const StepIds& ids, uint4 (&kr)[CH], uint4 (&vr)[CH]) {
+    int sid = ids.b[0];                                     // the block of tokens stok .. stok + CH - 1
+#pragma unroll
+    for (int kt = 1; kt < KT; ++kt) sid = stok / BS == kt ? ids.b[kt] : sid;
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
       const int pos = i * STEP + stok + j;
-      const int blk = pos < nkeys ? (stok + j < BS ? ids.x : ids.y) : -1;
+      const int blk = pos < nkeys ? sid : -1;
       const bool ok = blk >= 0 && blk < p.num_blocks;
       const size_t off = (size_t)blk * block_stride + (size_t)(pos % BS) * D + col * 8;
       kr[j] = ok ? *reinterpret_cast<const uint4*>(kpool + off) : make_uint4(0u, 0u, 0u, 0u);
@@ -188,35 +209,40 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
   // transposing-read address of this lane inside a V tile: token 4 g4 + c16/4, dims 4 (c16%4) ..
   const int vrd = (g4 * 4 + (c16 >> 2)) * P::VSTR + 4 * (c16 & 3);
 
-  auto compute = [&](int i, int buf, int2 ids) {
+  auto compute = [&](int i, int buf, const StepIds& ids) {
     const int k0 = i * STEP;
     if (k0 <= wave_last_pos) {                              // wave-uniform: some key of the step is visible
       // blocks of this step that the table maps outside the pool are skipped
-      const bool blk_ok[2] = {ids.x >= 0 && ids.x < p.num_blocks, ids.y >= 0 && ids.y < p.num_blocks};
+      bool blk_ok[KT];
+      bool all_ok = true;
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        blk_ok[kt] = ids.b[kt] >= 0 && ids.b[kt] < p.num_blocks;
+        all_ok = all_ok && blk_ok[kt];
+      }
       // every key of the step visible to every row of the wave: no per-element mask
-      const bool interior = k0 + STEP - 1 <= wave_first_pos && k0 + STEP <= nkeys && blk_ok[0] && blk_ok[1] &&
-                            wave_rows_real;
-      f32x4_t S[RW][2];
+      const bool interior = k0 + STEP - 1 <= wave_first_pos && k0 + STEP <= nkeys && all_ok && wave_rows_real;
+      f32x4_t S[RW][KT];
 #pragma unroll
       for (int g = 0; g < RW; ++g)
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) S[g][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int kt = 0; kt < KT; ++kt) S[g][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           const uint4 kf = *reinterpret_cast<const uint4*>(&sm.k[buf][(kt * 16 + c16) * P::KSTR + c * 32 + g4 * 8]);
 #pragma unroll
           for (int g = 0; g < RW; ++g) S[g][kt] = Op::mma(kf, qf[g][c], S[g][kt]);
         }
-      uint4 pk[RW];
+      uint4 pk[RW][NS];
 #pragma unroll
       for (int g = 0; g < RW; ++g) {
-        float s[2][4];
+        float s[KT][4];
         float mx = -__builtin_inff();
         if (interior) {
 #pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
+          for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               s[kt][r] = S[g][kt][r] * p.qk_scale;
@@ -224,7 +250,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
             }
         } else {
 #pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
+          for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const int kpos = k0 + kt * BS + g4 * 4 + r;
@@ -249,27 +275,33 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
           m[g] = mn;
         }
         const float mref = m[g] == -__builtin_inff() ? 0.f : m[g];   // nothing visible yet: weights are 0
-        float pr[2][4];
+        float pr[KT][4];
         float ps = 0.f;
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             pr[kt][r] = exp2_fast(s[kt][r] - mref);
             ps += pr[kt][r];
           }
         lsum[g] += ps;
-        pk[g] = make_uint4(Op::pack(pr[0][0], pr[0][1]), Op::pack(pr[0][2], pr[0][3]), Op::pack(pr[1][0], pr[1][1]),
-                           Op::pack(pr[1][2], pr[1][3]));
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns)
+          pk[g][ns] = make_uint4(Op::pack(pr[2 * ns][0], pr[2 * ns][1]), Op::pack(pr[2 * ns][2], pr[2 * ns][3]),
+                                 Op::pack(pr[2 * ns + 1][0], pr[2 * ns + 1][1]),
+                                 Op::pack(pr[2 * ns + 1][2], pr[2 * ns + 1][3]));
       }
 #pragma unroll
-      for (int dt = 0; dt < ND; ++dt) {
-        const uint2 lo = read_tr16(&sm.v[buf][vrd + dt * 16]);                 // tokens 4 g4 + m
-        const uint2 hi = read_tr16(&sm.v[buf][vrd + 16 * P::VSTR + dt * 16]);  // tokens 16 + 4 g4 + m
-        const uint4 vf = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
-        for (int g = 0; g < RW; ++g) O[g][dt] = Op::mma(vf, pk[g], O[g][dt]);
-      }
+        for (int dt = 0; dt < ND; ++dt) {
+          const uint16_t* vb = &sm.v[buf][vrd + 32 * ns * P::VSTR + dt * 16];
+          const uint2 lo = read_tr16(vb);                   // tokens 32 ns + 4 g4 + m
+          const uint2 hi = read_tr16(vb + 16 * P::VSTR);    // tokens 32 ns + 16 + 4 g4 + m
+          const uint4 vf = make_uint4(lo.x, lo.y, hi.x, hi.y);
+#pragma unroll
+          for (int g = 0; g < RW; ++g) O[g][dt] = Op::mma(vf, pk[g][ns], O[g][dt]);
+        }
     }
   };
 
@@ -278,19 +310,19 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
   // waits to be stored; block ids come three steps ahead.  Unrolled by two so
   // both register sets are named statically.
   uint4 kA[CH], vA[CH], kB[CH], vB[CH];
-  int2 id0 = ids_of(0), id1 = ids_of(1), id2 = ids_of(2);
+  StepIds id0 = ids_of(0), id1 = ids_of(1), id2 = ids_of(2);
   if (nsteps > 0) load_step(0, id0, kA, vA);
   if (nsteps > 1) load_step(1, id1, kB, vB);
   if (nsteps > 0) store_step(0, kA, vA);
   __syncthreads();
   for (int i = 0; i < nsteps; i += 2) {
-    const int2 id3 = ids_of(i + 3);
+    const StepIds id3 = ids_of(i + 3);
     if (i + 2 < nsteps) load_step(i + 2, id2, kA, vA);
     compute(i, 0, id0);
     if (i + 1 < nsteps) store_step(1, kB, vB);
     __syncthreads();
     if (i + 1 >= nsteps) break;                             // workgroup-uniform
-    const int2 id4 = ids_of(i + 4);
+    const StepIds id4 = ids_of(i + 4);
     if (i + 3 < nsteps) load_step(i + 3, id3, kB, vB);
     compute(i + 1, 1, id1);
     if (i + 2 < nsteps) store_step(0, kA, vA);
@@ -319,9 +351,6 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
   }
 }
 
-#ifndef PKV_PREFILL_RW
-#define PKV_PREFILL_RW 2
-#endif
 
 bool prefill_supported(int q_dtype, int kv_dtype, int head_dim, int block_size) {
   return q_dtype == kv_dtype && (q_dtype == F16::kId || q_dtype == BF16::kId) && (head_dim == 64 || head_dim == 128) &&
