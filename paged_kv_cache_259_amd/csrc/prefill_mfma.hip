@@ -64,6 +64,9 @@ constexpr float kRescale = 8.f;
 #ifndef PKV_PREFILL_NS
 #define PKV_PREFILL_NS 2      // 32-token PV k-steps per pipeline step
 #endif
+#ifndef PKV_PREFILL_AHEAD
+#define PKV_PREFILL_AHEAD 1   // steps between loading a step's K/V rows and computing it
+#endif
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
@@ -185,7 +188,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
     for (int kt = 0; kt < KT; ++kt) r.b[kt] = KT * st + kt < nkblk ? table[KT * st + kt] : -1;
     return r;
   };
-  auto load_step = [&](int i, const StepIds& ids, uint4 (&kr)[CH], uint4 (&vr)[CH]) {
+  auto load_step = [&](int i, StepIds ids, uint4 (&kr)[CH], uint4 (&vr)[CH]) {
     int sid = ids.b[0];                                     // the block of tokens stok .. stok + CH - 1
 #pragma unroll
     for (int kt = 1; kt < KT; ++kt) sid = stok / BS == kt ? ids.b[kt] : sid;
@@ -209,7 +212,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
   // transposing-read address of this lane inside a V tile: token 4 g4 + c16/4, dims 4 (c16%4) ..
   const int vrd = (g4 * 4 + (c16 >> 2)) * P::VSTR + 4 * (c16 & 3);
 
-  auto compute = [&](int i, int buf, const StepIds& ids) {
+  auto compute = [&](int i, int buf, StepIds ids) {
     const int k0 = i * STEP;
     if (k0 <= wave_last_pos) {                              // wave-uniform: some key of the step is visible
       // blocks of this step that the table maps outside the pool are skipped
@@ -305,6 +308,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
     }
   };
 
+#if PKV_PREFILL_AHEAD == 2
   // Pipeline: K/V rows of step i+2 are loaded into one register set while step i
   // is computed from LDS and step i+1 (loaded a step earlier into the other set)
   // waits to be stored; block ids come three steps ahead.  Unrolled by two so
@@ -331,6 +335,27 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
     id1 = id3;
     id2 = id4;
   }
+#else
+  // Pipeline: K/V rows of step i+1 are loaded into registers while step i is
+  // computed from LDS, then stored to the other LDS buffer; block ids come two
+  // steps ahead.
+  uint4 kA[CH], vA[CH];
+  StepIds id0 = ids_of(0), id1 = ids_of(1);
+  if (nsteps > 0) {
+    load_step(0, id0, kA, vA);
+    store_step(0, kA, vA);
+  }
+  __syncthreads();
+  for (int i = 0; i < nsteps; ++i) {
+    const StepIds id2 = ids_of(i + 2);
+    if (i + 1 < nsteps) load_step(i + 1, id1, kA, vA);
+    compute(i, i & 1, id0);
+    if (i + 1 < nsteps) store_step((i + 1) & 1, kA, vA);
+    __syncthreads();
+    id0 = id1;
+    id1 = id2;
+  }
+#endif
 
   // normalise and write: lane l holds out[row wrow0 + 16 g + c16][dims 16 dt + 4 g4 + r]
 #pragma unroll
