@@ -348,7 +348,7 @@ __device__ int seq_of_rank(const int32_t* context_lens, int S, int ctx_cap, int 
     before -= chunk_total;
   }
   __syncthreads();
-  return *s_pick;
+  return __builtin_amdgcn_readfirstlane(*s_pick);           // the same in every lane: keep it scalar
 }
 
 struct AttnParams {

@@ -146,7 +146,11 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
   const int wave_last_pos = wave_first_pos + 16 * RW - 1;   // causal limit of the wave's rows
   const bool wave_rows_real = wrow0 + 16 * RW <= n;
 
-  // B operand of QK: Q^T, lane l holds query row wrow0 + 16 g + c16, dims 32c + 8 g4 .. +8
+  // B operand of QK: Q^T, lane l holds query row wrow0 + 16 g + c16, dims 32c + 8 g4 .. +8.
+  // With a negative scale Q enters negated (sign bits flipped, exact), so the
+  // logit scale qs applied to the products is never negative.
+  const uint32_t qsign = p.qk_scale < 0.f ? 0x80008000u : 0u;
+  const float qs = fabsf(p.qk_scale);
   uint4 qf[RW][NC];
   int qpos[RW];
   bool qreal[RW];
@@ -158,8 +162,10 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
     const uint16_t* qp =
         reinterpret_cast<const uint16_t*>(p.q) + ((size_t)(q0 + (qreal[g] ? qrow : 0)) * p.num_heads + h) * D;
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
-      qf[g][c] = qreal[g] ? *reinterpret_cast<const uint4*>(qp + c * 32 + g4 * 8) : make_uint4(0u, 0u, 0u, 0u);
+    for (int c = 0; c < NC; ++c) {
+      const uint4 v = qreal[g] ? *reinterpret_cast<const uint4*>(qp + c * 32 + g4 * 8) : make_uint4(0u, 0u, 0u, 0u);
+      qf[g][c] = make_uint4(v.x ^ qsign, v.y ^ qsign, v.z ^ qsign, v.w ^ qsign);
+    }
   }
 
   float m[RW], lsum[RW];
@@ -241,6 +247,8 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
       uint4 pk[RW][NS];
 #pragma unroll
       for (int g = 0; g < RW; ++g) {
+        // logits in the log2 domain are qs * S; on interior steps the scale is
+        // folded into the exp2 argument (max commutes with qs >= 0)
         float s[KT][4];
         float mx = -__builtin_inff();
         if (interior) {
@@ -248,9 +256,10 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
           for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              s[kt][r] = S[g][kt][r] * p.qk_scale;
+              s[kt][r] = S[g][kt][r];
               mx = fmaxf(mx, s[kt][r]);
             }
+          mx *= qs;
         } else {
 #pragma unroll
           for (int kt = 0; kt < KT; ++kt)
@@ -258,7 +267,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
             for (int r = 0; r < 4; ++r) {
               const int kpos = k0 + kt * BS + g4 * 4 + r;
               const bool vis = blk_ok[kt] && kpos < nkeys && kpos <= qpos[g] && qreal[g];
-              s[kt][r] = vis ? S[g][kt][r] * p.qk_scale : -__builtin_inff();
+              s[kt][r] = vis ? S[g][kt][r] * qs : -__builtin_inff();
               mx = fmaxf(mx, s[kt][r]);
             }
         }
@@ -280,13 +289,23 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
         const float mref = m[g] == -__builtin_inff() ? 0.f : m[g];   // nothing visible yet: weights are 0
         float pr[KT][4];
         float ps = 0.f;
+        if (interior) {
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
+          for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            pr[kt][r] = exp2_fast(s[kt][r] - mref);
-            ps += pr[kt][r];
-          }
+            for (int r = 0; r < 4; ++r) {
+              pr[kt][r] = exp2_fast(fmaf(s[kt][r], qs, -mref));
+              ps += pr[kt][r];
+            }
+        } else {
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              pr[kt][r] = exp2_fast(s[kt][r] - mref);
+              ps += pr[kt][r];
+            }
+        }
         lsum[g] += ps;
 #pragma unroll
         for (int ns = 0; ns < NS; ++ns)

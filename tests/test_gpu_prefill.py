@@ -103,6 +103,20 @@ def test_prefill_matches_oracle(ops, H, KVH, d, dt, chunk, prior):
     assert err < TOL[dt][0] + TOL[dt][1] * 8
 
 
+@pytest.mark.parametrize("scale", [-0.07, 0.0])
+def test_prefill_negative_and_zero_scale(ops, scale):
+    """Any finite scale: a negative one (Q enters negated) and zero (uniform weights)."""
+    case = PrefillCase(_w(4, 2, 128, "bf16", 2), DEV, chunk=(100, 40), prior=(90, 0))
+    out = torch.full_like(case.inp.q, float("nan"))
+    ops.paged_prefill_attention(out, case.inp.q, case.k_cache, case.v_cache, torch.from_numpy(case.tables).to(DEV),
+                                torch.from_numpy(case.ctx).to(DEV), torch.from_numpy(case.qsl).to(DEV), scale,
+                                100, int(case.ctx.max()))
+    torch.cuda.synchronize()
+    ref = oracle.prefill_ref(as_f64(case.inp.q), as_f64(case.k_cache), as_f64(case.v_cache), case.tables, case.ctx,
+                             case.qsl, scale, 16)
+    check_close(as_f64(out), ref, TOL["bf16"], f"scale {scale}")
+
+
 def test_prefill_chunks_match_decode_for_one_token(ops):
     """A chunk of one token is a decode step: same numbers as the decode kernel (to tolerance)."""
     chunk, prior = (1,) * 5, (0, 15, 16, 300, 1000)
