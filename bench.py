@@ -4,7 +4,9 @@
 
 With a prefill workload (prefill_llama13b_f16, prefill_gqa_bf16) the step is
 reshape_and_cache of the chunks' K/V followed by paged_prefill_attention, and
-the roofline is the dense MFMA peak instead of HBM.
+the roofline is the dense MFMA peak instead of HBM.  prefix_cache_llama13b_f16
+times a prefill step of requests sharing a system prompt with the host prefix
+cache off and on (value = the speedup).
 
 A step is one pass of the hot path over one synthetic decode batch, inputs
 resident in HBM: reshape_and_cache writes every sequence's new key/value into
@@ -254,6 +256,119 @@ def main_prefill(args, w):
     print(json.dumps(result))
 
 
+def main_prefix_cache(args, w):
+    """A prefill step of requests sharing a system prompt, without and with the prefix cache.
+
+    Without: every request writes and attends its whole prompt.  With: the first
+    request does; the others hit the shared prompt's full blocks and write and
+    attend only their own tokens as a chunk over the cached context.  Each flow
+    is reshape_and_cache + one batched paged_prefill_attention call.
+    """
+    import torch
+    from paged_kv_cache_259_amd import ops, synth
+    from paged_kv_cache_259_amd.block_manager import BlockManager
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = synth.make_prefix_cache_inputs(w, device=dev)
+    R, L = w.num_requests, w.shared_len + w.unique_len
+    stream = torch.cuda.current_stream()
+    shape = (inp.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
+    flows = {}
+    for cache in (False, True):
+        bm = BlockManager(inp.num_blocks, w.block_size, inp.free_list, prefix_cache=cache)
+        slots, rows, chunk = [], [], []
+        for r in range(R):
+            if cache:
+                sl, cached = bm.add_sequence_cached(r, inp.prompts[r])
+            else:
+                sl, cached = bm.add_sequence(r, L), 0
+            slots += sl
+            rows += list(range(r * L + cached, (r + 1) * L))
+            chunk.append(L - cached)
+        rows_t = torch.tensor(rows, dtype=torch.int64, device=dev)
+        f = {"slots": torch.tensor(slots, dtype=torch.int64, device=dev), "q": inp.q.index_select(0, rows_t),
+             "k": inp.k.index_select(0, rows_t), "v": inp.v.index_select(0, rows_t),
+             "tables": torch.from_numpy(bm.block_table_array(list(range(R)), w.max_blocks_per_seq)).to(dev),
+             "ctx": torch.full((R,), L, dtype=torch.int32, device=dev),
+             "qsl": torch.from_numpy(np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)).to(dev),
+             "chunk": np.array(chunk, np.int64), "kc": torch.empty(shape, dtype=inp.q.dtype, device=dev),
+             "cached_blocks": bm.cached_blocks()}
+        f["kv"] = torch.empty_like(f["kc"])
+        f["out"] = torch.empty_like(f["q"])
+        flows["cache" if cache else "no_cache"] = f
+
+    def run(f):
+        ops.reshape_and_cache(f["k"], f["v"], f["kc"], f["kv"], f["slots"], stream=stream)
+        ops.paged_prefill_attention(f["out"], f["q"], f["kc"], f["kv"], f["tables"], f["ctx"], f["qsl"],
+                                    w.softmax_scale, int(f["chunk"].max()), L, stream=stream)
+
+    res = {}
+    for name, f in flows.items():
+        for _ in range(args.warmup):
+            run(f)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            run(f)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        flops = prefill_flops(w, np.full(R, L, np.int64), f["chunk"])
+        res[name] = {"ms_per_step": round(ms, 4), "query_tokens": int(f["chunk"].sum()),
+                     "kv_tokens_written": int(f["chunk"].sum()), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                     "cached_blocks": f["cached_blocks"]}
+    speedup = res["no_cache"]["ms_per_step"] / res["cache"]["ms_per_step"]
+    fc = flows["cache"]
+    flops_c = prefill_flops(w, np.full(R, L, np.int64), fc["chunk"])
+    result = {
+        "metric": "prefill step time of requests sharing a system prompt, prefix cache off / on",
+        "value": round(speedup, 3), "unit": "x", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": res["cache"]["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded token ids and N(0,1) q/K/V; shared-prefix K/V identical across requests)",
+        "config": {"workload": w.name, "requests": R, "shared_len": w.shared_len, "unique_len": w.unique_len},
+        "flows": res,
+        "roofline": {"bound": "mfma", "kernel": "reshape_and_cache + paged_prefill_attention (prefix cache on)",
+                     "achieved": round(flops_c / (res["cache"]["ms_per_step"] * 1e-3) / 1e12, 2),
+                     "peak": MFMA_PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s",
+                     "frac": round(flops_c / (res["cache"]["ms_per_step"] * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[w.dtype], 4),
+                     "traffic": None, "algorithmic_flops_per_call": int(flops_c)},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_prefix(w, inp, fc, args.cpu_seconds)
+    print(json.dumps(result))
+
+
+def cpu_baseline_prefix(w, inp, f, budget_s):
+    """The oracle's prefill_ref on the cached flow's chunks, one request at a time, until the budget is spent."""
+    import oracle
+    import torch
+    from threadpoolctl import threadpool_info
+    L = w.shared_len + w.unique_len
+    tables = f["tables"].cpu().numpy()
+    qsl = f["qsl"].cpu().numpy()
+    done, flops, spent = 0, 0, 0.0
+    for r in range(w.num_requests):
+        n = int(f["chunk"][r])
+        kp = _BlockSubset(f["kc"], tables[r, : -(-L // w.block_size)])
+        vp = _BlockSubset(f["kv"], tables[r, : -(-L // w.block_size)])
+        q = f["q"][int(qsl[r]):int(qsl[r + 1])].cpu().to(torch.float64).numpy()
+        t0 = time.perf_counter()
+        oracle.prefill_ref(q, kp, vp, tables[r:r + 1], np.array([L]), np.array([0, n]), w.softmax_scale, w.block_size)
+        spent += time.perf_counter() - t0
+        done += 1
+        flops += prefill_flops(w, np.array([L], np.int64), np.array([n], np.int64))
+        if spent > budget_s:
+            break
+    blas_threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"first {done} of {w.num_requests} requests' chunks of the cached flow, fp64 numpy oracle, "
+                      f"{spent:.1f} s wall",
+            "host_cores_available": len(os.sched_getaffinity(0))}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -270,6 +385,8 @@ def main():
     w = synth.WORKLOADS[args.workload]
     if isinstance(w, synth.PrefillWorkload):
         return main_prefill(args, w)
+    if isinstance(w, synth.PrefixCacheWorkload):
+        return main_prefix_cache(args, w)
     if not isinstance(w, synth.DecodeWorkload):
         raise SystemExit("bench.py times decode workloads (llama13b_f16, gqa_bf16, long_splitk_bf16, tiny_f32)")
     part = w.partition_size if args.partition is None else args.partition

@@ -19,6 +19,16 @@ physical block holds which tokens is host work, done here:
   chuỗi").  Sequences are served in the order the caller asks; the last holder
   of a shared block writes in place because its count has dropped to 1.
 
+With ``prefix_cache=True`` full blocks are also shared across requests: a full
+block is identified by its tokens and, through a chained key, by every token
+before it ([PA/sharing]: hashing whole blocks extends sharing across requests
+-- prompt caching; [vLLM-rev] feature list: prefix caching).  A request whose
+prompt starts with cached blocks points its table at them (reference count + 1)
+and only the remaining tokens need K/V written.  A cached block whose count
+drops to 0 keeps its contents and key until the free list is empty; then the
+least recently released one is reused.  A lookup compares the stored parent key
+and tokens exactly, so a hash collision can only cause a miss.
+
 Running out of blocks raises ``OutOfBlocks``.  Preemption is the caller's
 decision; ``preemption_victims`` gives the order the pages describe (requests
 served first come, first served; the most recent ones are preempted first, all
@@ -27,7 +37,7 @@ blocks to a second, host-side pool and back, returning the (src, dst) pairs for
 ``swap_blocks``.
 """
 
-from collections import deque
+from collections import OrderedDict, deque
 
 import numpy as np
 
@@ -37,7 +47,7 @@ class OutOfBlocks(RuntimeError):
 
 
 class BlockManager:
-    def __init__(self, num_blocks, block_size, free_list=None, num_host_blocks=0):
+    def __init__(self, num_blocks, block_size, free_list=None, num_host_blocks=0, prefix_cache=False):
         if num_blocks <= 0 or block_size <= 0 or num_host_blocks < 0:
             raise ValueError("num_blocks and block_size must be positive")
         self.num_blocks = int(num_blocks)
@@ -54,22 +64,37 @@ class BlockManager:
         self._host_free = deque(range(self.num_host_blocks))
         self.host_refcount = np.zeros(self.num_host_blocks, dtype=np.int64)
         self.swapped = {}          # seq -> host block table (lengths stay in self.lengths)
+        # prefix cache: key -> block, block -> (key, parent key, tokens), released cached blocks (LRU order)
+        self.prefix_cache = bool(prefix_cache)
+        self._cached = {}
+        self._block_key = {}
+        self._evictable = OrderedDict()
 
     # -- allocation ---------------------------------------------------------
     def _take(self):
-        if not self._free:
+        if self._free:
+            b = self._free.popleft()
+        elif self._evictable:                   # reuse the least recently released cached block
+            b, _ = self._evictable.popitem(last=False)
+            key = self._block_key.pop(b)[0]
+            if self._cached.get(key) == b:
+                del self._cached[key]
+        else:
             raise OutOfBlocks("no free physical block left")
-        b = self._free.popleft()
         self.refcount[b] = 1
         return b
 
     def _release(self, b):
         self.refcount[b] -= 1
         if self.refcount[b] == 0:
-            self._free.append(b)
+            if b in self._block_key:            # keep the contents for a later prefix hit
+                self._evictable[b] = None
+            else:
+                self._free.append(b)
 
     def num_free(self):
-        return len(self._free)
+        """Blocks available to allocations (free, plus released cached blocks)."""
+        return len(self._free) + len(self._evictable)
 
     def add_sequence(self, seq, n_tokens=0):
         """Register ``seq`` holding ``n_tokens`` tokens; returns the flat slots of those tokens."""
@@ -78,6 +103,50 @@ class BlockManager:
         self.tables[seq] = []
         self.lengths[seq] = 0
         return [self.append_slot(seq)[0] for _ in range(n_tokens)]
+
+    def add_sequence_cached(self, seq, token_ids):
+        """Register ``seq`` with its prompt, reusing cached full blocks of a matching prefix.
+
+        Returns ``(slots, cached)``: ``cached`` leading tokens already have their
+        K/V in the pool (whole blocks, a multiple of block_size); ``slots`` are
+        the flat slots of tokens ``cached ..`` that the caller must write.  The
+        new full blocks are registered in the cache (their contents are the
+        caller's writes, issued before any later reader runs).
+        """
+        if not self.prefix_cache:
+            raise RuntimeError("prefix cache not enabled")
+        if seq in self.tables:
+            raise KeyError(f"sequence {seq} already exists")
+        tokens = [int(t) for t in token_ids]
+        bs = self.block_size
+        table, parent, cached, hit = [], None, 0, True
+        for j in range(len(tokens) // bs):
+            blk_tokens = tuple(tokens[j * bs:(j + 1) * bs])
+            key = hash((parent, blk_tokens))
+            b = self._cached.get(key) if hit else None
+            if b is not None and self._block_key[b] == (key, parent, blk_tokens):
+                if self.refcount[b] == 0:
+                    del self._evictable[b]
+                self.refcount[b] += 1
+                cached += bs
+            else:
+                hit = False                     # the cached part is a prefix: stop at the first miss
+                b = self._take()
+                old = self._cached.get(key)
+                if old is None or self.refcount[old] == 0:
+                    self._cached[key] = b
+                self._block_key[b] = (key, parent, blk_tokens)
+            table.append(b)
+            parent = key
+        if len(tokens) % bs:
+            table.append(self._take())          # the partial last block is private
+        self.tables[seq] = table
+        self.lengths[seq] = len(tokens)
+        return [table[p // bs] * bs + p % bs for p in range(cached, len(tokens))], cached
+
+    def cached_blocks(self):
+        """Blocks currently registered in the prefix cache."""
+        return len(self._block_key)
 
     def append_slot(self, seq):
         """Reserve the slot of ``seq``'s next token.
@@ -174,8 +243,8 @@ class BlockManager:
         for s in seqs:
             self.swapped[s] = [to_host[b] for b in self.tables.pop(s)]
         for b in holders:
-            self.refcount[b] = 0
-            self._free.append(b)
+            self.refcount[b] = 1
+            self._release(b)                    # cached blocks stay reusable until overwritten
         return list(to_host.items())
 
     def swap_in(self, seqs):

@@ -148,6 +148,32 @@ PREFILL_GQA_BF16 = PrefillWorkload(
     seed=25907, num_seqs=16, num_heads=64, num_kv_heads=8, head_dim=128, block_size=16, dtype="bf16",
     chunk=("fixed", (512,) * 16), prior=("uniform", 0, 7680), max_blocks_per_seq=512)
 
+@dataclass(frozen=True)
+class PrefixCacheWorkload:
+    """Requests that share a system prompt, prefilled with and without the prefix cache."""
+    name: str
+    seed: int
+    num_requests: int
+    shared_len: int
+    unique_len: int
+    num_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    dtype: str
+    max_blocks_per_seq: int
+
+    @property
+    def softmax_scale(self):
+        return 1.0 / math.sqrt(self.head_dim)
+
+
+PREFIX_CACHE_LLAMA13B_F16 = PrefixCacheWorkload(
+    name="prefix caching, LLaMA-13B-shaped layer: 16 requests = a shared 2048-token system prompt + 512 own "
+         "tokens each, 40/40 heads, d128, fp16, bs16",
+    seed=25908, num_requests=16, shared_len=2048, unique_len=512, num_heads=40, num_kv_heads=40, head_dim=128,
+    block_size=16, dtype="f16", max_blocks_per_seq=160)
+
 WORKLOADS = {
     "tiny_f32": TINY_F32,
     "llama13b_f16": LLAMA13B_F16,
@@ -156,6 +182,7 @@ WORKLOADS = {
     "shared_prefix_fp8": SHARED_PREFIX_FP8,
     "prefill_llama13b_f16": PREFILL_LLAMA13B_F16,
     "prefill_gqa_bf16": PREFILL_GQA_BF16,
+    "prefix_cache_llama13b_f16": PREFIX_CACHE_LLAMA13B_F16,
 }
 
 
@@ -301,3 +328,36 @@ def make_prefill_inputs(w: PrefillWorkload, device="cpu", chunk=None, prior=None
     k_new = randn(gen, (T, KVH, d), dt, device)
     v_new = randn(gen, (T, KVH, d), dt, device)
     return PrefillInputs(w, n, ctx, qsl, free_list, nb, q, k_cache, v_cache, k_new, v_new)
+
+
+@dataclass
+class PrefixCacheInputs:
+    workload: PrefixCacheWorkload
+    prompts: list                  # token ids per request (shared prefix + own tokens)
+    free_list: list
+    num_blocks: int
+    q: torch.Tensor                # [requests * prompt_len, H, d] queries of every prompt token
+    k: torch.Tensor                # [requests * prompt_len, KVH, d] K of every prompt token
+    v: torch.Tensor
+
+
+def make_prefix_cache_inputs(w: PrefixCacheWorkload, device="cpu"):
+    """Token ids (shared prefix, then each request's own) -> free-list permutation -> q -> K -> V.
+    K/V of a shared-prefix token are the same in every request."""
+    rng = np.random.default_rng(w.seed)
+    shared = rng.integers(0, 32000, w.shared_len).tolist()
+    prompts = [shared + rng.integers(0, 32000, w.unique_len).tolist() for _ in range(w.num_requests)]
+    L = w.shared_len + w.unique_len
+    nb = int(math.ceil(1.1 * w.num_requests * (-(-L // w.block_size))))
+    free_list = rng.permutation(nb).tolist()
+    gen = make_generator(w.seed, device)
+    dt = DTYPES[w.dtype]
+    R, H, KVH, d = w.num_requests, w.num_heads, w.num_kv_heads, w.head_dim
+    q = randn(gen, (R * L, H, d), dt, device)
+    k_sh = randn(gen, (w.shared_len, KVH, d), dt, device)
+    v_sh = randn(gen, (w.shared_len, KVH, d), dt, device)
+    k_own = randn(gen, (R, w.unique_len, KVH, d), dt, device)
+    v_own = randn(gen, (R, w.unique_len, KVH, d), dt, device)
+    k = torch.cat([torch.cat([k_sh, k_own[r]]) for r in range(R)])
+    v = torch.cat([torch.cat([v_sh, v_own[r]]) for r in range(R)])
+    return PrefixCacheInputs(w, prompts, free_list, nb, q, k, v)

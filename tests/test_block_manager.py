@@ -197,3 +197,104 @@ def test_free_swapped_sequence_releases_host_blocks():
     bm.add_sequence(1, 17)
     with pytest.raises(OutOfBlocks):
         bm.swap_out([1])                          # 5 blocks do not fit 4 host blocks
+
+
+# ---------------------------------------------------------------------------
+# prefix caching: full blocks shared across requests by chained keys
+# ---------------------------------------------------------------------------
+
+def _kv_of_prefix(tokens, KVH, d):
+    """K/V rows of the token at position len(tokens)-1: a fixed function of the whole prefix,
+    as a model's would be (identical prefixes give identical rows)."""
+    rng = np.random.default_rng(abs(hash(tuple(tokens))) % (2 ** 32))
+    return rng.standard_normal((KVH, d)), rng.standard_normal((KVH, d))
+
+
+def _write_prompt(bm, seq, tokens, kp, vp, model, KVH, d):
+    slots, cached = bm.add_sequence_cached(seq, tokens)
+    model.new(seq)
+    for p in range(len(tokens)):
+        k, v = _kv_of_prefix(tokens[:p + 1], KVH, d)
+        model.append(seq, k, v)
+        if p >= cached:
+            kp, vp = reshape_ref(k[None], v[None], kp, vp, np.array([slots[p - cached]]), bm.block_size)
+    return kp, vp, cached
+
+
+def _check_all(bm, kp, vp, model, KVH):
+    for s in bm.tables:
+        for h in range(KVH):
+            np.testing.assert_array_equal(gather_tokens(kp, bm.tables[s], bm.lengths[s], bm.block_size, h),
+                                          model.keys(s)[:, h])
+            np.testing.assert_array_equal(gather_tokens(vp, bm.tables[s], bm.lengths[s], bm.block_size, h),
+                                          model.values(s)[:, h])
+
+
+def test_prefix_cache_hits_whole_matching_blocks_only():
+    bs, KVH, d, NB = 4, 2, 3, 40
+    bm = BlockManager(NB, bs, free_list=np.random.default_rng(3).permutation(NB), prefix_cache=True)
+    kp, vp = np.full((NB, KVH, bs, d), np.nan), np.full((NB, KVH, bs, d), np.nan)
+    model = ContiguousSequences()
+    a = list(range(100, 118))                                   # 4 full blocks + 2
+    kp, vp, cached = _write_prompt(bm, "a", a, kp, vp, model, KVH, d)
+    assert cached == 0 and bm.cached_blocks() == 4
+    b = a[:14] + [7, 8, 9, 10, 11]                              # diverges inside block 3
+    kp, vp, cached = _write_prompt(bm, "b", b, kp, vp, model, KVH, d)
+    assert cached == 12 and bm.tables["b"][:3] == bm.tables["a"][:3] and bm.tables["b"][3] != bm.tables["a"][3]
+    assert all(bm.refcount[x] == 2 for x in bm.tables["a"][:3])
+    c = [5] + a[1:]                                             # differs in the first token: no hit at all
+    kp, vp, cached = _write_prompt(bm, "c", c, kp, vp, model, KVH, d)
+    assert cached == 0 and not set(bm.tables["c"]) & set(bm.tables["a"])
+    _check_all(bm, kp, vp, model, KVH)
+    # same blocks of tokens under a different prefix are different blocks
+    d2 = a[4:8] + a[4:8]
+    _, cached = bm.add_sequence_cached("d", d2)
+    assert cached == 0
+    assert int(bm.refcount.sum()) == sum(len(t) for t in bm.tables.values())
+
+
+def test_prefix_cache_survives_release_until_reused_lru():
+    bs, KVH, d, NB = 4, 1, 2, 10
+    bm = BlockManager(NB, bs, prefix_cache=True)
+    kp, vp = np.full((NB, KVH, bs, d), np.nan), np.full((NB, KVH, bs, d), np.nan)
+    model = ContiguousSequences()
+    p1, p2 = list(range(8)), list(range(50, 58))                # 2 full blocks each
+    kp, vp, _ = _write_prompt(bm, 1, p1, kp, vp, model, KVH, d)
+    kp, vp, _ = _write_prompt(bm, 2, p2, kp, vp, model, KVH, d)
+    t1, t2 = list(bm.tables[1]), list(bm.tables[2])
+    bm.free_sequence(1)
+    bm.free_sequence(2)
+    assert bm.num_free() == NB and bm.cached_blocks() == 4
+    # a request with p1 again reuses p1's blocks without writing anything
+    kp, vp, cached = _write_prompt(bm, 3, p1, kp, vp, model, KVH, d)
+    assert cached == 8 and bm.tables[3] == t1
+    # fill the pool: the free list goes first, then released cached blocks in release order (p2's)
+    bm.add_sequence(4, 6 * bs)
+    assert set(bm.tables[4]).isdisjoint(t1) and set(bm.tables[4]).isdisjoint(t2)
+    bm.add_sequence(5, 1)
+    assert bm.tables[5] == [t2[0]] and bm.cached_blocks() == 3
+    bm.free_sequence(4)
+    _, cached = bm.add_sequence_cached(6, p2)                   # p2's first block is gone: a miss
+    assert cached == 0                                          # (its second is cached, but hits stop at a miss)
+    model_check = ContiguousSequences()
+    model_check.new(3)
+    for p in range(8):
+        model_check.append(3, *_kv_of_prefix(p1[:p + 1], KVH, d))
+    for h in range(KVH):
+        np.testing.assert_array_equal(gather_tokens(kp, bm.tables[3], 8, bs, h), model_check.keys(3)[:, h])
+
+
+def test_prefix_cache_swap_out_keeps_cache_consistent():
+    bs, KVH, d, NB = 4, 1, 2, 12
+    bm = BlockManager(NB, bs, num_host_blocks=8, prefix_cache=True)
+    bm.add_sequence_cached("x", list(range(8)))
+    pairs = bm.swap_out(["x"])
+    assert len(pairs) == 2
+    # the swapped-out blocks stay reusable (content intact until reused) ...
+    _, cached = bm.add_sequence_cached("y", list(range(8)))
+    assert cached == 8
+    bm.free_sequence("y")
+    # ... and once overwritten they are no longer hits
+    bm.add_sequence("z", NB * bs)
+    _, cached = bm.add_sequence_cached("w", [])
+    assert cached == 0 and bm.cached_blocks() == 0
