@@ -3,7 +3,7 @@
     python -m paged_kv_cache_259_amd.profiling trace DIR
         per-kernel call count and durations from a ``--kernel-trace`` run.
     python -m paged_kv_cache_259_amd.profiling counters FETCH_DIR WRITE_DIR --workload W --calibrate-copy N
-        HBM bytes per attention call from a ``--pmc FETCH_SIZE`` run and a
+        HBM bytes per attention call (decode or prefill kernels) from a ``--pmc FETCH_SIZE`` run and a
         ``--pmc WRITE_SIZE`` run of ``bench.py --calibrate-copy N``.  The runs'
         one copy_blocks call over N block pairs is a plain copy of known size
         (N blocks read and N written in each pool); the counters' reading on it
@@ -64,20 +64,22 @@ def counters(fetch_dir, write_dir, workload, n_pairs, out=sys.stdout):
     import bench
     from paged_kv_cache_259_amd import synth
     w = synth.WORKLOADS[workload]
-    elt = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}[w.kv_dtype]
+    elt = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}[getattr(w, "kv_dtype", None) or w.dtype]
     block_bytes = w.num_kv_heads * w.block_size * w.head_dim * elt
     f = _counter(fetch_dir, "FETCH_SIZE")
     wr = _counter(write_dir, "WRITE_SIZE")
-    copies = sorted((k for k in f if k[0] == "copy_blocks_kernel"), key=lambda k: -f[k])
-    if not copies:
-        raise SystemExit("no copy_blocks calibration dispatch in the FETCH_SIZE run")
-    cal = copies[0]
+    # the calibration copy is the copy_blocks dispatch whose grid is n_pairs x (workgroups per block);
+    # other copy_blocks dispatches (copy-on-write pairs, swaps) have other grids
+    grid = n_pairs * ((block_bytes // 16 + 255) // 256) * 256
+    cal = ("copy_blocks_kernel", grid)
+    if cal not in f or cal not in wr:
+        raise SystemExit(f"no copy_blocks dispatch with grid {grid} (the calibration copy) in the counter runs")
     copy_bytes = 2 * n_pairs * block_bytes          # K and V pools, each read once and written once
     fs, ws = copy_bytes / (f[cal] * 1024), copy_bytes / (wr[cal] * 1024)
     print(f"calibration: copy_blocks of {n_pairs} block pairs ({copy_bytes / 1e9:.3f} GB read, same written): "
           f"FETCH_SIZE {f[cal]:.1f} KiB (scale {fs:.4f}), WRITE_SIZE {wr[cal]:.1f} KiB (scale {ws:.4f})", file=out)
     total_r = total_w = 0.0
-    for k in sorted(k for k in f if k[0].startswith("attn_")):
+    for k in sorted(k for k in f if k[0].startswith(("attn_", "prefill_"))):
         rb, wb = f[k] * 1024 * fs, wr.get(k, 0.0) * 1024 * ws
         total_r += rb
         total_w += wb
@@ -93,7 +95,7 @@ def counters(fetch_dir, write_dir, workload, n_pairs, out=sys.stdout):
     table[workload] = {"kernel_source_hash": bench.kernel_source_hash(), "bytes_per_call": int(total_r + total_w),
                        "read_bytes": int(total_r), "write_bytes": int(total_w),
                        "fetch_scale": round(fs, 5), "write_scale": round(ws, 5),
-                       "summary": f"profiles/paged_attention_decode_{workload}.md"}
+                       "summary": f"profiles/{'paged_prefill_attention' if workload.startswith('prefill') else 'paged_attention_decode'}_{workload}.md"}
     with open(path, "w") as fh:
         json.dump(table, fh, indent=1)
         fh.write("\n")
