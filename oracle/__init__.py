@@ -31,13 +31,14 @@ Sources cited in this package (page title, then section):
 * [vLLM-rev]  "vLLM PagedAttention: uma revolução no throughput de inferência
   de LLMs", feature list: chunked prefill (a long prompt's prefill split into
   chunks), prefix caching, prefill compute-bound vs decode bandwidth-bound.
-* [OFP8]  the OCP 8-bit floating point specification (E4M3 "FN" encoding) --
-  not on the pages; the pages only say "8-bit".  It fixes the codec.
+* [OFP8]  the OCP 8-bit floating point specification (E4M3 "FN" and E5M2
+  encodings) -- not on the pages; the pages only say "8-bit".  It fixes the codecs.
 
 Readings where the pages are silent are listed in each function's docstring.
 """
 
 from .e4m3_ref import decode_e4m3, encode_e4m3, dequant_e4m3, E4M3_MAX  # noqa: F401
+from .e5m2_ref import decode_e5m2, encode_e5m2, dequant_e5m2, dequant_per_head, E5M2_MAX  # noqa: F401
 from .paged_attention_ref import (  # noqa: F401
     blocks_needed,
     take_blocks,

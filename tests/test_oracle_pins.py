@@ -477,3 +477,61 @@ def test_contiguous_model_fork_is_independent():
     np.testing.assert_array_equal(m.keys(0), rows)
     np.testing.assert_array_equal(m.keys(1)[:3], rows)
     np.testing.assert_array_equal(m.values(1)[3], np.full((1, 4), 8))
+
+
+# ---------------------------------------------------------------------------
+# E5M2 codec: OCP definition, torch's float8_e5m2 cast, the fp16 prefix property
+# ---------------------------------------------------------------------------
+from oracle import e5m2_ref  # noqa: E402
+
+
+def test_e5m2_decode_all_codes_match_torch_float8():
+    ours = e5m2_ref.decode_e5m2(np.arange(256))
+    lib = torch.arange(256, dtype=torch.uint8).view(torch.float8_e5m2).to(torch.float64).numpy()
+    nan = np.isnan(lib)
+    assert np.array_equal(np.isnan(ours), nan) and nan.sum() == 6
+    np.testing.assert_array_equal(ours[~nan], lib[~nan])
+
+
+def test_e5m2_codes_are_the_top_byte_of_fp16():
+    """E5M2 shares fp16's sign and exponent fields: code << 8 is the fp16 bit pattern of the same value."""
+    codes = np.arange(256, dtype=np.uint16)
+    as_f16 = (codes << 8).astype(np.uint16).view(np.float16).astype(np.float64)
+    ours = e5m2_ref.decode_e5m2(codes.astype(np.uint8))
+    nan = np.isnan(ours)
+    assert np.array_equal(np.isnan(as_f16), nan)
+    np.testing.assert_array_equal(as_f16[~nan], ours[~nan])
+
+
+def test_e5m2_closed_forms():
+    d = e5m2_ref.decode_e5m2
+    assert d(0x7B) == 57344.0 and d(0xFB) == -57344.0
+    assert d(0x01) == 2.0 ** -16 and d(0x04) == 2.0 ** -14 and d(0x3C) == 1.0
+    assert d(0x7C) == np.inf and d(0xFC) == -np.inf and np.isnan(d(0x7D))
+    assert e5m2_ref.encode_e5m2(np.float32(np.nan), 1.0) == 0x7F
+    assert e5m2_ref.encode_e5m2(np.array([-np.nan], np.float32), 1.0)[0] == 0xFF
+    assert e5m2_ref.encode_e5m2(np.array([np.inf, -np.inf, 1e9], np.float32), 1.0).tolist() == [0x7B, 0xFB, 0x7B]
+    assert e5m2_ref.encode_e5m2(np.array([-0.0], np.float32), 1.0)[0] == 0x80
+    # 1.125 lies halfway between 1.0 (m=0) and 1.25 (m=1): ties to the even mantissa
+    assert e5m2_ref.encode_e5m2(np.array([1.125, 1.375], np.float32), 1.0).tolist() == [0x3C, 0x3E]
+
+
+@pytest.mark.parametrize("scale", [1.0, 2.0 ** -5, 3.7 / 57344.0])
+def test_e5m2_encode_every_fp16_pattern_matches_torch(scale):
+    x = torch.arange(65536, dtype=torch.int32).to(torch.int16).view(torch.float16).to(torch.float32)
+    q = (x / torch.tensor(scale, dtype=torch.float32))
+    ours = e5m2_ref.encode_e5m2(x.numpy(), scale)
+    lib = q.to(torch.float8_e5m2).view(torch.uint8).numpy()
+    finite = torch.isfinite(q).numpy() & (np.abs(q.numpy()) <= 57344.0)
+    np.testing.assert_array_equal(ours[finite], lib[finite])
+    big = ~finite & ~np.isnan(q.numpy())
+    assert np.all((ours[big] & 0x7F) == 0x7B)                  # saturated, sign kept
+    assert np.all(np.isnan(e5m2_ref.decode_e5m2(ours[np.isnan(q.numpy())])))
+
+
+def test_dequant_per_head_scales_each_head():
+    codes = np.random.default_rng(3).integers(0, 0x7B, (5, 3, 4, 8)).astype(np.uint8)
+    scales = np.array([0.5, 2.0, 0.125], np.float32)
+    got = e5m2_ref.dequant_per_head(codes, scales, e5m2_ref.decode_e5m2)
+    for h in range(3):
+        np.testing.assert_array_equal(got[:, h], e5m2_ref.dequant_e5m2(codes[:, h], scales[h]))
