@@ -24,8 +24,12 @@
  *   contiguous `[block_size][head_dim]` block of [PA/paging]'s example.
  *   A flat slot is `block * block_size + offset`.
  * - Element types (`*_dtype`): PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3 (OCP
- *   E4M3 "FN": bias 7, max +-448, no infinity, NaN = S.1111.111; the stored
- *   value is code * scale with one fp32 scale per pool).
+ *   E4M3 "FN": bias 7, max +-448, no infinity, NaN = S.1111.111), PKV_FP8_E5M2
+ *   (OCP E5M2: bias 15, max +-57344, S.11111.00 infinity, other S.11111.xx NaN).
+ *   An 8-bit cache stores code * scale: one fp32 scale per pool (k_scale,
+ *   v_scale), or one per kv head when the optional device arrays k_scales /
+ *   v_scales ([num_kv_heads] fp32, positive finite; not checked on the host) are
+ *   given -- then they replace the pool's scale.
  * - Return: PKV_OK (0) or a negative status (see pkv_status_string).  Every
  *   argument check runs on the host before anything is enqueued, so an error
  *   return means nothing was launched.  PKV_ERR_LAUNCH reports a HIP launch
@@ -50,6 +54,7 @@ extern "C" {
 #define PKV_F16 1
 #define PKV_BF16 2
 #define PKV_FP8_E4M3 3
+#define PKV_FP8_E5M2 4
 
 /* status codes */
 #define PKV_OK 0
@@ -120,8 +125,9 @@ size_t pkv_attention_workspace_bytes(int num_seqs, int num_heads, int num_kv_hea
  * out          [num_seqs][num_heads][head_dim], q_dtype (fp32/f16/bf16); written, must
  *              not alias any input.  Rounded to nearest even from fp32.
  * q            [num_seqs][num_heads][head_dim], q_dtype.
- * k_cache, v_cache  pools as above, kv_dtype.  With PKV_FP8_E4M3 the values are
- *              code * k_scale (resp. v_scale); k_scale / v_scale are ignored otherwise.
+ * k_cache, v_cache  pools as above, kv_dtype.  With an 8-bit kv_dtype the values
+ *              are code * k_scale (resp. v_scale), or code * k_scales[g] with the
+ *              per-head arrays; scales are ignored for 16/32-bit caches.
  * block_tables [num_seqs][max_blocks_per_seq] int32; entries past ceil(ctx/bs) are never read.
  * context_lens [num_seqs] int32.
  * seq_order    optional [num_seqs] int32 device array: the sequences longest
@@ -150,7 +156,8 @@ size_t pkv_attention_workspace_bytes(int num_seqs, int num_heads, int num_kv_hea
  * workspace    device buffer of at least pkv_attention_workspace_bytes(...) bytes
  *              (may be NULL when that is 0).  Contents on entry are ignored.
  * Supported: head_dim 64/128/256; block_size 8/16/32 (16 for the MFMA family);
- *   (q, kv) dtypes (f32,f32), (f16,f16), (bf16,bf16), (f16,fp8), (bf16,fp8).
+ *   (q, kv) dtypes (f32,f32), (f16,f16), (bf16,bf16), and f16 or bf16 q over
+ *   either 8-bit cache.
  *   Grouped heads (G > 1) with 16-bit q run on MFMA; everything else on the
  *   vector family.
  */
@@ -161,6 +168,7 @@ int pkv_paged_attention_decode(void* out, const void* q,
                                int num_seqs, int num_heads, int num_kv_heads, int head_dim,
                                int block_size, int num_blocks, int max_context_len,
                                float scale, float k_scale, float v_scale,
+                               const float* k_scales, const float* v_scales,
                                int q_dtype, int kv_dtype, int partition_size,
                                void* workspace, size_t workspace_bytes, void* stream);
 
@@ -171,16 +179,18 @@ int pkv_paged_attention_decode(void* out, const void* q,
  *
  * For token i with sigma = slot_mapping[i] >= 0, for every kv head h:
  *   k_cache[sigma / bs][h][sigma % bs][:] = enc(key[i][h][:])   (value likewise)
- * enc is a bit copy when src_dtype == kv_dtype, and for PKV_FP8_E4M3 the code of
- * nearest_e4m3(clamp(fp32(x) / scale, -448, 448)) with IEEE fp32 division, ties
- * to even mantissa, NaN -> 0x7F | sign.  sigma < 0 (padding) and
- * sigma >= num_blocks * block_size are skipped.
+ * enc is a bit copy when src_dtype == kv_dtype, and for an 8-bit cache the code
+ * of nearest(clamp(fp32(x) / scale, -max, max)) with IEEE fp32 division, ties to
+ * even mantissa, NaN -> 0x7F | sign (max 448 for E4M3, 57344 for E5M2; the scale
+ * is the pool's, or k_scales[h] / v_scales[h] for kv head h).  sigma < 0
+ * (padding) and sigma >= num_blocks * block_size are skipped.
  *
  * key, value   [num_tokens][num_kv_heads][head_dim], src_dtype (f32/f16/bf16).
  * slot_mapping [num_tokens] int64.  Slots must be distinct within one call
  *              (two tokens to one slot leave either value).
- * k_scale, v_scale  FP8 encode scales (positive, finite); ignored otherwise.
- * Supported: src_dtype == kv_dtype, or src f32/f16/bf16 -> kv PKV_FP8_E4M3;
+ * k_scale, v_scale  8-bit encode scales (positive, finite); ignored otherwise, and
+ *              replaced by k_scales / v_scales (device, [num_kv_heads]) when given.
+ * Supported: src_dtype == kv_dtype, or src f32/f16/bf16 -> an 8-bit kv_dtype;
  *   head_dim a multiple of 16 up to 1024; any block_size >= 1.
  * num_tokens == 0 is a no-op returning PKV_OK.
  */
@@ -188,7 +198,8 @@ int pkv_reshape_and_cache(const void* key, const void* value,
                           void* k_cache, void* v_cache, const int64_t* slot_mapping,
                           int num_tokens, int num_kv_heads, int head_dim, int block_size,
                           int num_blocks, int src_dtype, int kv_dtype,
-                          float k_scale, float v_scale, void* stream);
+                          float k_scale, float v_scale, const float* k_scales, const float* v_scales,
+                          void* stream);
 
 /*
  * pkv_copy_blocks -- block-level copy-on-write ([KVpag]: before writing into a

@@ -305,6 +305,7 @@ void attn_vector_kernel(AttnParams p) {
   if (p.num_slices > 0) {
     // balanced slices: head fastest, then slice
     const int head = (int)(L % (uint32_t)p.num_heads);
+    apply_head_scales(p, head / p.group);
     const int k = (int)(L / (uint32_t)p.num_heads);
     const int S = p.num_seqs;
     block_prefix<NW * 64>(p.context_lens, S, p.ctx_cap, BS, sm.prefix, sm.wsum);
@@ -342,6 +343,7 @@ void attn_vector_kernel(AttnParams p) {
   // fixed partitions of partition_blocks blocks (one pass when num_partitions == 1)
   int seq, head, part;
   decode_work_id(L, p.num_seqs, p.num_heads, seq, head, part);
+  apply_head_scales(p, head / p.group);
   if (p.longest_first) {                                    // one pass only
     if (p.seq_order) {
       const int o = p.seq_order[seq];
@@ -411,7 +413,7 @@ bool vector_supported(int q_dtype, int kv_dtype, int d, int bs) {
   int kv_bytes;
   if (q_dtype == 0 && kv_dtype == 0) kv_bytes = 4;
   else if ((q_dtype == 1 || q_dtype == 2) && kv_dtype == q_dtype) kv_bytes = 2;
-  else if ((q_dtype == 1 || q_dtype == 2) && kv_dtype == 3) kv_bytes = 1;
+  else if ((q_dtype == 1 || q_dtype == 2) && (kv_dtype == 3 || kv_dtype == 4)) kv_bytes = 1;
   else return false;
   const int lpr = d * kv_bytes / 16;
   const int rpw = 64 / lpr;
@@ -424,6 +426,8 @@ hipError_t launch_attention_vector(const AttnParams& p, int q_dtype, int kv_dtyp
   if (q_dtype == 2 && kv_dtype == 2) return launch_vec_d<BF16, BF16>(p, d, bs, stream);
   if (q_dtype == 1 && kv_dtype == 3) return launch_vec_d<F16, FP8>(p, d, bs, stream);
   if (q_dtype == 2 && kv_dtype == 3) return launch_vec_d<BF16, FP8>(p, d, bs, stream);
+  if (q_dtype == 1 && kv_dtype == 4) return launch_vec_d<F16, BF8>(p, d, bs, stream);
+  if (q_dtype == 2 && kv_dtype == 4) return launch_vec_d<BF16, BF8>(p, d, bs, stream);
   return hipErrorInvalidValue;
 }
 

@@ -33,6 +33,8 @@ struct ReshapeParams {
   int block_size;
   float k_scale;
   float v_scale;
+  const float* k_scales;      // per kv head, or NULL
+  const float* v_scales;
 };
 
 // Bit copy: 16 bytes of source -> 16 bytes of cache.
@@ -59,8 +61,9 @@ __global__ __launch_bounds__(256) void reshape_copy_kernel(ReshapeParams p) {
   *reinterpret_cast<uint4*>(reinterpret_cast<char*>(p.v_cache) + dst * T::bytes) = vv;
 }
 
-// Encode: 16 bytes of source (4 fp32 or 8 16-bit values) -> 4 or 8 E4M3 codes.
-template <class S>
+// Encode: 16 bytes of source (4 fp32 or 8 16-bit values) -> 4 or 8 codes of
+// 8-bit format F (E4M3 or E5M2), with the pool's or the kv head's scale.
+template <class S, class F>
 __global__ __launch_bounds__(256) void reshape_fp8_kernel(ReshapeParams p) {
   constexpr int V = 16 / S::bytes;
   const int chunks_per_row = p.head_dim / V;
@@ -79,6 +82,8 @@ __global__ __launch_bounds__(256) void reshape_fp8_kernel(ReshapeParams p) {
   const size_t dst = (((size_t)blk * p.num_kv_heads + h) * p.block_size + off) * (size_t)p.head_dim + (size_t)c * V;
   const uint4 kr = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(p.key) + src * S::bytes);
   const uint4 vr = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(p.value) + src * S::bytes);
+  const float ks = p.k_scales ? p.k_scales[h] : p.k_scale;
+  const float vs = p.v_scales ? p.v_scales[h] : p.v_scale;
   float kf[V], vf[V];
   Unpack<S>::run(kr, kf);
   Unpack<S>::run(vr, vf);
@@ -88,8 +93,8 @@ __global__ __launch_bounds__(256) void reshape_fp8_kernel(ReshapeParams p) {
     uint32_t a = 0, b = 0;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      a |= e4m3_encode_scaled(kf[4 * j + t], p.k_scale) << (8 * t);
-      b |= e4m3_encode_scaled(vf[4 * j + t], p.v_scale) << (8 * t);
+      a |= fp8_encode_scaled<F>(kf[4 * j + t], ks) << (8 * t);
+      b |= fp8_encode_scaled<F>(vf[4 * j + t], vs) << (8 * t);
     }
     kc[j] = a;
     vc[j] = b;
@@ -108,19 +113,25 @@ __global__ __launch_bounds__(256) void reshape_fp8_kernel(ReshapeParams p) {
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
                                     const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
                                     int head_dim, int block_size, int num_blocks, int src_dtype, int kv_dtype,
-                                    float k_scale, float v_scale, hipStream_t stream) {
+                                    float k_scale, float v_scale, const float* k_scales, const float* v_scales,
+                                    hipStream_t stream) {
   ReshapeParams p{key, value, k_cache, v_cache, slot_mapping, (int64_t)num_blocks * block_size,
-                  num_tokens, num_kv_heads, head_dim, block_size, k_scale, v_scale};
+                  num_tokens, num_kv_heads, head_dim, block_size, k_scale, v_scale, k_scales, v_scales};
   const int src_bytes = src_dtype == 0 ? 4 : 2;
   const size_t chunks = (size_t)num_tokens * num_kv_heads * (head_dim * src_bytes / 16);
   const dim3 grid((unsigned)((chunks + 255) / 256));
   if (kv_dtype == src_dtype) {
     if (src_bytes == 4) hipLaunchKernelGGL(reshape_copy_kernel<F32>, grid, dim3(256), 0, stream, p);
     else hipLaunchKernelGGL(reshape_copy_kernel<F16>, grid, dim3(256), 0, stream, p);  // 16-bit: raw bits
-  } else if (kv_dtype == 3) {
-    if (src_dtype == 0) hipLaunchKernelGGL(reshape_fp8_kernel<F32>, grid, dim3(256), 0, stream, p);
-    else if (src_dtype == 1) hipLaunchKernelGGL(reshape_fp8_kernel<F16>, grid, dim3(256), 0, stream, p);
-    else if (src_dtype == 2) hipLaunchKernelGGL(reshape_fp8_kernel<BF16>, grid, dim3(256), 0, stream, p);
+  } else if (kv_dtype == FP8::kId) {
+    if (src_dtype == 0) hipLaunchKernelGGL((reshape_fp8_kernel<F32, FP8>), grid, dim3(256), 0, stream, p);
+    else if (src_dtype == 1) hipLaunchKernelGGL((reshape_fp8_kernel<F16, FP8>), grid, dim3(256), 0, stream, p);
+    else if (src_dtype == 2) hipLaunchKernelGGL((reshape_fp8_kernel<BF16, FP8>), grid, dim3(256), 0, stream, p);
+    else return hipErrorInvalidValue;
+  } else if (kv_dtype == BF8::kId) {
+    if (src_dtype == 0) hipLaunchKernelGGL((reshape_fp8_kernel<F32, BF8>), grid, dim3(256), 0, stream, p);
+    else if (src_dtype == 1) hipLaunchKernelGGL((reshape_fp8_kernel<F16, BF8>), grid, dim3(256), 0, stream, p);
+    else if (src_dtype == 2) hipLaunchKernelGGL((reshape_fp8_kernel<BF16, BF8>), grid, dim3(256), 0, stream, p);
     else return hipErrorInvalidValue;
   } else {
     return hipErrorInvalidValue;
@@ -203,13 +214,14 @@ extern "C" {
 int pkv_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
                           const int64_t* slot_mapping, int num_tokens, int num_kv_heads, int head_dim,
                           int block_size, int num_blocks, int src_dtype, int kv_dtype, float k_scale, float v_scale,
-                          void* stream) {
+                          const float* k_scales, const float* v_scales, void* stream) {
   if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
     return PKV_ERR_BAD_SIZE;
   if (src_dtype != PKV_F32 && src_dtype != PKV_F16 && src_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
-  if (kv_dtype != src_dtype && kv_dtype != PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;
+  const bool fp8 = kv_dtype == PKV_FP8_E4M3 || kv_dtype == PKV_FP8_E5M2;
+  if (kv_dtype != src_dtype && !fp8) return PKV_ERR_UNSUPPORTED;
   if (head_dim % 16 != 0 || head_dim > 1024) return PKV_ERR_UNSUPPORTED;
-  if (kv_dtype == PKV_FP8_E4M3 && !(good_scale(k_scale) && good_scale(v_scale))) return PKV_ERR_SCALE;
+  if (fp8 && !((k_scales || good_scale(k_scale)) && (v_scales || good_scale(v_scale)))) return PKV_ERR_SCALE;
   if ((double)num_tokens * num_kv_heads * head_dim / 4.0 > 2147483647.0 * 256.0) return PKV_ERR_BAD_SIZE;
   if (num_tokens == 0) return PKV_OK;
   if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PKV_ERR_NULL_POINTER;
@@ -217,8 +229,8 @@ int pkv_reshape_and_cache(const void* key, const void* value, void* k_cache, voi
   (void)hipGetLastError();
   return launch_status(launch_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, num_tokens,
                                                      num_kv_heads, head_dim, block_size, num_blocks, src_dtype,
-                                                     kv_dtype, k_scale, v_scale,
-                                                     reinterpret_cast<hipStream_t>(stream)));
+                                                     kv_dtype, k_scale, v_scale, fp8 ? k_scales : nullptr,
+                                                     fp8 ? v_scales : nullptr, reinterpret_cast<hipStream_t>(stream)));
 }
 
 int pkv_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, int num_pairs, int num_kv_heads,

@@ -72,7 +72,8 @@ int make_plan(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int b
       max_context_len < 0)
     return PKV_ERR_BAD_SIZE;
   if (num_heads % num_kv_heads != 0) return PKV_ERR_HEAD_GROUPING;
-  if (pkv::dtype_bytes(q_dtype) == 0 || q_dtype == PKV_FP8_E4M3 || pkv::dtype_bytes(kv_dtype) == 0) return PKV_ERR_UNSUPPORTED;
+  if (pkv::dtype_bytes(q_dtype) != 2 && q_dtype != PKV_F32) return PKV_ERR_UNSUPPORTED;
+  if (pkv::dtype_bytes(kv_dtype) == 0) return PKV_ERR_UNSUPPORTED;
   if (partition_size < 0 || (partition_size > 0 && partition_size % block_size != 0)) return PKV_ERR_PARTITION;
   const int group = num_heads / num_kv_heads;
   const bool vec_ok = pkv::vector_supported(q_dtype, kv_dtype, head_dim, block_size);
@@ -187,6 +188,7 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
                                const int32_t* seq_order,
                                int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
                                int num_blocks, int max_context_len, float scale, float k_scale, float v_scale,
+                               const float* k_scales, const float* v_scales,
                                int q_dtype, int kv_dtype, int partition_size, void* workspace,
                                size_t workspace_bytes, void* stream) {
   Plan pl;
@@ -195,7 +197,8 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
   if (st != PKV_OK) return st;
   if (max_blocks_per_seq <= 0 || num_blocks <= 0) return PKV_ERR_BAD_SIZE;
   if (!isfinite(scale)) return PKV_ERR_BAD_SIZE;
-  if (kv_dtype == PKV_FP8_E4M3 && !(pkv::good_scale(k_scale) && pkv::good_scale(v_scale))) return PKV_ERR_SCALE;
+  const bool fp8 = kv_dtype == PKV_FP8_E4M3 || kv_dtype == PKV_FP8_E5M2;
+  if (fp8 && !((k_scales || pkv::good_scale(k_scale)) && (v_scales || pkv::good_scale(v_scale)))) return PKV_ERR_SCALE;
   if (num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PKV_ERR_NULL_POINTER;
   if (!pkv::aligned16(out) || !pkv::aligned16(q) || !pkv::aligned16(k_cache) || !pkv::aligned16(v_cache)) return PKV_ERR_UNSUPPORTED;
@@ -240,9 +243,10 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
   }
   if (cap > cap_table) cap = cap_table;
   p.ctx_cap = (int)(cap < 2147483647LL ? cap : 2147483647LL);
-  const bool fp8 = kv_dtype == PKV_FP8_E4M3;
-  p.qk_scale = scale * kLog2e * (fp8 ? k_scale : 1.f);
-  p.v_scale = fp8 ? v_scale : 1.f;
+  p.k_scales = fp8 ? k_scales : nullptr;
+  p.v_scales = fp8 ? v_scales : nullptr;
+  p.qk_scale = scale * kLog2e * (fp8 && !k_scales ? k_scale : 1.f);
+  p.v_scale = fp8 && !v_scales ? v_scale : 1.f;
   p.total_wgs = (uint32_t)(pl.mode == kSlices ? (size_t)pl.num_parts * pl.units
                                               : (size_t)num_seqs * pl.units * pl.num_parts);
   p.xcd_chunk = (uint32_t)xcd_chunk_for(pl.mode);

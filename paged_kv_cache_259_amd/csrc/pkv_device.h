@@ -15,7 +15,8 @@ namespace pkv {
 struct F32 { static constexpr int bytes = 4; static constexpr int kId = 0; };
 struct F16 { static constexpr int bytes = 2; static constexpr int kId = 1; };
 struct BF16 { static constexpr int bytes = 2; static constexpr int kId = 2; };
-struct FP8 { static constexpr int bytes = 1; static constexpr int kId = 3; };
+struct FP8 { static constexpr int bytes = 1; static constexpr int kId = 3; };    // OCP E4M3 "FN"
+struct BF8 { static constexpr int bytes = 1; static constexpr int kId = 4; };    // OCP E5M2
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
@@ -70,6 +71,19 @@ template <> struct Unpack<FP8> {
   static constexpr int N = 16;
   __device__ __forceinline__ static void run(const uint4& r, float* f) {
     fp8x4_to_f32(r.x, f); fp8x4_to_f32(r.y, f + 4); fp8x4_to_f32(r.z, f + 8); fp8x4_to_f32(r.w, f + 12);
+  }
+};
+// E5M2 decode: an E5M2 code is the top byte of the fp16 with the same value
+// (same sign and exponent fields, 2 of fp16's 10 mantissa bits), so the code
+// shifted into the high byte of a half is exact, infinities and NaN included.
+__device__ __forceinline__ void bf8x4_to_f32(uint32_t u, float* f) {
+  f16x2_to_f32(((u & 0xffu) << 8) | ((u & 0xff00u) << 16), f[0], f[1]);
+  f16x2_to_f32(((u >> 8) & 0xff00u) | (u & 0xff000000u), f[2], f[3]);
+}
+template <> struct Unpack<BF8> {
+  static constexpr int N = 16;
+  __device__ __forceinline__ static void run(const uint4& r, float* f) {
+    bf8x4_to_f32(r.x, f); bf8x4_to_f32(r.y, f + 4); bf8x4_to_f32(r.z, f + 8); bf8x4_to_f32(r.w, f + 12);
   }
 };
 
@@ -132,6 +146,36 @@ __device__ __forceinline__ uint32_t e4m3_encode_scaled(float x, float scale) {
   const uint32_t u = f32_as_u32(x);
   if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fu | ((u >> 24) & 0x80u);
   return e4m3_encode(x / scale);
+}
+
+// E5M2 encode (OCP): nearest code with ties to even mantissa, saturating to
+// +-57344 (also for +-inf: the cache stores finite values), NaN -> 0x7F | sign.
+__device__ __forceinline__ uint32_t e5m2_encode(float v) {
+  const uint32_t u = f32_as_u32(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t ua = u & 0x7fffffffu;
+  if (ua > 0x7f800000u) return 0x7fu | sign;          // NaN
+  if (ua >= 0x47600000u) return 0x7bu | sign;         // |v| >= 57344 (and inf): saturate
+  if (ua < 0x38800000u) {                              // |v| < 2^-14: subnormal step 2^-16
+    const float k = __builtin_rintf(u32_as_f32(ua) * 65536.0f);  // exact scaling, RNE
+    return sign | (uint32_t)k;                         // k == 4 is the smallest normal
+  }
+  // normal: keep 2 mantissa bits of the fp32 pattern, round to nearest even
+  const uint32_t r = ua + 0xfffffu + ((ua >> 21) & 1u);
+  const uint32_t e = (r >> 23) - 127u + 15u;           // E5M2 biased exponent (1..30)
+  const uint32_t m = (r >> 21) & 3u;
+  return sign | (e << 2) | m;
+}
+
+// Code of x / scale in 8-bit format F (FP8 = E4M3, BF8 = E5M2).
+template <class F> __device__ __forceinline__ uint32_t fp8_encode_scaled(float x, float scale);
+template <> __device__ __forceinline__ uint32_t fp8_encode_scaled<FP8>(float x, float scale) {
+  return e4m3_encode_scaled(x, scale);
+}
+template <> __device__ __forceinline__ uint32_t fp8_encode_scaled<BF8>(float x, float scale) {
+  const uint32_t u = f32_as_u32(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fu | ((u >> 24) & 0x80u);
+  return e5m2_encode(x / scale);
 }
 
 // ---------------------------------------------------------------------------
@@ -374,11 +418,20 @@ struct AttnParams {
   int longest_first;       // one pass: workgroup r takes the r-th longest sequence
   const int32_t* seq_order;  // one pass: the caller's longest-first order (else derived in-workgroup)
   int* ws_prefix;          // [S+1] block prefix, written by workgroup 0 in slice mode
+  const float* k_scales;   // [num_kv_heads] per-head 8-bit scales, or NULL (then k_scale is in qk_scale)
+  const float* v_scales;   // [num_kv_heads] or NULL (then v_scale applies)
   float qk_scale;          // scale * log2(e) * k_scale
   float v_scale;
   uint32_t total_wgs;
   uint32_t xcd_chunk;       // see xcd_remap
 };
+
+// Per-head 8-bit scales of kv head g folded into the workgroup's copy of the
+// parameters (the pool-wide scales are already in qk_scale / v_scale otherwise).
+__device__ __forceinline__ void apply_head_scales(AttnParams& p, int g) {
+  if (p.k_scales) p.qk_scale *= p.k_scales[g];
+  if (p.v_scales) p.v_scale *= p.v_scales[g];
+}
 
 struct ReduceParams {
   void* out;

@@ -15,7 +15,7 @@ inline int dtype_bytes(int dt) {
   switch (dt) {
     case PKV_F32: return 4;
     case PKV_F16: case PKV_BF16: return 2;
-    case PKV_FP8_E4M3: return 1;
+    case PKV_FP8_E4M3: case PKV_FP8_E5M2: return 1;
   }
   return 0;
 }
@@ -38,7 +38,8 @@ hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim, hipSt
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
                                     const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
                                     int head_dim, int block_size, int num_blocks, int src_dtype, int kv_dtype,
-                                    float k_scale, float v_scale, hipStream_t stream);
+                                    float k_scale, float v_scale, const float* k_scales, const float* v_scales,
+                                    hipStream_t stream);
 hipError_t launch_copy_blocks(const void* src_k, const void* src_v, int src_blocks, void* dst_k, void* dst_v,
                               int dst_blocks, const int64_t* pairs, int num_pairs, int64_t block_bytes,
                               hipStream_t stream);

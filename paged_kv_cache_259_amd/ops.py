@@ -22,7 +22,7 @@ if not os.path.exists(LIB_PATH):
 
 _lib = ctypes.CDLL(LIB_PATH)
 
-F32, F16, BF16, FP8_E4M3 = 0, 1, 2, 3
+F32, F16, BF16, FP8_E4M3, FP8_E5M2 = 0, 1, 2, 3, 4
 PATH_VECTOR, PATH_MFMA = 0, 1
 
 _c_int, _c_float, _c_size, _vp = ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
@@ -40,10 +40,11 @@ _lib.pkv_paged_attention_decode.argtypes = (
     [_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp]
     + [_c_int] * 7
     + [_c_float] * 3
+    + [_vp, _vp]
     + [_c_int] * 3
     + [_vp, _c_size, _vp])
 _lib.pkv_reshape_and_cache.restype = _c_int
-_lib.pkv_reshape_and_cache.argtypes = [_vp] * 5 + [_c_int] * 7 + [_c_float] * 2 + [_vp]
+_lib.pkv_reshape_and_cache.argtypes = [_vp] * 5 + [_c_int] * 7 + [_c_float] * 2 + [_vp, _vp, _vp]
 _lib.pkv_copy_blocks.restype = _c_int
 _lib.pkv_copy_blocks.argtypes = [_vp, _vp, _vp] + [_c_int] * 6 + [_vp]
 _lib.pkv_paged_prefill_attention.restype = _c_int
@@ -78,6 +79,8 @@ def dtype_code(t: torch.dtype):
         return BF16
     if t in (torch.uint8, torch.float8_e4m3fn):
         return FP8_E4M3
+    if t == torch.float8_e5m2:
+        return FP8_E5M2
     raise TypeError(f"unsupported dtype {t}")
 
 
@@ -89,6 +92,15 @@ def _stream(stream):
 
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _head_scales(t, kvh, device):
+    """Optional per-kv-head scale array: fp32 [kvh], contiguous, on the pools' device."""
+    if t is None:
+        return None
+    if t.dtype != torch.float32 or t.shape != (kvh,) or not t.is_contiguous() or t.device != device:
+        raise ValueError("per-head scales must be a contiguous float32 [num_kv_heads] tensor on the pools' device")
+    return t
 
 
 def library_version():
@@ -114,14 +126,16 @@ def attention_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, block
 
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
                            k_scale=1.0, v_scale=1.0, partition_size=0, workspace=None, num_blocks=None,
-                           seq_order=None, stream=None):
+                           seq_order=None, k_scales=None, v_scales=None, stream=None):
     """out[s, h] = softmax(scale * K_s q[s, h]) V_s over each sequence's paged context.
 
     out, q: [S, H, d]; k_cache, v_cache: [NB, KVH, bs, d]; block_tables: int32
     [S, maxblk]; context_lens: int32 [S].  ``workspace``: a device uint8 tensor
     of at least ``attention_workspace_bytes(...)`` bytes (allocated here if None).
     ``seq_order``: optional int32 [S] device tensor, the sequences longest first
-    (scheduling only; see ``BlockManager.longest_first``).
+    (scheduling only; see ``BlockManager.longest_first``).  8-bit caches: uint8 /
+    float8_e4m3fn pools are E4M3, float8_e5m2 pools E5M2; ``k_scales`` /
+    ``v_scales`` (float32 [KVH]) replace the pool-wide scales per kv head.
     """
     S, H, d = q.shape
     NB, KVH, bs, d2 = k_cache.shape
@@ -148,7 +162,8 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     _check(_lib.pkv_paged_attention_decode(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1],
         _ptr(context_lens), _ptr(seq_order), S, H, KVH, d, bs, NB if num_blocks is None else num_blocks, max_context_len,
-        float(scale), float(k_scale), float(v_scale), qd, kvd, partition_size, ws_ptr, ws_bytes,
+        float(scale), float(k_scale), float(v_scale), _ptr(_head_scales(k_scales, KVH, k_cache.device)),
+        _ptr(_head_scales(v_scales, KVH, k_cache.device)), qd, kvd, partition_size, ws_ptr, ws_bytes,
         _stream(stream)), "pkv_paged_attention_decode")
     return out
 
@@ -183,7 +198,8 @@ def paged_prefill_attention(out, q, k_cache, v_cache, block_tables, context_lens
     return out
 
 
-def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, k_scale=1.0, v_scale=1.0, stream=None):
+def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, k_scale=1.0, v_scale=1.0, k_scales=None,
+                      v_scales=None, stream=None):
     """k_cache[slot // bs, h, slot % bs] = enc(key[i, h]) for every token i (slot < 0 skipped)."""
     T, KVH, d = key.shape
     NB, KVH2, bs, d2 = k_cache.shape
@@ -196,7 +212,9 @@ def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, k_scale=1.0, v
             raise ValueError("all tensors must be contiguous")
     _check(_lib.pkv_reshape_and_cache(
         _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), T, KVH, d, bs, NB,
-        dtype_code(key.dtype), dtype_code(k_cache.dtype), float(k_scale), float(v_scale), _stream(stream)),
+        dtype_code(key.dtype), dtype_code(k_cache.dtype), float(k_scale), float(v_scale),
+        _ptr(_head_scales(k_scales, KVH, k_cache.device)), _ptr(_head_scales(v_scales, KVH, k_cache.device)),
+        _stream(stream)),
         "pkv_reshape_and_cache")
 
 

@@ -97,10 +97,10 @@ def test_attention_plan_rejects(lib, args, status):
 
 
 def _decode(lib, num_seqs=2, H=4, KVH=4, d=128, bs=16, NB=8, max_ctx=64, ks=1.0, vs=1.0, qd=1, kvd=1, part=0,
-            ws=None, ws_bytes=0, ptr=FAKE):
+            ws=None, ws_bytes=0, ptr=FAKE, kss=None, vss=None):
     return lib.pkv_paged_attention_decode(ptr, FAKE, FAKE, FAKE, FAKE, 4, FAKE, None, num_seqs, H, KVH, d, bs, NB, max_ctx,
-                                          ctypes.c_float(0.1), ctypes.c_float(ks), ctypes.c_float(vs), qd, kvd, part,
-                                          ws, ws_bytes, None)
+                                          ctypes.c_float(0.1), ctypes.c_float(ks), ctypes.c_float(vs), kss, vss, qd,
+                                          kvd, part, ws, ws_bytes, None)
 
 
 def test_decode_host_checks(lib):
@@ -111,6 +111,10 @@ def test_decode_host_checks(lib):
     assert _decode(lib, max_ctx=1000, part=256, ws=FAKE, ws_bytes=16) == -6
     assert _decode(lib, kvd=3, ks=0.0) == -8
     assert _decode(lib, kvd=3, vs=float("inf")) == -8
+    assert _decode(lib, kvd=4, ks=-1.0) == -8                   # E5M2 cache: same scale rule
+    assert _decode(lib, kvd=4, ks=0.0, vs=0.0, kss=FAKE, vss=FAKE, ptr=None) == -1   # per-head arrays replace them
+    assert _decode(lib, qd=3, kvd=3) == -4 and _decode(lib, qd=4, kvd=4) == -4     # 8-bit queries: no
+    assert _decode(lib, kvd=5) == -4
     assert _decode(lib, ptr=None) == -1
     assert _decode(lib, ptr=ctypes.c_void_p(0x10004)) == -4    # misaligned output
     assert _decode(lib, NB=0) == -2
@@ -119,12 +123,15 @@ def test_decode_host_checks(lib):
 def test_reshape_and_copy_host_checks(lib):
     f = ctypes.c_float
     r = lib.pkv_reshape_and_cache
-    assert r(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 4, 128, 16, 8, 1, 1, f(1), f(1), None) == 0
-    assert r(FAKE, FAKE, FAKE, FAKE, FAKE, 5, 4, 128, 16, 8, 1, 2, f(1), f(1), None) == -4
-    assert r(FAKE, FAKE, FAKE, FAKE, FAKE, 5, 4, 120, 16, 8, 1, 1, f(1), f(1), None) == -4
-    assert r(FAKE, FAKE, FAKE, FAKE, FAKE, 5, 4, 128, 16, 8, 1, 3, f(-1), f(1), None) == -8
-    assert r(FAKE, None, FAKE, FAKE, FAKE, 5, 4, 128, 16, 8, 1, 1, f(1), f(1), None) == -1
-    assert r(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 4, 128, 16, 8, 1, 1, f(1), f(1), None) == -2
+    assert r(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 4, 128, 16, 8, 1, 1, f(1), f(1), None, None, None) == 0
+    assert r(FAKE, FAKE, FAKE, FAKE, FAKE, 5, 4, 128, 16, 8, 1, 2, f(1), f(1), None, None, None) == -4
+    assert r(FAKE, FAKE, FAKE, FAKE, FAKE, 5, 4, 120, 16, 8, 1, 1, f(1), f(1), None, None, None) == -4
+    assert r(FAKE, FAKE, FAKE, FAKE, FAKE, 5, 4, 128, 16, 8, 1, 3, f(-1), f(1), None, None, None) == -8
+    assert r(FAKE, None, FAKE, FAKE, FAKE, 5, 4, 128, 16, 8, 1, 1, f(1), f(1), None, None, None) == -1
+    assert r(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 4, 128, 16, 8, 1, 1, f(1), f(1), None, None, None) == -2
+    assert r(FAKE, FAKE, FAKE, FAKE, FAKE, 5, 4, 128, 16, 8, 1, 4, f(0), f(1), None, None, None) == -8
+    assert r(FAKE, FAKE, FAKE, FAKE, None, 5, 4, 128, 16, 8, 1, 4, f(0), f(0), FAKE, FAKE, None) == -1
+    assert r(FAKE, FAKE, FAKE, FAKE, FAKE, 5, 4, 128, 16, 8, 3, 4, f(1), f(1), None, None, None) == -4
     c = lib.pkv_copy_blocks
     assert c(FAKE, FAKE, FAKE, 0, 4, 128, 16, 8, 1, None) == 0
     assert c(FAKE, FAKE, FAKE, 3, 1, 4, 1, 8, 3, None) == -4      # 4-byte blocks: not 16-byte units
