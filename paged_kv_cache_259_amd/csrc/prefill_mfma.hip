@@ -29,6 +29,8 @@
 //            element j%4 of the 4 values at lane 4m + j/4's address, for
 //            m = 0..3; lane (c16, g4) points at token 4 g4 + c16/4, dims
 //            d0 + 4 (c16%4) .. +3, so it receives V[4 g4 + m][d0 + c16].
+#include <type_traits>
+
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -218,19 +220,17 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
   // transposing-read address of this lane inside a V tile: token 4 g4 + c16/4, dims 4 (c16%4) ..
   const int vrd = (g4 * 4 + (c16 >> 2)) * P::VSTR + 4 * (c16 & 3);
 
-  auto compute = [&](int i, int buf, StepIds ids) {
+  // One step of the wave's rows.  `masked` (a compile-time tag) selects the
+  // variant with the per-element causal / context / skipped-block mask; steps
+  // whose every key is visible to every row of the wave run the other one, so
+  // interior steps carry no mask arithmetic at all.
+  auto step_body = [&](int i, int buf, StepIds ids, auto masked) {
+    constexpr bool interior = !decltype(masked)::value;
     const int k0 = i * STEP;
-    if (k0 <= wave_last_pos) {                              // wave-uniform: some key of the step is visible
-      // blocks of this step that the table maps outside the pool are skipped
+    {
       bool blk_ok[KT];
-      bool all_ok = true;
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        blk_ok[kt] = ids.b[kt] >= 0 && ids.b[kt] < p.num_blocks;
-        all_ok = all_ok && blk_ok[kt];
-      }
-      // every key of the step visible to every row of the wave: no per-element mask
-      const bool interior = k0 + STEP - 1 <= wave_first_pos && k0 + STEP <= nkeys && all_ok && wave_rows_real;
+      for (int kt = 0; kt < KT; ++kt) blk_ok[kt] = ids.b[kt] >= 0 && ids.b[kt] < p.num_blocks;
       f32x4_t S[RW][KT];
 #pragma unroll
       for (int g = 0; g < RW; ++g)
@@ -251,7 +251,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
         // folded into the exp2 argument (max commutes with qs >= 0)
         float s[KT][4];
         float mx = -__builtin_inff();
-        if (interior) {
+        if constexpr (interior) {
 #pragma unroll
           for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
@@ -289,7 +289,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
         const float mref = m[g] == -__builtin_inff() ? 0.f : m[g];   // nothing visible yet: weights are 0
         float pr[KT][4];
         float ps = 0.f;
-        if (interior) {
+        if constexpr (interior) {
 #pragma unroll
           for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
@@ -325,6 +325,20 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
           for (int g = 0; g < RW; ++g) O[g][dt] = Op::mma(vf, pk[g][ns], O[g][dt]);
         }
     }
+  };
+  // Steps [0, n_open) are open to every row of the workgroup: every key is
+  // before the first row's position and inside the context.  With a table
+  // whose entries all lie in the pool they run without the mask (padding rows
+  // past the chunk are never written, so they need none either).
+  bool table_ok = true;
+  for (int b = tid; b < nkblk; b += P::NW * 64) table_ok = table_ok && table[b] >= 0 && table[b] < p.num_blocks;
+  table_ok = __syncthreads_and(table_ok);
+  int n_open = (base + row0 + 1 < nkeys ? base + row0 + 1 : nkeys) / STEP;
+  n_open = table_ok && n_open > 0 ? n_open : 0;
+  auto compute_open = [&](int i, int buf, StepIds ids) { step_body(i, buf, ids, std::false_type{}); };
+  auto compute = [&](int i, int buf, StepIds ids) {
+    if (i * STEP > wave_last_pos) return;                   // wave-uniform: no key of the step is visible
+    step_body(i, buf, ids, std::true_type{});
   };
 
 #if PKV_PREFILL_AHEAD == 2
@@ -365,7 +379,16 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
     store_step(0, kA, vA);
   }
   __syncthreads();
-  for (int i = 0; i < nsteps; ++i) {
+  for (int i = 0; i < n_open; ++i) {
+    const StepIds id2 = ids_of(i + 2);
+    if (i + 1 < nsteps) load_step(i + 1, id1, kA, vA);
+    compute_open(i, i & 1, id0);
+    if (i + 1 < nsteps) store_step((i + 1) & 1, kA, vA);
+    __syncthreads();
+    id0 = id1;
+    id1 = id2;
+  }
+  for (int i = n_open; i < nsteps; ++i) {
     const StepIds id2 = ids_of(i + 2);
     if (i + 1 < nsteps) load_step(i + 1, id1, kA, vA);
     compute(i, i & 1, id0);
