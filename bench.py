@@ -9,10 +9,12 @@ times a prefill step of requests sharing a system prompt with the host prefix
 cache off and on (value = the speedup).
 
 A step is one pass of the hot path over one synthetic decode batch, inputs
-resident in HBM: reshape_and_cache writes every sequence's new key/value into
-the slot the block manager gave it, then paged_attention_decode attends over
-each sequence's paged context (the split-context reduce included when the plan
-uses one).  The block manager's host bookkeeping (tables, slots, the
+resident in HBM: every sequence's new key/value goes into the slot the block
+manager gave it and each sequence attends over its paged context, the new
+token included -- one paged_attention_decode_append launch (the split-context
+reduce included when the plan uses one).  The same step as two launches
+(reshape_and_cache, then paged_attention_decode) is timed too and reported
+under "components".  The block manager's host bookkeeping (tables, slots, the
 longest-first sequence order) is built before the timed region.
 
 Reported separately under "components" (not part of the step):
@@ -22,11 +24,11 @@ Reported separately under "components" (not part of the step):
   pinned host pool and back in (the preemption path), GB/s over the host link.
 
 Prints one JSON line:
-* value      algorithmic KV bytes read per step / step time (GB/s), the step
-             being reshape_and_cache + attention;
-* roofline   the attention call (its kernels) against MI355X's 8 TB/s HBM;
-             achieved = algorithmic bytes per call / mean call time (HIP events
-             on the stream the kernels run on);
+* value      algorithmic KV bytes read per step / step time (GB/s);
+* roofline   the step's launch against MI355X's 8 TB/s HBM; achieved =
+             algorithmic bytes per call (K/V of every context token, q, out,
+             table entries, lengths, the new tokens read and written) / mean call
+             time (HIP events on the stream the kernels run on);
 * cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload.
 """
 
@@ -436,15 +438,32 @@ def main():
         ops.paged_attention_decode(out, inp.q, inp.k_cache, inp.v_cache, tables, ctx, w.softmax_scale, max_ctx,
                                    partition_size=part, workspace=workspace, seq_order=order, stream=stream)
 
+    def step():                          # the whole step in one launch: write the new tokens, attend
+        ops.paged_attention_decode_append(out, inp.q, inp.k_cache, inp.v_cache, inp.k_new, inp.v_new, slots, tables,
+                                          ctx, w.softmax_scale, max_ctx, partition_size=part, workspace=workspace,
+                                          seq_order=order, stream=stream)
+
     for _ in range(args.warmup):
         reshape()
         attend()
+        step()
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    # the timed step: decode with append
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for i in range(K):
+        evs[i][0].record(stream)
+        step()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_step = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in range(K)])
+    step_ms = float(np.mean(t_step))
+    # the same step as two launches (reshape_and_cache, then decode), for the components
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     for i in range(K):
         ev[i][0].record(stream)
         reshape()
@@ -452,11 +471,9 @@ def main():
         attend()
         ev[i][2].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     t_reshape = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)])
     t_attn = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)])
-    t_step = np.array([ev[i][0].elapsed_time(ev[i][2]) for i in range(K)])
-    step_ms = float(np.mean(t_step))
+    t_split = np.array([ev[i][0].elapsed_time(ev[i][2]) for i in range(K)])
 
     # ---- copy_blocks on copy-on-write pairs shaped like the shared-prefix workload (timed separately)
     sp = synth.SHARED_PREFIX_FP8
@@ -505,8 +522,9 @@ def main():
 
     elt_q, elt_kv = inp.q.element_size(), inp.k_cache.element_size()
     kv_bytes, alg_bytes = algorithmic_bytes(w, ctx_np.astype(np.int64), elt_q, elt_kv)
+    append_bytes = 2 * w.num_seqs * w.num_kv_heads * w.head_dim * (inp.k_new.element_size() + elt_kv) + 8 * w.num_seqs
     attn_ms = float(np.mean(t_attn))
-    achieved = alg_bytes / (attn_ms * 1e-3) / 1e9
+    achieved = (alg_bytes + append_bytes) / (step_ms * 1e-3) / 1e9
     traffic = measured_traffic(args.workload)
     result = {
         "metric": "paged decode KV-read GB/s (% of HBM peak) + sequences/sec per decode step",
@@ -531,10 +549,14 @@ def main():
         "seq_per_s": round(w.num_seqs / (step_ms * 1e-3), 1),
         "kv_bytes_per_step": kv_bytes,
         "components": {
+            "paged_attention_decode_append_us": round(step_ms * 1e3, 2),
+            "paged_attention_decode_append_median_us": round(float(np.median(t_step)) * 1e3, 2),
+            "two_launch_step_us": round(float(np.mean(t_split)) * 1e3, 2),
             "reshape_and_cache_us": round(float(np.mean(t_reshape)) * 1e3, 2),
             "paged_attention_decode_us": round(attn_ms * 1e3, 2),
             "paged_attention_decode_median_us": round(float(np.median(t_attn)) * 1e3, 2),
             "attention_kv_gbps": round(kv_bytes / (attn_ms * 1e-3) / 1e9, 1),
+            "attention_pct_of_hbm_peak": round(100.0 * alg_bytes / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
             "copy_blocks_us": round(copy_us, 2),
             "copy_blocks_pairs": n_pairs,
             "copy_blocks_gbps": round(2 * 2 * n_pairs * block_bytes / (copy_us * 1e-6) / 1e9, 1),
@@ -546,13 +568,14 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_attention_decode (attention kernel + split-context reduce when planned)",
+            "kernel": "paged_attention_decode_append (attention kernel writing the new tokens, + split-context "
+                      "reduce when planned)",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "algorithmic_bytes_per_call": alg_bytes,
+            "algorithmic_bytes_per_call": alg_bytes + append_bytes,
         },
     }
     if not args.no_cpu_baseline:

@@ -1,7 +1,7 @@
 /*
  * pkv.h -- C ABI of the paged-KV decode library for AMD MI355X (gfx950).
  *
- * Five data-path calls and their helpers.  The library is stateless: the host
+ * Six data-path calls and their helpers.  The library is stateless: the host
  * owns the block bookkeeping (which physical block holds which tokens,
  * reference counts, copy-on-write decisions); the library moves bytes and
  * attends.  Sources cited (page title, then section):
@@ -171,6 +171,35 @@ int pkv_paged_attention_decode(void* out, const void* q,
                                const float* k_scales, const float* v_scales,
                                int q_dtype, int kv_dtype, int partition_size,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pkv_paged_attention_decode_append -- one decode step in one launch: each
+ * sequence's new token is written into the pool and then attended over, with
+ * the new token included ([KVpag]: decode produces one token at a time and
+ * attends over the cache of every token seen so far, its own included).
+ *
+ * Same result as pkv_reshape_and_cache(key, value, k_cache, v_cache,
+ * slot_mapping, num_tokens = num_seqs, ...) followed by
+ * pkv_paged_attention_decode(...) with the same arguments, without the second
+ * launch: for each sequence s the workgroup that reads s's last block first
+ * writes row s of key / value (each [num_seqs][num_kv_heads][head_dim], q_dtype;
+ * bit copy or the 8-bit encode of pkv_reshape_and_cache) into slot
+ * slot_mapping[s], then attends.
+ * Preconditions: slot_mapping[s] is the slot of position context_lens[s] - 1
+ * of sequence s (the host's block manager returns exactly that), and no two
+ * sequences share it.  Slots < 0 or past the pool are skipped; a sequence with
+ * context 0 writes nothing.  k_cache / v_cache are written, so they are not const.
+ */
+int pkv_paged_attention_decode_append(void* out, const void* q, void* k_cache, void* v_cache,
+                                      const void* key, const void* value, const int64_t* slot_mapping,
+                                      const int32_t* block_tables, int max_blocks_per_seq,
+                                      const int32_t* context_lens, const int32_t* seq_order,
+                                      int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                                      int block_size, int num_blocks, int max_context_len,
+                                      float scale, float k_scale, float v_scale,
+                                      const float* k_scales, const float* v_scales,
+                                      int q_dtype, int kv_dtype, int partition_size,
+                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * pkv_reshape_and_cache -- write each new token's key and value into the pool

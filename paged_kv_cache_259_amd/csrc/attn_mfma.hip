@@ -302,6 +302,8 @@ void attn_mfma_kernel(AttnParams p) {
       const int which = start <= a ? 0 : 1;
       int ctx = p.context_lens[s];
       ctx = ctx < 0 ? 0 : (ctx > p.ctx_cap ? p.ctx_cap : ctx);
+      if (p.new_k && j1 == end - start)                     // this segment holds the sequence's last block
+        append_new_row<T, T, D, A::BS, NW * 64>(p, s, kvh, (j1 - 1 - j0) % NW);
       st.init();
       A::attend(p, s, kvh, ctx, j0, j1, w, c16, g4, st);
       const int64_t prow = complete ? -1 : ((int64_t)k * 2 + which) * p.num_heads + (int64_t)kvh * p.group;
@@ -332,6 +334,8 @@ void attn_mfma_kernel(AttnParams p) {
   if (b_begin >= nblk && (part > 0 || !direct)) return;     // empty partition
   int b_end = b_begin + p.partition_blocks;
   b_end = b_end < nblk ? b_end : nblk;
+  if (p.new_k && nblk > 0 && b_end == nblk)                 // this workgroup reads the last block
+    append_new_row<T, T, D, A::BS, NW * 64>(p, seq, kvh, (nblk - 1 - b_begin) % NW);
   st.init();
   A::attend(p, seq, kvh, ctx, b_begin, b_end, w, c16, g4, st);
   // partition rows are [seq][head][partition]

@@ -329,6 +329,8 @@ void attn_vector_kernel(AttnParams p) {
       const int which = start <= a ? 0 : 1;              // first or last segment of this slice
       int ctx = p.context_lens[s];
       ctx = ctx < 0 ? 0 : (ctx > p.ctx_cap ? p.ctx_cap : ctx);
+      if (p.new_k && j1 == end - start)                     // this segment holds the sequence's last block
+        append_new_row<QT, KT, D, BS, NW * 64>(p, s, head / p.group, (j1 - 1 - j0) % NW);
       st.init();
       A::attend(p, s, head, ctx, j0, j1, w, row, col, st);
       const int64_t prow = complete ? -1 : ((int64_t)k * 2 + which) * p.num_heads + head;
@@ -361,6 +363,8 @@ void attn_vector_kernel(AttnParams p) {
   if (b_begin >= nblk && (part > 0 || !direct)) return;     // empty partition
   int b_end = b_begin + p.partition_blocks;
   b_end = b_end < nblk ? b_end : nblk;
+  if (p.new_k && nblk > 0 && b_end == nblk)                 // this workgroup reads the last block
+    append_new_row<QT, KT, D, BS, NW * 64>(p, seq, head / p.group, (nblk - 1 - b_begin) % NW);
   st.init();
   A::attend(p, seq, head, ctx, b_begin, b_end, w, row, col, st);
   const int64_t prow = direct ? -1 : ((int64_t)seq * p.num_heads + head) * p.num_partitions + part;

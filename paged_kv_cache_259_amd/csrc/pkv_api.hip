@@ -183,14 +183,17 @@ size_t pkv_attention_workspace_bytes(int num_seqs, int num_heads, int num_kv_hea
   return pl.ws_bytes;
 }
 
-int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
-                               const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
-                               const int32_t* seq_order,
-                               int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
-                               int num_blocks, int max_context_len, float scale, float k_scale, float v_scale,
-                               const float* k_scales, const float* v_scales,
-                               int q_dtype, int kv_dtype, int partition_size, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Decode, optionally writing each sequence's new token first (new_k != NULL).
+int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache, const void* new_k,
+                const void* new_v, const int64_t* slot_mapping, const int32_t* block_tables, int max_blocks_per_seq,
+                const int32_t* context_lens, const int32_t* seq_order, int num_seqs, int num_heads, int num_kv_heads,
+                int head_dim, int block_size, int num_blocks, int max_context_len, float scale, float k_scale,
+                float v_scale, const float* k_scales, const float* v_scales, int q_dtype, int kv_dtype,
+                int partition_size, void* workspace, size_t workspace_bytes, void* stream) {
   Plan pl;
   int st = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len, partition_size,
                      q_dtype, kv_dtype, &pl);
@@ -202,6 +205,10 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
   if (num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PKV_ERR_NULL_POINTER;
   if (!pkv::aligned16(out) || !pkv::aligned16(q) || !pkv::aligned16(k_cache) || !pkv::aligned16(v_cache)) return PKV_ERR_UNSUPPORTED;
+  if (new_k) {
+    if (!new_v || !slot_mapping) return PKV_ERR_NULL_POINTER;
+    if (!pkv::aligned16(new_k) || !pkv::aligned16(new_v)) return PKV_ERR_UNSUPPORTED;
+  }
   if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes || !pkv::aligned16(workspace)))
     return PKV_ERR_WORKSPACE;
 
@@ -243,6 +250,11 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
   }
   if (cap > cap_table) cap = cap_table;
   p.ctx_cap = (int)(cap < 2147483647LL ? cap : 2147483647LL);
+  p.new_k = new_k;
+  p.new_v = new_v;
+  p.slot_mapping = new_k ? slot_mapping : nullptr;
+  p.enc_k_scale = k_scale;
+  p.enc_v_scale = v_scale;
   p.k_scales = fp8 ? k_scales : nullptr;
   p.v_scales = fp8 ? v_scales : nullptr;
   p.qk_scale = scale * kLog2e * (fp8 && !k_scales ? k_scale : 1.f);
@@ -273,6 +285,36 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, co
     e = pkv::launch_attention_reduce(r, q_dtype, head_dim, s);
   }
   return pkv::launch_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+                               const int32_t* seq_order, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                               int block_size, int num_blocks, int max_context_len, float scale, float k_scale,
+                               float v_scale, const float* k_scales, const float* v_scales, int q_dtype, int kv_dtype,
+                               int partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(out, q, k_cache, v_cache, nullptr, nullptr, nullptr, block_tables, max_blocks_per_seq,
+                     context_lens, seq_order, num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_context_len, scale, k_scale, v_scale, k_scales, v_scales, q_dtype, kv_dtype, partition_size,
+                     workspace, workspace_bytes, stream);
+}
+
+int pkv_paged_attention_decode_append(void* out, const void* q, void* k_cache, void* v_cache, const void* key,
+                                      const void* value, const int64_t* slot_mapping, const int32_t* block_tables,
+                                      int max_blocks_per_seq, const int32_t* context_lens, const int32_t* seq_order,
+                                      int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+                                      int num_blocks, int max_context_len, float scale, float k_scale, float v_scale,
+                                      const float* k_scales, const float* v_scales, int q_dtype, int kv_dtype,
+                                      int partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs > 0 && (!key || !value || !slot_mapping)) return PKV_ERR_NULL_POINTER;
+  return decode_impl(out, q, k_cache, v_cache, num_seqs > 0 ? key : nullptr, value, slot_mapping, block_tables,
+                     max_blocks_per_seq, context_lens, seq_order, num_seqs, num_heads, num_kv_heads, head_dim,
+                     block_size, num_blocks, max_context_len, scale, k_scale, v_scale, k_scales, v_scales, q_dtype,
+                     kv_dtype, partition_size, workspace, workspace_bytes, stream);
 }
 
 int pkv_paged_prefill_attention(void* out, const void* q, const void* k_cache, const void* v_cache,

@@ -418,6 +418,14 @@ struct AttnParams {
   int longest_first;       // one pass: workgroup r takes the r-th longest sequence
   const int32_t* seq_order;  // one pass: the caller's longest-first order (else derived in-workgroup)
   int* ws_prefix;          // [S+1] block prefix, written by workgroup 0 in slice mode
+  // decode with append: sequence s's new token (row s of new_k / new_v, q's
+  // dtype) goes to slot slot_mapping[s] before the attention reads it; NULL
+  // new_k for a plain decode.  enc_*_scale: the pool-wide 8-bit encode scales.
+  const void* new_k;
+  const void* new_v;
+  const int64_t* slot_mapping;
+  float enc_k_scale;
+  float enc_v_scale;
   const float* k_scales;   // [num_kv_heads] per-head 8-bit scales, or NULL (then k_scale is in qk_scale)
   const float* v_scales;   // [num_kv_heads] or NULL (then v_scale applies)
   float qk_scale;          // scale * log2(e) * k_scale
@@ -425,6 +433,64 @@ struct AttnParams {
   uint32_t total_wgs;
   uint32_t xcd_chunk;       // see xcd_remap
 };
+
+// Decode with append: the wave that will load sequence seq's last block (wave
+// `owner` of the workgroup) writes that sequence's new K/V row for kv head g
+// into its slot (bit copy, or the 8-bit encode with the pool's or the head's
+// scale) and waits for the stores before going on, so its own later loads see
+// the row; the other waves do not wait, and no other workgroup reads the row in
+// this launch.  Several query-head workgroups sharing a kv head each write the
+// same bytes.  Called by every thread of the workgroup (the wave index is
+// uniform).
+template <class ST, class KT, int D, int BS, int NT>
+__device__ void append_new_row(const AttnParams& p, int seq, int g, int owner) {
+  if ((int)(threadIdx.x >> 6) != owner) return;
+  constexpr int NT_ = 64;                                   // the owner wave's lanes do the writes
+  (void)NT;
+  const int64_t slot = p.slot_mapping[seq];
+  if (slot >= 0 && slot < (int64_t)p.num_blocks * BS) {
+    constexpr int V = 16 / ST::bytes;                       // source elements per 16-byte chunk
+    const int64_t blk = slot / BS, off = slot - blk * BS;
+    const size_t src = ((size_t)seq * p.num_kv_heads + g) * D;
+    const size_t dst = (((size_t)blk * p.num_kv_heads + g) * BS + off) * D;
+    for (int c = threadIdx.x & 63; c < D / V; c += NT_) {
+      const uint4 kr = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(p.new_k) + (src + c * V) * ST::bytes);
+      const uint4 vr = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(p.new_v) + (src + c * V) * ST::bytes);
+      char* kd = reinterpret_cast<char*>(const_cast<void*>(p.k_cache));
+      char* vd = reinterpret_cast<char*>(const_cast<void*>(p.v_cache));
+      if constexpr (KT::kId == ST::kId) {
+        *reinterpret_cast<uint4*>(kd + (dst + c * V) * KT::bytes) = kr;
+        *reinterpret_cast<uint4*>(vd + (dst + c * V) * KT::bytes) = vr;
+      } else {                                              // 8-bit cache
+        const float ks = p.k_scales ? p.k_scales[g] : p.enc_k_scale;
+        const float vs = p.v_scales ? p.v_scales[g] : p.enc_v_scale;
+        float kf[V], vf[V];
+        Unpack<ST>::run(kr, kf);
+        Unpack<ST>::run(vr, vf);
+        uint32_t kc[V / 4], vc[V / 4];
+#pragma unroll
+        for (int j = 0; j < V / 4; ++j) {
+          uint32_t a = 0, b = 0;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            a |= fp8_encode_scaled<KT>(kf[4 * j + t], ks) << (8 * t);
+            b |= fp8_encode_scaled<KT>(vf[4 * j + t], vs) << (8 * t);
+          }
+          kc[j] = a;
+          vc[j] = b;
+        }
+        if constexpr (V == 8) {
+          *reinterpret_cast<uint2*>(kd + dst + c * V) = make_uint2(kc[0], kc[1]);
+          *reinterpret_cast<uint2*>(vd + dst + c * V) = make_uint2(vc[0], vc[1]);
+        } else {
+          *reinterpret_cast<uint32_t*>(kd + dst + c * V) = kc[0];
+          *reinterpret_cast<uint32_t*>(vd + dst + c * V) = vc[0];
+        }
+      }
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");   // stores done before this wave's later loads
+}
 
 // Per-head 8-bit scales of kv head g folded into the workgroup's copy of the
 // parameters (the pool-wide scales are already in qk_scale / v_scale otherwise).

@@ -43,6 +43,10 @@ _lib.pkv_paged_attention_decode.argtypes = (
     + [_vp, _vp]
     + [_c_int] * 3
     + [_vp, _c_size, _vp])
+_lib.pkv_paged_attention_decode_append.restype = _c_int
+_lib.pkv_paged_attention_decode_append.argtypes = (
+    [_vp] * 7 + [_vp, _c_int, _vp, _vp] + [_c_int] * 7 + [_c_float] * 3 + [_vp, _vp] + [_c_int] * 3
+    + [_vp, _c_size, _vp])
 _lib.pkv_reshape_and_cache.restype = _c_int
 _lib.pkv_reshape_and_cache.argtypes = [_vp] * 5 + [_c_int] * 7 + [_c_float] * 2 + [_vp, _vp, _vp]
 _lib.pkv_copy_blocks.restype = _c_int
@@ -55,7 +59,7 @@ _lib.pkv_swap_blocks.argtypes = [_vp, _vp, _c_int, _vp, _vp, _c_int, _vp] + [_c_
 EXPORTED_SYMBOLS = (
     "pkv_status_string", "pkv_version", "pkv_attention_plan", "pkv_attention_workspace_bytes",
     "pkv_paged_attention_decode", "pkv_reshape_and_cache", "pkv_copy_blocks", "pkv_swap_blocks",
-    "pkv_paged_prefill_attention",
+    "pkv_paged_prefill_attention", "pkv_paged_attention_decode_append",
 )
 
 
@@ -195,6 +199,49 @@ def paged_prefill_attention(out, q, k_cache, v_cache, block_tables, context_lens
         _ptr(context_lens), _ptr(query_start_loc), S, T, H, KVH, d, bs, NB if num_blocks is None else num_blocks,
         int(max_query_len), int(max_context_len), float(scale), dtype_code(q.dtype), dtype_code(k_cache.dtype),
         _stream(stream)), "pkv_paged_prefill_attention")
+    return out
+
+
+def paged_attention_decode_append(out, q, k_cache, v_cache, key, value, slot_mapping, block_tables, context_lens,
+                                  scale, max_context_len, k_scale=1.0, v_scale=1.0, partition_size=0,
+                                  workspace=None, num_blocks=None, seq_order=None, k_scales=None, v_scales=None,
+                                  stream=None):
+    """reshape_and_cache of each sequence's new token (key/value [S, KVH, d] in q's dtype, slot_mapping int64 [S])
+    followed by paged_attention_decode, in one launch."""
+    S, H, d = q.shape
+    NB, KVH, bs, d2 = k_cache.shape
+    if d2 != d or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch between q/out and the pools")
+    if tuple(key.shape) != (S, KVH, d) or tuple(value.shape) != (S, KVH, d):
+        raise ValueError("key/value must be [num_seqs, num_kv_heads, head_dim]")
+    if key.dtype != q.dtype or value.dtype != q.dtype:
+        raise TypeError("key/value must have q's dtype")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (S,):
+        raise TypeError("slot_mapping must be int64 [num_seqs]")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables must be [S, maxblk] and context_lens [S]")
+    for t in (out, q, k_cache, v_cache, key, value, slot_mapping, block_tables, context_lens):
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    if out.dtype != q.dtype:
+        raise TypeError("out must have q's dtype")
+    if seq_order is not None and (seq_order.dtype != torch.int32 or seq_order.shape != (S,)
+                                  or not seq_order.is_contiguous()):
+        raise ValueError("seq_order must be a contiguous int32 [S] tensor")
+    qd, kvd = dtype_code(q.dtype), dtype_code(k_cache.dtype)
+    need = attention_workspace_bytes(S, H, KVH, d, bs, max_context_len, partition_size, qd, kvd)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _ptr(workspace) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.pkv_paged_attention_decode_append(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(key), _ptr(value), _ptr(slot_mapping),
+        _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), _ptr(seq_order), S, H, KVH, d, bs,
+        NB if num_blocks is None else num_blocks, max_context_len, float(scale), float(k_scale), float(v_scale),
+        _ptr(_head_scales(k_scales, KVH, k_cache.device)), _ptr(_head_scales(v_scales, KVH, k_cache.device)),
+        qd, kvd, partition_size, ws_ptr, ws_bytes, _stream(stream)), "pkv_paged_attention_decode_append")
     return out
 
 
