@@ -47,8 +47,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic.json")
-KERNEL_SOURCES = ["attn_vector.hip", "attn_mfma.hip", "attn_reduce.hip", "prefill_mfma.hip", "pkv_device.h",
-                  "pkv_api.hip"]
+KERNEL_SOURCES = ["attn_vector.h", "attn_vector.hip", "attn_mfma.h", "attn_mfma.hip", "attn_append.hip",
+                  "attn_reduce.hip", "prefill_mfma.hip", "pkv_device.h", "pkv_api.hip"]
 
 
 def parse():

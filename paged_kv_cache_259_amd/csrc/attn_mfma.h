@@ -1,0 +1,391 @@
+// attn_mfma.h -- paged decode attention for grouped-query heads on the
+// CDNA4 matrix cores.  One workgroup per (sequence, kv head, context
+// partition); the G query heads that share the kv head ("PagedAttention",
+// Ultralytics glossary, section "Các kỹ thuật liên quan": grouped-query
+// attention shares K/V heads between query heads) are the 16 columns of the
+// MFMA tiles (padded with zero queries when G < 16), so each K/V tile is read
+// from HBM once for the whole group.
+//
+// Per 16-token block (tile = 16 rows x D, contiguous):
+//   QK:  S[token][head] = sum_k K[token][k] Q[head][k]
+//        v_mfma_f32_16x16x32 (bf16/f16), A = K tile rows, B = Q^T, D/32 steps.
+//        Lane l feeds token l%16, dims 32c + 8(l/16) .. +8 (one 16-byte load).
+//        Result: lane l holds S[token 4(l/16)+r][head l%16], r = 0..3.
+//   online softmax per head (column): block max over the 16 tokens = max over
+//        the lane's 4 values, then over lanes l^16 and l^32.
+//   PV:  O^T[dcol][head] += sum_k V[tok_k][8*dcol+e] P[head][tok_k]
+//        v_mfma_f32_16x16x4 f32, A = V^T, B = P^T, one MFMA per (token group
+//        tg, element e): lane l feeds V[4(l/16)+tg][8(l%16)+e] (from a plain
+//        row-major 16-byte load of token 4(l/16)+tg) and P[head l%16][token
+//        4(l/16)+tg] -- which is exactly register r = tg of its QK result, so
+//        no shuffle or transpose is needed between the two products, and P
+//        stays fp32.
+//        O_e: lane l holds O[head l%16][dim 8(4(l/16)+r)+e], r = 0..3.
+//
+// Two kernels share the body: attn_mfma_kernel (plain decode) and
+// attn_mfma_append_kernel (decode that first writes each sequence's new K/V
+// row).  attn_mfma.hip instantiates the first, attn_append.hip the second.
+#pragma once
+#include "pkv_device.h"
+
+namespace pkv {
+
+template <class T> struct MfmaOp;
+template <> struct MfmaOp<BF16> {
+  typedef bf16x8_t vec;
+  __device__ __forceinline__ static f32x4_t qk(const uint4& a, const uint4& b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(vec, a), __builtin_bit_cast(vec, b), c, 0, 0, 0);
+  }
+};
+template <> struct MfmaOp<F16> {
+  typedef f16x8_t vec;
+  __device__ __forceinline__ static f32x4_t qk(const uint4& a, const uint4& b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(vec, a), __builtin_bit_cast(vec, b), c, 0, 0, 0);
+  }
+};
+
+template <class T, int D, int NW, bool PIPE>
+struct MfmaAttention {
+  static constexpr int BS = 16;
+  static constexpr int NC = D / 32;                 // QK steps of 32 dims
+  static constexpr int NH = D / 128;                // 128-element halves of a V row (16 lanes x 8)
+  static constexpr size_t ROW_BYTES = (size_t)D * 2;
+  static constexpr size_t TILE_BYTES = ROW_BYTES * BS;
+  static constexpr int RS = D + 1;                  // padded LDS row stride against bank conflicts
+  static_assert(D % 128 == 0, "MFMA family needs head_dim 128 or 256");
+
+  struct Smem {
+    float m[NW][16], l[NW][16];
+    float o[NW][16 * RS];
+    alignas(16) int prefix[kMaxSliceSeqs + 4];
+    int wsum[NW];
+  };
+
+  struct State {
+    float m;                 // running max of head c16 (same in all four row groups)
+    float lsum;              // this lane's share of the running exp-sum of head c16
+    f32x4_t O[NH][8];
+    __device__ void init() {
+      m = -__builtin_inff();
+      lsum = 0.f;
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) O[hh][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+
+  // One block's tiles in registers: K as the QK A operand (token c16, NC
+  // 16-byte chunks), V as row-major 16-byte loads of tokens 4*g4 + tg.
+  struct Tiles {
+    uint4 k[NC];
+    uint4 v[4][NH];
+    bool ok;
+  };
+
+  // Rows at or past `valid` (the last block's tail) are not loaded: their
+  // registers are never used unmasked.
+  __device__ static void issue(const AttnParams& p, const char* kbase, const char* vbase, size_t block_stride,
+                               int blk, int valid, int c16, int g4, Tiles& t) {
+    t.ok = blk >= 0 && blk < p.num_blocks;
+    if (!t.ok) return;                                  // wave-uniform
+    const char* kp = kbase + (size_t)blk * block_stride;
+    const char* vp = vbase + (size_t)blk * block_stride;
+    if (c16 < valid) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) t.k[c] = *reinterpret_cast<const uint4*>(kp + c * 64);
+    }
+#pragma unroll
+    for (int tg = 0; tg < 4; ++tg) {
+      if (g4 * 4 + tg < valid) {
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh) t.v[tg][hh] = *reinterpret_cast<const uint4*>(vp + tg * ROW_BYTES + hh * 256);
+      }
+    }
+  }
+
+  __device__ static void consume(const AttnParams& p, const uint4* qop, Tiles& t, int valid, int g4, State& st) {
+    if (!t.ok) return;                                  // wave-uniform
+    f32x4_t S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NC; ++c) S = MfmaOp<T>::qk(t.k[c], qop[c], S);
+    float s[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[r] = S[r] * p.qk_scale;
+    if (valid < BS) {                                   // wave-uniform: the last, partial block
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool v = g4 * 4 + r < valid;
+        s[r] = v ? s[r] : -__builtin_inff();
+        if (!v) {
+#pragma unroll
+          for (int hh = 0; hh < NH; ++hh) t.v[r][hh] = make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
+    }
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mx = fmaxf(mx, swz_xor16(mx));
+    mx = fmaxf(mx, xor32(mx));
+    const float mn = fmaxf(st.m, mx);                   // finite: every block has a real token
+    const float alpha = exp2_fast(st.m - mn);
+    float pr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pr[r] = exp2_fast(s[r] - mn);
+    st.lsum = st.lsum * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+    st.m = mn;
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) st.O[hh][e] *= alpha;
+#pragma unroll
+    for (int tg = 0; tg < 4; ++tg) {
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh) {
+        float vf[8];
+        Unpack<T>::run(t.v[tg][hh], vf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          st.O[hh][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[e], pr[tg], st.O[hh][e], 0, 0, 0);
+      }
+    }
+  }
+
+  // Blocks [j0, j1) of sequence `seq` for the query heads of kv head `kvh`;
+  // wave w takes blocks j0 + w, j0 + w + NW, ...  With PIPE the next block's
+  // tiles are in flight while the current one is consumed.  Block ids come 64
+  // at a time from one VGPR (lane t holds the t-th id) through readlane.
+  __device__ static void attend(const AttnParams& p, int seq, int kvh, int ctx, int j0, int j1, int w, int c16,
+                                int g4, State& st) {
+    const int first = j0 + w;
+    const int n = first < j1 ? (j1 - first + NW - 1) / NW : 0;
+    if (n == 0) return;                                 // wave-uniform
+    const int G = p.group;
+    // B operand of QK: Q[head c16][32c + 8 g4 .. +8]; zero for padding heads.
+    uint4 qop[NC];
+    {
+      const bool real = c16 < G;
+      const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) +
+                             ((size_t)seq * p.num_heads + (size_t)kvh * G + (real ? c16 : 0)) * D;
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        qop[c] = real ? *reinterpret_cast<const uint4*>(qrow + c * 32 + g4 * 8) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    const int32_t* table = p.block_tables + (size_t)seq * p.max_blocks_per_seq;
+    const char* kbase = reinterpret_cast<const char*>(p.k_cache) + (size_t)kvh * TILE_BYTES + c16 * ROW_BYTES + g4 * 16;
+    const char* vbase =
+        reinterpret_cast<const char*>(p.v_cache) + (size_t)kvh * TILE_BYTES + (g4 * 4) * ROW_BYTES + c16 * 16;
+    const size_t block_stride = TILE_BYTES * (size_t)p.num_kv_heads;
+    const int lane = threadIdx.x & 63;
+    auto load_ids = [&](int chunk) -> int {
+      const int i = chunk * 64 + lane;
+      return i < n ? table[first + i * NW] : -1;
+    };
+    int ids = load_ids(0);
+    int ids_next = n > 64 ? load_ids(1) : -1;
+    int chunk = 0;
+    auto id_of = [&](int i) -> int {                    // called with i = 0, 1, 2, ... in order
+      if ((i >> 6) != chunk) {
+        chunk = i >> 6;
+        ids = ids_next;
+        ids_next = (chunk + 1) * 64 < n ? load_ids(chunk + 1) : -1;
+      }
+      return __builtin_amdgcn_readlane(ids, i & 63);
+    };
+    auto valid_of = [&](int i) -> int {                 // real tokens in the wave's i-th block
+      const int r = ctx - (first + i * NW) * BS;
+      return r < BS ? r : BS;
+    };
+    Tiles a;
+    issue(p, kbase, vbase, block_stride, id_of(0), valid_of(0), c16, g4, a);
+    if constexpr (PIPE) {
+      Tiles b;
+      for (int i = 0; i < n; i += 2) {
+        if (i + 1 < n) issue(p, kbase, vbase, block_stride, id_of(i + 1), valid_of(i + 1), c16, g4, b);
+        consume(p, qop, a, valid_of(i), g4, st);
+        if (i + 1 < n) {
+          if (i + 2 < n) issue(p, kbase, vbase, block_stride, id_of(i + 2), valid_of(i + 2), c16, g4, a);
+          consume(p, qop, b, valid_of(i + 1), g4, st);
+        }
+      }
+    } else {
+      for (int i = 0; i < n; ++i) {
+        if (i > 0) issue(p, kbase, vbase, block_stride, id_of(i), valid_of(i), c16, g4, a);
+        consume(p, qop, a, valid_of(i), g4, st);
+      }
+    }
+  }
+
+  // Merge the waves through LDS (only the G real heads) and write the normalised
+  // outputs (prow_base < 0) or the fp32 summary row prow_base + h * prow_stride
+  // of the workspace for head h of the group.  Called by every thread; ends
+  // with a barrier.
+  __device__ static void finish(const AttnParams& p, State& st, Smem& sm, int seq, int kvh, int64_t prow_base,
+                                int64_t prow_stride, int tid, int w, int c16, int g4) {
+    const int G = p.group;
+    float lsum = st.lsum;
+    lsum += swz_xor16(lsum);
+    lsum += xor32(lsum);
+    if (c16 < G) {
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sm.o[w][c16 * RS + hh * 128 + (g4 * 4 + r) * 8 + e] = st.O[hh][e][r];
+      if (g4 == 0) { sm.m[w][c16] = st.m; sm.l[w][c16] = lsum; }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < G * D; idx += NW * 64) {
+      const int h = idx / D;
+      const int d = idx - h * D;
+      float M = -__builtin_inff();
+#pragma unroll
+      for (int i = 0; i < NW; ++i) M = fmaxf(M, sm.m[i][h]);
+      float o = 0.f, Lsum = 0.f;
+#pragma unroll
+      for (int i = 0; i < NW; ++i) {
+        const float wt = (sm.m[i][h] == -__builtin_inff()) ? 0.f : exp2_fast(sm.m[i][h] - M);
+        Lsum += wt * sm.l[i][h];
+        o += wt * sm.o[i][h * RS + d];
+      }
+      if (prow_base < 0) {
+        const size_t sh = (size_t)seq * p.num_heads + (size_t)kvh * G + h;
+        store_elem<T>(p.out, sh * D + d, Lsum > 0.f ? o * (p.v_scale / Lsum) : 0.f);
+      } else {
+        const int64_t prow = prow_base + h * prow_stride;
+        p.ws_o[(size_t)prow * D + d] = o * p.v_scale;
+        if (d == 0) { p.ws_m[prow] = M; p.ws_l[prow] = Lsum; }
+      }
+    }
+    __syncthreads();
+  }
+};
+
+#ifndef PKV_MFMA_WAVES_PER_EU
+#define PKV_MFMA_WAVES_PER_EU 4
+#endif
+#ifndef PKV_MFMA_WAVES_PER_EU_PIPE
+#define PKV_MFMA_WAVES_PER_EU_PIPE 3
+#endif
+template <class T, int D, int NW, bool PIPE, bool APPEND>
+__device__ __forceinline__ void attn_mfma_body(AttnParams p) {
+  using A = MfmaAttention<T, D, NW, PIPE>;
+  __shared__ typename A::Smem sm;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c16 = lane & 15;   // QK: token row of A / head column of B and of the result
+  const int g4 = lane >> 4;    // 0..3
+  const uint32_t L = xcd_remap(blockIdx.x, p.total_wgs, p.xcd_chunk);
+  typename A::State st;
+
+  if (p.num_slices > 0) {
+    const int kvh = (int)(L % (uint32_t)p.num_kv_heads);
+    const int k = (int)(L / (uint32_t)p.num_kv_heads);
+    const int S = p.num_seqs;
+    block_prefix<NW * 64>(p.context_lens, S, p.ctx_cap, A::BS, sm.prefix, sm.wsum);
+    if (blockIdx.x == 0)
+      for (int i = tid; i <= S; i += NW * 64) p.ws_prefix[i] = sm.prefix[i];
+    const int64_t total = sm.prefix[S];
+    const int64_t a = slice_begin(k, total, p.num_slices), b = slice_begin(k + 1, total, p.num_slices);
+    if (a >= b) return;
+    int lo = 1, hi = S;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (sm.prefix[mid] > a) hi = mid; else lo = mid + 1;
+    }
+    int s = lo - 1;
+    int64_t pos = a;
+    while (pos < b) {
+      const int start = sm.prefix[s], end = sm.prefix[s + 1];
+      const int j0 = (int)(pos - start);
+      const int j1 = (int)((b < end ? b : end) - start);
+      const bool complete = start >= a && end <= b;
+      const int which = start <= a ? 0 : 1;
+      int ctx = p.context_lens[s];
+      ctx = ctx < 0 ? 0 : (ctx > p.ctx_cap ? p.ctx_cap : ctx);
+      if (APPEND && j1 == end - start)                      // this segment holds the sequence's last block
+        append_new_row<T, T, D, A::BS, NW * 64>(p, s, kvh, (j1 - 1 - j0) % NW);
+      st.init();
+      A::attend(p, s, kvh, ctx, j0, j1, w, c16, g4, st);
+      const int64_t prow = complete ? -1 : ((int64_t)k * 2 + which) * p.num_heads + (int64_t)kvh * p.group;
+      A::finish(p, st, sm, s, kvh, prow, 1, tid, w, c16, g4);
+      pos = end;
+      ++s;
+      while (s < S && sm.prefix[s + 1] <= pos) ++s;
+    }
+    return;
+  }
+
+  int seq, kvh, part;
+  decode_work_id(L, p.num_seqs, p.num_kv_heads, seq, kvh, part);
+  if (p.longest_first) {                                    // one pass only
+    if (p.seq_order) {
+      const int o = p.seq_order[seq];
+      seq = o < 0 ? 0 : (o >= p.num_seqs ? p.num_seqs - 1 : o);
+    } else {
+      seq = seq_of_rank<NW * 64>(p.context_lens, p.num_seqs, p.ctx_cap, A::BS, seq, sm.prefix, sm.wsum);
+    }
+  }
+  int ctx = p.context_lens[seq];
+  ctx = ctx < 0 ? 0 : (ctx > p.ctx_cap ? p.ctx_cap : ctx);
+  const int nblk = (ctx + A::BS - 1) / A::BS;
+  const int b_begin = part * p.partition_blocks;
+  // a context that fits in one partition is finished here; the reduce skips it
+  const bool direct = p.num_partitions == 1 || nblk <= p.partition_blocks;
+  if (b_begin >= nblk && (part > 0 || !direct)) return;     // empty partition
+  int b_end = b_begin + p.partition_blocks;
+  b_end = b_end < nblk ? b_end : nblk;
+  if (APPEND && nblk > 0 && b_end == nblk)                  // this workgroup reads the last block
+    append_new_row<T, T, D, A::BS, NW * 64>(p, seq, kvh, (nblk - 1 - b_begin) % NW);
+  st.init();
+  A::attend(p, seq, kvh, ctx, b_begin, b_end, w, c16, g4, st);
+  // partition rows are [seq][head][partition]
+  const int64_t prow = direct ? -1 : ((int64_t)seq * p.num_heads + (int64_t)kvh * p.group) * p.num_partitions + part;
+  A::finish(p, st, sm, seq, kvh, prow, p.num_partitions, tid, w, c16, g4);
+}
+
+#define PKV_MFMA_WAVES(D, PIPE) ((D) == 128 ? ((PIPE) ? PKV_MFMA_WAVES_PER_EU_PIPE : PKV_MFMA_WAVES_PER_EU) : 1)
+template <class T, int D, int NW, bool PIPE>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PKV_MFMA_WAVES(D, PIPE))))
+void attn_mfma_kernel(AttnParams p) {
+  attn_mfma_body<T, D, NW, PIPE, false>(p);
+}
+
+template <class T, int D, int NW, bool PIPE>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PKV_MFMA_WAVES(D, PIPE))))
+void attn_mfma_append_kernel(AttnParams p) {
+  attn_mfma_body<T, D, NW, PIPE, true>(p);
+}
+
+#ifndef PKV_MFMA_NW
+#define PKV_MFMA_NW 4
+#endif
+#ifndef PKV_MFMA_PIPE
+#define PKV_MFMA_PIPE 1
+#endif
+template <bool APPEND, class T, int D>
+static hipError_t launch_mfma(const AttnParams& p, hipStream_t stream) {
+  constexpr int NW = PKV_MFMA_NW;
+  constexpr bool PIPE = PKV_MFMA_PIPE != 0;
+  if constexpr (APPEND)
+    hipLaunchKernelGGL((attn_mfma_append_kernel<T, D, NW, PIPE>), dim3(p.total_wgs), dim3(NW * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_mfma_kernel<T, D, NW, PIPE>), dim3(p.total_wgs), dim3(NW * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+// q dtype (= kv dtype) and head_dim -> instantiation; the cases mfma_supported accepts.
+template <bool APPEND>
+static hipError_t launch_mfma_family(const AttnParams& p, int q_dtype, int d, hipStream_t stream) {
+  if (q_dtype == 2) {
+    if (d == 128) return launch_mfma<APPEND, BF16, 128>(p, stream);
+    if (d == 256) return launch_mfma<APPEND, BF16, 256>(p, stream);
+  } else if (q_dtype == 1) {
+    if (d == 128) return launch_mfma<APPEND, F16, 128>(p, stream);
+    if (d == 256) return launch_mfma<APPEND, F16, 256>(p, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pkv

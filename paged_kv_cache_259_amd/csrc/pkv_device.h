@@ -337,7 +337,7 @@ __device__ __forceinline__ int order_key(int nblk) {
 }
 
 template <int NT>
-__device__ int seq_of_rank(const int32_t* context_lens, int S, int ctx_cap, int bs, int r, int* s_cnt, int* s_pick) {
+__device__ __forceinline__ int seq_of_rank(const int32_t* context_lens, int S, int ctx_cap, int bs, int r, int* s_cnt, int* s_pick) {
   constexpr int NWV = NT / 64;
   constexpr int CHUNKS = (kMaxSliceSeqs + NT - 1) / NT;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;

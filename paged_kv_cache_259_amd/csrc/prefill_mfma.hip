@@ -146,7 +146,6 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
   const int wrow0 = row0 + 16 * RW * w;                     // the wave's first row
   const int wave_first_pos = base + wrow0;
   const int wave_last_pos = wave_first_pos + 16 * RW - 1;   // causal limit of the wave's rows
-  const bool wave_rows_real = wrow0 + 16 * RW <= n;
 
   // B operand of QK: Q^T, lane l holds query row wrow0 + 16 g + c16, dims 32c + 8 g4 .. +8.
   // With a negative scale Q enters negated (sign bits flipped, exact), so the
