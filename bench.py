@@ -6,7 +6,10 @@ With a prefill workload (prefill_llama13b_f16, prefill_gqa_bf16) the step is
 reshape_and_cache of the chunks' K/V followed by paged_prefill_attention, and
 the roofline is the dense MFMA peak instead of HBM.  prefix_cache_llama13b_f16
 times a prefill step of requests sharing a system prompt with the host prefix
-cache off and on (value = the speedup).
+cache off and on (value = the speedup).  shared_prefix_fp8 times the next
+decode step of parallel samples that share their prompts' blocks, over fp8
+(E4M3) pools: the copy-on-write copies the step needs plus the decode with
+append, KV bytes counted logical (per sample) and unique (per physical block).
 
 A step is one pass of the hot path over one synthetic decode batch, inputs
 resident in HBM: every sequence's new key/value goes into the slot the block
@@ -387,6 +390,180 @@ def cpu_baseline_prefix(w, inp, f, budget_s):
             "host_cores_available": len(os.sched_getaffinity(0))}
 
 
+def unique_kv_bytes(tables, ctx, bs, row_bytes):
+    """KV bytes of the distinct physical blocks the step reads: each block once, with the most tokens any
+    sequence uses of it."""
+    used = {}
+    for s in range(len(ctx)):
+        n = int(ctx[s])
+        for j in range(-(-n // bs)):
+            b = int(tables[s, j])
+            used[b] = max(used.get(b, 0), min(bs, n - j * bs))
+    return sum(used.values()) * row_bytes
+
+
+def main_shared_prefix(args, w):
+    """The next decode step of every sample of the shared-prefix workload (fp8 pools, copy-on-write).
+
+    Untimed set-up by the host driver: each prompt's K/V written once and shared
+    by its samples; continuations appended one token per step, copying a shared
+    partly filled block on a sample's first write into it; one decode over every
+    sample.  The timed step: the block manager gives every sample the slot of
+    its next token (copy-on-write pairs where that slot's block is still
+    shared), then copy_blocks over those pairs (when any) and one
+    paged_attention_decode_append launch that writes each sample's new token and
+    attends.  Repeating the step rewrites the same bytes, so every timed step
+    does the same work.  The set-up is host-bound (hundreds of small launches),
+    so the warm-up runs at least 25 ms of steps (more than ``--warmup`` steps if
+    need be; the JSON reports the count) to bring the GPU back to full clocks.
+    """
+    import torch
+    from paged_kv_cache_259_amd import ops, synth
+    from paged_kv_cache_259_amd.shared_prefix import run_shared_prefix
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = synth.make_shared_prefix_inputs(w, device=dev)
+    t_setup = time.perf_counter()
+    res = run_shared_prefix(inp, dev)
+    torch.cuda.synchronize()
+    t_setup = time.perf_counter() - t_setup
+    bm, kc, vc = res["block_manager"], res["k_cache"], res["v_cache"]
+    ks, vs = res["k_scale"], res["v_scale"]
+    seqs = list(range(w.num_seqs))
+    slots, pairs = [], []
+    for s in seqs:
+        slot, pair = bm.append_slot(s)
+        slots.append(slot)
+        if pair is not None:
+            pairs.append(pair)
+    tables_np = bm.block_table_array(seqs, w.max_blocks_per_seq)
+    ctx_np = bm.context_lens_array(seqs)
+    tables, ctx = torch.from_numpy(tables_np).to(dev), torch.from_numpy(ctx_np).to(dev)
+    order = torch.from_numpy(bm.longest_first(seqs, group_shared=True)).to(dev)   # forks of a prompt together
+    slot_t = torch.tensor(slots, dtype=torch.int64, device=dev)
+    pair_t = torch.tensor(pairs, dtype=torch.int64, device=dev).reshape(-1, 2)
+    k_new, v_new = synth.draw_step_kv(inp, len(seqs), dev)
+    q = synth.draw_query(inp, len(seqs), dev)
+    out = torch.empty_like(q)
+    max_ctx = int(ctx_np.max())
+    qd, kvd = ops.dtype_code(q.dtype), ops.dtype_code(kc.dtype)
+    plan = ops.attention_plan(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size, max_ctx, 0, qd, kvd)
+    ws_bytes = ops.attention_workspace_bytes(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size,
+                                             max_ctx, 0, qd, kvd)
+    workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def cow():
+        if len(pairs):
+            ops.copy_blocks(kc, vc, pair_t, stream=stream)
+
+    def attend():
+        ops.paged_attention_decode_append(out, q, kc, vc, k_new, v_new, slot_t, tables, ctx, w.softmax_scale, max_ctx,
+                                          k_scale=ks, v_scale=vs, workspace=workspace, seq_order=order, stream=stream)
+
+    warm, t_warm = 0, time.perf_counter()
+    while warm < args.warmup or time.perf_counter() - t_warm < 0.025:
+        cow()
+        attend()
+        torch.cuda.synchronize()
+        warm += 1
+    K = args.steps
+
+    def timed(fn):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+        for i in range(K):
+            ev[i][0].record(stream)
+            fn()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        return np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+
+    t_step = timed(lambda: (cow(), attend()))
+    t_attn = timed(attend)
+    t_cow = timed(cow) if len(pairs) else None
+    step_ms, attn_ms = float(np.mean(t_step)), float(np.mean(t_attn))
+    if args.calibrate_copy:
+        calibration_copy(w, kc.dtype, args.calibrate_copy, stream)
+
+    row_bytes = w.num_kv_heads * w.head_dim * 2 * kc.element_size()
+    kv_logical, alg_bytes = algorithmic_bytes(w, ctx_np.astype(np.int64), q.element_size(), kc.element_size())
+    kv_unique = unique_kv_bytes(tables_np, ctx_np, w.block_size, row_bytes)
+    append_bytes = 2 * w.num_seqs * w.num_kv_heads * w.head_dim * (k_new.element_size() + kc.element_size()) \
+        + 8 * w.num_seqs
+    unique_alg = alg_bytes - kv_logical + kv_unique
+    result = {
+        "metric": "paged decode KV-read GB/s (% of HBM peak) + sequences/sec per decode step",
+        "value": round(kv_logical / (step_ms * 1e-3) / 1e9, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": warm, "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3",
+        "data": "synthetic (seeded N(0,1) prompt and continuation K/V in fp16, encoded to E4M3 with amax/448 "
+                "scales; uniform continuation lengths)",
+        "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_heads": w.num_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
+                   "q_dtype": w.q_dtype, "kv_dtype": w.kv_dtype, "sum_context": int(ctx_np.sum()),
+                   "max_context": max_ctx, "num_blocks": w.num_blocks,
+                   "plan": {"path": ["vector", "mfma"][plan[0]], "partition_tokens": plan[1],
+                            "num_partitions": plan[2]}},
+        "pct_of_hbm_peak": round(100.0 * kv_logical / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+        "seq_per_s": round(w.num_seqs / (step_ms * 1e-3), 1),
+        "kv_bytes_per_step": {"logical": kv_logical, "unique": kv_unique},
+        "unique_gbps": round(kv_unique / (step_ms * 1e-3) / 1e9, 1),
+        "sharing": {"logical_blocks": res["logical_blocks"], "unique_blocks": res["unique_blocks"],
+                    "cow_pairs_during_generation": res["cow_pairs"], "cow_pairs_this_step": len(pairs),
+                    "setup_s": round(t_setup, 2)},
+        "components": {"copy_blocks_us": None if t_cow is None else round(float(np.mean(t_cow)) * 1e3, 2),
+                       "paged_attention_decode_append_us": round(attn_ms * 1e3, 2),
+                       "paged_attention_decode_append_median_us": round(float(np.median(t_attn)) * 1e3, 2)},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "paged_attention_decode_append over fp8 pools (achieved counts each physical block once; "
+                      "the logical rate, each sample reading its whole context, is value)",
+            "achieved": round((unique_alg + append_bytes) / (attn_ms * 1e-3) / 1e9, 1),
+            "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round((unique_alg + append_bytes) / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "traffic": measured_traffic(args.workload),
+            "algorithmic_bytes_per_call": unique_alg + append_bytes,
+            "logical_bytes_per_call": alg_bytes + append_bytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_shared(w, q, kc, vc, ks, vs, tables_np, ctx_np, args.cpu_seconds)
+    print(json.dumps(result))
+
+
+def cpu_baseline_shared(w, q, kc, vc, ks, vs, tables, ctx, budget_s):
+    """The oracle on whole samples (all heads) over the dequantised E4M3 codes, until the budget is spent."""
+    import oracle
+    import torch
+    from threadpoolctl import threadpool_info
+    qh = q.cpu().to(torch.float64).numpy()
+    done, kv_bytes, spent = 0, 0, 0.0
+    for s in range(len(ctx)):
+        n = int(ctx[s])
+        nb = -(-n // w.block_size)
+        blocks = torch.from_numpy(tables[s, :nb].astype(np.int64)).to(kc.device)
+        kcodes = kc.index_select(0, blocks).cpu().numpy()
+        vcodes = vc.index_select(0, blocks).cpu().numpy()
+        local = np.arange(nb, dtype=np.int32)[None, :]
+        t0 = time.perf_counter()
+        kp = oracle.decode_e4m3(kcodes) * np.float64(np.float32(ks))
+        vp = oracle.decode_e4m3(vcodes) * np.float64(np.float32(vs))
+        oracle.attend_ref(qh[s:s + 1], kp, vp, local, ctx[s:s + 1], w.softmax_scale, w.block_size)
+        spent += time.perf_counter() - t0
+        done += 1
+        kv_bytes += n * w.num_kv_heads * w.head_dim * 2
+        if spent > budget_s:
+            break
+    blas_threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    return {"value": round(kv_bytes / spent / 1e9, 6), "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
+            "seq_per_s": round(done / spent, 3),
+            "sample": f"first {done} of {len(ctx)} samples of the same decode step, all {w.num_heads} heads "
+                      f"({kv_bytes / 1e6:.1f} MB of logical E4M3 KV, dequantised by the oracle), fp64 numpy "
+                      f"oracle, {spent:.1f} s wall",
+            "host_cores_available": len(os.sched_getaffinity(0))}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -405,6 +582,8 @@ def main():
         return main_prefill(args, w)
     if isinstance(w, synth.PrefixCacheWorkload):
         return main_prefix_cache(args, w)
+    if isinstance(w, synth.SharedPrefixWorkload):
+        return main_shared_prefix(args, w)
     if not isinstance(w, synth.DecodeWorkload):
         raise SystemExit("bench.py times decode workloads (llama13b_f16, gqa_bf16, long_splitk_bf16, tiny_f32)")
     part = w.partition_size if args.partition is None else args.partition

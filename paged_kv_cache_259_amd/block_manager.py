@@ -285,14 +285,27 @@ class BlockManager:
     def context_lens_array(self, seqs):
         return np.array([self.lengths[s] for s in seqs], dtype=np.int32)
 
-    def longest_first(self, seqs):
+    def longest_first(self, seqs, group_shared=False):
         """Positions 0..len(seqs)-1 ordered by decreasing context length (ties by position).
 
         A scheduling hint for the one-pass attention launch: long contexts start
         first.  Any permutation gives the same attention results.
+
+        With ``group_shared``, sequences whose tables start with the same
+        physical block (forks of one prompt) stay adjacent: groups are ordered
+        by their longest member, members by length.  Their workgroups then run
+        at about the same time and read each shared block close together, so
+        the reads after the first can come from the cache instead of HBM.
         """
         lens = self.context_lens_array(seqs)
-        return np.argsort(-lens, kind="stable").astype(np.int32)
+        if not group_shared:
+            return np.argsort(-lens, kind="stable").astype(np.int32)
+        first = [self.tables[s][0] if len(self.tables[s]) else -1 - i for i, s in enumerate(seqs)]
+        group_len = {}
+        for f, n in zip(first, lens):
+            group_len[f] = max(group_len.get(f, 0), int(n))
+        order = sorted(range(len(seqs)), key=lambda i: (-group_len[first[i]], first[i], -int(lens[i]), i))
+        return np.array(order, dtype=np.int32)
 
     def slot(self, seq, pos):
         t = self.tables[seq]

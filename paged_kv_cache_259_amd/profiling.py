@@ -3,14 +3,17 @@
     python -m paged_kv_cache_259_amd.profiling trace DIR
         per-kernel call count and durations from a ``--kernel-trace`` run.
     python -m paged_kv_cache_259_amd.profiling counters FETCH_DIR WRITE_DIR --workload W --calibrate-copy N
-        HBM bytes per attention call (decode or prefill kernels) from a ``--pmc FETCH_SIZE`` run and a
+        HBM bytes per timed call from a ``--pmc FETCH_SIZE`` run and a
         ``--pmc WRITE_SIZE`` run of ``bench.py --calibrate-copy N``.  The runs'
         one copy_blocks call over N block pairs is a plain copy of known size
         (N blocks read and N written in each pool); the counters' reading on it
         gives the factor that turns each counter into bytes.  Writes the entry
         for W into profiles/attention_traffic.json, keyed by the hash of the
         attention kernels' sources, so bench.py reports it only while the
-        kernels are unchanged.
+        kernels are unchanged.  The timed call of a decode workload is decode
+        with append (the attn_*_append_kernel launch, plus the split-context
+        reduce when planned); the plain decode kernels of the same run are
+        listed but not counted.  For a prefill workload it is the prefill kernel.
 """
 
 import argparse
@@ -59,6 +62,13 @@ def _counter(d, counter):
     return {k: sum(v) / len(v) for k, v in agg.items()}
 
 
+def _in_timed_call(kernel):
+    """Kernels of the call bench.py times: decode with append (+ its reduce) or prefill."""
+    if kernel.startswith("prefill_"):
+        return True
+    return "_append_" in kernel or kernel.startswith(("attn_reduce", "attn_slice_finish"))
+
+
 def counters(fetch_dir, write_dir, workload, n_pairs, out=sys.stdout):
     sys.path.insert(0, ROOT)
     import bench
@@ -81,11 +91,14 @@ def counters(fetch_dir, write_dir, workload, n_pairs, out=sys.stdout):
     total_r = total_w = 0.0
     for k in sorted(k for k in f if k[0].startswith(("attn_", "prefill_"))):
         rb, wb = f[k] * 1024 * fs, wr.get(k, 0.0) * 1024 * ws
-        total_r += rb
-        total_w += wb
+        counted = _in_timed_call(k[0])
+        if counted:
+            total_r += rb
+            total_w += wb
         print(f"{k[0][:58]:58s} grid {k[1]:8d}  FETCH_SIZE {f[k]:12.1f} KiB -> {rb / 1e6:9.2f} MB read;  "
-              f"WRITE_SIZE {wr.get(k, 0.0):10.1f} KiB -> {wb / 1e6:7.2f} MB written", file=out)
-    print(f"attention call total: {total_r / 1e6:.2f} MB read + {total_w / 1e6:.2f} MB written = "
+              f"WRITE_SIZE {wr.get(k, 0.0):10.1f} KiB -> {wb / 1e6:7.2f} MB written"
+              f"{'' if counted else '  (plain decode, not the timed call)'}", file=out)
+    print(f"timed call total: {total_r / 1e6:.2f} MB read + {total_w / 1e6:.2f} MB written = "
           f"{(total_r + total_w) / 1e6:.2f} MB", file=out)
     path = os.path.join(ROOT, "profiles", "attention_traffic.json")
     table = {}

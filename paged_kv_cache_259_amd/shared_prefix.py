@@ -78,7 +78,7 @@ def run_shared_prefix(inp: synth.SharedPrefixInputs, device, on_step=None, on_pr
     ops.paged_attention_decode(out, q, k_cache, v_cache, torch.from_numpy(tables).to(device),
                                torch.from_numpy(ctx).to(device), w.softmax_scale, int(ctx.max()),
                                k_scale=k_scale, v_scale=v_scale,
-                               seq_order=torch.from_numpy(bm.longest_first(seqs)).to(device))
+                               seq_order=torch.from_numpy(bm.longest_first(seqs, group_shared=True)).to(device))
     return {
         "block_manager": bm, "k_cache": k_cache, "v_cache": v_cache, "k_scale": k_scale, "v_scale": v_scale,
         "tables": tables, "context_lens": ctx, "q": q, "out": out, "cow_pairs": n_pairs,

@@ -79,6 +79,14 @@ class SharedPrefixWorkload:
     def softmax_scale(self):
         return 1.0 / math.sqrt(self.head_dim)
 
+    @property
+    def num_kv_heads(self):          # multi-head attention: one kv head per query head
+        return self.num_heads
+
+    @property
+    def num_seqs(self):              # every sample is a sequence
+        return self.num_prompts * self.samples_per_prompt
+
 
 @dataclass(frozen=True)
 class PrefillWorkload:

@@ -298,3 +298,42 @@ def test_prefix_cache_swap_out_keeps_cache_consistent():
     bm.add_sequence("z", NB * bs)
     _, cached = bm.add_sequence_cached("w", [])
     assert cached == 0 and bm.cached_blocks() == 0
+
+
+def test_longest_first_grouped_keeps_forks_together():
+    """Forks of one prompt stay adjacent, groups by their longest member, members by length; a permutation."""
+    rng = np.random.default_rng(21)
+    bm = BlockManager(4000, 16, free_list=rng.permutation(4000))
+    seqs, sid = [], 0
+    for p in range(9):
+        bm.add_sequence(sid, int(rng.integers(1, 300)))
+        root = sid
+        seqs.append(sid)
+        sid += 1
+        for _ in range(int(rng.integers(0, 4))):
+            bm.fork(root, sid)
+            for _ in range(int(rng.integers(0, 60))):
+                bm.append_slot(sid)
+            seqs.append(sid)
+            sid += 1
+    bm.add_sequence(sid, 0)                           # an empty sequence is a group of its own
+    seqs.append(sid)
+    perm = rng.permutation(len(seqs))
+    seqs = [seqs[i] for i in perm]
+    order = bm.longest_first(seqs, group_shared=True)
+    assert sorted(order.tolist()) == list(range(len(seqs)))
+    lens = bm.context_lens_array(seqs)
+    first = [bm.tables[s][0] if bm.tables[s] else None for s in seqs]
+    runs = []                                          # (group, member lengths) in order
+    for i in order:
+        key = first[i] if first[i] is not None else ("empty", i)
+        if not runs or runs[-1][0] != key:
+            runs.append((key, []))
+        runs[-1][1].append(int(lens[i]))
+    keys = [k for k, _ in runs]
+    assert len(keys) == len(set(keys)), "a group is split"
+    assert all(m == sorted(m, reverse=True) for _, m in runs)
+    tops = [max(m) for _, m in runs]
+    assert tops == sorted(tops, reverse=True)
+    # without sharing the grouped order is the plain longest-first order's lengths
+    assert np.array_equal(np.sort(lens)[::-1], lens[bm.longest_first(seqs)])
