@@ -50,8 +50,13 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic.json")
-KERNEL_SOURCES = ["attn_vector.h", "attn_vector.hip", "attn_mfma.h", "attn_mfma.hip", "attn_append.hip",
-                  "attn_reduce.hip", "prefill_mfma.hip", "pkv_device.h", "pkv_api.hip"]
+# sources of the kernels each kind of workload times (a change to any of them
+# retires that kind's recorded HBM traffic)
+KERNEL_SOURCES = {
+    "decode": ["attn_vector.h", "attn_vector.hip", "attn_mfma.h", "attn_mfma.hip", "attn_append.hip",
+               "attn_reduce.hip", "pkv_device.h", "pkv_api.hip"],
+    "prefill": ["prefill_mfma.hip", "pkv_device.h", "pkv_api.hip"],
+}
 
 
 def parse():
@@ -68,9 +73,13 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_hash():
+def kernel_kind(workload):
+    return "prefill" if workload.startswith("prefill") else "decode"
+
+
+def kernel_source_hash(workload):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[kernel_kind(workload)]:
         with open(os.path.join(ROOT, "paged_kv_cache_259_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -84,7 +93,7 @@ def measured_traffic(workload):
     except (OSError, ValueError):
         return None
     entry = t.get(workload)
-    if not entry or entry.get("kernel_source_hash") != kernel_source_hash():
+    if not entry or entry.get("kernel_source_hash") != kernel_source_hash(workload):
         return None
     return entry.get("bytes_per_call")
 

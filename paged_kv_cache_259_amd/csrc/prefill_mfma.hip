@@ -8,18 +8,24 @@
 //
 // One workgroup of 4 waves per (sequence, 128-query tile, query head); wave w
 // owns query rows 32w .. 32w+31 of the tile as two 16-row groups.  Per step of
-// 32 tokens (two 16-token blocks):
-//   staging  256 threads load the step's K and V rows (16-byte loads through
-//            the block table) into registers one step ahead, then store them to
-//            LDS row-major [token][dim] with 16-byte stores.
+// 64 tokens (four 16-token blocks):
+//   staging  the step's K and V rows go from the pool straight into LDS, one
+//            step ahead, with global_load_lds_dwordx4: each instruction of a
+//            wave fills 1 KiB of LDS (lane i's 16 bytes at 16 i), so a wave
+//            chooses which 16-byte chunk of which token row each lane fetches
+//            (through the block table).  Rows are D elements with no padding;
+//            the chunk order inside a row is XOR-swizzled (K and V differently)
+//            so the fragment reads below hit distinct LDS banks.  No register
+//            staging and no LDS store instructions; each wave waits for its own
+//            loads before the step's barrier.
 //   QK       S^T[token][query] = sum_k K[token][k] Q[query][k]
 //            v_mfma_f32_16x16x32 (f16/bf16), A = K rows from LDS (read once,
 //            used by both row groups), B = Q^T held in registers; lane l gets
 //            tokens 4(l/16)+r and 16+4(l/16)+r (r = 0..3) of query l%16.
 //   softmax  causal / context mask (only on steps that straddle a boundary),
-//            max over the 32 tokens (the lane's 8 values, then lanes l^16 and
-//            l^32), exp2 in the log2 domain against a reference max that moves
-//            only when a row's max grows by more than 2^8.
+//            max over the step's 64 tokens (the lane's 16 values, then lanes
+//            l^16 and l^32), exp2 in the log2 domain against a reference max
+//            that moves only when a row's max grows by more than 2^8.
 //   PV       O^T[dim][query] += sum_k V^T[dim][token_k] P^T[token_k][query]
 //            v_mfma_f32_16x16x32 again: the contraction index k of lane group
 //            l/16 is its 8 tokens above, so B = P^T is exactly the lane's own
@@ -66,12 +72,33 @@ constexpr float kRescale = 8.f;
 #ifndef PKV_PREFILL_NS
 #define PKV_PREFILL_NS 2      // 32-token PV k-steps per pipeline step
 #endif
-#ifndef PKV_PREFILL_AHEAD
-#define PKV_PREFILL_AHEAD 1   // steps between loading a step's K/V rows and computing it
+#ifndef PKV_PREFILL_NW
+#define PKV_PREFILL_NW 4      // waves per workgroup
+#endif
+#ifndef PKV_PREFILL_WAVES_PER_EU
+#define PKV_PREFILL_WAVES_PER_EU 2   // occupancy the register allocation must allow
 #endif
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+
+// Source of the 16-byte chunks of tokens that are not loaded (past the keys, or
+// in a block outside the pool): zeros, so V rows that get weight 0 stay finite.
+static __device__ __align__(16) const uint16_t kZeroChunk[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima): this wave's
+// loads into LDS have landed
+__device__ __forceinline__ void wait_lds_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// One global_load_lds_dwordx4: lane l's 16 bytes at src go to LDS bytes
+// dst + 16 l .. +15 (dst wave-uniform).  The LDS it fills is read only after
+// wait_lds_loads() and a barrier, and is filled only after the barrier that
+// ends the step that last read it.
+__device__ __forceinline__ void load_lds16(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 16, 0, 0);
+}
 
 // ds_read_b64_tr_b16 on an LDS address (8-byte aligned)
 __device__ __forceinline__ uint2 read_tr16(const uint16_t* lds) {
@@ -85,30 +112,38 @@ struct Prefill {
   static constexpr int NS = PKV_PREFILL_NS;     // PV k-steps (32 tokens each) per step
   static constexpr int STEP = 32 * NS;          // tokens per step
   static constexpr int KT = STEP / 16;          // blocks per step
-  static constexpr int NW = 4;
+  static constexpr int NW = PKV_PREFILL_NW;
   static constexpr int BM = NW * 16 * RW;       // query rows per workgroup
   static constexpr int NC = D / 32;             // QK k-steps of 32 dims
   static constexpr int ND = D / 16;             // PV output tiles of 16 dims
   static constexpr int CPR = D / 8;             // 16-byte chunks per token row
-  static constexpr int CH = STEP * CPR / (NW * 64);   // chunks per thread per tensor per step
-  static constexpr int KSTR = D + 8;            // LDS row stride of K (elements)
-  static constexpr int VSTR = D + 16;           // LDS row stride of V: 4 rows of a transposing read hit distinct banks
-  static_assert(CH == 1 || CH == 2 || CH == 4, "staging: 1, 2 or 4 chunks per thread per step");
+  static constexpr int RPI = 1024 / (2 * D);    // token rows per load instruction (64 lanes x 16 bytes)
+  static constexpr int NQ = STEP / RPI;         // load instructions per tensor per step
+  static constexpr int QPW = NQ / NW;           // ... per wave
+  static constexpr int RPB = 256 / (2 * D);     // token rows per 256 bytes (one pass over the 64 LDS banks)
+  static_assert(NQ % NW == 0 && RPI <= BS && BS % RPI == 0, "staging shape");
+  static constexpr int TILE = STEP * D;         // elements of one K or V buffer
 
-  struct Smem {
-    alignas(16) uint16_t k[2][STEP * KSTR];
-    alignas(16) uint16_t v[2][STEP * VSTR];
-  };
+  // Chunk swizzles: logical chunk c of row r sits at chunk c ^ f(r) of the row.
+  // K fragment reads take rows r0..r0+15 at one logical chunk: f_K spreads them
+  // over all bank groups.  The transposing V reads take 8 consecutive rows x 2
+  // adjacent chunks per 32 lanes: f_V is even, so a chunk pair stays a pair,
+  // and distinct per row.
+  __device__ __forceinline__ static int swz_k(int r) { return (r / RPB) % CPR; }
+  __device__ __forceinline__ static int swz_v(int r) { return 2 * ((r / RPB) % (CPR / 2)); }
 };
 
 template <class T, int D, int RW>
-__global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
+__global__ __launch_bounds__(PKV_PREFILL_NW * 64) __attribute__((amdgpu_waves_per_eu(PKV_PREFILL_WAVES_PER_EU)))
+void prefill_mfma_kernel(PrefillParams p) {
   using P = Prefill<T, D, RW>;
   using Op = PrefillOp<T>;
-  constexpr int STEP = P::STEP, BS = P::BS, NC = P::NC, ND = P::ND, CPR = P::CPR, CH = P::CH, KT = P::KT,
+  constexpr int STEP = P::STEP, BS = P::BS, NC = P::NC, ND = P::ND, CPR = P::CPR, KT = P::KT,
                 NS = P::NS;
   struct StepIds { int b[KT]; };                            // block ids of one step (-1 past the keys)
-  __shared__ typename P::Smem sm;
+  // two buffers per tensor as separate objects: the compiler then sees that
+  // loads into one never alias reads of the other and adds no wait between them
+  __shared__ __align__(16) uint16_t sK0[P::TILE], sK1[P::TILE], sV0[P::TILE], sV1[P::TILE];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -123,8 +158,8 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
   const int h = (int)(rest % (uint32_t)p.num_heads);
   int seq = (int)(rest / (uint32_t)p.num_heads);
   if (p.longest_first)   // LDS scratch borrowed from the K tiles, which are first written after its last barrier
-    seq = seq_of_rank<P::NW * 64>(p.context_lens, p.num_seqs, p.ctx_cap, BS, seq, reinterpret_cast<int*>(&sm.k[0][0]),
-                                  reinterpret_cast<int*>(&sm.k[1][0]));
+    seq = seq_of_rank<P::NW * 64>(p.context_lens, p.num_seqs, p.ctx_cap, BS, seq, reinterpret_cast<int*>(sK0),
+                                  reinterpret_cast<int*>(sK1));
   const int kvh = h / p.group;
 
   // rows [q0, q1) of q / out; offsets are clamped to the num_tokens rows that exist
@@ -141,7 +176,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
   const int base = ctx - n_all;                             // position of query row 0 (< 0: no position)
   const int rows_here = (n - row0) < P::BM ? (n - row0) : P::BM;
   int nkeys = base + row0 + rows_here;                      // keys 0 .. nkeys-1 serve this tile
-  nkeys = nkeys > ctx ? ctx : (nkeys < 0 ? 0 : nkeys);
+  nkeys = __builtin_amdgcn_readfirstlane(nkeys > ctx ? ctx : (nkeys < 0 ? 0 : nkeys));   // uniform: scalar loop bounds and table reads
   const int nsteps = (nkeys + STEP - 1) / STEP;
   const int wrow0 = row0 + 16 * RW * w;                     // the wave's first row
   const int wave_first_pos = base + wrow0;
@@ -179,51 +214,66 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
     for (int dt = 0; dt < ND; ++dt) O[g][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  const int32_t* table = p.block_tables + (size_t)seq * p.max_blocks_per_seq;
+  // The table is read through the constant address space: it is not written
+  // during the launch, so its (uniform) entries come with scalar loads, whose
+  // waits do not wait for the K/V loads in flight.
+  typedef const __attribute__((address_space(4))) int32_t const_i32_t;
+  const_i32_t* table = (const_i32_t*)(p.block_tables + (size_t)seq * p.max_blocks_per_seq);
   const size_t block_stride = (size_t)p.num_kv_heads * BS * D;             // elements
   const uint16_t* kpool = reinterpret_cast<const uint16_t*>(p.k_cache) + (size_t)kvh * BS * D;
   const uint16_t* vpool = reinterpret_cast<const uint16_t*>(p.v_cache) + (size_t)kvh * BS * D;
 
-  // staging assignment: 16-byte chunk column `col` of tokens stok .. stok + CH - 1
-  const int col = tid % CPR;
-  const int stok = (tid / CPR) * CH;
   const int nkblk = (nkeys + BS - 1) / BS;
   // block ids of step st; uniform, so scalar loads
+  // (every read is in the row's first nkblk entries; all KT issue before any is used)
   auto ids_of = [&](int st) -> StepIds {
     StepIds r;
+    const int last = nkblk > 0 ? nkblk - 1 : 0;
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) r.b[kt] = KT * st + kt < nkblk ? table[KT * st + kt] : -1;
+    for (int kt = 0; kt < KT; ++kt) {
+      const int j = KT * st + kt;
+      r.b[kt] = __builtin_amdgcn_readfirstlane(table[j < last ? j : last]);
+    }
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) r.b[kt] = KT * st + kt < nkblk ? r.b[kt] : -1;
     return r;
   };
-  auto load_step = [&](int i, StepIds ids, uint4 (&kr)[CH], uint4 (&vr)[CH]) {
-    int sid = ids.b[0];                                     // the block of tokens stok .. stok + CH - 1
+  // Load step i's K and V rows into LDS buffers kb, vb: instruction q of the
+  // step (wave-uniform) fills rows q*RPI .. q*RPI+RPI-1; lane l fetches the
+  // logical chunk that the swizzle puts at position l % CPR of row l / CPR.
+  const int dma_row = lane / CPR, dma_pos = lane % CPR;
+  auto load_step = [&](int i, StepIds ids, uint16_t* kb, uint16_t* vb) {
 #pragma unroll
-    for (int kt = 1; kt < KT; ++kt) sid = stok / BS == kt ? ids.b[kt] : sid;
+    for (int j = 0; j < P::QPW; ++j) {
+      const int q = w * P::QPW + j;
+      const int r = q * P::RPI + dma_row;                  // token row of the step
+      int blk = ids.b[0];                                  // uniform: an instruction stays in one block
 #pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      const int pos = i * STEP + stok + j;
-      const int blk = pos < nkeys ? sid : -1;
-      const bool ok = blk >= 0 && blk < p.num_blocks;
-      const size_t off = (size_t)blk * block_stride + (size_t)(pos % BS) * D + col * 8;
-      kr[j] = ok ? *reinterpret_cast<const uint4*>(kpool + off) : make_uint4(0u, 0u, 0u, 0u);
-      vr[j] = ok ? *reinterpret_cast<const uint4*>(vpool + off) : make_uint4(0u, 0u, 0u, 0u);
+      for (int kt = 1; kt < KT; ++kt) blk = (q * P::RPI) / BS == kt ? ids.b[kt] : blk;   // no dynamic indexing
+      const bool ok = blk >= 0 && blk < p.num_blocks && i * STEP + r < nkeys;
+      const size_t row_off = (size_t)blk * block_stride + (size_t)(r % BS) * D;
+      const uint16_t* ks = ok ? kpool + row_off + (dma_pos ^ P::swz_k(r)) * 8 : kZeroChunk;
+      const uint16_t* vs = ok ? vpool + row_off + (dma_pos ^ P::swz_v(r)) * 8 : kZeroChunk;
+      load_lds16(ks, kb + q * 512);
+      load_lds16(vs, vb + q * 512);
     }
   };
-  auto store_step = [&](int buf, const uint4 (&kr)[CH], const uint4 (&vr)[CH]) {
-#pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      *reinterpret_cast<uint4*>(&sm.k[buf][(stok + j) * P::KSTR + col * 8]) = kr[j];
-      *reinterpret_cast<uint4*>(&sm.v[buf][(stok + j) * P::VSTR + col * 8]) = vr[j];
-    }
-  };
-  // transposing-read address of this lane inside a V tile: token 4 g4 + c16/4, dims 4 (c16%4) ..
-  const int vrd = (g4 * 4 + (c16 >> 2)) * P::VSTR + 4 * (c16 & 3);
+  // Per-lane fragment addresses (elements) inside a buffer; the swizzles do not
+  // change under the added multiples of 16 rows.
+  // K: row c16 (+16 kt), logical chunk 4c + g4 -> chunk 4 (c ^ sk/4) + (g4 ^ sk%4)
+  //    with sk = swz_k(c16).
+  // V (transposing read): row vr = 4 g4 + c16/4 (+32 ns, +16 for the second
+  //    half), dims 16 dt + 4 (c16 % 4) .. +3 = logical chunk 2 dt + (c16 % 4)/2,
+  //    half c16 % 2; swz_v is even, so the chunk is 2 (dt ^ swz_v(vr)/2) + (c16 % 4)/2.
+  const int kbase = c16 * D + (g4 ^ (P::swz_k(c16) & 3)) * 8, ksw = P::swz_k(c16) & ~3;
+  const int vr = 4 * g4 + (c16 >> 2);
+  const int vbase = vr * D + 8 * ((c16 & 3) >> 1) + 4 * (c16 & 1), vsw = P::swz_v(vr) / 2;
 
   // One step of the wave's rows.  `masked` (a compile-time tag) selects the
   // variant with the per-element causal / context / skipped-block mask; steps
   // whose every key is visible to every row of the wave run the other one, so
   // interior steps carry no mask arithmetic at all.
-  auto step_body = [&](int i, int buf, StepIds ids, auto masked) {
+  auto step_body = [&](int i, const uint16_t* kb, const uint16_t* vb, StepIds ids, auto masked) __attribute__((always_inline)) {
     constexpr bool interior = !decltype(masked)::value;
     const int k0 = i * STEP;
     {
@@ -239,7 +289,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          const uint4 kf = *reinterpret_cast<const uint4*>(&sm.k[buf][(kt * 16 + c16) * P::KSTR + c * 32 + g4 * 8]);
+          const uint4 kf = *reinterpret_cast<const uint4*>(kb + kt * 16 * D + kbase + ((4 * c) ^ ksw) * 8);
 #pragma unroll
           for (int g = 0; g < RW; ++g) S[g][kt] = Op::mma(kf, qf[g][c], S[g][kt]);
         }
@@ -316,9 +366,9 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
       for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt) {
-          const uint16_t* vb = &sm.v[buf][vrd + 32 * ns * P::VSTR + dt * 16];
-          const uint2 lo = read_tr16(vb);                   // tokens 32 ns + 4 g4 + m
-          const uint2 hi = read_tr16(vb + 16 * P::VSTR);    // tokens 32 ns + 16 + 4 g4 + m
+          const uint16_t* va = vb + 32 * ns * D + vbase + ((dt ^ vsw) * 16);
+          const uint2 lo = read_tr16(va);                   // tokens 32 ns + 4 g4 + m
+          const uint2 hi = read_tr16(va + 16 * D);          // tokens 32 ns + 16 + 4 g4 + m
           const uint4 vf = make_uint4(lo.x, lo.y, hi.x, hi.y);
 #pragma unroll
           for (int g = 0; g < RW; ++g) O[g][dt] = Op::mma(vf, pk[g][ns], O[g][dt]);
@@ -333,70 +383,43 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillParams p) {
   for (int b = tid; b < nkblk; b += P::NW * 64) table_ok = table_ok && table[b] >= 0 && table[b] < p.num_blocks;
   table_ok = __syncthreads_and(table_ok);
   int n_open = (base + row0 + 1 < nkeys ? base + row0 + 1 : nkeys) / STEP;
-  n_open = table_ok && n_open > 0 ? n_open : 0;
-  auto compute_open = [&](int i, int buf, StepIds ids) { step_body(i, buf, ids, std::false_type{}); };
-  auto compute = [&](int i, int buf, StepIds ids) {
+  n_open = __builtin_amdgcn_readfirstlane(table_ok && n_open > 0 ? n_open : 0);   // uniform (a scalar loop bound)
+  auto compute_open = [&](int i, const uint16_t* kb, const uint16_t* vb, StepIds ids) __attribute__((always_inline)) {
+    step_body(i, kb, vb, ids, std::false_type{});
+  };
+  auto compute = [&](int i, const uint16_t* kb, const uint16_t* vb, StepIds ids) __attribute__((always_inline)) {
     if (i * STEP > wave_last_pos) return;                   // wave-uniform: no key of the step is visible
-    step_body(i, buf, ids, std::true_type{});
+    step_body(i, kb, vb, ids, std::true_type{});
   };
 
-#if PKV_PREFILL_AHEAD == 2
-  // Pipeline: K/V rows of step i+2 are loaded into one register set while step i
-  // is computed from LDS and step i+1 (loaded a step earlier into the other set)
-  // waits to be stored; block ids come three steps ahead.  Unrolled by two so
-  // both register sets are named statically.
-  uint4 kA[CH], vA[CH], kB[CH], vB[CH];
-  StepIds id0 = ids_of(0), id1 = ids_of(1), id2 = ids_of(2);
-  if (nsteps > 0) load_step(0, id0, kA, vA);
-  if (nsteps > 1) load_step(1, id1, kB, vB);
-  if (nsteps > 0) store_step(0, kA, vA);
-  __syncthreads();
-  for (int i = 0; i < nsteps; i += 2) {
-    const StepIds id3 = ids_of(i + 3);
-    if (i + 2 < nsteps) load_step(i + 2, id2, kA, vA);
-    compute(i, 0, id0);
-    if (i + 1 < nsteps) store_step(1, kB, vB);
-    __syncthreads();
-    if (i + 1 >= nsteps) break;                             // workgroup-uniform
-    const StepIds id4 = ids_of(i + 4);
-    if (i + 3 < nsteps) load_step(i + 3, id3, kB, vB);
-    compute(i + 1, 1, id1);
-    if (i + 2 < nsteps) store_step(0, kA, vA);
-    __syncthreads();
-    id0 = id2;
-    id1 = id3;
-    id2 = id4;
-  }
-#else
-  // Pipeline: K/V rows of step i+1 are loaded into registers while step i is
-  // computed from LDS, then stored to the other LDS buffer; block ids come two
-  // steps ahead.
-  uint4 kA[CH], vA[CH];
+  // Pipeline: step i+1's rows are loaded into the other buffer pair while step
+  // i is computed; block ids come two steps ahead.  Even steps use buffers 0,
+  // odd steps 1; the loops run in pairs of steps from an even step, so every
+  // access names its buffer statically (an odd open step, if any, runs with
+  // the mask: same result).
   StepIds id0 = ids_of(0), id1 = ids_of(1);
-  if (nsteps > 0) {
-    load_step(0, id0, kA, vA);
-    store_step(0, kA, vA);
-  }
+  if (nsteps > 0) load_step(0, id0, sK0, sV0);
+  wait_lds_loads();
   __syncthreads();
-  for (int i = 0; i < n_open; ++i) {
+  auto one = [&](int i, auto open, uint16_t* kc, uint16_t* vc, uint16_t* kn, uint16_t* vn)
+      __attribute__((always_inline)) {
     const StepIds id2 = ids_of(i + 2);
-    if (i + 1 < nsteps) load_step(i + 1, id1, kA, vA);
-    compute_open(i, i & 1, id0);
-    if (i + 1 < nsteps) store_step((i + 1) & 1, kA, vA);
+    if (i + 1 < nsteps) load_step(i + 1, id1, kn, vn);
+    if constexpr (decltype(open)::value) compute_open(i, kc, vc, id0); else compute(i, kc, vc, id0);
+    wait_lds_loads();
     __syncthreads();
     id0 = id1;
     id1 = id2;
-  }
-  for (int i = n_open; i < nsteps; ++i) {
-    const StepIds id2 = ids_of(i + 2);
-    if (i + 1 < nsteps) load_step(i + 1, id1, kA, vA);
-    compute(i, i & 1, id0);
-    if (i + 1 < nsteps) store_step((i + 1) & 1, kA, vA);
-    __syncthreads();
-    id0 = id1;
-    id1 = id2;
-  }
-#endif
+  };
+  n_open &= ~1;
+  auto steps = [&](int i, int end, auto open) __attribute__((always_inline)) {   // steps [i, end) from an even i
+    for (; i < end; i += 2) {
+      one(i, open, sK0, sV0, sK1, sV1);
+      if (i + 1 < end) one(i + 1, open, sK1, sV1, sK0, sV0);
+    }
+  };
+  steps(0, n_open, std::true_type{});
+  steps(n_open, nsteps, std::false_type{});
 
   // normalise and write: lane l holds out[row wrow0 + 16 g + c16][dims 16 dt + 4 g4 + r]
 #pragma unroll
@@ -427,7 +450,7 @@ int prefill_tile_rows() { return Prefill<F16, 128, PKV_PREFILL_RW>::BM; }
 
 template <class T, int D>
 static hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((prefill_mfma_kernel<T, D, PKV_PREFILL_RW>), dim3(p.total_wgs), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((prefill_mfma_kernel<T, D, PKV_PREFILL_RW>), dim3(p.total_wgs), dim3(PKV_PREFILL_NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 

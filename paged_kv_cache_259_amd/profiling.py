@@ -105,7 +105,7 @@ def counters(fetch_dir, write_dir, workload, n_pairs, out=sys.stdout):
     if os.path.exists(path):
         with open(path) as fh:
             table = json.load(fh)
-    table[workload] = {"kernel_source_hash": bench.kernel_source_hash(), "bytes_per_call": int(total_r + total_w),
+    table[workload] = {"kernel_source_hash": bench.kernel_source_hash(workload), "bytes_per_call": int(total_r + total_w),
                        "read_bytes": int(total_r), "write_bytes": int(total_w),
                        "fetch_scale": round(fs, 5), "write_scale": round(ws, 5),
                        "summary": f"profiles/{'paged_prefill_attention' if workload.startswith('prefill') else 'paged_attention_decode'}_{workload}.md"}
