@@ -158,8 +158,9 @@ size_t pkv_attention_workspace_bytes(int num_seqs, int num_heads, int num_kv_hea
  * Supported: head_dim 64/128/256; block_size 8/16/32 (16 for the MFMA family);
  *   (q, kv) dtypes (f32,f32), (f16,f16), (bf16,bf16), and f16 or bf16 q over
  *   either 8-bit cache.
- *   Grouped heads (G > 1) with 16-bit q run on MFMA; everything else on the
- *   vector family.
+ *   Grouped heads (2 <= G <= 16, head_dim 128 or 256, block_size 16) with
+ *   16-bit q over a cache of q's type or either 8-bit format run on the matrix
+ *   cores; everything else on the vector family.
  */
 int pkv_paged_attention_decode(void* out, const void* q,
                                const void* k_cache, const void* v_cache,

@@ -14,8 +14,8 @@ hipError_t launch_attention_vector_append(const AttnParams& p, int q_dtype, int 
   return launch_vector_family<true>(p, q_dtype, kv_dtype, d, bs, stream);
 }
 
-hipError_t launch_attention_mfma_append(const AttnParams& p, int q_dtype, int d, hipStream_t stream) {
-  return launch_mfma_family<true>(p, q_dtype, d, stream);
+hipError_t launch_attention_mfma_append(const AttnParams& p, int q_dtype, int kv_dtype, int d, hipStream_t stream) {
+  return launch_mfma_family<true>(p, q_dtype, kv_dtype, d, stream);
 }
 
 }  // namespace pkv

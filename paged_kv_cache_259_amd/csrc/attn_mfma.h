@@ -22,10 +22,19 @@
 //        stays fp32.
 //        O_e: lane l holds O[head l%16][dim 8(4(l/16)+r)+e], r = 0..3.
 //
+// 8-bit caches (E4M3, E5M2; "PagedAttention", Ultralytics glossary, section
+// "Các kỹ thuật liên quan": an 8-bit KV cache) read half the bytes.  K codes are
+// converted exactly to q's 16-bit type for the QK MFMA (lane group l/16 then
+// holds dims D/4 (l/16) .. +D/4 of its token, two 16-byte loads at D = 128, and
+// the query operand follows that contraction order); V codes convert exactly
+// to fp32 for the PV MFMA.  k_scale scales the logits, v_scale the output.
+//
 // Two kernels share the body: attn_mfma_kernel (plain decode) and
 // attn_mfma_append_kernel (decode that first writes each sequence's new K/V
 // row).  attn_mfma.hip instantiates the first, attn_append.hip the second.
 #pragma once
+#include <type_traits>
+
 #include "pkv_device.h"
 
 namespace pkv {
@@ -44,13 +53,56 @@ template <> struct MfmaOp<F16> {
   }
 };
 
-template <class T, int D, int NW, bool PIPE>
+// 8-bit K/V (E4M3 = FP8, E5M2 = BF8) as MFMA operands.  Both formats convert
+// exactly to f16, bf16 and fp32, so the products and sums are those of the
+// 16-bit path over the dequantised values; the scales are applied to the
+// logits (k) and to the output (v).
+template <class KT> __device__ __forceinline__ void kv8x4_to_f32(uint32_t u, float* f);
+template <> __device__ __forceinline__ void kv8x4_to_f32<FP8>(uint32_t u, float* f) { fp8x4_to_f32(u, f); }
+template <> __device__ __forceinline__ void kv8x4_to_f32<BF8>(uint32_t u, float* f) { bf8x4_to_f32(u, f); }
+
+// Eight 8-bit codes (two words) -> eight elements of the 16-bit MFMA type T.
+template <class T, class KT>
+__device__ __forceinline__ uint4 kv8x8_to_16(uint32_t a, uint32_t b) {
+  if constexpr (std::is_same<T, F16>::value && std::is_same<KT, BF8>::value) {
+    // an E5M2 code is the high byte of the f16 with the same value
+    return make_uint4(__builtin_amdgcn_perm(a, a, 0x010c000cu), __builtin_amdgcn_perm(a, a, 0x030c020cu),
+                      __builtin_amdgcn_perm(b, b, 0x010c000cu), __builtin_amdgcn_perm(b, b, 0x030c020cu));
+  } else {
+    float f[8];
+    kv8x4_to_f32<KT>(a, f);
+    kv8x4_to_f32<KT>(b, f + 4);
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (std::is_same<T, BF16>::value) {
+        const bf162_t h = {(__bf16)f[2 * i], (__bf16)f[2 * i + 1]};
+        w[i] = __builtin_bit_cast(uint32_t, h);
+      } else {
+        const half2_t h = {(_Float16)f[2 * i], (_Float16)f[2 * i + 1]};
+        w[i] = __builtin_bit_cast(uint32_t, h);
+      }
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// T: the q type and MFMA operand type (f16 / bf16); KT: the cache type, T itself
+// or one of the 8-bit formats.
+template <class T, class KT, int D, int NW, bool PIPE>
 struct MfmaAttention {
   static constexpr int BS = 16;
   static constexpr int NC = D / 32;                 // QK steps of 32 dims
   static constexpr int NH = D / 128;                // 128-element halves of a V row (16 lanes x 8)
-  static constexpr size_t ROW_BYTES = (size_t)D * 2;
+  static constexpr bool KV8 = KT::bytes == 1;
+  static constexpr size_t ROW_BYTES = (size_t)D * KT::bytes;
   static constexpr size_t TILE_BYTES = ROW_BYTES * BS;
+  static constexpr int NK = KV8 ? NC / 2 : NC;      // 16-byte K loads per lane per block
+  // QK contraction order.  16-bit: MFMA step c takes dims 32c + 8 g4 .. +8 of
+  // lane group g4 (one 16-byte load per step).  8-bit: lane group g4 holds the
+  // contiguous dims g4 D/4 .. +D/4 (D/4 bytes, whole 16-byte loads) and step c
+  // takes 8 of them; the query operand follows the same order.
+  __device__ __forceinline__ static int k_dim(int c, int g4) { return KV8 ? g4 * (D / 4) + 8 * c : 32 * c + 8 * g4; }
   static constexpr int RS = D + 1;                  // padded LDS row stride against bank conflicts
   static_assert(D % 128 == 0, "MFMA family needs head_dim 128 or 256");
 
@@ -75,11 +127,12 @@ struct MfmaAttention {
     }
   };
 
-  // One block's tiles in registers: K as the QK A operand (token c16, NC
-  // 16-byte chunks), V as row-major 16-byte loads of tokens 4*g4 + tg.
+  // One block's tiles in registers: K as the QK A operand (token c16, NK
+  // 16-byte loads), V as row-major loads of 8 elements of tokens 4*g4 + tg.
+  typedef typename std::conditional<KV8, uint2, uint4>::type VLoad;
   struct Tiles {
-    uint4 k[NC];
-    uint4 v[4][NH];
+    uint4 k[NK];
+    VLoad v[4][NH];
     bool ok;
   };
 
@@ -93,13 +146,14 @@ struct MfmaAttention {
     const char* vp = vbase + (size_t)blk * block_stride;
     if (c16 < valid) {
 #pragma unroll
-      for (int c = 0; c < NC; ++c) t.k[c] = *reinterpret_cast<const uint4*>(kp + c * 64);
+      for (int c = 0; c < NK; ++c) t.k[c] = *reinterpret_cast<const uint4*>(kp + c * (KV8 ? 16 : 64));
     }
 #pragma unroll
     for (int tg = 0; tg < 4; ++tg) {
       if (g4 * 4 + tg < valid) {
 #pragma unroll
-        for (int hh = 0; hh < NH; ++hh) t.v[tg][hh] = *reinterpret_cast<const uint4*>(vp + tg * ROW_BYTES + hh * 256);
+        for (int hh = 0; hh < NH; ++hh)
+          t.v[tg][hh] = *reinterpret_cast<const VLoad*>(vp + tg * ROW_BYTES + hh * 128 * KT::bytes);
       }
     }
   }
@@ -108,7 +162,14 @@ struct MfmaAttention {
     if (!t.ok) return;                                  // wave-uniform
     f32x4_t S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < NC; ++c) S = MfmaOp<T>::qk(t.k[c], qop[c], S);
+    for (int c = 0; c < NC; ++c) {
+      if constexpr (KV8) {
+        const uint4& k = t.k[c / 2];
+        S = MfmaOp<T>::qk((c & 1) ? kv8x8_to_16<T, KT>(k.z, k.w) : kv8x8_to_16<T, KT>(k.x, k.y), qop[c], S);
+      } else {
+        S = MfmaOp<T>::qk(t.k[c], qop[c], S);
+      }
+    }
     float s[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) s[r] = S[r] * p.qk_scale;
@@ -119,7 +180,7 @@ struct MfmaAttention {
         s[r] = v ? s[r] : -__builtin_inff();
         if (!v) {
 #pragma unroll
-          for (int hh = 0; hh < NH; ++hh) t.v[r][hh] = make_uint4(0u, 0u, 0u, 0u);
+          for (int hh = 0; hh < NH; ++hh) t.v[r][hh] = VLoad{};
         }
       }
     }
@@ -142,7 +203,12 @@ struct MfmaAttention {
 #pragma unroll
       for (int hh = 0; hh < NH; ++hh) {
         float vf[8];
-        Unpack<T>::run(t.v[tg][hh], vf);
+        if constexpr (KV8) {
+          kv8x4_to_f32<KT>(t.v[tg][hh].x, vf);
+          kv8x4_to_f32<KT>(t.v[tg][hh].y, vf + 4);
+        } else {
+          Unpack<T>::run(t.v[tg][hh], vf);
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           st.O[hh][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[e], pr[tg], st.O[hh][e], 0, 0, 0);
@@ -168,12 +234,13 @@ struct MfmaAttention {
                              ((size_t)seq * p.num_heads + (size_t)kvh * G + (real ? c16 : 0)) * D;
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        qop[c] = real ? *reinterpret_cast<const uint4*>(qrow + c * 32 + g4 * 8) : make_uint4(0u, 0u, 0u, 0u);
+        qop[c] = real ? *reinterpret_cast<const uint4*>(qrow + k_dim(c, g4)) : make_uint4(0u, 0u, 0u, 0u);
     }
     const int32_t* table = p.block_tables + (size_t)seq * p.max_blocks_per_seq;
-    const char* kbase = reinterpret_cast<const char*>(p.k_cache) + (size_t)kvh * TILE_BYTES + c16 * ROW_BYTES + g4 * 16;
+    const char* kbase = reinterpret_cast<const char*>(p.k_cache) + (size_t)kvh * TILE_BYTES + c16 * ROW_BYTES +
+                        (KV8 ? g4 * (D / 4) : g4 * 16);
     const char* vbase =
-        reinterpret_cast<const char*>(p.v_cache) + (size_t)kvh * TILE_BYTES + (g4 * 4) * ROW_BYTES + c16 * 16;
+        reinterpret_cast<const char*>(p.v_cache) + (size_t)kvh * TILE_BYTES + (g4 * 4) * ROW_BYTES + c16 * 8 * KT::bytes;
     const size_t block_stride = TILE_BYTES * (size_t)p.num_kv_heads;
     const int lane = threadIdx.x & 63;
     auto load_ids = [&](int chunk) -> int {
@@ -267,9 +334,9 @@ struct MfmaAttention {
 #ifndef PKV_MFMA_WAVES_PER_EU_PIPE
 #define PKV_MFMA_WAVES_PER_EU_PIPE 3
 #endif
-template <class T, int D, int NW, bool PIPE, bool APPEND>
+template <class T, class KT, int D, int NW, bool PIPE, bool APPEND>
 __device__ __forceinline__ void attn_mfma_body(AttnParams p) {
-  using A = MfmaAttention<T, D, NW, PIPE>;
+  using A = MfmaAttention<T, KT, D, NW, PIPE>;
   __shared__ typename A::Smem sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -281,6 +348,7 @@ __device__ __forceinline__ void attn_mfma_body(AttnParams p) {
 
   if (p.num_slices > 0) {
     const int kvh = (int)(L % (uint32_t)p.num_kv_heads);
+    apply_head_scales(p, kvh);
     const int k = (int)(L / (uint32_t)p.num_kv_heads);
     const int S = p.num_seqs;
     block_prefix<NW * 64>(p.context_lens, S, p.ctx_cap, A::BS, sm.prefix, sm.wsum);
@@ -305,7 +373,7 @@ __device__ __forceinline__ void attn_mfma_body(AttnParams p) {
       int ctx = p.context_lens[s];
       ctx = ctx < 0 ? 0 : (ctx > p.ctx_cap ? p.ctx_cap : ctx);
       if (APPEND && j1 == end - start)                      // this segment holds the sequence's last block
-        append_new_row<T, T, D, A::BS, NW * 64>(p, s, kvh, (j1 - 1 - j0) % NW);
+        append_new_row<T, KT, D, A::BS, NW * 64>(p, s, kvh, (j1 - 1 - j0) % NW);
       st.init();
       A::attend(p, s, kvh, ctx, j0, j1, w, c16, g4, st);
       const int64_t prow = complete ? -1 : ((int64_t)k * 2 + which) * p.num_heads + (int64_t)kvh * p.group;
@@ -319,6 +387,7 @@ __device__ __forceinline__ void attn_mfma_body(AttnParams p) {
 
   int seq, kvh, part;
   decode_work_id(L, p.num_seqs, p.num_kv_heads, seq, kvh, part);
+  apply_head_scales(p, kvh);
   if (p.longest_first) {                                    // one pass only
     if (p.seq_order) {
       const int o = p.seq_order[seq];
@@ -337,7 +406,7 @@ __device__ __forceinline__ void attn_mfma_body(AttnParams p) {
   int b_end = b_begin + p.partition_blocks;
   b_end = b_end < nblk ? b_end : nblk;
   if (APPEND && nblk > 0 && b_end == nblk)                  // this workgroup reads the last block
-    append_new_row<T, T, D, A::BS, NW * 64>(p, seq, kvh, (nblk - 1 - b_begin) % NW);
+    append_new_row<T, KT, D, A::BS, NW * 64>(p, seq, kvh, (nblk - 1 - b_begin) % NW);
   st.init();
   A::attend(p, seq, kvh, ctx, b_begin, b_end, w, c16, g4, st);
   // partition rows are [seq][head][partition]
@@ -346,16 +415,16 @@ __device__ __forceinline__ void attn_mfma_body(AttnParams p) {
 }
 
 #define PKV_MFMA_WAVES(D, PIPE) ((D) == 128 ? ((PIPE) ? PKV_MFMA_WAVES_PER_EU_PIPE : PKV_MFMA_WAVES_PER_EU) : 1)
-template <class T, int D, int NW, bool PIPE>
+template <class T, class KT, int D, int NW, bool PIPE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PKV_MFMA_WAVES(D, PIPE))))
 void attn_mfma_kernel(AttnParams p) {
-  attn_mfma_body<T, D, NW, PIPE, false>(p);
+  attn_mfma_body<T, KT, D, NW, PIPE, false>(p);
 }
 
-template <class T, int D, int NW, bool PIPE>
+template <class T, class KT, int D, int NW, bool PIPE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PKV_MFMA_WAVES(D, PIPE))))
 void attn_mfma_append_kernel(AttnParams p) {
-  attn_mfma_body<T, D, NW, PIPE, true>(p);
+  attn_mfma_body<T, KT, D, NW, PIPE, true>(p);
 }
 
 #ifndef PKV_MFMA_NW
@@ -364,26 +433,36 @@ void attn_mfma_append_kernel(AttnParams p) {
 #ifndef PKV_MFMA_PIPE
 #define PKV_MFMA_PIPE 1
 #endif
-template <bool APPEND, class T, int D>
+template <bool APPEND, class T, class KT, int D>
 static hipError_t launch_mfma(const AttnParams& p, hipStream_t stream) {
   constexpr int NW = PKV_MFMA_NW;
   constexpr bool PIPE = PKV_MFMA_PIPE != 0;
   if constexpr (APPEND)
-    hipLaunchKernelGGL((attn_mfma_append_kernel<T, D, NW, PIPE>), dim3(p.total_wgs), dim3(NW * 64), 0, stream, p);
+    hipLaunchKernelGGL((attn_mfma_append_kernel<T, KT, D, NW, PIPE>), dim3(p.total_wgs), dim3(NW * 64), 0, stream,
+                       p);
   else
-    hipLaunchKernelGGL((attn_mfma_kernel<T, D, NW, PIPE>), dim3(p.total_wgs), dim3(NW * 64), 0, stream, p);
+    hipLaunchKernelGGL((attn_mfma_kernel<T, KT, D, NW, PIPE>), dim3(p.total_wgs), dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
-// q dtype (= kv dtype) and head_dim -> instantiation; the cases mfma_supported accepts.
+template <bool APPEND, class T, class KT>
+static hipError_t launch_mfma_d(const AttnParams& p, int d, hipStream_t stream) {
+  if (d == 128) return launch_mfma<APPEND, T, KT, 128>(p, stream);
+  if (d == 256) return launch_mfma<APPEND, T, KT, 256>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+// (q dtype, kv dtype, head_dim) -> instantiation; the cases mfma_supported accepts.
 template <bool APPEND>
-static hipError_t launch_mfma_family(const AttnParams& p, int q_dtype, int d, hipStream_t stream) {
-  if (q_dtype == 2) {
-    if (d == 128) return launch_mfma<APPEND, BF16, 128>(p, stream);
-    if (d == 256) return launch_mfma<APPEND, BF16, 256>(p, stream);
-  } else if (q_dtype == 1) {
-    if (d == 128) return launch_mfma<APPEND, F16, 128>(p, stream);
-    if (d == 256) return launch_mfma<APPEND, F16, 256>(p, stream);
+static hipError_t launch_mfma_family(const AttnParams& p, int q_dtype, int kv_dtype, int d, hipStream_t stream) {
+  if (q_dtype == BF16::kId) {
+    if (kv_dtype == BF16::kId) return launch_mfma_d<APPEND, BF16, BF16>(p, d, stream);
+    if (kv_dtype == FP8::kId) return launch_mfma_d<APPEND, BF16, FP8>(p, d, stream);
+    if (kv_dtype == BF8::kId) return launch_mfma_d<APPEND, BF16, BF8>(p, d, stream);
+  } else if (q_dtype == F16::kId) {
+    if (kv_dtype == F16::kId) return launch_mfma_d<APPEND, F16, F16>(p, d, stream);
+    if (kv_dtype == FP8::kId) return launch_mfma_d<APPEND, F16, FP8>(p, d, stream);
+    if (kv_dtype == BF8::kId) return launch_mfma_d<APPEND, F16, BF8>(p, d, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -7,12 +7,13 @@
 namespace pkv {
 
 bool mfma_supported(int q_dtype, int kv_dtype, int d, int bs, int group) {
-  return (q_dtype == 1 || q_dtype == 2) && kv_dtype == q_dtype && (d == 128 || d == 256) && bs == 16 &&
-         group >= 2 && group <= 16;
+  return (q_dtype == F16::kId || q_dtype == BF16::kId) &&
+         (kv_dtype == q_dtype || kv_dtype == FP8::kId || kv_dtype == BF8::kId) && (d == 128 || d == 256) &&
+         bs == 16 && group >= 2 && group <= 16;
 }
 
-hipError_t launch_attention_mfma(const AttnParams& p, int q_dtype, int d, hipStream_t stream) {
-  return launch_mfma_family<false>(p, q_dtype, d, stream);
+hipError_t launch_attention_mfma(const AttnParams& p, int q_dtype, int kv_dtype, int d, hipStream_t stream) {
+  return launch_mfma_family<false>(p, q_dtype, kv_dtype, d, stream);
 }
 
 }  // namespace pkv

@@ -267,8 +267,8 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   (void)hipGetLastError();  // start from a clean error state
   hipError_t e;
   if (pl.path == PKV_PATH_MFMA)
-    e = new_k ? pkv::launch_attention_mfma_append(p, q_dtype, head_dim, s)
-              : pkv::launch_attention_mfma(p, q_dtype, head_dim, s);
+    e = new_k ? pkv::launch_attention_mfma_append(p, q_dtype, kv_dtype, head_dim, s)
+              : pkv::launch_attention_mfma(p, q_dtype, kv_dtype, head_dim, s);
   else
     e = new_k ? pkv::launch_attention_vector_append(p, q_dtype, kv_dtype, head_dim, block_size, s)
               : pkv::launch_attention_vector(p, q_dtype, kv_dtype, head_dim, block_size, s);

@@ -28,11 +28,12 @@ bool mfma_supported(int q_dtype, int kv_dtype, int head_dim, int block_size, int
 
 hipError_t launch_attention_vector(const AttnParams& p, int q_dtype, int kv_dtype, int head_dim, int block_size,
                                    hipStream_t stream);
-hipError_t launch_attention_mfma(const AttnParams& p, int q_dtype, int head_dim, hipStream_t stream);
+hipError_t launch_attention_mfma(const AttnParams& p, int q_dtype, int kv_dtype, int head_dim, hipStream_t stream);
 // the same launches for decode with append (p.new_k set): separate kernels
 hipError_t launch_attention_vector_append(const AttnParams& p, int q_dtype, int kv_dtype, int head_dim,
                                           int block_size, hipStream_t stream);
-hipError_t launch_attention_mfma_append(const AttnParams& p, int q_dtype, int head_dim, hipStream_t stream);
+hipError_t launch_attention_mfma_append(const AttnParams& p, int q_dtype, int kv_dtype, int head_dim,
+                                        hipStream_t stream);
 hipError_t launch_attention_reduce(const ReduceParams& p, int out_dtype, int head_dim, hipStream_t stream);
 
 bool prefill_supported(int q_dtype, int kv_dtype, int head_dim, int block_size);

@@ -36,6 +36,9 @@ CASES = [
     ("fp32", "f32", None, 4, 4, 64, 16, [40, 17, 1, 64], 0),
     ("e4m3", "f16", "e4m3", 8, 4, 128, 16, [1, 90, 600, 31], 0),
     ("e5m2 per head", "bf16", "e5m2", 8, 4, 128, 16, [77, 400, 2], 64),
+    ("e4m3 mha", "bf16", "e4m3", 4, 4, 128, 16, [200, 3, 35], 0),
+    ("e5m2 mha per head", "f16", "e5m2", 4, 4, 128, 16, [90, 17, 600], 64),
+    ("e4m3 gqa d256", "f16", "e4m3", 8, 2, 256, 16, [150, 1, 47], 0),
 ]
 
 

@@ -77,12 +77,19 @@ def test_reshape_per_head_scales(ops, fmt):
         assert np.array_equal(_codes(vg)[:, h:h + 1], ev), f"V head {h}"
 
 
+# (H, KVH, d): grouped heads run on the matrix-core family, one query head per
+# kv head on the vector family
+HEADS = [(8, 4, 128), (8, 8, 128), (8, 2, 256)]
+
+
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
 @pytest.mark.parametrize("qdt", [torch.float16, torch.bfloat16])
 @pytest.mark.parametrize("per_head", [False, True])
 @pytest.mark.parametrize("partition", [0, 64])
-def test_attention_8bit_caches(ops, fmt, qdt, per_head, partition):
-    H, KVH, d, bs = 8, 4, 128, 16
+@pytest.mark.parametrize("heads", HEADS, ids=["gqa_d128", "mha_d128", "gqa_d256"])
+def test_attention_8bit_caches(ops, fmt, qdt, per_head, partition, heads):
+    H, KVH, d = heads
+    bs = 16
     lens = [1, 17, 300, 129, 64]
     rng = np.random.default_rng(13)
     nblk = sum(-(-n // bs) for n in lens)
@@ -101,8 +108,8 @@ def test_attention_8bit_caches(ops, fmt, qdt, per_head, partition):
     codes_k, codes_v = codes_k.astype(np.uint8), codes_v.astype(np.uint8)
     decode = oracle.decode_e4m3 if fmt == "e4m3" else e5m2_ref.decode_e5m2
     if per_head:
-        ks = np.array([0.01, 0.02, 0.004, 0.03], np.float32)
-        vs = np.array([0.5, 0.25, 1.0, 0.125], np.float32)
+        ks = np.array([0.01, 0.02, 0.004, 0.03, 0.015, 0.007, 0.02, 0.01], np.float32)[:KVH]
+        vs = np.array([0.5, 0.25, 1.0, 0.125, 0.3, 0.6, 0.2, 0.9], np.float32)[:KVH]
         kp = oracle.dequant_per_head(codes_k, ks, decode)
         vp = oracle.dequant_per_head(codes_v, vs, decode)
         kw = dict(k_scales=torch.from_numpy(ks).to(DEV), v_scales=torch.from_numpy(vs).to(DEV), k_scale=0.0,
