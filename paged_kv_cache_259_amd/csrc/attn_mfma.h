@@ -13,14 +13,15 @@
 //        Result: lane l holds S[token 4(l/16)+r][head l%16], r = 0..3.
 //   online softmax per head (column): block max over the 16 tokens = max over
 //        the lane's 4 values, then over lanes l^16 and l^32.
-//   PV:  O^T[dcol][head] += sum_k V[tok_k][8*dcol+e] P[head][tok_k]
-//        v_mfma_f32_16x16x4 f32, A = V^T, B = P^T, one MFMA per (token group
-//        tg, element e): lane l feeds V[4(l/16)+tg][8(l%16)+e] (from a plain
-//        row-major 16-byte load of token 4(l/16)+tg) and P[head l%16][token
-//        4(l/16)+tg] -- which is exactly register r = tg of its QK result, so
-//        no shuffle or transpose is needed between the two products, and P
-//        stays fp32.
-//        O_e: lane l holds O[head l%16][dim 8(4(l/16)+r)+e], r = 0..3.
+//   PV:  O^T[dim][head] += sum_k V^T[dim][tok_k] P^T[tok_k][head]
+//        v_mfma_f32_16x16x16 (f16/bf16), one per 16 dims.  B = P^T: the
+//        contraction index of lane group l/16 is tokens 4(l/16) .. +3, which
+//        are exactly the lane's four QK results, so nothing moves between the
+//        two products.  P enters as its 16-bit rounding plus the 16-bit
+//        rounding of the remainder (two MFMAs), about 16 bits of each weight.
+//        A = V^T: each wave stages its V tile (row-major, q's type) in its own
+//        LDS rows and reads it back with the transposing ds_read_b64_tr_b16.
+//        O[dt]: lane l holds O[head l%16][dim 16 dt + 4(l/16) + r], r = 0..3.
 //
 // 8-bit caches (E4M3, E5M2; "PagedAttention", Ultralytics glossary, section
 // "Các kỹ thuật liên quan": an 8-bit KV cache) read half the bytes.  K codes are
@@ -40,10 +41,25 @@
 namespace pkv {
 
 template <class T> struct MfmaOp;
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 template <> struct MfmaOp<BF16> {
   typedef bf16x8_t vec;
   __device__ __forceinline__ static f32x4_t qk(const uint4& a, const uint4& b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(vec, a), __builtin_bit_cast(vec, b), c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static f32x4_t pv(const uint2& a, const uint2& b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a), __builtin_bit_cast(s16x4_t, b), c,
+                                                     0, 0, 0);
+  }
+  // p rounded to bf16, and what that rounding left out, rounded again
+  __device__ __forceinline__ static void split(const float* p, uint2& hi, uint2& lo) {
+    bf16x4_t h = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
+    bf16x4_t l = {(__bf16)(p[0] - (float)h[0]), (__bf16)(p[1] - (float)h[1]), (__bf16)(p[2] - (float)h[2]),
+                  (__bf16)(p[3] - (float)h[3])};
+    hi = __builtin_bit_cast(uint2, h);
+    lo = __builtin_bit_cast(uint2, l);
   }
 };
 template <> struct MfmaOp<F16> {
@@ -51,7 +67,26 @@ template <> struct MfmaOp<F16> {
   __device__ __forceinline__ static f32x4_t qk(const uint4& a, const uint4& b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(vec, a), __builtin_bit_cast(vec, b), c, 0, 0, 0);
   }
+  __device__ __forceinline__ static f32x4_t pv(const uint2& a, const uint2& b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a), __builtin_bit_cast(f16x4_t, b), c, 0,
+                                                 0, 0);
+  }
+  __device__ __forceinline__ static void split(const float* p, uint2& hi, uint2& lo) {
+    f16x4_t h = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+    f16x4_t l = {(_Float16)(p[0] - (float)h[0]), (_Float16)(p[1] - (float)h[1]), (_Float16)(p[2] - (float)h[2]),
+                 (_Float16)(p[3] - (float)h[3])};
+    hi = __builtin_bit_cast(uint2, h);
+    lo = __builtin_bit_cast(uint2, l);
+  }
 };
+
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+// ds_read_b64_tr_b16 (8-byte aligned LDS address): within each 16-lane group,
+// output lane j gets element j%4 of the 4 elements at lane 4m + j/4's address,
+// m = 0..3.
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* lds) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(lds)));
+}
 
 // 8-bit K/V (E4M3 = FP8, E5M2 = BF8) as MFMA operands.  Both formats convert
 // exactly to f16, bf16 and fp32, so the products and sums are those of the
@@ -104,11 +139,17 @@ struct MfmaAttention {
   // takes 8 of them; the query operand follows the same order.
   __device__ __forceinline__ static int k_dim(int c, int g4) { return KV8 ? g4 * (D / 4) + 8 * c : 32 * c + 8 * g4; }
   static constexpr int RS = D + 1;                  // padded LDS row stride against bank conflicts
+  static constexpr int ND = D / 16;                 // PV output tiles of 16 dims
+  static constexpr int VRS = D + 16;                // LDS row stride of a staged V tile (elements): the
+                                                    // 16 rows x 32 bytes of a transposing read cover every bank
   static_assert(D % 128 == 0, "MFMA family needs head_dim 128 or 256");
 
   struct Smem {
     float m[NW][16], l[NW][16];
-    float o[NW][16 * RS];
+    union {                                         // attend uses vt, finish o (after a barrier)
+      float o[NW][16 * RS];
+      alignas(16) uint16_t vt[NW][16 * VRS];        // each wave's V tile in q's type, row-major
+    };
     alignas(16) int prefix[kMaxSliceSeqs + 4];
     int wsum[NW];
   };
@@ -116,14 +157,12 @@ struct MfmaAttention {
   struct State {
     float m;                 // running max of head c16 (same in all four row groups)
     float lsum;              // this lane's share of the running exp-sum of head c16
-    f32x4_t O[NH][8];
+    f32x4_t O[ND];           // O[dt]: lane l holds O[head l%16][dim 16 dt + 4(l/16) + r], r = 0..3
     __device__ void init() {
       m = -__builtin_inff();
       lsum = 0.f;
 #pragma unroll
-      for (int hh = 0; hh < NH; ++hh)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) O[hh][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int dt = 0; dt < ND; ++dt) O[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
   };
 
@@ -158,7 +197,8 @@ struct MfmaAttention {
     }
   }
 
-  __device__ static void consume(const AttnParams& p, const uint4* qop, Tiles& t, int valid, int g4, State& st) {
+  __device__ static void consume(const AttnParams& p, const uint4* qop, Tiles& t, int valid, int c16, int g4,
+                                 uint16_t* vt, State& st) {
     if (!t.ok) return;                                  // wave-uniform
     f32x4_t S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -195,24 +235,31 @@ struct MfmaAttention {
     st.lsum = st.lsum * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
     st.m = mn;
 #pragma unroll
-    for (int hh = 0; hh < NH; ++hh)
+    for (int dt = 0; dt < ND; ++dt) st.O[dt] *= alpha;
+    // PV on 16x16x16 MFMAs.  B = P^T: the contraction index of lane group g4 is
+    // tokens 4 g4 .. +3, exactly the lane's four weights; P enters as a 16-bit
+    // part and the 16-bit rounding of what it left out, so the product keeps
+    // about 16 bits of each weight.  A = V^T: the wave stages its tile in LDS
+    // (row-major, q's type) and reads it back transposed: lane 4m + q of group
+    // g4 points at token 4 g4 + m, dims 16 dt + 4q .. +3, so output lane j
+    // receives V[4 g4 + m][16 dt + j] for m = 0..3.
 #pragma unroll
-      for (int e = 0; e < 8; ++e) st.O[hh][e] *= alpha;
-#pragma unroll
-    for (int tg = 0; tg < 4; ++tg) {
+    for (int tg = 0; tg < 4; ++tg)
 #pragma unroll
       for (int hh = 0; hh < NH; ++hh) {
-        float vf[8];
-        if constexpr (KV8) {
-          kv8x4_to_f32<KT>(t.v[tg][hh].x, vf);
-          kv8x4_to_f32<KT>(t.v[tg][hh].y, vf + 4);
-        } else {
-          Unpack<T>::run(t.v[tg][hh], vf);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          st.O[hh][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[e], pr[tg], st.O[hh][e], 0, 0, 0);
+        uint4 v16;
+        if constexpr (KV8) v16 = kv8x8_to_16<T, KT>(t.v[tg][hh].x, t.v[tg][hh].y);
+        else v16 = t.v[tg][hh];
+        *reinterpret_cast<uint4*>(vt + (4 * g4 + tg) * VRS + 128 * hh + 8 * c16) = v16;
       }
+    uint2 phi, plo;
+    MfmaOp<T>::split(pr, phi, plo);
+    const uint16_t* vr = vt + (4 * g4 + (c16 >> 2)) * VRS + 4 * (c16 & 3);
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) {
+      const uint2 a = lds_read_tr16(vr + 16 * dt);
+      st.O[dt] = MfmaOp<T>::pv(a, phi, st.O[dt]);
+      st.O[dt] = MfmaOp<T>::pv(a, plo, st.O[dt]);
     }
   }
 
@@ -221,7 +268,7 @@ struct MfmaAttention {
   // tiles are in flight while the current one is consumed.  Block ids come 64
   // at a time from one VGPR (lane t holds the t-th id) through readlane.
   __device__ static void attend(const AttnParams& p, int seq, int kvh, int ctx, int j0, int j1, int w, int c16,
-                                int g4, State& st) {
+                                int g4, uint16_t* vt, State& st) {
     const int first = j0 + w;
     const int n = first < j1 ? (j1 - first + NW - 1) / NW : 0;
     if (n == 0) return;                                 // wave-uniform
@@ -268,16 +315,16 @@ struct MfmaAttention {
       Tiles b;
       for (int i = 0; i < n; i += 2) {
         if (i + 1 < n) issue(p, kbase, vbase, block_stride, id_of(i + 1), valid_of(i + 1), c16, g4, b);
-        consume(p, qop, a, valid_of(i), g4, st);
+        consume(p, qop, a, valid_of(i), c16, g4, vt, st);
         if (i + 1 < n) {
           if (i + 2 < n) issue(p, kbase, vbase, block_stride, id_of(i + 2), valid_of(i + 2), c16, g4, a);
-          consume(p, qop, b, valid_of(i + 1), g4, st);
+          consume(p, qop, b, valid_of(i + 1), c16, g4, vt, st);
         }
       }
     } else {
       for (int i = 0; i < n; ++i) {
         if (i > 0) issue(p, kbase, vbase, block_stride, id_of(i), valid_of(i), c16, g4, a);
-        consume(p, qop, a, valid_of(i), g4, st);
+        consume(p, qop, a, valid_of(i), c16, g4, vt, st);
       }
     }
   }
@@ -292,13 +339,12 @@ struct MfmaAttention {
     float lsum = st.lsum;
     lsum += swz_xor16(lsum);
     lsum += xor32(lsum);
+    __syncthreads();                                    // every wave is done with its V tile (o shares it)
     if (c16 < G) {
 #pragma unroll
-      for (int hh = 0; hh < NH; ++hh)
+      for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sm.o[w][c16 * RS + hh * 128 + (g4 * 4 + r) * 8 + e] = st.O[hh][e][r];
+        for (int r = 0; r < 4; ++r) sm.o[w][c16 * RS + 16 * dt + 4 * g4 + r] = st.O[dt][r];
       if (g4 == 0) { sm.m[w][c16] = st.m; sm.l[w][c16] = lsum; }
     }
     __syncthreads();
@@ -375,7 +421,7 @@ __device__ __forceinline__ void attn_mfma_body(AttnParams p) {
       if (APPEND && j1 == end - start)                      // this segment holds the sequence's last block
         append_new_row<T, KT, D, A::BS, NW * 64>(p, s, kvh, (j1 - 1 - j0) % NW);
       st.init();
-      A::attend(p, s, kvh, ctx, j0, j1, w, c16, g4, st);
+      A::attend(p, s, kvh, ctx, j0, j1, w, c16, g4, sm.vt[w], st);
       const int64_t prow = complete ? -1 : ((int64_t)k * 2 + which) * p.num_heads + (int64_t)kvh * p.group;
       A::finish(p, st, sm, s, kvh, prow, 1, tid, w, c16, g4);
       pos = end;
@@ -408,7 +454,7 @@ __device__ __forceinline__ void attn_mfma_body(AttnParams p) {
   if (APPEND && nblk > 0 && b_end == nblk)                  // this workgroup reads the last block
     append_new_row<T, KT, D, A::BS, NW * 64>(p, seq, kvh, (nblk - 1 - b_begin) % NW);
   st.init();
-  A::attend(p, seq, kvh, ctx, b_begin, b_end, w, c16, g4, st);
+  A::attend(p, seq, kvh, ctx, b_begin, b_end, w, c16, g4, sm.vt[w], st);
   // partition rows are [seq][head][partition]
   const int64_t prow = direct ? -1 : ((int64_t)seq * p.num_heads + (int64_t)kvh * p.group) * p.num_partitions + part;
   A::finish(p, st, sm, seq, kvh, prow, p.num_partitions, tid, w, c16, g4);
