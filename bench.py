@@ -73,6 +73,27 @@ def parse():
     return ap.parse_args()
 
 
+WARMUP_MIN_S = 0.05
+
+
+def warm_up(fn, steps):
+    """Run ``fn`` at least ``steps`` times and for at least WARMUP_MIN_S of GPU time.
+
+    After the host-bound set-up (inputs, block tables) the GPU needs a few
+    milliseconds of work to return to full clocks; a fixed count of short steps
+    does not always cover that.  Returns the number of warm-up steps run.
+    """
+    import torch
+    n, t0 = 0, time.perf_counter()
+    while n < steps or time.perf_counter() - t0 < WARMUP_MIN_S:
+        fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
 def kernel_kind(workload):
     return "prefill" if workload.startswith("prefill") else "decode"
 
@@ -107,13 +128,17 @@ def algorithmic_bytes(w, ctx, elt_q, elt_kv):
 
 
 class _BlockSubset:
-    """float64 host copy of some pool blocks, read as pool[block, kv_head] by the oracle."""
+    """float64 host copy of some pool blocks, read as pool[block, kv_head] by the oracle.
 
-    def __init__(self, pool, blocks):
+    ``decode`` turns an 8-bit pool's codes into values (the oracle's decoder
+    times the scale); other pools are widened to float64.
+    """
+
+    def __init__(self, pool, blocks, decode=None):
         import torch
         ids = sorted(set(int(b) for b in blocks))
         rows = pool.index_select(0, torch.tensor(ids, dtype=torch.int64, device=pool.device))
-        host = rows.cpu().to(torch.float64).numpy()
+        host = decode(rows.cpu().numpy()) if decode else rows.cpu().to(torch.float64).numpy()
         self._rows = {b: host[i] for i, b in enumerate(ids)}
         self.shape = tuple(pool.shape)
         self.dtype = np.float64
@@ -134,12 +159,15 @@ def cpu_baseline(w, inp, tables, ctx, budget_s):
     from threadpoolctl import threadpool_info
     q = inp["q"].cpu().to(torch.float64).numpy()
     elt = inp["k"].element_size()
+    decode = None
+    if getattr(w, "kv8", False):                      # E4M3 codes -> values, as the oracle reads them
+        decode = lambda c: oracle.decode_e4m3(c) * np.float64(np.float32(w.kv_scale))
     done, kv_bytes, spent = 0, 0, 0.0
     for s in range(w.num_seqs):
         n = int(ctx[s])
         blocks = tables[s, : -(-n // w.block_size)]
-        kp = _BlockSubset(inp["k"], blocks)
-        vp = _BlockSubset(inp["v"], blocks)
+        kp = _BlockSubset(inp["k"], blocks, decode)
+        vp = _BlockSubset(inp["v"], blocks, decode)
         t0 = time.perf_counter()
         oracle.attend_ref(q[s:s + 1], kp, vp, tables[s:s + 1], ctx[s:s + 1], w.softmax_scale, w.block_size)
         spent += time.perf_counter() - t0
@@ -240,10 +268,7 @@ def main_prefill(args, w):
         ops.paged_prefill_attention(out, inp.q, inp.k_cache, inp.v_cache, tables, ctx, qsl, w.softmax_scale, max_q,
                                     max_ctx, stream=stream)
 
-    for _ in range(args.warmup):
-        reshape()
-        attend()
-    torch.cuda.synchronize()
+    warm = warm_up(lambda: (reshape(), attend()), args.warmup)
     K = args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     torch.cuda.synchronize()
@@ -266,7 +291,7 @@ def main_prefill(args, w):
     result = {
         "metric": "paged chunked-prefill attention TFLOP/s (% of dense MFMA peak) + prefill tokens/s per layer step",
         "value": round(flops / (step_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
-        "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True, "scaling": "weak",
+        "warmup": warm, "ms_per_step": round(step_ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) q/K/V, uniform prior context lengths, shuffled block tables)",
         "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_heads": w.num_heads,
@@ -333,11 +358,9 @@ def main_prefix_cache(args, w):
         ops.paged_prefill_attention(f["out"], f["q"], f["kc"], f["kv"], f["tables"], f["ctx"], f["qsl"],
                                     w.softmax_scale, int(f["chunk"].max()), L, stream=stream)
 
-    res = {}
+    res, warms = {}, []
     for name, f in flows.items():
-        for _ in range(args.warmup):
-            run(f)
-        torch.cuda.synchronize()
+        warms.append(warm_up(lambda: run(f), args.warmup))
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(args.steps):
@@ -354,7 +377,7 @@ def main_prefix_cache(args, w):
     flops_c = prefill_flops(w, np.full(R, L, np.int64), fc["chunk"])
     result = {
         "metric": "prefill step time of requests sharing a system prompt, prefix cache off / on",
-        "value": round(speedup, 3), "unit": "x", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "value": round(speedup, 3), "unit": "x", "n_gpus": 1, "steps": args.steps, "warmup": min(warms),
         "ms_per_step": res["cache"]["ms_per_step"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded token ids and N(0,1) q/K/V; shared-prefix K/V identical across requests)",
@@ -422,9 +445,7 @@ def main_shared_prefix(args, w):
     shared), then copy_blocks over those pairs (when any) and one
     paged_attention_decode_append launch that writes each sample's new token and
     attends.  Repeating the step rewrites the same bytes, so every timed step
-    does the same work.  The set-up is host-bound (hundreds of small launches),
-    so the warm-up runs at least 25 ms of steps (more than ``--warmup`` steps if
-    need be; the JSON reports the count) to bring the GPU back to full clocks.
+    does the same work.
     """
     import torch
     from paged_kv_cache_259_amd import ops, synth
@@ -471,12 +492,7 @@ def main_shared_prefix(args, w):
         ops.paged_attention_decode_append(out, q, kc, vc, k_new, v_new, slot_t, tables, ctx, w.softmax_scale, max_ctx,
                                           k_scale=ks, v_scale=vs, workspace=workspace, seq_order=order, stream=stream)
 
-    warm, t_warm = 0, time.perf_counter()
-    while warm < args.warmup or time.perf_counter() - t_warm < 0.025:
-        cow()
-        attend()
-        torch.cuda.synchronize()
-        warm += 1
+    warm = warm_up(lambda: (cow(), attend()), args.warmup)
     K = args.steps
 
     def timed(fn):
@@ -594,7 +610,7 @@ def main():
     if isinstance(w, synth.SharedPrefixWorkload):
         return main_shared_prefix(args, w)
     if not isinstance(w, synth.DecodeWorkload):
-        raise SystemExit("bench.py times decode workloads (llama13b_f16, gqa_bf16, long_splitk_bf16, tiny_f32)")
+        raise SystemExit("unknown workload kind: " + args.workload)
     part = w.partition_size if args.partition is None else args.partition
 
     # ---- inputs: seeded, generated on the device; tables from the host block manager
@@ -618,24 +634,21 @@ def main():
     workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     out = torch.empty_like(inp.q)
     stream = torch.cuda.current_stream()
+    kvs = dict(k_scale=w.kv_scale, v_scale=w.kv_scale) if w.kv8 else {}
 
     def reshape():
-        ops.reshape_and_cache(inp.k_new, inp.v_new, inp.k_cache, inp.v_cache, slots, stream=stream)
+        ops.reshape_and_cache(inp.k_new, inp.v_new, inp.k_cache, inp.v_cache, slots, stream=stream, **kvs)
 
     def attend():
         ops.paged_attention_decode(out, inp.q, inp.k_cache, inp.v_cache, tables, ctx, w.softmax_scale, max_ctx,
-                                   partition_size=part, workspace=workspace, seq_order=order, stream=stream)
+                                   partition_size=part, workspace=workspace, seq_order=order, stream=stream, **kvs)
 
     def step():                          # the whole step in one launch: write the new tokens, attend
         ops.paged_attention_decode_append(out, inp.q, inp.k_cache, inp.v_cache, inp.k_new, inp.v_new, slots, tables,
                                           ctx, w.softmax_scale, max_ctx, partition_size=part, workspace=workspace,
-                                          seq_order=order, stream=stream)
+                                          seq_order=order, stream=stream, **kvs)
 
-    for _ in range(args.warmup):
-        reshape()
-        attend()
-        step()
-    torch.cuda.synchronize()
+    warm = warm_up(lambda: (reshape(), attend(), step()), args.warmup)
 
     K = args.steps
     # the timed step: decode with append
@@ -720,13 +733,15 @@ def main():
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
+        "warmup": warm,
         "ms_per_step": round(step_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.kv_dtype,
-        "data": "synthetic (seeded N(0,1) q/K/V, lognormal context lengths, shuffled block tables)",
+        "data": ("synthetic (seeded N(0,1) q and new K/V, uniform E4M3 pool codes, lognormal context lengths, "
+                 "shuffled block tables)" if w.kv8 else
+                 "synthetic (seeded N(0,1) q/K/V, lognormal context lengths, shuffled block tables)"),
         "config": {
             "workload": w.name, "num_seqs": w.num_seqs, "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads,
             "head_dim": w.head_dim, "block_size": w.block_size, "q_dtype": w.q_dtype, "kv_dtype": w.kv_dtype,

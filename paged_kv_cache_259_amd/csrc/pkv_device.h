@@ -449,43 +449,40 @@ __device__ void append_new_row(const AttnParams& p, int seq, int g, int owner) {
   (void)NT;
   const int64_t slot = p.slot_mapping[seq];
   if (slot >= 0 && slot < (int64_t)p.num_blocks * BS) {
-    constexpr int V = 16 / ST::bytes;                       // source elements per 16-byte chunk
     const int64_t blk = slot / BS, off = slot - blk * BS;
     const size_t src = ((size_t)seq * p.num_kv_heads + g) * D;
     const size_t dst = (((size_t)blk * p.num_kv_heads + g) * BS + off) * D;
-    for (int c = threadIdx.x & 63; c < D / V; c += NT_) {
-      const uint4 kr = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(p.new_k) + (src + c * V) * ST::bytes);
-      const uint4 vr = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(p.new_v) + (src + c * V) * ST::bytes);
-      char* kd = reinterpret_cast<char*>(const_cast<void*>(p.k_cache));
-      char* vd = reinterpret_cast<char*>(const_cast<void*>(p.v_cache));
-      if constexpr (KT::kId == ST::kId) {
-        *reinterpret_cast<uint4*>(kd + (dst + c * V) * KT::bytes) = kr;
-        *reinterpret_cast<uint4*>(vd + (dst + c * V) * KT::bytes) = vr;
-      } else {                                              // 8-bit cache
-        const float ks = p.k_scales ? p.k_scales[g] : p.enc_k_scale;
-        const float vs = p.v_scales ? p.v_scales[g] : p.enc_v_scale;
-        float kf[V], vf[V];
-        Unpack<ST>::run(kr, kf);
-        Unpack<ST>::run(vr, vf);
-        uint32_t kc[V / 4], vc[V / 4];
+    char* kd = reinterpret_cast<char*>(const_cast<void*>(p.k_cache));
+    char* vd = reinterpret_cast<char*>(const_cast<void*>(p.v_cache));
+    if constexpr (KT::kId == ST::kId) {                     // bit copy in 16-byte chunks
+      constexpr int V = 16 / ST::bytes;
+      for (int c = threadIdx.x & 63; c < D / V; c += NT_) {
+        const char* ks = reinterpret_cast<const char*>(p.new_k) + (src + c * V) * ST::bytes;
+        const char* vs = reinterpret_cast<const char*>(p.new_v) + (src + c * V) * ST::bytes;
+        *reinterpret_cast<uint4*>(kd + (dst + c * V) * KT::bytes) = *reinterpret_cast<const uint4*>(ks);
+        *reinterpret_cast<uint4*>(vd + (dst + c * V) * KT::bytes) = *reinterpret_cast<const uint4*>(vs);
+      }
+    } else {                                                // 8-bit cache: each lane encodes D/64 elements
+      constexpr int EPL = D / 64;
+      static_assert(EPL == 1 || EPL == 2 || EPL == 4, "head_dim 64, 128 or 256");
+      const float ks = p.k_scales ? p.k_scales[g] : p.enc_k_scale;
+      const float vs = p.v_scales ? p.v_scales[g] : p.enc_v_scale;
+      const int c = threadIdx.x & 63;
+      uint32_t kc = 0, vc = 0;
 #pragma unroll
-        for (int j = 0; j < V / 4; ++j) {
-          uint32_t a = 0, b = 0;
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            a |= fp8_encode_scaled<KT>(kf[4 * j + t], ks) << (8 * t);
-            b |= fp8_encode_scaled<KT>(vf[4 * j + t], vs) << (8 * t);
-          }
-          kc[j] = a;
-          vc[j] = b;
-        }
-        if constexpr (V == 8) {
-          *reinterpret_cast<uint2*>(kd + dst + c * V) = make_uint2(kc[0], kc[1]);
-          *reinterpret_cast<uint2*>(vd + dst + c * V) = make_uint2(vc[0], vc[1]);
-        } else {
-          *reinterpret_cast<uint32_t*>(kd + dst + c * V) = kc[0];
-          *reinterpret_cast<uint32_t*>(vd + dst + c * V) = vc[0];
-        }
+      for (int e = 0; e < EPL; ++e) {
+        kc |= fp8_encode_scaled<KT>(load_elem<ST>(p.new_k, src + c * EPL + e), ks) << (8 * e);
+        vc |= fp8_encode_scaled<KT>(load_elem<ST>(p.new_v, src + c * EPL + e), vs) << (8 * e);
+      }
+      if constexpr (EPL == 4) {
+        *reinterpret_cast<uint32_t*>(kd + dst + c * EPL) = kc;
+        *reinterpret_cast<uint32_t*>(vd + dst + c * EPL) = vc;
+      } else if constexpr (EPL == 2) {
+        *reinterpret_cast<uint16_t*>(kd + dst + c * EPL) = (uint16_t)kc;
+        *reinterpret_cast<uint16_t*>(vd + dst + c * EPL) = (uint16_t)vc;
+      } else {
+        *reinterpret_cast<uint8_t*>(kd + dst + c) = (uint8_t)kc;
+        *reinterpret_cast<uint8_t*>(vd + dst + c) = (uint8_t)vc;
       }
     }
   }

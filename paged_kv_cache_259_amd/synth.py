@@ -50,10 +50,20 @@ class DecodeWorkload:
     pool_slack: float = 1.2
     partition_size: int = 0      # 0 -> library's automatic choice
     scale: float = 0.0           # 0 -> 1/sqrt(head_dim)
+    kv_scale: float = 1.0        # 8-bit caches: the pool-wide k_scale and v_scale
+    code_max: int = 0x5F         # 8-bit caches: largest magnitude code drawn for the pools
 
     @property
     def softmax_scale(self):
         return self.scale if self.scale > 0 else 1.0 / math.sqrt(self.head_dim)
+
+    @property
+    def kv8(self):
+        return DTYPES[self.kv_dtype] == torch.uint8
+
+    @property
+    def src_dtype(self):         # type of the new tokens' K/V (an 8-bit cache encodes them)
+        return self.q_dtype if self.kv8 else self.kv_dtype
 
 
 @dataclass(frozen=True)
@@ -130,6 +140,15 @@ GQA_BF16 = DecodeWorkload(
     q_dtype="bf16", kv_dtype="bf16", lengths=("lognormal", 1000, 0.6, 32, 4096),
     max_blocks_per_seq=256)
 
+# The GQA shape over an E4M3 cache: pool codes drawn uniformly over magnitudes
+# 0 .. 0x5F (|value| <= 30 before the scale) with random signs.
+GQA_FP8 = DecodeWorkload(
+    name="GQA decode over an E4M3 cache, one layer: 256 seqs, 64 q heads over 8 kv heads, d128, bf16 q, "
+         "fp8 E4M3 K/V (scale 0.05), bs16, lognormal ctx median 1000 in [32,4096]",
+    seed=25909, num_seqs=256, num_heads=64, num_kv_heads=8, head_dim=128, block_size=16,
+    q_dtype="bf16", kv_dtype="fp8_e4m3", lengths=("lognormal", 1000, 0.6, 32, 4096),
+    max_blocks_per_seq=256, kv_scale=0.05)
+
 LONG_SPLITK_BF16 = DecodeWorkload(
     name="long-context split-K decode: 8 seqs ctx uniform [32768,131072], 32 q / 8 kv heads, "
          "d128, bf16, bs16, partitions of 512 tokens, 70000-block pool",
@@ -187,6 +206,7 @@ WORKLOADS = {
     "llama13b_f16": LLAMA13B_F16,
     "gqa_bf16": GQA_BF16,
     "long_splitk_bf16": LONG_SPLITK_BF16,
+    "gqa_fp8": GQA_FP8,
     "shared_prefix_fp8": SHARED_PREFIX_FP8,
     "prefill_llama13b_f16": PREFILL_LLAMA13B_F16,
     "prefill_gqa_bf16": PREFILL_GQA_BF16,
@@ -223,6 +243,13 @@ def randn(gen, shape, dtype, device):
     return x.to(dtype)
 
 
+def codes8(gen, shape, code_max, device):
+    """uint8 codes: magnitude uniform in 0 .. code_max, random sign bit."""
+    mag = torch.randint(0, code_max + 1, shape, generator=gen, dtype=torch.int32, device=device)
+    sign = torch.randint(0, 2, shape, generator=gen, dtype=torch.int32, device=device)
+    return (mag | (sign << 7)).to(torch.uint8)
+
+
 def make_generator(seed, device):
     g = torch.Generator(device=device)
     g.manual_seed(int(seed))
@@ -253,10 +280,15 @@ def make_decode_inputs(w: DecodeWorkload, device="cpu", lengths=None):
     qdt, kvdt = DTYPES[w.q_dtype], DTYPES[w.kv_dtype]
     S, H, KVH, d, bs = w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size
     q = randn(gen, (S, H, d), qdt, device)
-    k_cache = randn(gen, (nb, KVH, bs, d), kvdt, device)
-    v_cache = randn(gen, (nb, KVH, bs, d), kvdt, device)
-    k_new = randn(gen, (S, KVH, d), kvdt, device)
-    v_new = randn(gen, (S, KVH, d), kvdt, device)
+    if w.kv8:
+        k_cache = codes8(gen, (nb, KVH, bs, d), w.code_max, device)
+        v_cache = codes8(gen, (nb, KVH, bs, d), w.code_max, device)
+    else:
+        k_cache = randn(gen, (nb, KVH, bs, d), kvdt, device)
+        v_cache = randn(gen, (nb, KVH, bs, d), kvdt, device)
+    srcdt = DTYPES[w.src_dtype]
+    k_new = randn(gen, (S, KVH, d), srcdt, device)
+    v_new = randn(gen, (S, KVH, d), srcdt, device)
     return DecodeInputs(w, ctx, free_list, nb, q, k_cache, v_cache, k_new, v_new)
 
 

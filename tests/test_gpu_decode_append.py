@@ -39,6 +39,7 @@ CASES = [
     ("e4m3 mha", "bf16", "e4m3", 4, 4, 128, 16, [200, 3, 35], 0),
     ("e5m2 mha per head", "f16", "e5m2", 4, 4, 128, 16, [90, 17, 600], 64),
     ("e4m3 gqa d256", "f16", "e4m3", 8, 2, 256, 16, [150, 1, 47], 0),
+    ("e5m2 mha d64", "bf16", "e5m2", 4, 4, 64, 16, [61, 2, 300], 0),
 ]
 
 

@@ -37,40 +37,49 @@ def _decode_step(ops, w):
     ctx = bm.context_lens_array(seqs)
     k_before, v_before = inp.k_cache.clone(), inp.v_cache.clone()
     slot_t = torch.tensor(slots, dtype=torch.int64, device=DEV)
-    ops.reshape_and_cache(inp.k_new, inp.v_new, inp.k_cache, inp.v_cache, slot_t)
+    kvs = dict(k_scale=w.kv_scale, v_scale=w.kv_scale) if w.kv8 else {}
+    ops.reshape_and_cache(inp.k_new, inp.v_new, inp.k_cache, inp.v_cache, slot_t, **kvs)
     out = torch.empty_like(inp.q)
     order = torch.from_numpy(bm.longest_first(seqs)).to(DEV)       # as bench.py launches it
     ops.paged_attention_decode(out, inp.q, inp.k_cache, inp.v_cache, torch.from_numpy(tables).to(DEV),
                                torch.from_numpy(ctx).to(DEV), w.softmax_scale, int(ctx.max()),
-                               partition_size=w.partition_size, seq_order=order)
+                               partition_size=w.partition_size, seq_order=order, **kvs)
     torch.cuda.synchronize()
     return inp, tables, ctx, slots, k_before, v_before, out
 
 
-@pytest.mark.parametrize("name", ["llama13b_f16", "gqa_bf16", "long_splitk_bf16"])
+@pytest.mark.parametrize("name", ["llama13b_f16", "gqa_bf16", "long_splitk_bf16", "gqa_fp8"])
 def test_full_size_decode_step(ops, name):
     w = synth.WORKLOADS[name]
     inp, tables, ctx, slots, kb, vb, out = _decode_step(ops, w)
     print(f"{name}: S={w.num_seqs} sum ctx={int(ctx.sum())} max ctx={int(ctx.max())} blocks={inp.num_blocks}", flush=True)
-    # reshape_and_cache over the whole pool
+    # reshape_and_cache over the whole pool (an 8-bit pool holds the oracle's encoding of the new rows)
     bs = w.block_size
     blk = torch.tensor([s // bs for s in slots], device=DEV)
     off = torch.tensor([s % bs for s in slots], device=DEV)
+    bits = torch.uint8 if w.kv8 else torch.int16
     for before, after, new in ((kb, inp.k_cache, inp.k_new), (vb, inp.v_cache, inp.v_new)):
-        assert torch.equal(after[blk, :, off].view(torch.int16), new.view(torch.int16))
-        changed = (after.view(torch.int16) != before.view(torch.int16)).any(dim=-1)      # [NB, KVH, bs]
+        if w.kv8:
+            want = oracle.encode_e4m3(new.float().cpu().numpy(), w.kv_scale)
+            assert np.array_equal(after[blk, :, off].cpu().numpy(), want)
+        else:
+            assert torch.equal(after[blk, :, off].view(torch.int16), new.view(torch.int16))
+        changed = (after.view(bits) != before.view(bits)).any(dim=-1)                    # [NB, KVH, bs]
         changed[blk, :, off] = False
         assert not bool(changed.any()), "reshape_and_cache touched a slot it was not given"
     # attention on sampled outputs
     assert torch.isfinite(out.float()).all()
+    to_f64 = as_f64
+    if w.kv8:                                                       # stored codes, decoded by the oracle
+        to_f64 = lambda t: oracle.decode_e4m3(t.cpu().numpy()) * np.float64(np.float32(w.kv_scale))
     rng = np.random.default_rng(w.seed)
     picks = sample_pairs(rng, w.num_seqs, w.num_heads, 6, always=[int(np.argmax(ctx))])
     G = w.num_heads // w.num_kv_heads
     for s, h in picks:
         n = int(ctx[s])
         tab = tables[s, : -(-n // bs)]
-        kp = SparsePool(inp.k_cache, tab, as_f64)
-        vp = SparsePool(inp.v_cache, tab, as_f64)
+        kp = SparsePool(inp.k_cache, tab, to_f64)
+        vp = SparsePool(inp.v_cache, tab, to_f64)
         K = oracle.gather_tokens(kp, tables[s], n, bs, h // G)
         V = oracle.gather_tokens(vp, tables[s], n, bs, h // G)
         ref = oracle.attend_one_ref(as_f64(inp.q[s, h]), K, V, w.softmax_scale)
