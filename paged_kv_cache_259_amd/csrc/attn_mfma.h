@@ -27,8 +27,9 @@
 // "Các kỹ thuật liên quan": an 8-bit KV cache) read half the bytes.  K codes are
 // converted exactly to q's 16-bit type for the QK MFMA (lane group l/16 then
 // holds dims D/4 (l/16) .. +D/4 of its token, two 16-byte loads at D = 128, and
-// the query operand follows that contraction order); V codes convert exactly
-// to fp32 for the PV MFMA.  k_scale scales the logits, v_scale the output.
+// the query operand follows that contraction order); V codes likewise before
+// they are staged for the PV MFMA.  k_scale scales the logits, v_scale the
+// output.
 //
 // Two kernels share the body: attn_mfma_kernel (plain decode) and
 // attn_mfma_append_kernel (decode that first writes each sequence's new K/V
@@ -89,37 +90,36 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* lds) {
 }
 
 // 8-bit K/V (E4M3 = FP8, E5M2 = BF8) as MFMA operands.  Both formats convert
-// exactly to f16, bf16 and fp32, so the products and sums are those of the
-// 16-bit path over the dequantised values; the scales are applied to the
-// logits (k) and to the output (v).
-template <class KT> __device__ __forceinline__ void kv8x4_to_f32(uint32_t u, float* f);
-template <> __device__ __forceinline__ void kv8x4_to_f32<FP8>(uint32_t u, float* f) { fp8x4_to_f32(u, f); }
-template <> __device__ __forceinline__ void kv8x4_to_f32<BF8>(uint32_t u, float* f) { bf8x4_to_f32(u, f); }
+// exactly to f16 and bf16, so the products and sums are those of the 16-bit
+// path over the dequantised values; the scales are applied to the logits (k)
+// and to the output (v).
+// Two 8-bit codes (the low or high half of a word) -> two elements of the
+// 16-bit MFMA type T, through gfx950's scaled converts at scale 1 (exact:
+// checked on every code of both formats, both halves, NaN and infinity
+// classes included).
+template <class T, class KT> __device__ __forceinline__ uint32_t kv8x2_to_16(uint32_t u, bool hi);
+template <> __device__ __forceinline__ uint32_t kv8x2_to_16<BF16, FP8>(uint32_t u, bool hi) {
+  return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u, 1.0f, true)
+                                         : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u, 1.0f, false));
+}
+template <> __device__ __forceinline__ uint32_t kv8x2_to_16<BF16, BF8>(uint32_t u, bool hi) {
+  return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(u, 1.0f, true)
+                                         : __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(u, 1.0f, false));
+}
+template <> __device__ __forceinline__ uint32_t kv8x2_to_16<F16, FP8>(uint32_t u, bool hi) {
+  return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(u, 1.0f, true)
+                                         : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(u, 1.0f, false));
+}
+template <> __device__ __forceinline__ uint32_t kv8x2_to_16<F16, BF8>(uint32_t u, bool hi) {
+  return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(u, 1.0f, true)
+                                         : __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(u, 1.0f, false));
+}
 
 // Eight 8-bit codes (two words) -> eight elements of the 16-bit MFMA type T.
 template <class T, class KT>
 __device__ __forceinline__ uint4 kv8x8_to_16(uint32_t a, uint32_t b) {
-  if constexpr (std::is_same<T, F16>::value && std::is_same<KT, BF8>::value) {
-    // an E5M2 code is the high byte of the f16 with the same value
-    return make_uint4(__builtin_amdgcn_perm(a, a, 0x010c000cu), __builtin_amdgcn_perm(a, a, 0x030c020cu),
-                      __builtin_amdgcn_perm(b, b, 0x010c000cu), __builtin_amdgcn_perm(b, b, 0x030c020cu));
-  } else {
-    float f[8];
-    kv8x4_to_f32<KT>(a, f);
-    kv8x4_to_f32<KT>(b, f + 4);
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (std::is_same<T, BF16>::value) {
-        const bf162_t h = {(__bf16)f[2 * i], (__bf16)f[2 * i + 1]};
-        w[i] = __builtin_bit_cast(uint32_t, h);
-      } else {
-        const half2_t h = {(_Float16)f[2 * i], (_Float16)f[2 * i + 1]};
-        w[i] = __builtin_bit_cast(uint32_t, h);
-      }
-    }
-    return make_uint4(w[0], w[1], w[2], w[3]);
-  }
+  return make_uint4(kv8x2_to_16<T, KT>(a, false), kv8x2_to_16<T, KT>(a, true), kv8x2_to_16<T, KT>(b, false),
+                    kv8x2_to_16<T, KT>(b, true));
 }
 
 // T: the q type and MFMA operand type (f16 / bf16); KT: the cache type, T itself
