@@ -40,6 +40,8 @@ CASES = [
     ("e5m2 mha per head", "f16", "e5m2", 4, 4, 128, 16, [90, 17, 600], 64),
     ("e4m3 gqa d256", "f16", "e4m3", 8, 2, 256, 16, [150, 1, 47], 0),
     ("e5m2 mha d64", "bf16", "e5m2", 4, 4, 64, 16, [61, 2, 300], 0),
+    ("e4m3 gqa slices", "bf16", "e4m3", 8, 2, 128, 16, [2000, 1, 640], 0),
+    ("e5m2 gqa partitions", "f16", "e5m2", 8, 2, 128, 16, [3, 530, 64], 128),
 ]
 
 
@@ -73,8 +75,8 @@ def test_append_equals_write_then_decode(ops, case):
         nan = 0x7F
         if fmt == "e5m2":
             pool, vpool = pool.view(torch.float8_e5m2), vpool.view(torch.float8_e5m2)
-            kw = dict(k_scales=torch.tensor([0.02, 0.05, 0.01, 0.03], device=DEV),
-                      v_scales=torch.tensor([0.5, 0.2, 0.1, 1.0], device=DEV))
+            kw = dict(k_scales=torch.tensor([0.02, 0.05, 0.01, 0.03][:KVH], device=DEV),
+                      v_scales=torch.tensor([0.5, 0.2, 0.1, 1.0][:KVH], device=DEV))
         else:
             kw = dict(k_scale=0.04, v_scale=0.25)
     for s_ in slots:                                           # the newest positions are not written yet

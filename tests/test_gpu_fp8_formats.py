@@ -79,14 +79,14 @@ def test_reshape_per_head_scales(ops, fmt):
 
 # (H, KVH, d): grouped heads run on the matrix-core family, one query head per
 # kv head on the vector family
-HEADS = [(8, 4, 128), (8, 8, 128), (8, 2, 256)]
+HEADS = [(8, 4, 128), (8, 8, 128), (8, 2, 256), (16, 1, 128)]
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
 @pytest.mark.parametrize("qdt", [torch.float16, torch.bfloat16])
 @pytest.mark.parametrize("per_head", [False, True])
 @pytest.mark.parametrize("partition", [0, 64])
-@pytest.mark.parametrize("heads", HEADS, ids=["gqa_d128", "mha_d128", "gqa_d256"])
+@pytest.mark.parametrize("heads", HEADS, ids=["gqa_d128", "mha_d128", "gqa_d256", "g16_d128"])
 def test_attention_8bit_caches(ops, fmt, qdt, per_head, partition, heads):
     H, KVH, d = heads
     bs = 16
