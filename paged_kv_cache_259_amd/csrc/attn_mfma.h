@@ -41,6 +41,10 @@
 
 namespace pkv {
 
+// How far (log2 domain) a head's running max may rise above the reference the
+// weights are taken against before the accumulators are rescaled.
+constexpr float kLazyRescale = 8.f;
+
 template <class T> struct MfmaOp;
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
@@ -155,7 +159,7 @@ struct MfmaAttention {
   };
 
   struct State {
-    float m;                 // running max of head c16 (same in all four row groups)
+    float m;                 // reference max of head c16 (same in all four row groups; within 2^8 of the running max)
     float lsum;              // this lane's share of the running exp-sum of head c16
     f32x4_t O[ND];           // O[dt]: lane l holds O[head l%16][dim 16 dt + 4(l/16) + r], r = 0..3
     __device__ void init() {
@@ -224,18 +228,26 @@ struct MfmaAttention {
         }
       }
     }
-    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));   // finite: every block has a real token
     mx = fmaxf(mx, swz_xor16(mx));
     mx = fmaxf(mx, xor32(mx));
-    const float mn = fmaxf(st.m, mx);                   // finite: every block has a real token
-    const float alpha = exp2_fast(st.m - mn);
+    // The reference max st.m moves only when a head's block max exceeds it by
+    // more than kLazyRescale (log2 domain): the weights stay below 2^kLazyRescale,
+    // and the accumulators are rescaled on few blocks (a wave-uniform branch)
+    // instead of on every block.  The softmax does not depend on the reference.
+    const bool grow = mx > st.m + kLazyRescale;         // always on the first block (st.m = -inf)
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float mn = grow ? mx : st.m;
+      const float alpha = exp2_fast(st.m - mn);         // 0 on the first block, 1 for heads that did not grow
+      st.lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) st.O[dt] *= alpha;
+      st.m = mn;
+    }
     float pr[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) pr[r] = exp2_fast(s[r] - mn);
-    st.lsum = st.lsum * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-    st.m = mn;
-#pragma unroll
-    for (int dt = 0; dt < ND; ++dt) st.O[dt] *= alpha;
+    for (int r = 0; r < 4; ++r) pr[r] = exp2_fast(s[r] - st.m);
+    st.lsum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
     // PV on 16x16x16 MFMAs.  B = P^T: the contraction index of lane group g4 is
     // tokens 4 g4 .. +3, exactly the lane's four weights; P enters as a 16-bit
     // part and the 16-bit rounding of what it left out, so the product keeps
