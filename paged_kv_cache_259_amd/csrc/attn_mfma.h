@@ -237,8 +237,8 @@ struct MfmaAttention {
     // instead of on every block.  The softmax does not depend on the reference.
     const bool grow = mx > st.m + kLazyRescale;         // always on the first block (st.m = -inf)
     if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float alpha = grow ? exp2_fast(st.m - mx) : 1.f;   // 0 on the first block
       const float mn = grow ? mx : st.m;
-      const float alpha = exp2_fast(st.m - mn);         // 0 on the first block, 1 for heads that did not grow
       st.lsum *= alpha;
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt) st.O[dt] *= alpha;

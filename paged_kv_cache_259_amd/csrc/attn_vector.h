@@ -28,6 +28,10 @@
 
 namespace pkv {
 
+// How far (log2 domain) a row group's running max may rise above the reference
+// the weights are taken against before the accumulator is rescaled.
+constexpr float kLazyRescaleVec = 8.f;
+
 template <class QT, class KT, int VEC>
 struct QFrag {
   // fp32 query slice, pre-multiplied by nothing (the scale is applied to the
@@ -150,20 +154,30 @@ struct VectorAttention {
     float mb = s[0];
 #pragma unroll
     for (int i = 1; i < NI; ++i) mb = fmaxf(mb, s[i]);
-    const float mn = fmaxf(st.m, mb);
-    const bool live = mn != -__builtin_inff();              // false only for a row with no token yet
-    const float alpha = live ? exp2_fast(st.m - mn) : 1.f;
+    // The reference max st.m moves only when the row group's max exceeds it by
+    // more than kLazyRescaleVec (log2 domain), so the accumulator is rescaled on
+    // few blocks (a wave-uniform branch); the weights stay below 2^kLazyRescaleVec
+    // and the softmax does not depend on the reference.
+    const bool grow = mb > st.m + kLazyRescaleVec;        // a row with no token yet: mb = -inf, no growth
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      // 0 on a row group's first real block; rows that did not grow keep their
+      // scale (and a row with no token yet, m = -inf, must not form -inf - -inf)
+      const float alpha = grow ? exp2_fast(st.m - mb) : 1.f;
+      const float mn = grow ? mb : st.m;
+      st.l *= alpha;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) st.acc[e] *= alpha;
+      st.m = mn;
+    }
+    const bool live = st.m != -__builtin_inff();          // false only for a row with no token yet
     float pr[NI];
     float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      pr[i] = live ? exp2_fast(s[i] - mn) : 0.f;
+      pr[i] = live ? exp2_fast(s[i] - st.m) : 0.f;
       psum += pr[i];
     }
-    st.l = st.l * alpha + psum;
-    st.m = mn;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) st.acc[e] *= alpha;
+    st.l += psum;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       float vf[VEC];
