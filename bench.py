@@ -54,7 +54,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic.json")
 # retires that kind's recorded HBM traffic)
 KERNEL_SOURCES = {
     "decode": ["attn_vector.h", "attn_vector.hip", "attn_mfma.h", "attn_mfma.hip", "attn_append.hip",
-               "attn_reduce.hip", "pkv_device.h", "pkv_api.hip"],
+               "attn_reduce.hip", "attn_shared.hip", "pkv_device.h", "pkv_api.hip"],
     "prefill": ["prefill_mfma.hip", "pkv_device.h", "pkv_api.hip"],
 }
 
@@ -446,6 +446,12 @@ def main_shared_prefix(args, w):
     paged_attention_decode_append launch that writes each sample's new token and
     attends.  Repeating the step rewrites the same bytes, so every timed step
     does the same work.
+
+    The attention of the step is paged_attention_decode_shared: the samples of
+    a prompt form one group (BlockManager.shared_groups), and each block the
+    group shares is read once for all of them.  The same step through
+    paged_attention_decode_append (every sample reads its whole context) is
+    reported beside it.
     """
     import torch
     from paged_kv_cache_259_amd import ops, synth
@@ -483,16 +489,24 @@ def main_shared_prefix(args, w):
                                              max_ctx, 0, qd, kvd)
     workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
+    g_off, g_mem, g_shared = bm.shared_groups(seqs, 16 // (w.num_heads // w.num_kv_heads))
+    g_max = int(np.diff(g_off).max())
+    groups = [torch.from_numpy(a).to(dev) for a in (g_off, g_mem, g_shared)]
 
     def cow():
         if len(pairs):
             ops.copy_blocks(kc, vc, pair_t, stream=stream)
 
-    def attend():
+    def attend_each():                   # every sample reads its whole context
         ops.paged_attention_decode_append(out, q, kc, vc, k_new, v_new, slot_t, tables, ctx, w.softmax_scale, max_ctx,
                                           k_scale=ks, v_scale=vs, workspace=workspace, seq_order=order, stream=stream)
 
-    warm = warm_up(lambda: (cow(), attend()), args.warmup)
+    def attend():                        # shared blocks read once per group
+        ops.paged_attention_decode_shared(out, q, kc, vc, tables, ctx, *groups, g_max, w.softmax_scale, max_ctx,
+                                          key=k_new, value=v_new, slot_mapping=slot_t, k_scale=ks, v_scale=vs,
+                                          stream=stream)
+
+    warm = warm_up(lambda: (cow(), attend(), attend_each()), args.warmup)
     K = args.steps
 
     def timed(fn):
@@ -506,6 +520,7 @@ def main_shared_prefix(args, w):
 
     t_step = timed(lambda: (cow(), attend()))
     t_attn = timed(attend)
+    t_each = timed(attend_each)
     t_cow = timed(cow) if len(pairs) else None
     step_ms, attn_ms = float(np.mean(t_step)), float(np.mean(t_attn))
     if args.calibrate_copy:
@@ -536,14 +551,18 @@ def main_shared_prefix(args, w):
         "unique_gbps": round(kv_unique / (step_ms * 1e-3) / 1e9, 1),
         "sharing": {"logical_blocks": res["logical_blocks"], "unique_blocks": res["unique_blocks"],
                     "cow_pairs_during_generation": res["cow_pairs"], "cow_pairs_this_step": len(pairs),
+                    "groups": len(g_shared), "max_group_size": g_max,
+                    "shared_blocks_per_group": int(np.median(g_shared)) if len(g_shared) else 0,
                     "setup_s": round(t_setup, 2)},
         "components": {"copy_blocks_us": None if t_cow is None else round(float(np.mean(t_cow)) * 1e3, 2),
-                       "paged_attention_decode_append_us": round(attn_ms * 1e3, 2),
-                       "paged_attention_decode_append_median_us": round(float(np.median(t_attn)) * 1e3, 2)},
+                       "paged_attention_decode_shared_us": round(attn_ms * 1e3, 2),
+                       "paged_attention_decode_shared_median_us": round(float(np.median(t_attn)) * 1e3, 2),
+                       "paged_attention_decode_append_us": round(float(np.mean(t_each)) * 1e3, 2),
+                       "paged_attention_decode_append_median_us": round(float(np.median(t_each)) * 1e3, 2)},
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_attention_decode_append over fp8 pools (achieved counts each physical block once; "
-                      "the logical rate, each sample reading its whole context, is value)",
+            "kernel": "paged_attention_decode_shared with append over fp8 pools (achieved counts each physical block "
+                      "once; the logical rate, each sample reading its whole context, is value)",
             "achieved": round((unique_alg + append_bytes) / (attn_ms * 1e-3) / 1e9, 1),
             "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round((unique_alg + append_bytes) / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),

@@ -203,6 +203,51 @@ int pkv_paged_attention_decode_append(void* out, const void* q, void* k_cache, v
                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pkv_paged_attention_decode_shared -- the decode of pkv_paged_attention_decode
+ * (or, with key != NULL, of pkv_paged_attention_decode_append) for groups of
+ * sequences whose block tables start with the same physical blocks, as the
+ * samples forked from one prompt do ([KVpag] "Como funciona": forks share
+ * blocks through reference counts; [PA/sharing] "Chia sẻ block giữa các
+ * chuỗi": parallel samples share the prompt's blocks).  The outputs are the
+ * same attention (up to rounding order); a shared block is read once for all
+ * the members of its group instead of once per member.
+ *
+ * Groups: group g's members are group_members[group_offsets[g] ..
+ * group_offsets[g+1]) (device int32 arrays; group_offsets has num_groups + 1
+ * entries, each group at most max_group_size members).  The first
+ * group_shared_blocks[g] entries of every member's table must name the same
+ * physical blocks; the kernel reads them through the first member's table.
+ * Every sequence must belong to exactly one group (a sequence sharing nothing
+ * is a group of one, with 0 shared blocks); a sequence in no group gets no
+ * output row, one in two groups an unspecified one.  The kernel lowers the
+ * shared count to keep it below every member's newest token: shared blocks are
+ * always full, and a member's last block is always read as its own.  Out-of-
+ * range offsets and members are clamped or skipped.
+ *
+ * One workgroup per (group, kv head); the group's query rows for that kv head
+ * are the columns of the matrix-core tile, so max_group_size * G <= 16
+ * (G = num_heads / num_kv_heads, 1 for multi-head attention).
+ * Other arguments as pkv_paged_attention_decode_append (key, value,
+ * slot_mapping may all be NULL for a plain decode; k_cache / v_cache are
+ * written only when key is given).  No workspace, no split context: a group's
+ * work stays in its workgroups.
+ * Supported: f16 or bf16 q over a cache of q's type or either 8-bit format,
+ *   head_dim 128 or 256, block_size 16.
+ */
+int pkv_paged_attention_decode_shared(void* out, const void* q, void* k_cache, void* v_cache,
+                                      const void* key, const void* value, const int64_t* slot_mapping,
+                                      const int32_t* block_tables, int max_blocks_per_seq,
+                                      const int32_t* context_lens,
+                                      const int32_t* group_offsets, const int32_t* group_members,
+                                      const int32_t* group_shared_blocks, int num_groups,
+                                      int max_group_size,
+                                      int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                                      int block_size, int num_blocks, int max_context_len,
+                                      float scale, float k_scale, float v_scale,
+                                      const float* k_scales, const float* v_scales,
+                                      int q_dtype, int kv_dtype, void* stream);
+
+/*
  * pkv_reshape_and_cache -- write each new token's key and value into the pool
  * slot the host chose for it ([PA/paging] example: the token at position pos
  * goes to block table[pos / bs], offset pos % bs).

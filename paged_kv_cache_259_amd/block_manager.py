@@ -307,6 +307,54 @@ class BlockManager:
         order = sorted(range(len(seqs)), key=lambda i: (-group_len[first[i]], first[i], -int(lens[i]), i))
         return np.array(order, dtype=np.int32)
 
+    def shared_groups(self, seqs, max_group_size):
+        """Groups for the shared-block decode: positions of ``seqs`` whose tables
+        start with the same physical block, in chunks of at most ``max_group_size``.
+
+        Returns int32 arrays ``(offsets [G+1], members [len(seqs)], shared [G])``:
+        group g is ``members[offsets[g]:offsets[g+1]]`` and its first ``shared[g]``
+        table entries are the same physical blocks in every member (the longest
+        common prefix of their tables, lowered so that no member's newest token
+        falls inside it).  A sequence that shares nothing is a group of one with
+        0 shared blocks.  Groups are listed by decreasing work (blocks the
+        group's workgroups read), longest first, like ``longest_first``.
+        """
+        if max_group_size < 1:
+            raise ValueError("max_group_size must be at least 1")
+        bs = self.block_size
+        buckets = {}
+        for i, s in enumerate(seqs):
+            t = self.tables[s]
+            key = t[0] if len(t) else ("empty", i)
+            buckets.setdefault(key, []).append(i)
+        groups = []
+        for members in buckets.values():
+            # similar lengths together, so a chunk's members finish their own blocks at similar times
+            members = sorted(members, key=lambda i: (-self.lengths[seqs[i]], i))
+            for c in range(0, len(members), max_group_size):
+                chunk = members[c:c + max_group_size]
+                tabs = [self.tables[seqs[i]] for i in chunk]
+                lcp = min(len(t) for t in tabs)
+                for j in range(lcp):
+                    if any(t[j] != tabs[0][j] for t in tabs[1:]):
+                        lcp = j
+                        break
+                cap = min(max(self.lengths[seqs[i]] - 1, 0) // bs for i in chunk)
+                shared = min(lcp, cap) if len(chunk) > 1 else 0
+                work = shared + sum(len(t) - shared for t in tabs)
+                groups.append((work, chunk, shared))
+        groups.sort(key=lambda g: (-g[0], g[1][0]))
+        offsets = np.zeros(len(groups) + 1, dtype=np.int32)
+        members = np.zeros(len(seqs), dtype=np.int32)
+        shared = np.zeros(len(groups), dtype=np.int32)
+        pos = 0
+        for g, (_, chunk, sh) in enumerate(groups):
+            members[pos:pos + len(chunk)] = chunk
+            pos += len(chunk)
+            offsets[g + 1] = pos
+            shared[g] = sh
+        return offsets, members, shared
+
     def slot(self, seq, pos):
         t = self.tables[seq]
         return t[pos // self.block_size] * self.block_size + pos % self.block_size

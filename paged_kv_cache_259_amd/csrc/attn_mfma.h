@@ -201,8 +201,11 @@ struct MfmaAttention {
     }
   }
 
+  // MASK: only the lanes' columns with col_on take part in this block (the
+  // others keep their state: no score, no weight, no rescale).
+  template <bool MASK = false>
   __device__ static void consume(const AttnParams& p, const uint4* qop, Tiles& t, int valid, int c16, int g4,
-                                 uint16_t* vt, State& st) {
+                                 uint16_t* vt, State& st, bool col_on = true) {
     if (!t.ok) return;                                  // wave-uniform
     f32x4_t S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -217,6 +220,10 @@ struct MfmaAttention {
     float s[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) s[r] = S[r] * p.qk_scale;
+    if constexpr (MASK) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s[r] = col_on ? s[r] : -__builtin_inff();
+    }
     if (valid < BS) {                                   // wave-uniform: the last, partial block
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -229,6 +236,7 @@ struct MfmaAttention {
       }
     }
     float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));   // finite: every block has a real token
+                                                                // (-inf in a masked column, which never grows)
     mx = fmaxf(mx, swz_xor16(mx));
     mx = fmaxf(mx, xor32(mx));
     // The reference max st.m moves only when a head's block max exceeds it by
@@ -247,6 +255,10 @@ struct MfmaAttention {
     float pr[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) pr[r] = exp2_fast(s[r] - st.m);
+    if constexpr (MASK) {                               // a masked column may have no reference yet (-inf - -inf)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pr[r] = col_on ? pr[r] : 0.f;
+    }
     st.lsum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
     // PV on 16x16x16 MFMAs.  B = P^T: the contraction index of lane group g4 is
     // tokens 4 g4 .. +3, exactly the lane's four weights; P enters as a 16-bit
@@ -275,27 +287,37 @@ struct MfmaAttention {
     }
   }
 
-  // Blocks [j0, j1) of sequence `seq` for the query heads of kv head `kvh`;
-  // wave w takes blocks j0 + w, j0 + w + NW, ...  With PIPE the next block's
-  // tiles are in flight while the current one is consumed.  Block ids come 64
-  // at a time from one VGPR (lane t holds the t-th id) through readlane.
+  // B operand of QK for column c16: Q[row][k_dim(c, g4) .. +8] of the query
+  // row at element offset `qrow` (q is [rows][D]); zero for a padding column.
+  __device__ static void load_q(const AttnParams& p, bool real, size_t qrow, int g4, uint4* qop) {
+    const uint16_t* qr = reinterpret_cast<const uint16_t*>(p.q) + (real ? qrow : 0);
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      qop[c] = real ? *reinterpret_cast<const uint4*>(qr + k_dim(c, g4)) : make_uint4(0u, 0u, 0u, 0u);
+  }
+
+  // Blocks [j0, j1) of sequence `seq` for the query heads of kv head `kvh`.
   __device__ static void attend(const AttnParams& p, int seq, int kvh, int ctx, int j0, int j1, int w, int c16,
                                 int g4, uint16_t* vt, State& st) {
+    if (j0 + w >= j1) return;                           // wave-uniform: no block for this wave
+    const int G = p.group;
+    uint4 qop[NC];
+    load_q(p, c16 < G, ((size_t)seq * p.num_heads + (size_t)kvh * G + c16) * D, g4, qop);
+    walk<false>(p, p.block_tables + (size_t)seq * p.max_blocks_per_seq, kvh, ctx, j0, j1, w, c16, g4, vt, st, qop,
+                true);
+  }
+
+  // Blocks [j0, j1) of the table `table` (a context of ctx tokens) under the
+  // query operand qop; wave w takes blocks j0 + w, j0 + w + NW, ...  With PIPE
+  // the next block's tiles are in flight while the current one is consumed.
+  // Block ids come 64 at a time from one VGPR (lane t holds the t-th id)
+  // through readlane.  MASK / col_on: see consume.
+  template <bool MASK>
+  __device__ static void walk(const AttnParams& p, const int32_t* table, int kvh, int ctx, int j0, int j1, int w,
+                              int c16, int g4, uint16_t* vt, State& st, const uint4* qop, bool col_on) {
     const int first = j0 + w;
     const int n = first < j1 ? (j1 - first + NW - 1) / NW : 0;
     if (n == 0) return;                                 // wave-uniform
-    const int G = p.group;
-    // B operand of QK: Q[head c16][32c + 8 g4 .. +8]; zero for padding heads.
-    uint4 qop[NC];
-    {
-      const bool real = c16 < G;
-      const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) +
-                             ((size_t)seq * p.num_heads + (size_t)kvh * G + (real ? c16 : 0)) * D;
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-        qop[c] = real ? *reinterpret_cast<const uint4*>(qrow + k_dim(c, g4)) : make_uint4(0u, 0u, 0u, 0u);
-    }
-    const int32_t* table = p.block_tables + (size_t)seq * p.max_blocks_per_seq;
     const char* kbase = reinterpret_cast<const char*>(p.k_cache) + (size_t)kvh * TILE_BYTES + c16 * ROW_BYTES +
                         (KV8 ? g4 * (D / 4) : g4 * 16);
     const char* vbase =
@@ -327,32 +349,31 @@ struct MfmaAttention {
       Tiles b;
       for (int i = 0; i < n; i += 2) {
         if (i + 1 < n) issue(p, kbase, vbase, block_stride, id_of(i + 1), valid_of(i + 1), c16, g4, b);
-        consume(p, qop, a, valid_of(i), c16, g4, vt, st);
+        consume<MASK>(p, qop, a, valid_of(i), c16, g4, vt, st, col_on);
         if (i + 1 < n) {
           if (i + 2 < n) issue(p, kbase, vbase, block_stride, id_of(i + 2), valid_of(i + 2), c16, g4, a);
-          consume(p, qop, b, valid_of(i + 1), c16, g4, vt, st);
+          consume<MASK>(p, qop, b, valid_of(i + 1), c16, g4, vt, st, col_on);
         }
       }
     } else {
       for (int i = 0; i < n; ++i) {
         if (i > 0) issue(p, kbase, vbase, block_stride, id_of(i), valid_of(i), c16, g4, a);
-        consume(p, qop, a, valid_of(i), c16, g4, vt, st);
+        consume<MASK>(p, qop, a, valid_of(i), c16, g4, vt, st, col_on);
       }
     }
   }
 
-  // Merge the waves through LDS (only the G real heads) and write the normalised
-  // outputs (prow_base < 0) or the fp32 summary row prow_base + h * prow_stride
-  // of the workspace for head h of the group.  Called by every thread; ends
-  // with a barrier.
-  __device__ static void finish(const AttnParams& p, State& st, Smem& sm, int seq, int kvh, int64_t prow_base,
-                                int64_t prow_stride, int tid, int w, int c16, int g4) {
-    const int G = p.group;
+  // Merge the waves' states of columns 0 .. ncols-1 through LDS and hand each
+  // (column h, dim d) to store(h, d, M, L, o): M the merged max (log2 domain),
+  // L the merged exp-sum, o the unnormalised output.  Called by every thread;
+  // ends with a barrier.
+  template <class Store>
+  __device__ static void merge(State& st, Smem& sm, int ncols, int tid, int w, int c16, int g4, Store store) {
     float lsum = st.lsum;
     lsum += swz_xor16(lsum);
     lsum += xor32(lsum);
     __syncthreads();                                    // every wave is done with its V tile (o shares it)
-    if (c16 < G) {
+    if (c16 < ncols) {
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
@@ -360,7 +381,7 @@ struct MfmaAttention {
       if (g4 == 0) { sm.m[w][c16] = st.m; sm.l[w][c16] = lsum; }
     }
     __syncthreads();
-    for (int idx = tid; idx < G * D; idx += NW * 64) {
+    for (int idx = tid; idx < ncols * D; idx += NW * 64) {
       const int h = idx / D;
       const int d = idx - h * D;
       float M = -__builtin_inff();
@@ -373,6 +394,19 @@ struct MfmaAttention {
         Lsum += wt * sm.l[i][h];
         o += wt * sm.o[i][h * RS + d];
       }
+      store(h, d, M, Lsum, o);
+    }
+    __syncthreads();
+  }
+
+  // Merge the waves (only the G real heads) and write the normalised outputs
+  // (prow_base < 0) or the fp32 summary row prow_base + h * prow_stride of the
+  // workspace for head h of the group.  Called by every thread; ends with a
+  // barrier.
+  __device__ static void finish(const AttnParams& p, State& st, Smem& sm, int seq, int kvh, int64_t prow_base,
+                                int64_t prow_stride, int tid, int w, int c16, int g4) {
+    const int G = p.group;
+    merge(st, sm, G, tid, w, c16, g4, [&](int h, int d, float M, float Lsum, float o) {
       if (prow_base < 0) {
         const size_t sh = (size_t)seq * p.num_heads + (size_t)kvh * G + h;
         store_elem<T>(p.out, sh * D + d, Lsum > 0.f ? o * (p.v_scale / Lsum) : 0.f);
@@ -381,8 +415,7 @@ struct MfmaAttention {
         p.ws_o[(size_t)prow * D + d] = o * p.v_scale;
         if (d == 0) { p.ws_m[prow] = M; p.ws_l[prow] = Lsum; }
       }
-    }
-    __syncthreads();
+    });
   }
 };
 

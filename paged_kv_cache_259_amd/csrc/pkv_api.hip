@@ -322,6 +322,74 @@ int pkv_paged_attention_decode_append(void* out, const void* q, void* k_cache, v
                      kv_dtype, partition_size, workspace, workspace_bytes, stream);
 }
 
+int pkv_paged_attention_decode_shared(void* out, const void* q, void* k_cache, void* v_cache, const void* key,
+                                      const void* value, const int64_t* slot_mapping, const int32_t* block_tables,
+                                      int max_blocks_per_seq, const int32_t* context_lens,
+                                      const int32_t* group_offsets, const int32_t* group_members,
+                                      const int32_t* group_shared_blocks, int num_groups, int max_group_size,
+                                      int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+                                      int num_blocks, int max_context_len, float scale, float k_scale, float v_scale,
+                                      const float* k_scales, const float* v_scales, int q_dtype, int kv_dtype,
+                                      void* stream) {
+  if (num_seqs < 0 || num_groups < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      max_context_len < 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || max_group_size <= 0)
+    return PKV_ERR_BAD_SIZE;
+  if (num_heads % num_kv_heads != 0) return PKV_ERR_HEAD_GROUPING;
+  const int group = num_heads / num_kv_heads;
+  if ((long long)max_group_size * group > 16) return PKV_ERR_BAD_SIZE;   // one MFMA tile of columns
+  if (!pkv::shared_supported(q_dtype, kv_dtype, head_dim, block_size)) return PKV_ERR_UNSUPPORTED;
+  if (!isfinite(scale)) return PKV_ERR_BAD_SIZE;
+  const bool fp8 = kv_dtype == PKV_FP8_E4M3 || kv_dtype == PKV_FP8_E5M2;
+  if (fp8 && !((k_scales || pkv::good_scale(k_scale)) && (v_scales || pkv::good_scale(v_scale)))) return PKV_ERR_SCALE;
+  const long long wgs = (long long)num_groups * num_kv_heads;
+  if (wgs > 2147483647LL) return PKV_ERR_BAD_SIZE;
+  if (num_seqs == 0 || num_groups == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !group_offsets || !group_members ||
+      !group_shared_blocks)
+    return PKV_ERR_NULL_POINTER;
+  if (!pkv::aligned16(out) || !pkv::aligned16(q) || !pkv::aligned16(k_cache) || !pkv::aligned16(v_cache))
+    return PKV_ERR_UNSUPPORTED;
+  if (key) {
+    if (!value || !slot_mapping) return PKV_ERR_NULL_POINTER;
+    if (!pkv::aligned16(key) || !pkv::aligned16(value)) return PKV_ERR_UNSUPPORTED;
+  }
+  pkv::AttnParams p{};
+  p.out = out;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.num_seqs = num_seqs;
+  p.num_heads = num_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = group;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.num_partitions = 1;
+  const long long cap_table = (long long)max_blocks_per_seq * block_size;
+  const long long cap = ((long long)max_context_len + block_size - 1) / block_size * block_size;
+  const long long c = cap < cap_table ? cap : cap_table;
+  p.ctx_cap = (int)(c < 2147483647LL ? c : 2147483647LL);
+  p.new_k = key;
+  p.new_v = value;
+  p.slot_mapping = key ? slot_mapping : nullptr;
+  p.enc_k_scale = k_scale;
+  p.enc_v_scale = v_scale;
+  p.k_scales = fp8 ? k_scales : nullptr;
+  p.v_scales = fp8 ? v_scales : nullptr;
+  p.qk_scale = scale * kLog2e * (fp8 && !k_scales ? k_scale : 1.f);
+  p.v_scale = fp8 && !v_scales ? v_scale : 1.f;
+  p.total_wgs = (uint32_t)wgs;
+  p.grp_off = group_offsets;
+  p.grp_mem = group_members;
+  p.grp_shared = group_shared_blocks;
+  p.grp_max = max_group_size;
+  (void)hipGetLastError();
+  return pkv::launch_status(pkv::launch_attention_shared(p, q_dtype, kv_dtype, head_dim, key != nullptr,
+                                                         reinterpret_cast<hipStream_t>(stream)));
+}
+
 int pkv_paged_prefill_attention(void* out, const void* q, const void* k_cache, const void* v_cache,
                                 const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
                                 const int32_t* query_start_loc, int num_seqs, int num_tokens, int num_heads,

@@ -432,6 +432,13 @@ struct AttnParams {
   float v_scale;
   uint32_t total_wgs;
   uint32_t xcd_chunk;       // see xcd_remap
+  // shared-block decode only (attn_shared.hip): group g's members are
+  // grp_mem[grp_off[g] .. grp_off[g+1]) (at most grp_max of them); the first
+  // grp_shared[g] blocks of their tables are the same physical blocks.
+  const int32_t* grp_off;
+  const int32_t* grp_mem;
+  const int32_t* grp_shared;
+  int grp_max;
 };
 
 // Decode with append: the wave that will load sequence seq's last block (wave

@@ -34,6 +34,10 @@ hipError_t launch_attention_vector_append(const AttnParams& p, int q_dtype, int 
                                           int block_size, hipStream_t stream);
 hipError_t launch_attention_mfma_append(const AttnParams& p, int q_dtype, int kv_dtype, int head_dim,
                                         hipStream_t stream);
+// decode over groups of sequences sharing leading blocks (attn_shared.hip)
+bool shared_supported(int q_dtype, int kv_dtype, int head_dim, int block_size);
+hipError_t launch_attention_shared(const AttnParams& p, int q_dtype, int kv_dtype, int head_dim, bool append,
+                                   hipStream_t stream);
 hipError_t launch_attention_reduce(const ReduceParams& p, int out_dtype, int head_dim, hipStream_t stream);
 
 bool prefill_supported(int q_dtype, int kv_dtype, int head_dim, int block_size);

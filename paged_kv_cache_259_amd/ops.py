@@ -47,6 +47,10 @@ _lib.pkv_paged_attention_decode_append.restype = _c_int
 _lib.pkv_paged_attention_decode_append.argtypes = (
     [_vp] * 7 + [_vp, _c_int, _vp, _vp] + [_c_int] * 7 + [_c_float] * 3 + [_vp, _vp] + [_c_int] * 3
     + [_vp, _c_size, _vp])
+_lib.pkv_paged_attention_decode_shared.restype = _c_int
+_lib.pkv_paged_attention_decode_shared.argtypes = (
+    [_vp] * 7 + [_vp, _c_int, _vp] + [_vp] * 3 + [_c_int] * 2 + [_c_int] * 7 + [_c_float] * 3 + [_vp, _vp]
+    + [_c_int] * 2 + [_vp])
 _lib.pkv_reshape_and_cache.restype = _c_int
 _lib.pkv_reshape_and_cache.argtypes = [_vp] * 5 + [_c_int] * 7 + [_c_float] * 2 + [_vp, _vp, _vp]
 _lib.pkv_copy_blocks.restype = _c_int
@@ -59,7 +63,7 @@ _lib.pkv_swap_blocks.argtypes = [_vp, _vp, _c_int, _vp, _vp, _c_int, _vp] + [_c_
 EXPORTED_SYMBOLS = (
     "pkv_status_string", "pkv_version", "pkv_attention_plan", "pkv_attention_workspace_bytes",
     "pkv_paged_attention_decode", "pkv_reshape_and_cache", "pkv_copy_blocks", "pkv_swap_blocks",
-    "pkv_paged_prefill_attention", "pkv_paged_attention_decode_append",
+    "pkv_paged_prefill_attention", "pkv_paged_attention_decode_append", "pkv_paged_attention_decode_shared",
 )
 
 
@@ -242,6 +246,49 @@ def paged_attention_decode_append(out, q, k_cache, v_cache, key, value, slot_map
         NB if num_blocks is None else num_blocks, max_context_len, float(scale), float(k_scale), float(v_scale),
         _ptr(_head_scales(k_scales, KVH, k_cache.device)), _ptr(_head_scales(v_scales, KVH, k_cache.device)),
         qd, kvd, partition_size, ws_ptr, ws_bytes, _stream(stream)), "pkv_paged_attention_decode_append")
+    return out
+
+
+def paged_attention_decode_shared(out, q, k_cache, v_cache, block_tables, context_lens, group_offsets,
+                                  group_members, group_shared_blocks, max_group_size, scale, max_context_len,
+                                  key=None, value=None, slot_mapping=None, k_scale=1.0, v_scale=1.0, num_blocks=None,
+                                  k_scales=None, v_scales=None, stream=None):
+    """Decode (with append when key/value/slot_mapping are given) over groups of sequences whose tables start
+    with the same physical blocks; a shared block is read once per group.  group_offsets int32 [G+1],
+    group_members int32 [S], group_shared_blocks int32 [G] (see BlockManager.shared_groups)."""
+    S, H, d = q.shape
+    NB, KVH, bs, d2 = k_cache.shape
+    if d2 != d or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch between q/out and the pools")
+    if out.dtype != q.dtype:
+        raise TypeError("out must have q's dtype")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables must be [S, maxblk] and context_lens [S]")
+    G = group_shared_blocks.shape[0]
+    for name, t, n in (("group_offsets", group_offsets, G + 1), ("group_members", group_members, S),
+                       ("group_shared_blocks", group_shared_blocks, G)):
+        if t.dtype != torch.int32 or t.shape != (n,) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 [{n}] tensor")
+    append = key is not None
+    if append:
+        if tuple(key.shape) != (S, KVH, d) or tuple(value.shape) != (S, KVH, d):
+            raise ValueError("key/value must be [num_seqs, num_kv_heads, head_dim]")
+        if key.dtype != q.dtype or value.dtype != q.dtype:
+            raise TypeError("key/value must have q's dtype")
+        if slot_mapping is None or slot_mapping.dtype != torch.int64 or slot_mapping.shape != (S,):
+            raise TypeError("slot_mapping must be int64 [num_seqs]")
+    for t in (out, q, k_cache, v_cache, block_tables, context_lens) + ((key, value, slot_mapping) if append else ()):
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    _check(_lib.pkv_paged_attention_decode_shared(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(key), _ptr(value), _ptr(slot_mapping),
+        _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), _ptr(group_offsets), _ptr(group_members),
+        _ptr(group_shared_blocks), G, int(max_group_size), S, H, KVH, d, bs,
+        NB if num_blocks is None else num_blocks, int(max_context_len), float(scale), float(k_scale), float(v_scale),
+        _ptr(_head_scales(k_scales, KVH, k_cache.device)), _ptr(_head_scales(v_scales, KVH, k_cache.device)),
+        dtype_code(q.dtype), dtype_code(k_cache.dtype), _stream(stream)), "pkv_paged_attention_decode_shared")
     return out
 
 

@@ -12,7 +12,8 @@
         attention kernels' sources, so bench.py reports it only while the
         kernels are unchanged.  The timed call of a decode workload is decode
         with append (the attn_*_append_kernel launch, plus the split-context
-        reduce when planned); the plain decode kernels of the same run are
+        reduce when planned; for the shared-prefix workload the shared-block
+        decode with append); the other decode kernels of the same run are
         listed but not counted.  For a prefill workload it is the prefill kernel.
 """
 
@@ -62,10 +63,13 @@ def _counter(d, counter):
     return {k: sum(v) / len(v) for k, v in agg.items()}
 
 
-def _in_timed_call(kernel):
-    """Kernels of the call bench.py times: decode with append (+ its reduce) or prefill."""
+def _in_timed_call(kernel, workload):
+    """Kernels of the call bench.py times: decode with append (+ its reduce), the
+    shared-block decode with append (shared-prefix workload) or prefill."""
     if kernel.startswith("prefill_"):
         return True
+    if workload.startswith("shared_prefix"):
+        return kernel.startswith("attn_shared_append")
     return "_append_" in kernel or kernel.startswith(("attn_reduce", "attn_slice_finish"))
 
 
@@ -91,13 +95,13 @@ def counters(fetch_dir, write_dir, workload, n_pairs, out=sys.stdout):
     total_r = total_w = 0.0
     for k in sorted(k for k in f if k[0].startswith(("attn_", "prefill_"))):
         rb, wb = f[k] * 1024 * fs, wr.get(k, 0.0) * 1024 * ws
-        counted = _in_timed_call(k[0])
+        counted = _in_timed_call(k[0], workload)
         if counted:
             total_r += rb
             total_w += wb
         print(f"{k[0][:58]:58s} grid {k[1]:8d}  FETCH_SIZE {f[k]:12.1f} KiB -> {rb / 1e6:9.2f} MB read;  "
               f"WRITE_SIZE {wr.get(k, 0.0):10.1f} KiB -> {wb / 1e6:7.2f} MB written"
-              f"{'' if counted else '  (plain decode, not the timed call)'}", file=out)
+              f"{'' if counted else '  (not the timed call)'}", file=out)
     print(f"timed call total: {total_r / 1e6:.2f} MB read + {total_w / 1e6:.2f} MB written = "
           f"{(total_r + total_w) / 1e6:.2f} MB", file=out)
     path = os.path.join(ROOT, "profiles", "attention_traffic.json")

@@ -34,7 +34,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_symbols()
-    assert len(names) == 10
+    assert len(names) == 11
     for n in names:
         assert hasattr(lib, n), n
     nm = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
@@ -170,6 +170,28 @@ def test_prefill_host_checks(lib):
     assert call(NB=0) == -2 and call(mq=-1) == -2 and call(maxblk=0) == -2
     assert call(out=None) == -1 and call(tables=None) == -1
     assert call(out=ctypes.c_void_p(0x10008)) == -4             # misaligned output
+
+
+def test_shared_decode_host_checks(lib):
+    f = lib.pkv_paged_attention_decode_shared
+    sc = ctypes.c_float(0.1)
+
+    def call(S=8, G=2, gmax=4, H=8, KVH=8, d=128, bs=16, NB=64, mc=256, qd=1, kvd=1, out=FAKE, key=None, val=None,
+             slots=None, offs=FAKE, ks=1.0, vs=1.0, maxblk=16):
+        return f(out, FAKE, FAKE, FAKE, key, val, slots, FAKE, maxblk, FAKE, offs, FAKE, FAKE, G, gmax, S, H, KVH, d,
+                 bs, NB, mc, sc, ctypes.c_float(ks), ctypes.c_float(vs), None, None, qd, kvd, None)
+
+    assert call(S=0) == 0 and call(G=0) == 0                      # nothing to do
+    assert call(G=-1) == -2 and call(gmax=0) == -2 and call(NB=0) == -2 and call(maxblk=0) == -2
+    assert call(H=6, KVH=4) == -3
+    assert call(gmax=17) == -2                                    # more columns than one MFMA tile
+    assert call(H=16, KVH=4, gmax=5) == -2                        # 5 members x 4 heads > 16
+    assert call(H=16, KVH=4, gmax=4, out=None) == -1              # 4 x 4 fits: reaches the pointer checks
+    assert call(d=64) == -4 and call(bs=8) == -4 and call(qd=0, kvd=0) == -4 and call(qd=1, kvd=2) == -4
+    assert call(kvd=3, ks=0.0) == -8 and call(kvd=4, vs=float("nan")) == -8
+    assert call(out=None) == -1 and call(offs=None) == -1
+    assert call(key=FAKE) == -1                                   # append needs value and slots too
+    assert call(out=ctypes.c_void_p(0x10008)) == -4               # misaligned output
 
 
 def test_missing_library_fails_loudly():

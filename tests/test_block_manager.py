@@ -337,3 +337,48 @@ def test_longest_first_grouped_keeps_forks_together():
     assert tops == sorted(tops, reverse=True)
     # without sharing the grouped order is the plain longest-first order's lengths
     assert np.array_equal(np.sort(lens)[::-1], lens[bm.longest_first(seqs)])
+
+
+def test_shared_groups_cover_each_sequence_once_and_share_only_common_blocks():
+    """Groups for the shared-block decode: forks of one prompt together, in chunks of
+    at most the group size; the shared count is the longest common prefix of the
+    members' tables, kept below every member's newest token; groups longest first."""
+    rng = np.random.default_rng(3)
+    bm = BlockManager(400, 16, free_list=rng.permutation(400))
+    bm.add_sequence("A0", 40)
+    for i in range(1, 6):
+        bm.fork("A0", f"A{i}")
+    for i, extra in enumerate([0, 30, 1, 17, 5, 60]):
+        for _ in range(extra):
+            bm.append_slot(f"A{i}")
+    bm.add_sequence("B0", 31)
+    bm.fork("B0", "B1")
+    bm.append_slot("B1")                                  # copies B's second block
+    bm.append_slot("B0")                                  # B0 now 32 tokens: its newest in block 1
+    bm.add_sequence("C", 10)
+    bm.add_sequence("D", 0)
+    seqs = [f"A{i}" for i in range(6)] + ["B0", "B1", "C", "D"]
+    offs, mem, shared = bm.shared_groups(seqs, 4)
+    assert offs[0] == 0 and offs[-1] == len(seqs) and np.all(np.diff(offs) >= 1) and np.all(np.diff(offs) <= 4)
+    assert sorted(mem.tolist()) == list(range(len(seqs)))
+    works = []
+    for g in range(len(shared)):
+        members = [seqs[i] for i in mem[offs[g]:offs[g + 1]]]
+        tabs = [bm.tables[s] for s in members]
+        lcp = 0
+        while all(len(t) > lcp for t in tabs) and len({t[lcp] for t in tabs}) == 1:
+            lcp += 1
+        cap = min(max(bm.lengths[s] - 1, 0) // 16 for s in members)
+        assert shared[g] == (min(lcp, cap) if len(members) > 1 else 0), (members, lcp, cap)
+        works.append(shared[g] + sum(len(t) - shared[g] for t in tabs))
+        if members[0].startswith("A") and len(members) > 1:
+            assert shared[g] == 2                         # 40-token prompt: two full blocks in common
+        if set(members) == {"B0", "B1"}:
+            assert shared[g] == 1                         # B0's newest token is in block 1
+    assert works == sorted(works, reverse=True)
+    groups = {frozenset(seqs[i] for i in mem[offs[g]:offs[g + 1]]) for g in range(len(shared))}
+    assert frozenset({"C"}) in groups and frozenset({"D"}) in groups
+    a_groups = [m for m in groups if any(s.startswith("A") for s in m)]
+    assert sorted(len(m) for m in a_groups) == [2, 4]     # six samples in chunks of four
+    with pytest.raises(ValueError):
+        bm.shared_groups(seqs, 0)

@@ -123,6 +123,19 @@ def test_shared_prefix_cow_workload(ops):
             cm.append(s, oracle.encode_e4m3(k.float().numpy(), ks), oracle.encode_e4m3(v.float().numpy(), vs))
     bs = w.block_size
     out = res["out"]
+    # the same decode with shared blocks read once per group of samples
+    seqs_all = list(range(w.num_prompts * n))
+    offs, mem, shared = bm.shared_groups(seqs_all, 16)
+    assert len(shared) == w.num_prompts and int(shared.min()) == L // bs   # the prompt's full blocks
+    out_sh = torch.full_like(res["q"], float("nan"))
+    ops.paged_attention_decode_shared(out_sh, res["q"], res["k_cache"], res["v_cache"],
+                                      torch.from_numpy(res["tables"]).to(DEV),
+                                      torch.from_numpy(res["context_lens"]).to(DEV),
+                                      *[torch.from_numpy(a).to(DEV) for a in (offs, mem, shared)],
+                                      int(np.diff(offs).max()), w.softmax_scale, int(res["context_lens"].max()),
+                                      k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out_sh.float()).all()
     for s in tracked:
         nctx = int(res["context_lens"][s])
         assert nctx == L + int(inp.cont_lens[s]) == cm.length(s)
@@ -137,6 +150,7 @@ def test_shared_prefix_cow_workload(ops):
             ref = oracle.attend_one_ref(as_f64(res["q"][s, h]), oracle.dequant_e4m3(cm.keys(s)[:, h], ks),
                                         oracle.dequant_e4m3(cm.values(s)[:, h], vs), w.softmax_scale)
             check_close(as_f64(out[s, h]), ref, TOL["fp8_e4m3"], f"sample {s} head {h}")
+            check_close(as_f64(out_sh[s, h]), ref, TOL["fp8_e4m3"], f"shared-block decode, sample {s} head {h}")
     # copy-on-write isolation: a new sample forks sample 0 and writes; every other output keeps its bits
     x = "extra"
     bm.fork(0, x)
