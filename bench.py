@@ -66,6 +66,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama13b_f16")
     ap.add_argument("--partition", type=int, default=None, help="override the workload's partition size")
+    ap.add_argument("--group-size", type=int, default=0,
+                    help="shared-prefix workload: samples per shared-block group (0: as many as one tile holds)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="bound on the oracle sample's CPU time")
     ap.add_argument("--calibrate-copy", type=int, default=0,
@@ -489,7 +491,7 @@ def main_shared_prefix(args, w):
                                              max_ctx, 0, qd, kvd)
     workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    g_off, g_mem, g_shared = bm.shared_groups(seqs, 16 // (w.num_heads // w.num_kv_heads))
+    g_off, g_mem, g_shared = bm.shared_groups(seqs, args.group_size or 16 // (w.num_heads // w.num_kv_heads))
     g_max = int(np.diff(g_off).max())
     groups = [torch.from_numpy(a).to(dev) for a in (g_off, g_mem, g_shared)]
 

@@ -102,7 +102,10 @@ __device__ __forceinline__ void attn_shared_body(AttnParams p) {
   });
 }
 
-#define PKV_SHARED_WAVES(D) ((D) == 128 ? PKV_MFMA_WAVES_PER_EU_PIPE : 1)
+#ifndef PKV_SHARED_WAVES_PER_EU
+#define PKV_SHARED_WAVES_PER_EU PKV_MFMA_WAVES_PER_EU_PIPE
+#endif
+#define PKV_SHARED_WAVES(D) ((D) == 128 ? PKV_SHARED_WAVES_PER_EU : 1)
 template <class T, class KT, int D, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PKV_SHARED_WAVES(D))))
 void attn_shared_kernel(AttnParams p) {
