@@ -434,7 +434,8 @@ __device__ __forceinline__ void attn_mfma_body(AttnParams p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c16 = lane & 15;   // QK: token row of A / head column of B and of the result
   const int g4 = lane >> 4;    // 0..3
-  const uint32_t L = xcd_remap(blockIdx.x, p.total_wgs, p.xcd_chunk);
+  const uint32_t L = p.head_run_units ? head_runs(blockIdx.x, p.head_run_units)
+                                       : xcd_remap(blockIdx.x, p.total_wgs, p.xcd_chunk);
   typename A::State st;
 
   if (p.num_slices > 0) {

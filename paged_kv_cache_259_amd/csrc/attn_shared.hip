@@ -33,8 +33,10 @@ __device__ __forceinline__ void attn_shared_body(AttnParams p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c16 = lane & 15;
   const int g4 = lane >> 4;
-  const int kvh = (int)(blockIdx.x % (uint32_t)p.num_kv_heads);
-  const int grp = (int)(blockIdx.x / (uint32_t)p.num_kv_heads);
+  const uint32_t L = p.head_run_units ? head_runs(blockIdx.x, p.head_run_units)
+                                       : xcd_remap(blockIdx.x, p.total_wgs, p.xcd_chunk);
+  const int kvh = (int)(L % (uint32_t)p.num_kv_heads);
+  const int grp = (int)(L / (uint32_t)p.num_kv_heads);
   apply_head_scales(p, kvh);
   const int G = p.group;
   const int S = p.num_seqs;

@@ -315,7 +315,8 @@ __device__ __forceinline__ void attn_vector_body(AttnParams p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int row = lane / A::LPR;
   const int col = lane % A::LPR;
-  const uint32_t L = xcd_remap(blockIdx.x, p.total_wgs, p.xcd_chunk);
+  const uint32_t L = p.head_run_units ? head_runs(blockIdx.x, p.head_run_units)
+                                       : xcd_remap(blockIdx.x, p.total_wgs, p.xcd_chunk);
   typename A::State st;
 
   if (p.num_slices > 0) {

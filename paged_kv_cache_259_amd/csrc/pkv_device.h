@@ -236,6 +236,18 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t i, uint32_t n, uint32_t c
   return ((k / chunk) * X + x) * chunk + (k % chunk);
 }
 
+// One-pass launches with U head units per sequence, U a multiple of 8: the
+// logical id of workgroup i, such that the XCD of i (i % 8) takes head units
+// [x U/8, (x+1) U/8) of every sequence.  Neighbouring (block, head) tiles of a
+// block -- one contiguous run in the pool -- are then read by one XCD, and a
+// given head always runs on the same XCD, so forks of a prompt launched
+// together meet their shared blocks in that XCD's L2.  A bijection on each
+// sequence's U ids.
+__device__ __forceinline__ uint32_t head_runs(uint32_t i, uint32_t units) {
+  const uint32_t r = i / units, w = i - r * units;
+  return r * units + (w & 7u) * (units >> 3) + (w >> 3);
+}
+
 // Logical work id -> (sequence, head unit, partition).  Partitions are the
 // slowest dimension.  With PKV_HEAD_FASTEST the head units of one sequence are
 // consecutive, so concurrent workgroups read the neighbouring per-head tiles of
@@ -432,6 +444,7 @@ struct AttnParams {
   float v_scale;
   uint32_t total_wgs;
   uint32_t xcd_chunk;       // see xcd_remap
+  uint32_t head_run_units;  // > 0: one pass, workgroup -> work id through head_runs (xcd_chunk unused)
   // shared-block decode only (attn_shared.hip): group g's members are
   // grp_mem[grp_off[g] .. grp_off[g+1]) (at most grp_max of them); the first
   // grp_shared[g] blocks of their tables are the same physical blocks.
