@@ -267,3 +267,19 @@ def test_sequence_order_only_schedules(ops, kind):
     for order in ("host", np.random.default_rng(17).permutation(len(lens)).astype(np.int32)):
         out = case.run(partition_size=0, seq_order=order)
         assert torch.equal(out.view(torch.int16), base.view(torch.int16))
+
+
+def test_xcd_orders_only_schedule(ops, monkeypatch):
+    """One-pass launches with 40 heads take the head-runs order (each XCD a run of 5
+    neighbouring heads of every sequence); runs of n work ids and the hardware order
+    (PKV_XCD_CHUNK) give identical bits."""
+    lens = tuple(int(x) for x in np.random.default_rng(18).integers(1, 257, size=23))
+    w = W(S=len(lens), H=40, KVH=40, d=128, q="f16", kv="f16", lens=lens, seed=18)
+    assert ops.attention_plan(len(lens), 40, 40, 128, 16, max(lens), 0, ops.F16, ops.F16)[2] == 1   # one pass
+    case = DecodeCase(w, DEV)
+    base = case.run(partition_size=0)
+    _check(case, base, "head runs")
+    for chunk in ("0", "8", "3"):
+        monkeypatch.setenv("PKV_XCD_CHUNK", chunk)
+        out = case.run(partition_size=0)
+        assert torch.equal(out.view(torch.int16), base.view(torch.int16)), f"PKV_XCD_CHUNK={chunk}"

@@ -182,3 +182,31 @@ def test_shared_decode_rejects_too_many_columns(ops):
     g = [torch.tensor(a, dtype=torch.int32, device=DEV) for a in ([0, 4], [0, 1, 2, 3], [0])]
     with pytest.raises(ops.PkvError):
         ops.paged_attention_decode_shared(torch.empty_like(q), q, pool, pool, t, c, *g, 5, 0.1, 1)   # 5 x 4 > 16
+
+
+def test_shared_decode_xcd_orders_only_schedule(ops, monkeypatch):
+    """16 heads: the shared-block decode takes the head-runs order; the hardware order
+    and runs of n work ids give identical bits."""
+    H, d, bs = 16, 128, 16
+    rng = np.random.default_rng(21)
+    bm, NB, seqs, slots, pairs = forked_batch(rng, [90, 33, 260], 4, 30, bs)
+    kc, vc, _ = make_pools(rng, None, "f16", NB, H, d, bs)
+    tables_np = bm.block_table_array(seqs, 32)
+    ctx_np = bm.context_lens_array(seqs)
+    g = [torch.from_numpy(a).to(DEV) for a in bm.shared_groups(seqs, 4)]
+    q = torch.from_numpy(rng.standard_normal((len(seqs), H, d)).astype(np.float32)).half().to(DEV)
+    k, v = kc.to(DEV), vc.to(DEV)
+    tables, ctx = torch.from_numpy(tables_np).to(DEV), torch.from_numpy(ctx_np).to(DEV)
+
+    def run():
+        out = torch.empty_like(q)
+        ops.paged_attention_decode_shared(out, q, k, v, tables, ctx, *g, 4, d ** -0.5, int(ctx_np.max()))
+        torch.cuda.synchronize()
+        return out
+
+    base = run()
+    ref = oracle.attend_ref(as_f64(q), as_f64(k), as_f64(v), tables_np, ctx_np, d ** -0.5, bs)
+    check_close(as_f64(base), ref, TOL["f16"], "shared-block decode, head runs")
+    for chunk in ("0", "8", "5"):
+        monkeypatch.setenv("PKV_XCD_CHUNK", chunk)
+        assert torch.equal(run().view(torch.int16), base.view(torch.int16)), f"PKV_XCD_CHUNK={chunk}"
