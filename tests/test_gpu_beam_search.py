@@ -1,6 +1,7 @@
 """Beam search on the GPU: per step copy_blocks (copy-on-write pairs), reshape_and_cache
-(the beams' new tokens) and decode attention over every beam, compared with the fp64
-oracle over each beam's own never-paged history."""
+(the beams' new tokens) and decode attention over every beam -- plain and shared-block
+(the beams' common table prefix read once) -- compared with the fp64 oracle over each
+beam's own never-paged history."""
 
 import numpy as np
 import pytest
@@ -38,6 +39,7 @@ def test_beam_search_steps_match_oracle(ops):
                           torch.tensor(slots, dtype=torch.int64, device=DEV))
     model.extend(0, k, v)
     beams, next_id = [0], 1
+    shared_seen = []
     for step in range(steps):
         n = len(beams)
         parents = [i if (i < n and rng.random() < 0.6) else int(rng.integers(n)) for i in range(width)]
@@ -67,4 +69,15 @@ def test_beam_search_steps_match_oracle(ops):
                 ref[i, h] = oracle.attend_one_ref(qn[i, h], keys[:, h // (H // KVH)], vals[:, h // (H // KVH)],
                                                   d ** -0.5)
         check_close(as_f64(out), ref, TOL["f16"], f"step {step}")
+        # the shared-block decode: the beams' common table prefix is read once for all of them
+        offs, mem, shared = bm.shared_groups(beams, 16 // (H // KVH))
+        out_sh = torch.full_like(q, float("nan"))
+        ops.paged_attention_decode_shared(out_sh, q, kc, vc, torch.from_numpy(tables).to(DEV),
+                                          torch.from_numpy(ctx).to(DEV),
+                                          *[torch.from_numpy(a).to(DEV) for a in (offs, mem, shared)],
+                                          int(np.diff(offs).max()), d ** -0.5, int(ctx.max()))
+        torch.cuda.synchronize()
+        check_close(as_f64(out_sh), ref, TOL["f16"], f"step {step}, shared-block decode ({shared.tolist()} shared)")
+        shared_seen.append(int(shared.max()))
     assert blocks_in_use(bm) < blocks_without_sharing(bm, beams)
+    assert max(shared_seen) >= 2                            # the prompt's blocks and more were read once
