@@ -5,10 +5,11 @@
 // online softmax ("PagedAttention", Ultralytics glossary, section "Các kỹ thuật
 // liên quan": FlashAttention-style tiling never forms the score row):
 //   M = max_p m_p;  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p
-// Many partitions: one 256-thread workgroup per (sequence, head); threads read
-// the partition maxima and sums in parallel, then stripes of threads walk the
-// partitions with float4 loads of o_p and combine through LDS.  Few partitions:
-// one wave per (sequence, head), see attn_reduce_small_kernel.
+// Many partitions: D/32 256-thread workgroups per (sequence, head), each for
+// 32 dims of the output row; threads read the partition maxima and sums in
+// parallel, then 32 stripes of 8 threads walk the partitions with float4 loads
+// of o_p and combine through LDS.  Few partitions: one wave per (sequence,
+// head), see attn_reduce_small_kernel.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -17,9 +18,13 @@ namespace pkv {
 template <class OT, int D>
 __global__ __launch_bounds__(256) void attn_reduce_kernel(ReduceParams p) {
   constexpr int NT = 256;
-  constexpr int CH = D / 4;              // float4 chunks of one output row
+  constexpr int DW = 32;                 // output dims of this workgroup
+  constexpr int DS = D / DW;             // workgroups per (sequence, head)
+  constexpr int CH = DW / 4;             // float4 chunks of the dims
   constexpr int STRIPES = NT / CH;       // partitions walked side by side
-  const int sh = blockIdx.x;             // sequence * num_heads + head
+  static_assert(D % DW == 0, "head_dim a multiple of 32");
+  const int sh = blockIdx.x / DS;        // sequence * num_heads + head
+  const int d0 = (blockIdx.x - sh * DS) * DW;
   const int seq = sh / p.num_heads;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -32,7 +37,7 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(ReduceParams p) {
   const size_t base = (size_t)sh * p.num_partitions;
 
   __shared__ float red[4];
-  __shared__ float sm[STRIPES][D];
+  __shared__ float sm[STRIPES][DW];
 
   float mx = -__builtin_inff();
   for (int i = tid; i < np; i += NT) mx = fmaxf(mx, p.ws_m[base + i]);
@@ -56,7 +61,7 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(ReduceParams p) {
 #pragma unroll 4
   for (int i = st; i < np; i += STRIPES) {
     const float wt = exp2_fast(p.ws_m[base + i] - M);
-    const float4 o = *reinterpret_cast<const float4*>(p.ws_o + (base + i) * D + c * 4);
+    const float4 o = *reinterpret_cast<const float4*>(p.ws_o + (base + i) * D + d0 + c * 4);
     acc.x += wt * o.x; acc.y += wt * o.y; acc.z += wt * o.z; acc.w += wt * o.w;
   }
   sm[st][c * 4 + 0] = acc.x;
@@ -65,11 +70,11 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(ReduceParams p) {
   sm[st][c * 4 + 3] = acc.w;
   __syncthreads();
   const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
-  for (int d = tid; d < D; d += NT) {
+  for (int d = tid; d < DW; d += NT) {
     float o = 0.f;
 #pragma unroll
     for (int s = 0; s < STRIPES; ++s) o += sm[s][d];
-    store_elem<OT>(p.out, (size_t)sh * D + d, o * inv);
+    store_elem<OT>(p.out, (size_t)sh * D + d0 + d, o * inv);
   }
 }
 
@@ -207,7 +212,7 @@ static hipError_t launch_reduce_d(const ReduceParams& p, int d, hipStream_t stre
     }
     return hipGetLastError();
   }
-  const dim3 grid((unsigned)units);
+  const dim3 grid((unsigned)(units * (d / 32)));         // D/32 workgroups per (sequence, head)
   switch (d) {
     case 64: hipLaunchKernelGGL((attn_reduce_kernel<OT, 64>), grid, dim3(256), 0, stream, p); break;
     case 128: hipLaunchKernelGGL((attn_reduce_kernel<OT, 128>), grid, dim3(256), 0, stream, p); break;

@@ -283,3 +283,17 @@ def test_xcd_orders_only_schedule(ops, monkeypatch):
         monkeypatch.setenv("PKV_XCD_CHUNK", chunk)
         out = case.run(partition_size=0)
         assert torch.equal(out.view(torch.int16), base.view(torch.int16)), f"PKV_XCD_CHUNK={chunk}"
+
+
+@pytest.mark.parametrize("H,KVH,d,dt", [(4, 4, 128, "f16"), (16, 2, 128, "bf16"), (4, 4, 64, "f16"),
+                                        (8, 2, 256, "bf16")], ids=["mha-d128", "gqa-d128", "mha-d64", "gqa-d256"])
+def test_many_partitions_reduce(ops, H, KVH, d, dt):
+    """More than 64 partitions per context (the striped reduce over head-dim slices):
+    every output against the oracle."""
+    lens = (1500, 1, 990, 1024, 16, 1100)
+    code = {"f16": ops.F16, "bf16": ops.BF16}[dt]
+    assert ops.attention_plan(len(lens), H, KVH, d, 16, max(lens), 16, code, code)[2] == 94
+    w = W(S=len(lens), H=H, KVH=KVH, d=d, q=dt, kv=dt, lens=lens, seed=31)
+    case = DecodeCase(w, DEV)
+    out = case.run(partition_size=16)                       # one block per partition
+    _check(case, out, f"many partitions {H}/{KVH} d{d} {dt}")
