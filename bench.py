@@ -24,7 +24,9 @@ Reported separately under "components" (not part of the step):
 * copy_blocks on copy-on-write pairs shaped like the shared-prefix workload
   (this workload shares no block);
 * swap_blocks: every block of the 16 most recent sequences swapped out to a
-  pinned host pool and back in (the preemption path), GB/s over the host link.
+  pinned host pool and back in (the preemption path), GB/s over the host link;
+* for a workload that states its partition size (long-context split-K), the
+  same step under the library's automatic plan, for comparison.
 
 Prints one JSON line:
 * value      algorithmic KV bytes read per step / step time (GB/s);
@@ -697,6 +699,33 @@ def main():
     t_attn = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)])
     t_split = np.array([ev[i][0].elapsed_time(ev[i][2]) for i in range(K)])
 
+    # ---- with a stated partition size: the same step under the library's automatic plan, for comparison
+    auto = None
+    if part:
+        auto_plan = ops.attention_plan(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size, max_ctx, 0,
+                                       qd, kvd)
+        auto_ws = torch.empty(max(ops.attention_workspace_bytes(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim,
+                                                                w.block_size, max_ctx, 0, qd, kvd), 256),
+                              dtype=torch.uint8, device=dev)
+
+        def step_auto():
+            ops.paged_attention_decode_append(out, inp.q, inp.k_cache, inp.v_cache, inp.k_new, inp.v_new, slots,
+                                              tables, ctx, w.softmax_scale, max_ctx, partition_size=0,
+                                              workspace=auto_ws, seq_order=order, stream=stream, **kvs)
+
+        warm_up(step_auto, 10)
+        ea = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+        for i in range(K):
+            ea[i][0].record(stream)
+            step_auto()
+            ea[i][1].record(stream)
+        torch.cuda.synchronize()
+        t_auto = float(np.mean([ea[i][0].elapsed_time(ea[i][1]) for i in range(K)]))
+        auto = {"plan": {"path": ["vector", "mfma"][auto_plan[0]],
+                         "mode": "balanced slices" if auto_plan[1] == 0 else "partitions",
+                         "slices_or_partitions": auto_plan[2]},
+                "step_us": round(t_auto * 1e3, 2)}
+
     # ---- copy_blocks on copy-on-write pairs shaped like the shared-prefix workload (timed separately)
     sp = synth.SHARED_PREFIX_FP8
     n_pairs = 3 * sp.num_prompts
@@ -748,6 +777,9 @@ def main():
     attn_ms = float(np.mean(t_attn))
     achieved = (alg_bytes + append_bytes) / (step_ms * 1e-3) / 1e9
     traffic = measured_traffic(args.workload)
+    if auto is not None:
+        auto["pct_of_hbm_peak"] = round(100.0 * (alg_bytes + append_bytes) / (auto["step_us"] * 1e-6) / 1e9
+                                        / HBM_PEAK_GBPS, 2)
     result = {
         "metric": "paged decode KV-read GB/s (% of HBM peak) + sequences/sec per decode step",
         "value": round(kv_bytes / (step_ms * 1e-3) / 1e9, 1),
@@ -785,6 +817,7 @@ def main():
             "copy_blocks_pairs": n_pairs,
             "copy_blocks_gbps": round(2 * 2 * n_pairs * block_bytes / (copy_us * 1e-6) / 1e9, 1),
             "wall_ms_per_step": round(wall / K * 1e3, 4),
+            "automatic_plan_step": auto,
             "swap_blocks": {"blocks": int(len(sw_blocks)), "sequences": n_sw, "bytes": int(sw_bytes),
                             "out_us": round(swap_out_ms * 1e3, 1), "in_us": round(swap_in_ms * 1e3, 1),
                             "out_gbps": round(sw_bytes / (swap_out_ms * 1e-3) / 1e9, 1),
