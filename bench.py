@@ -73,7 +73,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="bound on the oracle sample's CPU time")
     ap.add_argument("--calibrate-copy", type=int, default=0,
-                    help="also run one copy_blocks of this many blocks (HBM counter calibration)")
+                    help="also run one copy_blocks of this many blocks (HBM counter calibration); such a run "
+                         "skips the automatic-plan comparison, so its counters hold only the timed step")
     return ap.parse_args()
 
 
@@ -700,8 +701,9 @@ def main():
     t_split = np.array([ev[i][0].elapsed_time(ev[i][2]) for i in range(K)])
 
     # ---- with a stated partition size: the same step under the library's automatic plan, for comparison
+    # (not in counter runs, which must hold only the timed step's kernels)
     auto = None
-    if part:
+    if part and not args.calibrate_copy:
         auto_plan = ops.attention_plan(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size, max_ctx, 0,
                                        qd, kvd)
         auto_ws = torch.empty(max(ops.attention_workspace_bytes(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim,

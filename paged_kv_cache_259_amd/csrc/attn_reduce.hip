@@ -7,8 +7,9 @@
 //   M = max_p m_p;  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p
 // Many partitions: D/32 256-thread workgroups per (sequence, head), each for
 // 32 dims of the output row; threads read the partition maxima and sums in
-// parallel, then 32 stripes of 8 threads walk the partitions with float4 loads
-// of o_p and combine through LDS.  Few partitions: one wave per (sequence,
+// parallel, and 32 stripes of 8 threads walk the partitions with float4 loads
+// of o_p (the first 8 of each stripe issued with the maxima and sums), then
+// combine through LDS.  Few partitions: one wave per (sequence,
 // head), see attn_reduce_small_kernel.
 #include "pkv_device.h"
 #include "pkv_internal.h"
@@ -39,8 +40,27 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(ReduceParams p) {
   __shared__ float red[4];
   __shared__ float sm[STRIPES][DW];
 
-  float mx = -__builtin_inff();
-  for (int i = tid; i < np; i += NT) mx = fmaxf(mx, p.ws_m[base + i]);
+  // Every load a thread needs first is issued before any reduction: the max and
+  // sum of partition tid, and the rows (these dims) of its stripe's first PRE
+  // partitions st, st + STRIPES, ...  The merge then waits on one memory
+  // latency instead of three (maxima, sums, rows).
+  constexpr int PRE = 8;
+  const int c = tid % CH;
+  const int st = tid / CH;
+  float4 ov[PRE];
+  float om[PRE];
+#pragma unroll
+  for (int k = 0; k < PRE; ++k) {
+    const int i = st + k * STRIPES;
+    ov[k] = i < np ? *reinterpret_cast<const float4*>(p.ws_o + (base + i) * D + d0 + c * 4)
+                   : make_float4(0.f, 0.f, 0.f, 0.f);
+    om[k] = i < np ? p.ws_m[base + i] : -__builtin_inff();
+  }
+  const float m_own = tid < np ? p.ws_m[base + tid] : -__builtin_inff();
+  const float l_own = tid < np ? p.ws_l[base + tid] : 0.f;
+
+  float mx = m_own;
+  for (int i = tid + NT; i < np; i += NT) mx = fmaxf(mx, p.ws_m[base + i]);
   mx = wave_max(mx);
   if (lane == 0) red[w] = mx;
   __syncthreads();
@@ -48,18 +68,21 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(ReduceParams p) {
   M = (M == -__builtin_inff()) ? 0.f : M;   // no live partition: every weight below is 0
   __syncthreads();
 
-  float ls = 0.f;
-  for (int i = tid; i < np; i += NT) ls += exp2_fast(p.ws_m[base + i] - M) * p.ws_l[base + i];
+  float ls = exp2_fast(m_own - M) * l_own;
+  for (int i = tid + NT; i < np; i += NT) ls += exp2_fast(p.ws_m[base + i] - M) * p.ws_l[base + i];
   ls = wave_sum(ls);
   if (lane == 0) red[w] = ls;
   __syncthreads();
   const float Lsum = (red[0] + red[1]) + (red[2] + red[3]);
 
-  const int c = tid % CH;
-  const int st = tid / CH;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int k = 0; k < PRE; ++k) {
+    const float wt = exp2_fast(om[k] - M);                // 0 past np
+    acc.x += wt * ov[k].x; acc.y += wt * ov[k].y; acc.z += wt * ov[k].z; acc.w += wt * ov[k].w;
+  }
 #pragma unroll 4
-  for (int i = st; i < np; i += STRIPES) {
+  for (int i = st + PRE * STRIPES; i < np; i += STRIPES) {
     const float wt = exp2_fast(p.ws_m[base + i] - M);
     const float4 o = *reinterpret_cast<const float4*>(p.ws_o + (base + i) * D + d0 + c * 4);
     acc.x += wt * o.x; acc.y += wt * o.y; acc.z += wt * o.z; acc.w += wt * o.w;

@@ -180,7 +180,7 @@ const char* pkv_status_string(int status) {
   return "unknown status";
 }
 
-int pkv_version(void) { return 100; }
+int pkv_version(void) { return 200; }
 
 int pkv_attention_plan(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
                        int max_context_len, int partition_size, int q_dtype, int kv_dtype, int* path,

@@ -52,7 +52,7 @@ def test_status_strings(lib):
         s = lib.pkv_status_string(st)
         assert s and s != b"unknown status"
     assert lib.pkv_status_string(-99) == b"unknown status"
-    assert lib.pkv_version() == 100
+    assert lib.pkv_version() == 200
 
 
 def _plan(lib, *args):
