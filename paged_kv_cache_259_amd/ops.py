@@ -102,6 +102,15 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
 
+def _on_device(device, *tensors):
+    """Every tensor argument on the pools' GPU: the kernels dereference them all."""
+    if device.type != "cuda":
+        raise ValueError("the KV pools must be GPU tensors")
+    for t in tensors:
+        if t is not None and t.device != device:
+            raise ValueError(f"all tensor arguments must be on {device}; one is on {t.device}")
+
+
 def _head_scales(t, kvh, device):
     """Optional per-kv-head scale array: fp32 [kvh], contiguous, on the pools' device."""
     if t is None:
@@ -167,6 +176,7 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     if seq_order is not None and (seq_order.dtype != torch.int32 or seq_order.shape != (S,)
                                   or not seq_order.is_contiguous()):
         raise ValueError("seq_order must be a contiguous int32 [S] tensor")
+    _on_device(k_cache.device, out, q, v_cache, block_tables, context_lens, workspace, seq_order)
     _check(_lib.pkv_paged_attention_decode(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1],
         _ptr(context_lens), _ptr(seq_order), S, H, KVH, d, bs, NB if num_blocks is None else num_blocks, max_context_len,
@@ -198,6 +208,7 @@ def paged_prefill_attention(out, q, k_cache, v_cache, block_tables, context_lens
             raise ValueError("all tensors must be contiguous")
     if out.dtype != q.dtype:
         raise TypeError("out must have q's dtype")
+    _on_device(k_cache.device, out, q, v_cache, block_tables, context_lens, query_start_loc)
     _check(_lib.pkv_paged_prefill_attention(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1],
         _ptr(context_lens), _ptr(query_start_loc), S, T, H, KVH, d, bs, NB if num_blocks is None else num_blocks,
@@ -240,6 +251,8 @@ def paged_attention_decode_append(out, q, k_cache, v_cache, key, value, slot_map
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _ptr(workspace) if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _on_device(k_cache.device, out, q, v_cache, key, value, slot_mapping, block_tables, context_lens, workspace,
+               seq_order)
     _check(_lib.pkv_paged_attention_decode_append(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(key), _ptr(value), _ptr(slot_mapping),
         _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), _ptr(seq_order), S, H, KVH, d, bs,
@@ -282,6 +295,8 @@ def paged_attention_decode_shared(out, q, k_cache, v_cache, block_tables, contex
     for t in (out, q, k_cache, v_cache, block_tables, context_lens) + ((key, value, slot_mapping) if append else ()):
         if not t.is_contiguous():
             raise ValueError("all tensors must be contiguous")
+    _on_device(k_cache.device, out, q, v_cache, block_tables, context_lens, group_offsets, group_members,
+               group_shared_blocks, key, value, slot_mapping)
     _check(_lib.pkv_paged_attention_decode_shared(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(key), _ptr(value), _ptr(slot_mapping),
         _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), _ptr(group_offsets), _ptr(group_members),
@@ -304,6 +319,7 @@ def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, k_scale=1.0, v
     for t in (key, value, k_cache, v_cache, slot_mapping):
         if not t.is_contiguous():
             raise ValueError("all tensors must be contiguous")
+    _on_device(k_cache.device, key, value, v_cache, slot_mapping)
     _check(_lib.pkv_reshape_and_cache(
         _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), T, KVH, d, bs, NB,
         dtype_code(key.dtype), dtype_code(k_cache.dtype), float(k_scale), float(v_scale),
@@ -321,6 +337,7 @@ def copy_blocks(k_cache, v_cache, block_mapping, stream=None):
         raise TypeError("block_mapping must be int64 [num_pairs, 2]")
     if not (k_cache.is_contiguous() and v_cache.is_contiguous() and block_mapping.is_contiguous()):
         raise ValueError("all tensors must be contiguous")
+    _on_device(k_cache.device, v_cache, block_mapping)
     _check(_lib.pkv_copy_blocks(
         _ptr(k_cache), _ptr(v_cache), _ptr(block_mapping), block_mapping.shape[0], KVH, d, bs, NB,
         dtype_code(k_cache.dtype), _stream(stream)), "pkv_copy_blocks")

@@ -199,3 +199,33 @@ def test_missing_library_fails_loudly():
     r = subprocess.run([sys.executable, "-c", "import paged_kv_cache_259_amd.ops"], cwd=ROOT, env=env,
                        capture_output=True, text=True)
     assert r.returncode != 0 and "no CPU fallback" in r.stderr
+
+
+def test_bindings_refuse_host_tensors(lib):
+    """The kernels dereference every tensor argument, so the binding refuses host
+    tensors before anything reaches the library (no GPU needed to check)."""
+    import torch
+    from paged_kv_cache_259_amd import ops
+    S, H, d, NB, bs = 2, 4, 128, 8, 16
+    q = torch.zeros((S, H, d), dtype=torch.float16)
+    out = torch.empty_like(q)
+    pool = torch.zeros((NB, H, bs, d), dtype=torch.float16)
+    tables = torch.zeros((S, 2), dtype=torch.int32)
+    ctx = torch.ones(S, dtype=torch.int32)
+    kv = torch.zeros((S, H, d), dtype=torch.float16)
+    slots = torch.zeros(S, dtype=torch.int64)
+    calls = [
+        lambda: ops.paged_attention_decode(out, q, pool, pool, tables, ctx, 0.1, 1),
+        lambda: ops.paged_attention_decode_append(out, q, pool, pool, kv, kv, slots, tables, ctx, 0.1, 1),
+        lambda: ops.paged_attention_decode_shared(out, q, pool, pool, tables, ctx,
+                                                  torch.tensor([0, 2], dtype=torch.int32),
+                                                  torch.tensor([0, 1], dtype=torch.int32),
+                                                  torch.tensor([0], dtype=torch.int32), 2, 0.1, 1),
+        lambda: ops.paged_prefill_attention(out, q, pool, pool, tables, ctx, torch.tensor([0, 1, 2], dtype=torch.int32),
+                                            0.1, 1, 1),
+        lambda: ops.reshape_and_cache(kv, kv, pool, pool, slots),
+        lambda: ops.copy_blocks(pool, pool, torch.tensor([[0, 1]], dtype=torch.int64)),
+    ]
+    for i, call in enumerate(calls):
+        with pytest.raises(ValueError, match="GPU tensors"):
+            call()
