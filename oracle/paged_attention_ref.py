@@ -46,7 +46,8 @@ def blocks_needed(n_tokens, block_size):
     """
     if n_tokens < 0 or block_size <= 0:
         raise ValueError("n_tokens must be >= 0 and block_size > 0")
-    return -(-n_tokens // block_size)
+    full, rest = divmod(n_tokens, block_size)
+    return full + (1 if rest else 0)            # a partly filled last block still takes a block
 
 
 def take_blocks(free_list, n):
@@ -57,7 +58,9 @@ def take_blocks(free_list, n):
     """
     if n > len(free_list):
         raise RuntimeError("out of free blocks")
-    return [free_list.pop(0) for _ in range(n)]
+    taken = list(free_list[:n])
+    del free_list[:n]
+    return taken
 
 
 def slot_of(block_table, pos, block_size):

@@ -49,9 +49,6 @@ def test_worked_example_table_gather_and_waste():
     assert np.array_equal(gathered, keys) == g["expected_keys_intact"]
     assert len(table) * bs - n == g["expected_unused_slots_paged"]
     assert g["reservation_tokens"] - n == g["expected_unused_slots_reserved"]
-    # the example's own gather form: pool[table] flattened, cut to the request length
-    flat = pool_k[table, 0].reshape(-1, d)[:n]
-    assert np.array_equal(flat, keys)
 
 
 def test_tiny_workload_block_count():
@@ -535,3 +532,97 @@ def test_dequant_per_head_scales_each_head():
     got = e5m2_ref.dequant_per_head(codes, scales, e5m2_ref.decode_e5m2)
     for h in range(3):
         np.testing.assert_array_equal(got[:, h], e5m2_ref.dequant_e5m2(codes[:, h], scales[h]))
+
+
+# ---------------------------------------------------------------------------
+# 8-bit dequantisation at scales other than 1: stored value = code's value x the
+# fp32 scale ("PagedAttention", Ultralytics glossary, section "Các kỹ thuật
+# liên quan": the FP8 cache; one fp32 scale per pool or per kv head).  Pinned to
+# closed forms (the code of 1.0 reads back as the fp32 scale itself), to torch's
+# float8 decode times the fp32 scale, and to a half-step error bound whose step
+# is written from the formats' exponent ranges, not read off the oracle's table.
+# ---------------------------------------------------------------------------
+
+# 0.05 and 3.7/448 are not binary fractions, so their fp32 rounding differs from
+# the float64 value (a scale taken in float64 fails the exact checks); 2^-5 is
+# exact; 7.3 is above 1.
+DEQUANT_SCALES = [0.05, 2.0 ** -5, 3.7 / 448.0, 7.3]
+
+
+@pytest.mark.parametrize("scale", DEQUANT_SCALES)
+def test_e4m3_dequant_closed_forms_at_scale(scale):
+    s32 = float(np.float32(scale))
+    dq = lambda c: float(e4m3_ref.dequant_e4m3(np.uint8(c), scale))
+    assert dq(0x38) == s32                          # code of 1.0 reads back as the fp32 scale
+    assert dq(0xB8) == -s32
+    assert dq(0x40) == 2.0 * s32                    # 0 1000 000 = 2
+    assert dq(0x7E) == 448.0 * s32                  # largest finite code
+    assert dq(0x01) == 2.0 ** -9 * s32              # smallest subnormal
+    assert dq(0x00) == 0.0
+    if s32 != scale:
+        assert dq(0x38) != scale                    # the scale is the fp32 one, not the float64 argument
+
+
+@pytest.mark.parametrize("scale", DEQUANT_SCALES)
+def test_e5m2_dequant_closed_forms_at_scale(scale):
+    s32 = float(np.float32(scale))
+    dq = lambda c: float(e5m2_ref.dequant_e5m2(np.uint8(c), scale))
+    assert dq(0x3C) == s32                          # code of 1.0 reads back as the fp32 scale
+    assert dq(0xBC) == -s32
+    assert dq(0x40) == 2.0 * s32                    # 0 10000 00 = 2
+    assert dq(0x7B) == 57344.0 * s32                # largest finite code
+    assert dq(0x01) == 2.0 ** -16 * s32             # smallest subnormal
+    if s32 != scale:
+        assert dq(0x3C) != scale
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("scale", DEQUANT_SCALES)
+def test_dequant_all_codes_equal_torch_decode_times_fp32_scale(fmt, scale):
+    codes = np.arange(256, dtype=np.uint8)
+    tdt = torch.float8_e4m3fn if fmt == "e4m3" else torch.float8_e5m2
+    lib = torch.from_numpy(codes).view(tdt).to(torch.float64) * torch.tensor(scale, dtype=torch.float32).double()
+    lib = lib.numpy()
+    ours = (e4m3_ref.dequant_e4m3 if fmt == "e4m3" else e5m2_ref.dequant_e5m2)(codes, scale)
+    nan = np.isnan(lib)
+    assert np.array_equal(np.isnan(ours), nan)
+    np.testing.assert_array_equal(ours[~nan], lib[~nan])
+
+
+def _fp8_step(a, fmt):
+    """Spacing of the 8-bit values around magnitude a (in code units): 2^(e - mantissa bits), with the
+    exponent e = floor(log2 a) held at the smallest normal exponent below it (subnormals share that step)."""
+    mbits, emin = (3, -6) if fmt == "e4m3" else (2, -14)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 2.0 ** emin)))
+    return 2.0 ** (np.maximum(e, emin) - mbits)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("scale", [2.0 ** -5, 3.7 / 448.0, 0.05])
+def test_fp8_roundtrip_every_fp16_pattern_within_half_step(fmt, scale):
+    """|dequant(encode(x, s), s) - clip(x, +-max*s)| <= half a step (times s), plus the fp32 rounding of x / s."""
+    x = torch.arange(65536, dtype=torch.int32).to(torch.int16).view(torch.float16).to(torch.float64).numpy()
+    x = x[np.isfinite(x)]
+    s32 = float(np.float32(scale))
+    if fmt == "e4m3":
+        enc, dq, vmax = e4m3_ref.encode_e4m3, e4m3_ref.dequant_e4m3, 448.0
+    else:
+        enc, dq, vmax = e5m2_ref.encode_e5m2, e5m2_ref.dequant_e5m2, 57344.0
+    back = dq(enc(x, scale), scale)
+    target = np.clip(x, -vmax * s32, vmax * s32)
+    a = np.minimum(np.abs(x) / s32, vmax)
+    bound = _fp8_step(a, fmt) / 2 * s32 + 2.0 ** -23 * np.abs(x)
+    err = np.abs(back - target)
+    assert np.all(err <= bound), (x[np.argmax(err - bound)], float(np.max(err - bound)))
+    assert np.array_equal(np.signbit(back[x != 0]), np.signbit(x[x != 0]))
+
+
+def test_dequant_per_head_closed_form():
+    """Every code 1.0 under per-head scales reads back as each head's own fp32 scale."""
+    scales = np.array([0.05, 7.3, 3.7 / 448.0], np.float64)
+    for codes, dec in ((np.full((2, 3, 4, 8), 0x3C, np.uint8), e5m2_ref.decode_e5m2),
+                       (np.full((2, 3, 4, 8), 0x38, np.uint8), e4m3_ref.decode_e4m3)):
+        got = e5m2_ref.dequant_per_head(codes, scales, dec)
+        for h in range(3):
+            assert np.all(got[:, h] == float(np.float32(scales[h])))
