@@ -68,6 +68,10 @@ extern "C" {
 #define PKV_ERR_SCALE (-8)          /* an FP8 scale is not a positive finite number         */
 #define PKV_ERR_MEMORY_KIND (-9)    /* a buffer is neither device memory nor pinned host     */
                                     /* memory the device can address                         */
+#define PKV_ERR_SCRATCH_LIMIT (-10) /* the call needs more than PKV_STATIC_SCRATCH_BYTES         */
+
+/* Size of the static device scratch of pkv_paged_attention_decode_noalloc (one copy per GPU). */
+#define PKV_STATIC_SCRATCH_BYTES (48u << 20)
 
 /* attention kernel families reported by pkv_attention_plan */
 #define PKV_PATH_VECTOR 0  /* per-query-head vector kernel (wave shuffles, no MFMA)  */
@@ -172,6 +176,37 @@ int pkv_paged_attention_decode(void* out, const void* q,
                                const float* k_scales, const float* v_scales,
                                int q_dtype, int kv_dtype, int partition_size,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pkv_paged_attention_decode_noalloc -- pkv_paged_attention_decode for callers
+ * that cannot allocate device memory or pass a workspace: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.
+ *
+ * Same arguments, results and launches as pkv_paged_attention_decode without
+ * `workspace` / `workspace_bytes`: when the plan splits contexts, the fp32
+ * summaries go to a static device array of PKV_STATIC_SCRATCH_BYTES (48 MiB)
+ * inside the library instead.  Each GPU the library runs on holds its own copy
+ * from the first use until the process ends; its device address is looked up
+ * once per device, on the first call with that device current.  The call
+ * itself allocates nothing (no hipMalloc, no allocating library routine).
+ *
+ * A call whose plan needs more than PKV_STATIC_SCRATCH_BYTES
+ * (pkv_attention_workspace_bytes of the same shapes) returns
+ * PKV_ERR_SCRATCH_LIMIT and launches nothing.  PKV_ERR_LAUNCH also reports a
+ * failed address lookup.  Scratch contents on entry are ignored (nothing needs
+ * clearing).  Every call on one GPU shares that GPU's scratch: two calls whose
+ * kernels overlap on one GPU (different streams, no ordering between them)
+ * race on it and may give wrong outputs; calls on one stream are ordered and
+ * safe.
+ */
+int pkv_paged_attention_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                       const int32_t* block_tables, int max_blocks_per_seq,
+                                       const int32_t* context_lens, const int32_t* seq_order,
+                                       int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                                       int block_size, int num_blocks, int max_context_len,
+                                       float scale, float k_scale, float v_scale,
+                                       const float* k_scales, const float* v_scales,
+                                       int q_dtype, int kv_dtype, int partition_size, void* stream);
 
 /*
  * pkv_paged_attention_decode_append -- one decode step in one launch: each

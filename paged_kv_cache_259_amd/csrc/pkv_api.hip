@@ -6,6 +6,9 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "pkv.h"
 #include "pkv_internal.h"
 
@@ -176,6 +179,9 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_LAUNCH: return "HIP kernel launch failed";
     case PKV_ERR_SCALE: return "FP8 scale must be a positive finite number";
     case PKV_ERR_MEMORY_KIND: return "buffer is neither device memory nor pinned host memory";
+    case PKV_ERR_SCRATCH_LIMIT:
+      return "the call needs more split-context scratch than the library's static scratch holds "
+             "(PKV_STATIC_SCRATCH_BYTES); call pkv_paged_attention_decode with a workspace instead";
   }
   return "unknown status";
 }
@@ -464,6 +470,67 @@ int pkv_paged_prefill_attention(void* out, const void* q, const void* k_cache, c
   p.xcd_chunk = (uint32_t)(chunk < 0 ? 0 : (chunk > 4096 ? 4096 : chunk));
   (void)hipGetLastError();
   return pkv::launch_status(pkv::launch_prefill(p, q_dtype, head_dim, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Decode that allocates nothing: the split-context summaries go to a static
+// device array instead of a caller workspace.
+// ---------------------------------------------------------------------------
+namespace {
+
+// One copy per GPU, held from the library's first use on that GPU until the
+// process ends.  In host code `scratch` names a host-side stand-in; kernels get
+// the device address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[PKV_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch, looked up once per device.
+int static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PKV_ERR_LAUNCH;
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!ptr) {
+      if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return PKV_ERR_LAUNCH;
+      g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_paged_attention_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                       const int32_t* block_tables, int max_blocks_per_seq,
+                                       const int32_t* context_lens, const int32_t* seq_order, int num_seqs,
+                                       int num_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                       int max_context_len, float scale, float k_scale, float v_scale,
+                                       const float* k_scales, const float* v_scales, int q_dtype, int kv_dtype,
+                                       int partition_size, void* stream) {
+  Plan pl;
+  const int st = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len, partition_size,
+                           q_dtype, kv_dtype, &pl);
+  if (st != PKV_OK) return st;
+  if (pl.ws_bytes > PKV_STATIC_SCRATCH_BYTES) return PKV_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  if (pl.ws_bytes > 0 && num_seqs > 0) {
+    const int e = static_scratch(&ws);
+    if (e != PKV_OK) return e;
+  }
+  return decode_impl(out, q, k_cache, v_cache, nullptr, nullptr, nullptr, block_tables, max_blocks_per_seq,
+                     context_lens, seq_order, num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_context_len, scale, k_scale, v_scale, k_scales, v_scales, q_dtype, kv_dtype, partition_size,
+                     ws, ws ? (size_t)PKV_STATIC_SCRATCH_BYTES : 0, stream);
 }
 
 }  // extern "C"

@@ -43,6 +43,14 @@ _lib.pkv_paged_attention_decode.argtypes = (
     + [_vp, _vp]
     + [_c_int] * 3
     + [_vp, _c_size, _vp])
+_lib.pkv_paged_attention_decode_noalloc.restype = _c_int
+_lib.pkv_paged_attention_decode_noalloc.argtypes = (
+    [_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp]
+    + [_c_int] * 7
+    + [_c_float] * 3
+    + [_vp, _vp]
+    + [_c_int] * 3
+    + [_vp])
 _lib.pkv_paged_attention_decode_append.restype = _c_int
 _lib.pkv_paged_attention_decode_append.argtypes = (
     [_vp] * 7 + [_vp, _c_int, _vp, _vp] + [_c_int] * 7 + [_c_float] * 3 + [_vp, _vp] + [_c_int] * 3
@@ -64,7 +72,10 @@ EXPORTED_SYMBOLS = (
     "pkv_status_string", "pkv_version", "pkv_attention_plan", "pkv_attention_workspace_bytes",
     "pkv_paged_attention_decode", "pkv_reshape_and_cache", "pkv_copy_blocks", "pkv_swap_blocks",
     "pkv_paged_prefill_attention", "pkv_paged_attention_decode_append", "pkv_paged_attention_decode_shared",
+    "pkv_paged_attention_decode_noalloc",
 )
+
+STATIC_SCRATCH_BYTES = 48 << 20     # PKV_STATIC_SCRATCH_BYTES
 
 
 class PkvError(RuntimeError):
@@ -183,6 +194,40 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         float(scale), float(k_scale), float(v_scale), _ptr(_head_scales(k_scales, KVH, k_cache.device)),
         _ptr(_head_scales(v_scales, KVH, k_cache.device)), qd, kvd, partition_size, ws_ptr, ws_bytes,
         _stream(stream)), "pkv_paged_attention_decode")
+    return out
+
+
+def paged_attention_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+                                   k_scale=1.0, v_scale=1.0, partition_size=0, num_blocks=None, seq_order=None,
+                                   k_scales=None, v_scales=None, stream=None):
+    """paged_attention_decode without a workspace: the library's static per-GPU scratch holds the
+    split-context summaries, and nothing is allocated (for HIP graph capture and callers that cannot
+    allocate).  Raises PkvError (PKV_ERR_SCRATCH_LIMIT) when the plan needs more than
+    STATIC_SCRATCH_BYTES.  Calls that overlap on one GPU race on the scratch."""
+    S, H, d = q.shape
+    NB, KVH, bs, d2 = k_cache.shape
+    if d2 != d or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch between q/out and the pools")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables must be [S, maxblk] and context_lens [S]")
+    for t in (out, q, k_cache, v_cache, block_tables, context_lens):
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    if out.dtype != q.dtype:
+        raise TypeError("out must have q's dtype")
+    if seq_order is not None and (seq_order.dtype != torch.int32 or seq_order.shape != (S,)
+                                  or not seq_order.is_contiguous()):
+        raise ValueError("seq_order must be a contiguous int32 [S] tensor")
+    _on_device(k_cache.device, out, q, v_cache, block_tables, context_lens, seq_order)
+    _check(_lib.pkv_paged_attention_decode_noalloc(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1],
+        _ptr(context_lens), _ptr(seq_order), S, H, KVH, d, bs, NB if num_blocks is None else num_blocks,
+        max_context_len, float(scale), float(k_scale), float(v_scale),
+        _ptr(_head_scales(k_scales, KVH, k_cache.device)), _ptr(_head_scales(v_scales, KVH, k_cache.device)),
+        dtype_code(q.dtype), dtype_code(k_cache.dtype), partition_size, _stream(stream)),
+        "pkv_paged_attention_decode_noalloc")
     return out
 
 

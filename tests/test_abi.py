@@ -34,7 +34,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_symbols()
-    assert len(names) == 11
+    assert len(names) == 12
     for n in names:
         assert hasattr(lib, n), n
     nm = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
@@ -48,7 +48,7 @@ def test_binding_declares_the_same_symbols(lib):
 
 
 def test_status_strings(lib):
-    for st in range(0, -10, -1):
+    for st in range(0, -11, -1):
         s = lib.pkv_status_string(st)
         assert s and s != b"unknown status"
     assert lib.pkv_status_string(-99) == b"unknown status"
@@ -118,6 +118,25 @@ def test_decode_host_checks(lib):
     assert _decode(lib, ptr=None) == -1
     assert _decode(lib, ptr=ctypes.c_void_p(0x10004)) == -4    # misaligned output
     assert _decode(lib, NB=0) == -2
+
+
+def _noalloc(lib, num_seqs=2, H=4, KVH=4, d=128, bs=16, NB=8, max_ctx=64, qd=1, kvd=1, part=0, ptr=FAKE):
+    return lib.pkv_paged_attention_decode_noalloc(ptr, FAKE, FAKE, FAKE, FAKE, 4, FAKE, None, num_seqs, H, KVH, d, bs,
+                                                  NB, max_ctx, ctypes.c_float(0.1), ctypes.c_float(1.0),
+                                                  ctypes.c_float(1.0), None, None, qd, kvd, part, None)
+
+
+def test_noalloc_decode_host_checks(lib):
+    """Checks that return before any device call: the no-allocation decode refuses a plan whose
+    split-context summaries exceed the static scratch (and the usual argument errors)."""
+    assert _noalloc(lib, num_seqs=0) == 0
+    assert _noalloc(lib, H=6, KVH=4) == -3
+    assert _noalloc(lib, part=20) == -5
+    # 16-token partitions of 2M-token contexts: about 1 GB of summaries > 48 MiB
+    assert lib.pkv_attention_workspace_bytes(2, 4, 4, 128, 16, 2_000_000, 16, 1, 1) > 48 << 20
+    assert _noalloc(lib, max_ctx=2_000_000, part=16) == -10
+    assert _noalloc(lib, kvd=5) == -4
+    assert b"static scratch" in lib.pkv_status_string(-10)
 
 
 def test_reshape_and_copy_host_checks(lib):
