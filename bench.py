@@ -10,31 +10,44 @@ cache off and on (value = the speedup).  shared_prefix_fp8 times the next
 decode step of parallel samples that share their prompts' blocks, over fp8
 (E4M3) pools: the copy-on-write copies the step needs plus the decode with
 append, KV bytes counted logical (per sample) and unique (per physical block).
+stream_probe measures what HBM delivers to plain read-only kernels here.
 
 A step is one pass of the hot path over one synthetic decode batch, inputs
 resident in HBM: every sequence's new key/value goes into the slot the block
 manager gave it and each sequence attends over its paged context, the new
 token included -- one paged_attention_decode_append launch (the split-context
-reduce included when the plan uses one).  The same step as two launches
-(reshape_and_cache, then paged_attention_decode) is timed too and reported
-under "components".  The block manager's host bookkeeping (tables, slots, the
-longest-first sequence order) is built before the timed region.
+reduce included when the plan uses one).  The block manager's host
+bookkeeping (tables, slots, the longest-first sequence order) is built before
+the timed region.
 
-Reported separately under "components" (not part of the step):
-* copy_blocks on copy-on-write pairs shaped like the shared-prefix workload
-  (this workload shares no block);
-* swap_blocks: every block of the 16 most recent sequences swapped out to a
-  pinned host pool and back in (the preemption path), GB/s over the host link;
-* for a workload that states its partition size (long-context split-K), the
-  same step under the library's automatic plan, for comparison.
+Timing: K steps, each bracketed by HIP events on the stream the kernels run
+on.  Before every timed step 512 MiB are written and another 512 MiB read,
+outside the events, so L2 and the 256 MB Infinity Cache hold nothing of the
+step's inputs and no dirty lines of the flush itself (the headline); the same
+steps back to back are reported beside it.  Warm-up runs at least --warmup
+steps and at least 50 ms of GPU work (the first launches after the host-bound
+set-up run at low clocks); the JSON gives the count.
+
+Reported beside the step under "components" (not part of it): the same step
+as two launches (reshape_and_cache, then paged_attention_decode); copy_blocks
+on copy-on-write pairs shaped like the shared-prefix workload; swap_blocks of
+the 16 most recent sequences to a pinned host pool and back; for a workload
+that states its partition size (long-context split-K), the same step under the
+library's automatic plan; the HBM read probes (a streaming read and random
+2/4/8 KiB tile reads, libpkv_probe.so); and, with the default workload, the
+GQA bf16 step (flushed and back to back, its roofline fraction and oracle
+parity), so one default run covers both decode shapes the 70 % target names.
 
 Prints one JSON line:
 * value      algorithmic KV bytes read per step / step time (GB/s);
 * roofline   the step's launch against MI355X's 8 TB/s HBM; achieved =
              algorithmic bytes per call (K/V of every context token, q, out,
              table entries, lengths, the new tokens read and written) / mean call
-             time (HIP events on the stream the kernels run on);
-* cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload.
+             time;
+* pct_of_measured_stream_bw  achieved / the streaming-read probe's rate;
+* slot_utilisation  sum(ctx) / (block_size * blocks held);
+* cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload;
+  the GPU rows it recomputed give max_abs_err / max_rel_err.
 """
 
 import argparse
@@ -71,6 +84,8 @@ def parse():
     ap.add_argument("--group-size", type=int, default=0,
                     help="shared-prefix workload: samples per shared-block group (0: as many as one tile holds)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-components", action="store_true",
+                    help="default workload: skip the GQA step timed beside the headline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="bound on the oracle sample's CPU time")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="also run one copy_blocks of this many blocks (HBM counter calibration); such a run "
@@ -97,6 +112,110 @@ def warm_up(fn, steps):
             torch.cuda.synchronize()
     torch.cuda.synchronize()
     return n
+
+
+FLUSH_BYTES = 1 << 30          # 512 MiB written, then another 512 MiB read, between flushed steps
+
+
+class Flusher:
+    """Clears L2 and the 256 MB Infinity Cache between timed steps, outside the timed events.
+
+    Writes 512 MiB (torch fill) and then reads another 512 MiB (the probe's
+    streaming read): the write evicts whatever the caches held, and the read
+    leaves them holding clean lines of an unrelated buffer, so no write-back of
+    the flush's own dirty lines lands inside the next timed step.
+    """
+
+    def __init__(self, stream):
+        import torch
+        from paged_kv_cache_259_amd import probe
+        self.buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        self.sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+        self.half = FLUSH_BYTES // 2
+        self.stream, self.probe, self.n = stream, probe, 0
+
+    def __call__(self):
+        self.n += 1
+        self.buf[: self.half].fill_(self.n % 251)
+        self.probe.stream_read(self.buf[self.half:], self.half, 2048, self.sink, stream=self.stream)
+
+
+def timed_steps(fn, K, stream, flush=None):
+    """Per-step times (ms) of K calls of fn, each bracketed by HIP events on ``stream``; with ``flush``,
+    the caches are cleared before every step, outside the events."""
+    import torch
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        if flush is not None:
+            flush()
+        ev[i][0].record(stream)
+        fn()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in ev])
+
+
+def hbm_probe(stream, reps=10):
+    """What HBM delivers to read-only kernels on this machine: a streaming read of 1 GiB (best of three grid
+    sizes) and reads of random 2/4/8 KiB tiles (0.75 GB per launch), GB/s from HIP events."""
+    import torch
+    from paged_kv_cache_259_amd import probe
+    buf = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+
+    def rate(fn, nbytes):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+    stream_rates = {}
+    for wgs in (1024, 2048, 4096):
+        stream_rates[wgs] = rate(lambda: probe.stream_read(buf, buf.numel(), wgs, sink, stream=stream), buf.numel())
+    tiles = {}
+    wgs = 2048
+    for tb in (2048, 4096, 8192):
+        per_wave = (768 << 20) // (wgs * 4 * tb)
+        tiles[tb] = rate(lambda: probe.tile_read(buf, tb, wgs, per_wave, sink, stream=stream), wgs * 4 * per_wave * tb)
+    del buf
+    best = max(stream_rates, key=stream_rates.get)
+    return {"stream_read_gbps": round(stream_rates[best], 1), "stream_read_workgroups": best,
+            "stream_read_gbps_by_grid": {str(k): round(v, 1) for k, v in stream_rates.items()},
+            "tile_read_gbps": {f"{k // 1024}KiB": round(v, 1) for k, v in tiles.items()},
+            "probe": "libpkv_probe.so: 16-byte loads, 1 GiB buffer; random tiles at hashed indices, two per wave in "
+                     "flight, 2048 workgroups of 4 waves"}
+
+
+def slot_utilisation(ctx, bs):
+    """Share of the allocated slots holding a token: sum(ctx) / (bs * sum of blocks)."""
+    ctx = np.asarray(ctx, np.int64)
+    blocks = int(np.sum((ctx + bs - 1) // bs))
+    return round(float(np.sum(ctx)) / (bs * blocks), 5) if blocks else None
+
+
+def parity_of(got_rows, ref_rows, atol, rtol):
+    """max-abs / max-rel error of GPU rows against the oracle's, and the worst ratio to the tolerance.
+
+    max_rel_err is taken over elements with |ref| >= 0.01 (smaller references make the ratio meaningless).
+    """
+    got = np.asarray(got_rows, np.float64)
+    ref = np.asarray(ref_rows, np.float64)
+    err = np.abs(got - ref)
+    big = np.abs(ref) >= 1e-2
+    return {"max_abs_err": float(err.max()) if err.size else 0.0,
+            "max_rel_err": float((err[big] / np.abs(ref[big])).max()) if big.any() else 0.0,
+            "tol_ratio": float((err / (atol + rtol * np.abs(ref))).max()) if err.size else 0.0,
+            "tolerance": f"{atol:g} + {rtol:g} |ref| per element",
+            "elements": int(err.size)}
+
+
+TOLERANCE = {"f32": (1e-5, 1e-5)}    # 16-bit and 8-bit caches: (2e-3, 1e-2)
 
 
 def kernel_kind(workload):
@@ -152,12 +271,14 @@ class _BlockSubset:
         return self._rows[int(key[0])][key[1]]
 
 
-def cpu_baseline(w, inp, tables, ctx, budget_s):
+def cpu_baseline(w, inp, tables, ctx, budget_s, gpu_out=None):
     """Time the oracle on whole sequences (all heads) until the wall-time budget is spent.
 
     The oracle runs as it stands: numpy in float64, its BLAS calls free to use
     the BLAS library's thread pool (the thread count is reported as ``cores``).
     Host copies of the blocks each sequence uses are made outside the timing.
+    With ``gpu_out`` (the timed step's output), the sequences the oracle ran are
+    also compared with the GPU rows (``parity``: max-abs / max-rel error).
     """
     import oracle
     import torch
@@ -167,27 +288,33 @@ def cpu_baseline(w, inp, tables, ctx, budget_s):
     decode = None
     if getattr(w, "kv8", False):                      # E4M3 codes -> values, as the oracle reads them
         decode = lambda c: oracle.decode_e4m3(c) * np.float64(np.float32(w.kv_scale))
-    done, kv_bytes, spent = 0, 0, 0.0
+    done, kv_bytes, spent, refs = 0, 0, 0.0, []
     for s in range(w.num_seqs):
         n = int(ctx[s])
         blocks = tables[s, : -(-n // w.block_size)]
         kp = _BlockSubset(inp["k"], blocks, decode)
         vp = _BlockSubset(inp["v"], blocks, decode)
         t0 = time.perf_counter()
-        oracle.attend_ref(q[s:s + 1], kp, vp, tables[s:s + 1], ctx[s:s + 1], w.softmax_scale, w.block_size)
+        refs.append(oracle.attend_ref(q[s:s + 1], kp, vp, tables[s:s + 1], ctx[s:s + 1], w.softmax_scale,
+                                      w.block_size))
         spent += time.perf_counter() - t0
         done += 1
         kv_bytes += n * w.num_kv_heads * w.head_dim * 2 * elt
         if spent > budget_s:
             break
     blas_threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
-    return {
+    res = {
         "value": round(kv_bytes / spent / 1e9, 6), "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
         "seq_per_s": round(done / spent, 3),
         "sample": f"first {done} of {w.num_seqs} sequences of the same decode step, all {w.num_heads} heads "
                   f"({kv_bytes / 1e6:.1f} MB of KV), fp64 numpy oracle, {spent:.1f} s wall",
         "host_cores_available": len(os.sched_getaffinity(0)),
     }
+    if gpu_out is not None:
+        got = gpu_out[:done].cpu().to(torch.float64).numpy()
+        res["parity"] = parity_of(got, np.concatenate(refs), *TOLERANCE.get(w.kv_dtype, (2e-3, 1e-2)))
+        res["parity"]["rows"] = f"all {done * w.num_heads} (sequence, head) rows of the first {done} sequences"
+    return res
 
 
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}     # dense MFMA, MI355X
@@ -214,13 +341,14 @@ def prefill_flops(w, ctx, chunk):
     return 4 * w.head_dim * w.num_heads * pairs
 
 
-def cpu_baseline_prefill(w, inp, tables, ctx, budget_s):
-    """The oracle's prefill_ref, one whole sequence (all rows, all heads) at a time, until the budget is spent."""
+def cpu_baseline_prefill(w, inp, tables, ctx, budget_s, gpu_out=None):
+    """The oracle's prefill_ref, one whole sequence (all rows, all heads) at a time, until the budget is spent;
+    with ``gpu_out``, the rows it recomputed are compared with the GPU's (``parity``)."""
     import oracle
     import torch
     from threadpoolctl import threadpool_info
     qsl = inp.query_start_loc
-    done, flops, spent = 0, 0, 0.0
+    done, flops, spent, refs = 0, 0, 0.0, []
     for s in range(w.num_seqs):
         n, c = int(inp.chunk_lens[s]), int(ctx[s])
         blocks = tables[s, : -(-c // w.block_size)]
@@ -228,17 +356,23 @@ def cpu_baseline_prefill(w, inp, tables, ctx, budget_s):
         vp = _BlockSubset(inp.v_cache, blocks)
         q = inp.q[int(qsl[s]):int(qsl[s + 1])].cpu().to(torch.float64).numpy()
         t0 = time.perf_counter()
-        oracle.prefill_ref(q, kp, vp, tables[s:s + 1], ctx[s:s + 1], np.array([0, n]), w.softmax_scale, w.block_size)
+        refs.append(oracle.prefill_ref(q, kp, vp, tables[s:s + 1], ctx[s:s + 1], np.array([0, n]), w.softmax_scale,
+                                       w.block_size))
         spent += time.perf_counter() - t0
         done += 1
         flops += prefill_flops(w, ctx[s:s + 1].astype(np.int64), inp.chunk_lens[s:s + 1].astype(np.int64))
         if spent > budget_s:
             break
     blas_threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
-    return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
-            "sample": f"first {done} of {w.num_seqs} sequences of the same prefill step, all rows and heads, "
-                      f"fp64 numpy oracle, {spent:.1f} s wall",
-            "host_cores_available": len(os.sched_getaffinity(0))}
+    res = {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+           "sample": f"first {done} of {w.num_seqs} sequences of the same prefill step, all rows and heads, "
+                     f"fp64 numpy oracle, {spent:.1f} s wall",
+           "host_cores_available": len(os.sched_getaffinity(0))}
+    if gpu_out is not None:
+        got = gpu_out[: int(qsl[done])].cpu().to(torch.float64).numpy()
+        res["parity"] = parity_of(got, np.concatenate(refs), 2e-3, 1e-2)
+        res["parity"]["rows"] = f"every query row and head of the first {done} sequences"
+    return res
 
 
 def main_prefill(args, w):
@@ -275,9 +409,11 @@ def main_prefill(args, w):
 
     warm = warm_up(lambda: (reshape(), attend()), args.warmup)
     K = args.steps
+    flusher = Flusher(stream)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     torch.cuda.synchronize()
     for i in range(K):
+        flusher()
         ev[i][0].record(stream)
         reshape()
         ev[i][1].record(stream)
@@ -286,6 +422,7 @@ def main_prefill(args, w):
     torch.cuda.synchronize()
     t_attn = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)])
     t_step = np.array([ev[i][0].elapsed_time(ev[i][2]) for i in range(K)])
+    out_step = out.clone()
     flops = prefill_flops(w, ctx_np.astype(np.int64), inp.chunk_lens.astype(np.int64))
     attn_ms, step_ms = float(np.mean(t_attn)), float(np.mean(t_step))
     tokens = int(inp.chunk_lens.sum())
@@ -302,7 +439,12 @@ def main_prefill(args, w):
         "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_heads": w.num_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
                    "query_tokens": tokens, "sum_context": int(ctx_np.sum()), "max_context": max_ctx},
+        "timing": "mean of K steps, HIP events on the launch stream; before each step 512 MiB are written and "
+                  "another 512 MiB read (L2 and Infinity Cache cleared), outside the events",
         "tokens_per_s": round(tokens / (step_ms * 1e-3), 1),
+        "slot_utilisation": slot_utilisation(ctx_np, w.block_size),
+        "max_abs_err": None,
+        "max_rel_err": None,
         "components": {"reshape_and_cache_us": round(float(np.mean(t_step - t_attn)) * 1e3, 2),
                        "paged_prefill_attention_us": round(attn_ms * 1e3, 2),
                        "paged_prefill_attention_median_us": round(float(np.median(t_attn)) * 1e3, 2)},
@@ -312,7 +454,9 @@ def main_prefill(args, w):
                      "kv_bytes_per_call": int(ctx_np.sum()) * w.num_kv_heads * w.head_dim * 2 * inp.k_cache.element_size()},
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline_prefill(w, inp, tables_np, ctx_np, args.cpu_seconds)
+        cb = cpu_baseline_prefill(w, inp, tables_np, ctx_np, args.cpu_seconds, gpu_out=out_step)
+        result["cpu_baseline"] = cb
+        result["max_abs_err"], result["max_rel_err"] = cb["parity"]["max_abs_err"], cb["parity"]["max_rel_err"]
     print(json.dumps(result))
 
 
@@ -513,20 +657,17 @@ def main_shared_prefix(args, w):
 
     warm = warm_up(lambda: (cow(), attend(), attend_each()), args.warmup)
     K = args.steps
+    flusher = Flusher(stream)
 
     def timed(fn):
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
-        for i in range(K):
-            ev[i][0].record(stream)
-            fn()
-            ev[i][1].record(stream)
-        torch.cuda.synchronize()
-        return np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+        return timed_steps(fn, K, stream, flusher)
 
     t_step = timed(lambda: (cow(), attend()))
+    out_step = out.clone()
     t_attn = timed(attend)
     t_each = timed(attend_each)
     t_cow = timed(cow) if len(pairs) else None
+    t_hot = timed_steps(lambda: (cow(), attend()), K, stream)
     step_ms, attn_ms = float(np.mean(t_step)), float(np.mean(t_attn))
     if args.calibrate_copy:
         calibration_copy(w, kc.dtype, args.calibrate_copy, stream)
@@ -550,9 +691,14 @@ def main_shared_prefix(args, w):
                    "max_context": max_ctx, "num_blocks": w.num_blocks,
                    "plan": {"path": ["vector", "mfma"][plan[0]], "partition_tokens": plan[1],
                             "num_partitions": plan[2]}},
+        "timing": "mean of K steps, HIP events on the launch stream; before each step 512 MiB are written and "
+                  "another 512 MiB read (L2 and Infinity Cache cleared), outside the events",
         "pct_of_hbm_peak": round(100.0 * kv_logical / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
         "seq_per_s": round(w.num_seqs / (step_ms * 1e-3), 1),
         "kv_bytes_per_step": {"logical": kv_logical, "unique": kv_unique},
+        "slot_utilisation": slot_utilisation(ctx_np, w.block_size),
+        "max_abs_err": None,
+        "max_rel_err": None,
         "unique_gbps": round(kv_unique / (step_ms * 1e-3) / 1e9, 1),
         "sharing": {"logical_blocks": res["logical_blocks"], "unique_blocks": res["unique_blocks"],
                     "cow_pairs_during_generation": res["cow_pairs"], "cow_pairs_this_step": len(pairs),
@@ -560,6 +706,7 @@ def main_shared_prefix(args, w):
                     "shared_blocks_per_group": int(np.median(g_shared)) if len(g_shared) else 0,
                     "setup_s": round(t_setup, 2)},
         "components": {"copy_blocks_us": None if t_cow is None else round(float(np.mean(t_cow)) * 1e3, 2),
+                       "step_us_back_to_back": round(float(np.mean(t_hot)) * 1e3, 2),
                        "paged_attention_decode_shared_us": round(attn_ms * 1e3, 2),
                        "paged_attention_decode_shared_median_us": round(float(np.median(t_attn)) * 1e3, 2),
                        "paged_attention_decode_append_us": round(float(np.mean(t_each)) * 1e3, 2),
@@ -577,17 +724,20 @@ def main_shared_prefix(args, w):
         },
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline_shared(w, q, kc, vc, ks, vs, tables_np, ctx_np, args.cpu_seconds)
+        cb = cpu_baseline_shared(w, q, kc, vc, ks, vs, tables_np, ctx_np, args.cpu_seconds, gpu_out=out_step)
+        result["cpu_baseline"] = cb
+        result["max_abs_err"], result["max_rel_err"] = cb["parity"]["max_abs_err"], cb["parity"]["max_rel_err"]
     print(json.dumps(result))
 
 
-def cpu_baseline_shared(w, q, kc, vc, ks, vs, tables, ctx, budget_s):
-    """The oracle on whole samples (all heads) over the dequantised E4M3 codes, until the budget is spent."""
+def cpu_baseline_shared(w, q, kc, vc, ks, vs, tables, ctx, budget_s, gpu_out=None):
+    """The oracle on whole samples (all heads) over the dequantised E4M3 codes, until the budget is spent;
+    with ``gpu_out``, the samples it recomputed are compared with the GPU's rows (``parity``)."""
     import oracle
     import torch
     from threadpoolctl import threadpool_info
     qh = q.cpu().to(torch.float64).numpy()
-    done, kv_bytes, spent = 0, 0, 0.0
+    done, kv_bytes, spent, refs = 0, 0, 0.0, []
     for s in range(len(ctx)):
         n = int(ctx[s])
         nb = -(-n // w.block_size)
@@ -598,19 +748,23 @@ def cpu_baseline_shared(w, q, kc, vc, ks, vs, tables, ctx, budget_s):
         t0 = time.perf_counter()
         kp = oracle.decode_e4m3(kcodes) * np.float64(np.float32(ks))
         vp = oracle.decode_e4m3(vcodes) * np.float64(np.float32(vs))
-        oracle.attend_ref(qh[s:s + 1], kp, vp, local, ctx[s:s + 1], w.softmax_scale, w.block_size)
+        refs.append(oracle.attend_ref(qh[s:s + 1], kp, vp, local, ctx[s:s + 1], w.softmax_scale, w.block_size))
         spent += time.perf_counter() - t0
         done += 1
         kv_bytes += n * w.num_kv_heads * w.head_dim * 2
         if spent > budget_s:
             break
     blas_threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
-    return {"value": round(kv_bytes / spent / 1e9, 6), "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
-            "seq_per_s": round(done / spent, 3),
-            "sample": f"first {done} of {len(ctx)} samples of the same decode step, all {w.num_heads} heads "
-                      f"({kv_bytes / 1e6:.1f} MB of logical E4M3 KV, dequantised by the oracle), fp64 numpy "
-                      f"oracle, {spent:.1f} s wall",
-            "host_cores_available": len(os.sched_getaffinity(0))}
+    res = {"value": round(kv_bytes / spent / 1e9, 6), "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
+           "seq_per_s": round(done / spent, 3),
+           "sample": f"first {done} of {len(ctx)} samples of the same decode step, all {w.num_heads} heads "
+                     f"({kv_bytes / 1e6:.1f} MB of logical E4M3 KV, dequantised by the oracle), fp64 numpy "
+                     f"oracle, {spent:.1f} s wall",
+           "host_cores_available": len(os.sched_getaffinity(0))}
+    if gpu_out is not None:
+        res["parity"] = parity_of(gpu_out[:done].cpu().to(torch.float64).numpy(), np.concatenate(refs), 2e-3, 1e-2)
+        res["parity"]["rows"] = f"all (sample, head) rows of the first {done} samples"
+    return res
 
 
 def main():
@@ -621,11 +775,12 @@ def main():
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
-    from paged_kv_cache_259_amd import ops, synth
-    from paged_kv_cache_259_amd.block_manager import BlockManager
+    from paged_kv_cache_259_amd import synth
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload == "stream_probe":
+        return main_stream_probe(args)
     w = synth.WORKLOADS[args.workload]
     if isinstance(w, synth.PrefillWorkload):
         return main_prefill(args, w)
@@ -635,65 +790,153 @@ def main():
         return main_shared_prefix(args, w)
     if not isinstance(w, synth.DecodeWorkload):
         raise SystemExit("unknown workload kind: " + args.workload)
-    part = w.partition_size if args.partition is None else args.partition
+    return main_decode(args, w)
 
-    # ---- inputs: seeded, generated on the device; tables from the host block manager
-    inp = synth.make_decode_inputs(w, device=dev)
-    bm = BlockManager(inp.num_blocks, w.block_size, inp.free_list)
-    seqs = list(range(w.num_seqs))
-    for s in seqs:
-        bm.add_sequence(s, int(inp.context_lens[s]) - 1)           # cached before this step
-    slots = torch.tensor([bm.append_slot(s)[0] for s in seqs], dtype=torch.int64, device=dev)
-    tables_np = bm.block_table_array(seqs, w.max_blocks_per_seq)
-    ctx_np = bm.context_lens_array(seqs)
-    tables = torch.from_numpy(tables_np).to(dev)
-    ctx = torch.from_numpy(ctx_np).to(dev)
-    order = torch.from_numpy(bm.longest_first(seqs)).to(dev)      # host bookkeeping, like the tables
-    max_ctx = int(ctx_np.max())
-    qd, kvd = ops.dtype_code(inp.q.dtype), ops.dtype_code(inp.k_cache.dtype)
-    plan = ops.attention_plan(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size, max_ctx, part,
-                              qd, kvd)
-    ws_bytes = ops.attention_workspace_bytes(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size,
-                                             max_ctx, part, qd, kvd)
-    workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
-    out = torch.empty_like(inp.q)
+
+class DecodeState:
+    """One decode workload on the GPU: inputs drawn on the device, tables and slots from the host block manager
+    (the new token of every sequence gets its slot; the longest-first order is host bookkeeping too), and the
+    three ways to run its step."""
+
+    def __init__(self, w, part, dev, stream):
+        import torch
+        from paged_kv_cache_259_amd import ops, synth
+        from paged_kv_cache_259_amd.block_manager import BlockManager
+        self.w, self.part, self.stream = w, part, stream
+        self.inp = inp = synth.make_decode_inputs(w, device=dev)
+        bm = BlockManager(inp.num_blocks, w.block_size, inp.free_list)
+        self.seqs = seqs = list(range(w.num_seqs))
+        for s in seqs:
+            bm.add_sequence(s, int(inp.context_lens[s]) - 1)           # cached before this step
+        self.slots = torch.tensor([bm.append_slot(s)[0] for s in seqs], dtype=torch.int64, device=dev)
+        self.tables_np = bm.block_table_array(seqs, w.max_blocks_per_seq)
+        self.ctx_np = bm.context_lens_array(seqs)
+        self.tables = torch.from_numpy(self.tables_np).to(dev)
+        self.ctx = torch.from_numpy(self.ctx_np).to(dev)
+        self.order = torch.from_numpy(bm.longest_first(seqs)).to(dev)
+        self.max_ctx = int(self.ctx_np.max())
+        self.qd, self.kvd = ops.dtype_code(inp.q.dtype), ops.dtype_code(inp.k_cache.dtype)
+        self.plan = ops.attention_plan(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size,
+                                       self.max_ctx, part, self.qd, self.kvd)
+        ws_bytes = ops.attention_workspace_bytes(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size,
+                                                 self.max_ctx, part, self.qd, self.kvd)
+        self.workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+        self.out = torch.empty_like(inp.q)
+        self.kvs = dict(k_scale=w.kv_scale, v_scale=w.kv_scale) if w.kv8 else {}
+        elt_q, elt_kv = inp.q.element_size(), inp.k_cache.element_size()
+        self.kv_bytes, self.alg_bytes = algorithmic_bytes(w, self.ctx_np.astype(np.int64), elt_q, elt_kv)
+        self.append_bytes = (2 * w.num_seqs * w.num_kv_heads * w.head_dim * (inp.k_new.element_size() + elt_kv)
+                             + 8 * w.num_seqs)
+        self.step_bytes = self.alg_bytes + self.append_bytes
+
+    def reshape(self):
+        from paged_kv_cache_259_amd import ops
+        i = self.inp
+        ops.reshape_and_cache(i.k_new, i.v_new, i.k_cache, i.v_cache, self.slots, stream=self.stream, **self.kvs)
+
+    def attend(self, part=None, workspace=None):
+        from paged_kv_cache_259_amd import ops
+        i = self.inp
+        ops.paged_attention_decode(self.out, i.q, i.k_cache, i.v_cache, self.tables, self.ctx, self.w.softmax_scale,
+                                   self.max_ctx, partition_size=self.part if part is None else part,
+                                   workspace=self.workspace if workspace is None else workspace,
+                                   seq_order=self.order, stream=self.stream, **self.kvs)
+
+    def step(self, part=None, workspace=None):
+        """The whole step in one launch: write the new tokens, attend."""
+        from paged_kv_cache_259_amd import ops
+        i = self.inp
+        ops.paged_attention_decode_append(self.out, i.q, i.k_cache, i.v_cache, i.k_new, i.v_new, self.slots,
+                                          self.tables, self.ctx, self.w.softmax_scale, self.max_ctx,
+                                          partition_size=self.part if part is None else part,
+                                          workspace=self.workspace if workspace is None else workspace,
+                                          seq_order=self.order, stream=self.stream, **self.kvs)
+
+    def plan_json(self, plan=None):
+        plan = plan or self.plan
+        return {"path": ["vector", "mfma"][plan[0]], "partition_tokens": plan[1], "num_partitions": plan[2],
+                "mode": ("one pass" if plan[2] == 1 else "balanced slices" if plan[1] == 0 else "fixed partitions")}
+
+    def pct(self, ms, nbytes=None):
+        return 100.0 * (self.step_bytes if nbytes is None else nbytes) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS
+
+
+def decode_component(name, args, dev, stream, flusher, probe_gbps):
+    """Another decode workload timed in the same run (flushed and back to back); its oracle parity on a few
+    sequences unless the CPU baseline is off."""
+    from paged_kv_cache_259_amd import synth
+    w = synth.WORKLOADS[name]
+    st = DecodeState(w, w.partition_size, dev, stream)
+    warm_up(st.step, args.warmup)
+    t_flush = timed_steps(st.step, args.steps, stream, flusher)
+    t_hot = timed_steps(st.step, args.steps, stream)
+    out_step = st.out.clone()
+    ms, ms_hot = float(np.mean(t_flush)), float(np.mean(t_hot))
+    achieved = st.step_bytes / (ms * 1e-3) / 1e9
+    comp = {"workload": w.name, "plan": st.plan_json(), "step_us": round(ms * 1e3, 2),
+            "step_median_us": round(float(np.median(t_flush)) * 1e3, 2),
+            "step_us_back_to_back": round(ms_hot * 1e3, 2),
+            "kv_gbps": round(st.kv_bytes / (ms * 1e-3) / 1e9, 1),
+            "achieved_gbps": round(achieved, 1), "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "frac_back_to_back": round(st.pct(ms_hot) / 100, 4),
+            "pct_of_measured_stream_bw": round(100.0 * achieved / probe_gbps, 2) if probe_gbps else None,
+            "seq_per_s": round(w.num_seqs / (ms * 1e-3), 1),
+            "algorithmic_bytes_per_call": st.step_bytes,
+            "slot_utilisation": slot_utilisation(st.ctx_np, w.block_size),
+            "traffic": measured_traffic(name)}
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(w, {"q": st.inp.q, "k": st.inp.k_cache, "v": st.inp.v_cache}, st.tables_np, st.ctx_np,
+                          min(args.cpu_seconds, 5.0), gpu_out=out_step)
+        comp["parity"] = cb["parity"]
+        comp["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "sample")}
+    del st
+    return comp
+
+
+def main_stream_probe(args):
+    """What HBM delivers to read-only kernels on this machine (the decode roofline's achievable ceiling)."""
+    import torch
     stream = torch.cuda.current_stream()
-    kvs = dict(k_scale=w.kv_scale, v_scale=w.kv_scale) if w.kv8 else {}
+    res = hbm_probe(stream, reps=max(args.steps // 10, 5))
+    print(json.dumps({
+        "metric": "HBM read GB/s of a streaming read kernel and of random-tile reads (% of 8 TB/s)",
+        "value": res["stream_read_gbps"], "unit": "GB/s", "n_gpus": 1, "steps": max(args.steps // 10, 5),
+        "warmup": 3, "ms_per_step": None, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "u8", "data": "synthetic (1 GiB of ones)", "config": {"workload": "stream_probe"},
+        "pct_of_hbm_peak": round(100.0 * res["stream_read_gbps"] / HBM_PEAK_GBPS, 2), "probe": res,
+        "roofline": {"bound": "hbm", "kernel": "stream_read_kernel", "achieved": res["stream_read_gbps"],
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(res["stream_read_gbps"] / HBM_PEAK_GBPS, 4),
+                     "traffic": None}}))
 
-    def reshape():
-        ops.reshape_and_cache(inp.k_new, inp.v_new, inp.k_cache, inp.v_cache, slots, stream=stream, **kvs)
 
-    def attend():
-        ops.paged_attention_decode(out, inp.q, inp.k_cache, inp.v_cache, tables, ctx, w.softmax_scale, max_ctx,
-                                   partition_size=part, workspace=workspace, seq_order=order, stream=stream, **kvs)
+def main_decode(args, w):
+    import torch
+    from paged_kv_cache_259_amd import ops, synth
 
-    def step():                          # the whole step in one launch: write the new tokens, attend
-        ops.paged_attention_decode_append(out, inp.q, inp.k_cache, inp.v_cache, inp.k_new, inp.v_new, slots, tables,
-                                          ctx, w.softmax_scale, max_ctx, partition_size=part, workspace=workspace,
-                                          seq_order=order, stream=stream, **kvs)
+    dev = torch.device("cuda:0")
+    part = w.partition_size if args.partition is None else args.partition
+    stream = torch.cuda.current_stream()
+    st = DecodeState(w, part, dev, stream)
+    inp, tables_np, ctx_np, seqs = st.inp, st.tables_np, st.ctx_np, st.seqs
+    flusher = Flusher(stream)
 
-    warm = warm_up(lambda: (reshape(), attend(), step()), args.warmup)
-
+    warm = warm_up(lambda: (st.reshape(), st.attend(), st.step()), args.warmup)
     K = args.steps
-    # the timed step: decode with append
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
-    torch.cuda.synchronize()
+    # the timed step: decode with append, caches flushed before every step (the headline), then back to back
     t0 = time.perf_counter()
-    for i in range(K):
-        evs[i][0].record(stream)
-        step()
-        evs[i][1].record(stream)
-    torch.cuda.synchronize()
+    t_step = timed_steps(st.step, K, stream, flusher)
     wall = time.perf_counter() - t0
-    t_step = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in range(K)])
-    step_ms = float(np.mean(t_step))
+    out_step = st.out.clone()
+    t_hot = timed_steps(st.step, K, stream)
+    step_ms, hot_ms = float(np.mean(t_step)), float(np.mean(t_hot))
     # the same step as two launches (reshape_and_cache, then decode), for the components
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     for i in range(K):
+        flusher()
         ev[i][0].record(stream)
-        reshape()
+        st.reshape()
         ev[i][1].record(stream)
-        attend()
+        st.attend()
         ev[i][2].record(stream)
     torch.cuda.synchronize()
     t_reshape = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)])
@@ -704,29 +947,15 @@ def main():
     # (not in counter runs, which must hold only the timed step's kernels)
     auto = None
     if part and not args.calibrate_copy:
-        auto_plan = ops.attention_plan(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size, max_ctx, 0,
-                                       qd, kvd)
+        auto_plan = ops.attention_plan(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size, st.max_ctx,
+                                       0, st.qd, st.kvd)
         auto_ws = torch.empty(max(ops.attention_workspace_bytes(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim,
-                                                                w.block_size, max_ctx, 0, qd, kvd), 256),
+                                                                w.block_size, st.max_ctx, 0, st.qd, st.kvd), 256),
                               dtype=torch.uint8, device=dev)
-
-        def step_auto():
-            ops.paged_attention_decode_append(out, inp.q, inp.k_cache, inp.v_cache, inp.k_new, inp.v_new, slots,
-                                              tables, ctx, w.softmax_scale, max_ctx, partition_size=0,
-                                              workspace=auto_ws, seq_order=order, stream=stream, **kvs)
-
-        warm_up(step_auto, 10)
-        ea = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
-        for i in range(K):
-            ea[i][0].record(stream)
-            step_auto()
-            ea[i][1].record(stream)
-        torch.cuda.synchronize()
-        t_auto = float(np.mean([ea[i][0].elapsed_time(ea[i][1]) for i in range(K)]))
-        auto = {"plan": {"path": ["vector", "mfma"][auto_plan[0]],
-                         "mode": "balanced slices" if auto_plan[1] == 0 else "partitions",
-                         "slices_or_partitions": auto_plan[2]},
-                "step_us": round(t_auto * 1e3, 2)}
+        warm_up(lambda: st.step(0, auto_ws), 10)
+        t_auto = float(np.mean(timed_steps(lambda: st.step(0, auto_ws), K, stream, flusher)))
+        auto = {"plan": st.plan_json(auto_plan), "step_us": round(t_auto * 1e3, 2),
+                "pct_of_hbm_peak": round(st.pct(t_auto), 2)}
 
     # ---- copy_blocks on copy-on-write pairs shaped like the shared-prefix workload (timed separately)
     sp = synth.SHARED_PREFIX_FP8
@@ -773,15 +1002,17 @@ def main():
     if args.calibrate_copy:
         calibration_copy(w, inp.k_cache.dtype, args.calibrate_copy, stream)
 
-    elt_q, elt_kv = inp.q.element_size(), inp.k_cache.element_size()
-    kv_bytes, alg_bytes = algorithmic_bytes(w, ctx_np.astype(np.int64), elt_q, elt_kv)
-    append_bytes = 2 * w.num_seqs * w.num_kv_heads * w.head_dim * (inp.k_new.element_size() + elt_kv) + 8 * w.num_seqs
+    # ---- what HBM delivers to a read-only kernel here, and the GQA step beside the headline workload
+    probe = None if args.calibrate_copy else hbm_probe(stream)
+    probe_gbps = probe["stream_read_gbps"] if probe else None
+    gqa = None
+    if args.workload == "llama13b_f16" and not args.calibrate_copy and not args.no_components:
+        gqa = decode_component("gqa_bf16", args, dev, stream, flusher, probe_gbps)
+
+    kv_bytes, alg_bytes = st.kv_bytes, st.alg_bytes
     attn_ms = float(np.mean(t_attn))
-    achieved = (alg_bytes + append_bytes) / (step_ms * 1e-3) / 1e9
+    achieved = st.step_bytes / (step_ms * 1e-3) / 1e9
     traffic = measured_traffic(args.workload)
-    if auto is not None:
-        auto["pct_of_hbm_peak"] = round(100.0 * (alg_bytes + append_bytes) / (auto["step_us"] * 1e-6) / 1e9
-                                        / HBM_PEAK_GBPS, 2)
     result = {
         "metric": "paged decode KV-read GB/s (% of HBM peak) + sequences/sec per decode step",
         "value": round(kv_bytes / (step_ms * 1e-3) / 1e9, 1),
@@ -789,6 +1020,8 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": warm,
+        "warmup_requested": args.warmup,
+        "warmup_note": f"warm-up runs at least --warmup steps and at least {int(WARMUP_MIN_S * 1e3)} ms of GPU work",
         "ms_per_step": round(step_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -800,15 +1033,23 @@ def main():
         "config": {
             "workload": w.name, "num_seqs": w.num_seqs, "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads,
             "head_dim": w.head_dim, "block_size": w.block_size, "q_dtype": w.q_dtype, "kv_dtype": w.kv_dtype,
-            "sum_context": int(ctx_np.sum()), "max_context": max_ctx, "num_blocks": inp.num_blocks,
-            "plan": {"path": ["vector", "mfma"][plan[0]], "partition_tokens": plan[1], "num_partitions": plan[2]},
+            "sum_context": int(ctx_np.sum()), "max_context": st.max_ctx, "num_blocks": inp.num_blocks,
+            "plan": st.plan_json(),
         },
+        "timing": "mean of K steps, HIP events on the launch stream; before each step 512 MiB are written and "
+                  "another 512 MiB read (L2 and Infinity Cache cleared), outside the events",
         "pct_of_hbm_peak": round(100.0 * kv_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+        "pct_of_measured_stream_bw": round(100.0 * achieved / probe_gbps, 2) if probe_gbps else None,
         "seq_per_s": round(w.num_seqs / (step_ms * 1e-3), 1),
         "kv_bytes_per_step": kv_bytes,
+        "slot_utilisation": slot_utilisation(ctx_np, w.block_size),
+        "max_abs_err": None,
+        "max_rel_err": None,
         "components": {
             "paged_attention_decode_append_us": round(step_ms * 1e3, 2),
             "paged_attention_decode_append_median_us": round(float(np.median(t_step)) * 1e3, 2),
+            "step_us_back_to_back": round(hot_ms * 1e3, 2),
+            "frac_back_to_back": round(st.pct(hot_ms) / 100, 4),
             "two_launch_step_us": round(float(np.mean(t_split)) * 1e3, 2),
             "reshape_and_cache_us": round(float(np.mean(t_reshape)) * 1e3, 2),
             "paged_attention_decode_us": round(attn_ms * 1e3, 2),
@@ -824,6 +1065,8 @@ def main():
                             "out_us": round(swap_out_ms * 1e3, 1), "in_us": round(swap_in_ms * 1e3, 1),
                             "out_gbps": round(sw_bytes / (swap_out_ms * 1e-3) / 1e9, 1),
                             "in_gbps": round(sw_bytes / (swap_in_ms * 1e-3) / 1e9, 1)},
+            "hbm_probe": probe,
+            "gqa_bf16": gqa,
         },
         "roofline": {
             "bound": "hbm",
@@ -834,12 +1077,15 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "algorithmic_bytes_per_call": alg_bytes + append_bytes,
+            "algorithmic_bytes_per_call": st.step_bytes,
         },
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, {"q": inp.q, "k": inp.k_cache, "v": inp.v_cache}, tables_np,
-                                              ctx_np, args.cpu_seconds)
+        cb = cpu_baseline(w, {"q": inp.q, "k": inp.k_cache, "v": inp.v_cache}, tables_np, ctx_np, args.cpu_seconds,
+                          gpu_out=out_step)
+        result["cpu_baseline"] = cb
+        result["max_abs_err"] = cb["parity"]["max_abs_err"]
+        result["max_rel_err"] = cb["parity"]["max_rel_err"]
     print(json.dumps(result))
 
 

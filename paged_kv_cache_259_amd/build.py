@@ -3,7 +3,10 @@
     python -m paged_kv_cache_259_amd.build          # or: python paged_kv_cache_259_amd/build.py
 
 Each ``csrc/*.hip`` is compiled to an object in parallel under ``_build/``, then
-linked into ``paged_kv_cache_259_amd/libpkv.so``.  Flags:
+linked into ``paged_kv_cache_259_amd/libpkv.so``.  The benchmark's HBM read
+probes (``probe/*.hip``, include/pkv_probe.h) go into a library of their own,
+``paged_kv_cache_259_amd/libpkv_probe.so``, so the paged-KV library holds only
+the path.  Flags:
 * ``--offload-arch=gfx950``, ``-O3``, no fast-math;
 * ``-fhip-fp32-correctly-rounded-divide-sqrt``: the FP8 encode divides by the
   scale in IEEE single precision;
@@ -22,6 +25,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpkv.so")
+PROBE_SRC = os.path.join(PKG, "probe")
+PROBE_LIB = os.path.join(PKG, "libpkv_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -51,9 +56,19 @@ def _compile(src, extra=()):
     return obj, msgs
 
 
-def build(verbose=True, defines=(), out=None, build_dir=None, csrc=None):
+def _link(objs, lib):
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
+    os.replace(tmp, lib)
+
+
+def build(verbose=True, defines=(), out=None, build_dir=None, csrc=None, probe=True):
     """Compile and link; ``defines`` are extra -D flags (tuning constants), ``out`` the .so path,
-    ``csrc`` another source directory with the same files (default: the package's csrc/)."""
+    ``csrc`` another source directory with the same files (default: the package's csrc/);
+    ``probe`` also builds libpkv_probe.so (the default build does)."""
     global BUILD
     lib = out or LIB
     src_dir = csrc or CSRC
@@ -61,19 +76,22 @@ def build(verbose=True, defines=(), out=None, build_dir=None, csrc=None):
     os.makedirs(BUILD, exist_ok=True)
     extra = [f"-D{d}" for d in defines]
     srcs = sorted(os.path.join(src_dir, f) for f in os.listdir(src_dir) if f.endswith(".hip"))
+    if probe:
+        srcs += sorted(os.path.join(PROBE_SRC, f) for f in os.listdir(PROBE_SRC) if f.endswith(".hip"))
     with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         results = list(ex.map(lambda f: _compile(f, extra), srcs))
     for obj, msgs in results:
         if msgs.strip() and verbose:
             print(msgs)
-    tmp = lib + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *[o for o, _ in results]]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, lib)
+    objs = [o for o, _ in results]
+    probe_objs = [o for o in objs if os.path.basename(o)[:-2] in os.listdir(PROBE_SRC)] if probe else []
+    _link([o for o in objs if o not in probe_objs], lib)
     if verbose:
         print(f"built {lib}")
+    if probe_objs:
+        _link(probe_objs, PROBE_LIB)
+        if verbose:
+            print(f"built {PROBE_LIB}")
     return lib
 
 

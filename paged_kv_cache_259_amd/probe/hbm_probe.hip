@@ -1,0 +1,123 @@
+// hbm_probe.hip -- the read-rate probes declared in include/pkv_probe.h: what a
+// read-only kernel gets from HBM on the machine at hand, measured beside the
+// decode step by the benchmark.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pkv_probe.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kInFlight = 8;   // 16-byte loads per thread per round of the stream read
+
+__device__ __forceinline__ uint32_t fold(const uint4& v) { return v.x ^ v.y ^ v.z ^ v.w; }
+
+// Each wave reads whole 8 KiB chunks (eight 1 KiB loads of consecutive bytes,
+// all in flight together); wave w takes chunks w, w + W, w + 2W, ... of the
+// buffer (W waves in the grid), so at any time the grid reads one contiguous
+// stretch.  The bytes past the last whole chunk are read one 16-byte load per
+// lane.
+__global__ __launch_bounds__(kThreads) void stream_read_kernel(const uint4* __restrict__ buf, uint64_t n16,
+                                                               uint32_t salt, uint32_t* __restrict__ sink) {
+  constexpr uint64_t kChunk16 = 64 * kInFlight;            // 16-byte units per chunk
+  const int lane = threadIdx.x & 63;
+  const uint64_t waves = (uint64_t)gridDim.x * (kThreads / 64);
+  const uint64_t wave = (uint64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const uint64_t chunks = n16 / kChunk16;
+  uint32_t acc = 0;
+  for (uint64_t c = wave; c < chunks; c += waves) {
+    const uint4* p = buf + c * kChunk16 + lane;
+    uint4 v[kInFlight];
+#pragma unroll
+    for (int k = 0; k < kInFlight; ++k) v[k] = p[k * 64];
+#pragma unroll
+    for (int k = 0; k < kInFlight; ++k) acc ^= fold(v[k]);
+  }
+  for (uint64_t i = chunks * kChunk16 + wave * 64 + lane; i < n16; i += waves * 64) acc ^= fold(buf[i]);
+  if (acc == salt) sink[0] = acc;
+}
+
+__device__ __forceinline__ uint64_t tile_index(uint32_t wave, int i, uint32_t salt, uint64_t num_tiles) {
+  uint64_t x = (uint64_t)wave * 1000003ull + (uint64_t)i * 7919ull + salt;   // splitmix-style finaliser
+  x ^= x >> 33;
+  x *= 0xff51afd7ed558ccdull;
+  x ^= x >> 33;
+  return x % num_tiles;
+}
+
+template <int TILE>
+__global__ __launch_bounds__(kThreads) void tile_read_kernel(const uint4* __restrict__ buf, uint64_t num_tiles,
+                                                             int per_wave, uint32_t salt,
+                                                             uint32_t* __restrict__ sink) {
+  constexpr int LOADS = TILE / (64 * 16);   // 16-byte loads per lane per tile
+  const int lane = threadIdx.x & 63;
+  const uint32_t wave = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  uint32_t acc = 0;
+  uint4 a[LOADS], b[LOADS];
+  auto issue = [&](int i, uint4* t) {
+    const uint4* p = buf + tile_index(wave, i, salt, num_tiles) * (TILE / 16) + lane;
+#pragma unroll
+    for (int k = 0; k < LOADS; ++k) t[k] = p[k * 64];
+  };
+  auto use = [&](const uint4* t) {
+#pragma unroll
+    for (int k = 0; k < LOADS; ++k) acc ^= fold(t[k]);
+  };
+  if (per_wave <= 0) return;
+  issue(0, a);
+  for (int i = 0; i < per_wave; i += 2) {
+    if (i + 1 < per_wave) issue(i + 1, b);
+    use(a);
+    if (i + 1 < per_wave) {
+      if (i + 2 < per_wave) issue(i + 2, a);
+      use(b);
+    }
+  }
+  if (acc == salt) sink[0] = acc;
+}
+
+template <int TILE>
+hipError_t launch_tiles(const uint4* buf, uint64_t num_tiles, int wgs, int per_wave, uint32_t salt, uint32_t* sink,
+                        hipStream_t s) {
+  hipLaunchKernelGGL(tile_read_kernel<TILE>, dim3(wgs), dim3(kThreads), 0, s, buf, num_tiles, per_wave, salt, sink);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_probe_stream_read(const void* buf, size_t bytes, int num_workgroups, unsigned salt, unsigned* sink,
+                          void* stream) {
+  if (!buf || !sink) return -1;
+  if (bytes == 0 || bytes % 16 != 0 || num_workgroups <= 0 || (reinterpret_cast<uintptr_t>(buf) & 15u)) return -2;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(stream_read_kernel, dim3(num_workgroups), dim3(kThreads), 0,
+                     reinterpret_cast<hipStream_t>(stream), reinterpret_cast<const uint4*>(buf),
+                     (uint64_t)(bytes / 16), (uint32_t)salt, reinterpret_cast<uint32_t*>(sink));
+  return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+int pkv_probe_tile_read(const void* buf, size_t bytes, int tile_bytes, int num_workgroups, int tiles_per_wave,
+                        unsigned salt, unsigned* sink, void* stream) {
+  if (!buf || !sink) return -1;
+  if (num_workgroups <= 0 || tiles_per_wave <= 0 || (reinterpret_cast<uintptr_t>(buf) & 15u)) return -2;
+  if (tile_bytes != 1024 && tile_bytes != 2048 && tile_bytes != 4096 && tile_bytes != 8192) return -2;
+  const uint64_t num_tiles = bytes / (size_t)tile_bytes;   // whole tiles only: every load stays inside buf
+  if (num_tiles == 0) return -2;
+  const uint4* b = reinterpret_cast<const uint4*>(buf);
+  uint32_t* k = reinterpret_cast<uint32_t*>(sink);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  hipError_t e;
+  switch (tile_bytes) {
+    case 1024: e = launch_tiles<1024>(b, num_tiles, num_workgroups, tiles_per_wave, salt, k, s); break;
+    case 2048: e = launch_tiles<2048>(b, num_tiles, num_workgroups, tiles_per_wave, salt, k, s); break;
+    case 4096: e = launch_tiles<4096>(b, num_tiles, num_workgroups, tiles_per_wave, salt, k, s); break;
+    default: e = launch_tiles<8192>(b, num_tiles, num_workgroups, tiles_per_wave, salt, k, s); break;
+  }
+  return e == hipSuccess ? 0 : -7;
+}
+
+}  // extern "C"
