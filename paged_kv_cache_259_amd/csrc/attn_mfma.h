@@ -478,7 +478,32 @@ __device__ __forceinline__ void attn_mfma_body(AttnParams p) {
   }
 
   int seq, kvh, part;
-  decode_work_id(L, p.num_seqs, p.num_kv_heads, seq, kvh, part);
+  if (p.compact_partitions) {
+    // Fixed partitions: work id -> (kv head, position in the stream of
+    // (sequence, partition) units of that head), sequence by sequence, where
+    // sequence s owns max(1, its partitions) consecutive units (an empty
+    // context keeps one, which writes its zero output).  Only units with work
+    // exist; ids past the stream's end leave at once.
+    const int S = p.num_seqs;
+    kvh = (int)(L % (uint32_t)p.num_kv_heads);
+    const int pos = (int)(L / (uint32_t)p.num_kv_heads);
+    block_prefix<NW * 64>(p.context_lens, S, p.ctx_cap, p.partition_blocks * A::BS, sm.prefix, sm.wsum, true);
+    if (pos >= sm.prefix[S]) return;                        // uniform: past the stream
+    int lo = 1, hi = S;                                     // first i with prefix[i] > pos
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (sm.prefix[mid] > pos) hi = mid; else lo = mid + 1;
+    }
+    seq = lo - 1;
+    part = pos - sm.prefix[seq];
+  } else {
+    decode_work_id(L, p.num_seqs, p.num_kv_heads, seq, kvh, part);
+    // Fixed partitions: the last partition index first.  Shorter contexts have
+    // no partition at the high indices, so the workgroups that find nothing to
+    // do are dispatched while the GPU fills, and the grid ends with low
+    // partitions, which every context has.
+    if (p.num_partitions > 1 && PKV_PARTITIONS_REVERSED) part = p.num_partitions - 1 - part;
+  }
   apply_head_scales(p, kvh);
   if (p.longest_first) {                                    // one pass only
     if (p.seq_order) {

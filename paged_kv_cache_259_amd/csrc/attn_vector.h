@@ -362,6 +362,11 @@ __device__ __forceinline__ void attn_vector_body(AttnParams p) {
   // fixed partitions of partition_blocks blocks (one pass when num_partitions == 1)
   int seq, head, part;
   decode_work_id(L, p.num_seqs, p.num_heads, seq, head, part);
+  // Fixed partitions: the last partition index first.  Shorter contexts have
+  // no partition at the high indices, so the workgroups that find nothing to do
+  // are dispatched while the GPU fills, and the grid ends with low partitions,
+  // which every context has.
+  if (p.num_partitions > 1 && PKV_PARTITIONS_REVERSED) part = p.num_partitions - 1 - part;
   apply_head_scales(p, head / p.group);
   if (p.longest_first) {                                    // one pass only
     if (p.seq_order) {

@@ -88,6 +88,11 @@ uint32_t head_run_units_for(int mode, int units) {
   return units >= 16 && units % 8 == 0 ? (uint32_t)units : 0;
 }
 
+bool compact_partitions_env() {
+  const char* e = getenv("PKV_COMPACT_PARTITIONS");
+  return !(e && *e == '0');
+}
+
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 int make_plan(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size, int max_context_len,
@@ -289,6 +294,15 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   p.total_wgs = (uint32_t)(pl.mode == kSlices ? (size_t)pl.num_parts * pl.units
                                               : (size_t)num_seqs * pl.units * pl.num_parts);
   p.xcd_chunk = (uint32_t)xcd_chunk_for(pl.mode);
+  // Fixed partitions on the matrix-core family walk the units that exist,
+  // sequence by sequence, each XCD on one kv head (hardware order): long-context
+  // split-K at 512-token partitions 474.5 -> 464.5 us against the reversed
+  // partition-major grid.  PKV_COMPACT_PARTITIONS=0 keeps the grid.
+  if (pl.mode == kPartitions && pl.path == PKV_PATH_MFMA && num_seqs <= pkv::kMaxSliceSeqs &&
+      compact_partitions_env()) {
+    p.compact_partitions = 1;
+    if (xcd_chunk_env() < 0) p.xcd_chunk = 0;
+  }
   p.head_run_units = head_run_units_for(pl.mode, pl.units);
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

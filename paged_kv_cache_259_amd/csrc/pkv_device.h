@@ -255,6 +255,9 @@ __device__ __forceinline__ uint32_t head_runs(uint32_t i, uint32_t units) {
 #ifndef PKV_HEAD_FASTEST
 #define PKV_HEAD_FASTEST 1
 #endif
+#ifndef PKV_PARTITIONS_REVERSED
+#define PKV_PARTITIONS_REVERSED 1
+#endif
 __device__ __forceinline__ void decode_work_id(uint32_t L, int num_seqs, int num_units, int& seq, int& unit,
                                                int& part) {
   if constexpr (PKV_HEAD_FASTEST) {
@@ -296,7 +299,8 @@ __device__ __forceinline__ int slice_of(int64_t x, int64_t T, int ns) {
 // s_prefix[s] for s = 0..S (s_prefix[S] = T).  Every thread of the workgroup
 // calls it; NT threads, S <= kMaxSliceSeqs.  Ends with a barrier.
 template <int NT>
-__device__ void block_prefix(const int32_t* context_lens, int S, int ctx_cap, int bs, int* s_prefix, int* s_wsum) {
+__device__ void block_prefix(const int32_t* context_lens, int S, int ctx_cap, int bs, int* s_prefix, int* s_wsum,
+                             bool at_least_one = false) {
   constexpr int PER = (kMaxSliceSeqs + NT - 1) / NT;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int v[PER];
@@ -307,6 +311,7 @@ __device__ void block_prefix(const int32_t* context_lens, int S, int ctx_cap, in
     int c = idx < S ? context_lens[idx] : 0;
     c = c < 0 ? 0 : (c > ctx_cap ? ctx_cap : c);
     v[i] = (c + bs - 1) / bs;
+    if (at_least_one && idx < S && v[i] == 0) v[i] = 1;   // an empty context still owns one (zero-output) item
     local += v[i];
   }
   int x = local;
@@ -442,6 +447,8 @@ struct AttnParams {
   const float* v_scales;   // [num_kv_heads] or NULL (then v_scale applies)
   float qk_scale;          // scale * log2(e) * k_scale
   float v_scale;
+  int compact_partitions;   // fixed partitions: work ids walk the (sequence, partition) units that exist,
+                            // sequence by sequence, per head unit (else the partition-major grid)
   uint32_t total_wgs;
   uint32_t xcd_chunk;       // see xcd_remap
   uint32_t head_run_units;  // > 0: one pass, workgroup -> work id through head_runs (xcd_chunk unused)
