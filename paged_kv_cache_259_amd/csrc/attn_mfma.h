@@ -179,25 +179,29 @@ struct MfmaAttention {
     bool ok;
   };
 
-  // Rows at or past `valid` (the last block's tail) are not loaded: their
-  // registers are never used unmasked.
+  // Every lane loads unconditionally, so the compiler can count the loads in
+  // flight and wait only for the tile being consumed (a load under a per-lane
+  // condition makes it wait for every load, the next tile's too).  A row at or
+  // past `valid` (the last block's tail) reads the block's last real row
+  // instead -- the same cache lines, no extra memory traffic -- and consume
+  // masks it; a table entry outside the pool reads block 0 and the block is
+  // skipped.
   __device__ static void issue(const AttnParams& p, const char* kbase, const char* vbase, size_t block_stride,
                                int blk, int valid, int c16, int g4, Tiles& t) {
     t.ok = blk >= 0 && blk < p.num_blocks;
-    if (!t.ok) return;                                  // wave-uniform
-    const char* kp = kbase + (size_t)blk * block_stride;
-    const char* vp = vbase + (size_t)blk * block_stride;
-    if (c16 < valid) {
+    const size_t boff = (size_t)(t.ok ? blk : 0) * block_stride;
+    const int krow = c16 < valid ? c16 : valid - 1;     // valid >= 1: every block has a real token
+    const char* kp = kbase + boff + (ptrdiff_t)(krow - c16) * (ptrdiff_t)ROW_BYTES;
 #pragma unroll
-      for (int c = 0; c < NK; ++c) t.k[c] = *reinterpret_cast<const uint4*>(kp + c * (KV8 ? 16 : 64));
-    }
+    for (int c = 0; c < NK; ++c) t.k[c] = *reinterpret_cast<const uint4*>(kp + c * (KV8 ? 16 : 64));
+    const char* vp = vbase + boff;
 #pragma unroll
     for (int tg = 0; tg < 4; ++tg) {
-      if (g4 * 4 + tg < valid) {
+      const int row = g4 * 4 + tg;
+      const ptrdiff_t vrow = (ptrdiff_t)((row < valid ? row : valid - 1) - g4 * 4) * (ptrdiff_t)ROW_BYTES;
 #pragma unroll
-        for (int hh = 0; hh < NH; ++hh)
-          t.v[tg][hh] = *reinterpret_cast<const VLoad*>(vp + tg * ROW_BYTES + hh * 128 * KT::bytes);
-      }
+      for (int hh = 0; hh < NH; ++hh)
+        t.v[tg][hh] = *reinterpret_cast<const VLoad*>(vp + vrow + hh * 128 * KT::bytes);
     }
   }
 
@@ -346,14 +350,18 @@ struct MfmaAttention {
     Tiles a;
     issue(p, kbase, vbase, block_stride, id_of(0), valid_of(0), c16, g4, a);
     if constexpr (PIPE) {
+      // Both tile sets are refilled on every pass, also past the wave's last
+      // block (which is then loaded again -- cached, never consumed): loads
+      // under a branch would make the compiler wait for all loads in flight
+      // before each consume instead of only the consumed tile's.
       Tiles b;
       for (int i = 0; i < n; i += 2) {
-        if (i + 1 < n) issue(p, kbase, vbase, block_stride, id_of(i + 1), valid_of(i + 1), c16, g4, b);
+        const int i1 = i + 1 < n ? i + 1 : n - 1;
+        const int i2 = i + 2 < n ? i + 2 : n - 1;
+        issue(p, kbase, vbase, block_stride, id_of(i1), valid_of(i1), c16, g4, b);
         consume<MASK>(p, qop, a, valid_of(i), c16, g4, vt, st, col_on);
-        if (i + 1 < n) {
-          if (i + 2 < n) issue(p, kbase, vbase, block_stride, id_of(i + 2), valid_of(i + 2), c16, g4, a);
-          consume<MASK>(p, qop, b, valid_of(i + 1), c16, g4, vt, st, col_on);
-        }
+        issue(p, kbase, vbase, block_stride, id_of(i2), valid_of(i2), c16, g4, a);
+        if (i + 1 < n) consume<MASK>(p, qop, b, valid_of(i + 1), c16, g4, vt, st, col_on);
       }
     } else {
       for (int i = 0; i < n; ++i) {

@@ -119,20 +119,25 @@ struct VectorAttention {
     bool ok;
   };
 
-  // Rows at or past `valid` (the last block's tail) are not loaded: their
-  // registers are never used unmasked.
+  // Every lane loads unconditionally, so the compiler can count the loads in
+  // flight and wait only for the tile being consumed (a load under a per-lane
+  // condition makes it wait for every load, the next tile's too).  A row at or
+  // past `valid` (the last block's tail) reads the block's last real row
+  // instead -- the same cache lines, no extra memory traffic -- and consume
+  // masks it; a table entry outside the pool reads block 0 and the block is
+  // skipped.
   __device__ static void issue(const AttnParams& p, const char* kbase, const char* vbase, size_t block_stride,
                                int blk, int valid, int row, Tiles& t) {
     t.ok = blk >= 0 && blk < p.num_blocks;                  // out-of-pool entries are skipped
-    if (!t.ok) return;
-    const char* kp = kbase + (size_t)blk * block_stride;
-    const char* vp = vbase + (size_t)blk * block_stride;
+    const size_t boff = (size_t)(t.ok ? blk : 0) * block_stride;
+    const char* kp = kbase + boff;
+    const char* vp = vbase + boff;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      if (i * RPW + row < valid) {
-        t.k[i] = *reinterpret_cast<const uint4*>(kp + i * RPW * ROW_BYTES);
-        t.v[i] = *reinterpret_cast<const uint4*>(vp + i * RPW * ROW_BYTES);
-      }
+      const int r = i * RPW + row;                            // valid >= 1: every block has a real token
+      const ptrdiff_t off = (ptrdiff_t)((r < valid ? r : valid - 1) - row) * (ptrdiff_t)ROW_BYTES;
+      t.k[i] = *reinterpret_cast<const uint4*>(kp + off);
+      t.v[i] = *reinterpret_cast<const uint4*>(vp + off);
     }
   }
 
@@ -225,15 +230,19 @@ struct VectorAttention {
       const int r = ctx - (first + i * NW) * BS;
       return r < BS ? r : BS;
     };
+    // Both tile sets are refilled on every pass, also past the wave's last
+    // block (which is then loaded again -- cached, never consumed): loads under
+    // a branch would make the compiler wait for all loads in flight before
+    // each consume instead of only the consumed tile's.
     Tiles a, b;
     issue(p, kbase, vbase, block_stride, id_of(0), valid_of(0), row, a);
     for (int i = 0; i < n; i += 2) {
-      if (i + 1 < n) issue(p, kbase, vbase, block_stride, id_of(i + 1), valid_of(i + 1), row, b);
+      const int i1 = i + 1 < n ? i + 1 : n - 1;
+      const int i2 = i + 2 < n ? i + 2 : n - 1;
+      issue(p, kbase, vbase, block_stride, id_of(i1), valid_of(i1), row, b);
       consume(p, qf, a, first + i * NW, ctx, last_partial, row, st);
-      if (i + 1 < n) {
-        if (i + 2 < n) issue(p, kbase, vbase, block_stride, id_of(i + 2), valid_of(i + 2), row, a);
-        consume(p, qf, b, first + (i + 1) * NW, ctx, last_partial, row, st);
-      }
+      issue(p, kbase, vbase, block_stride, id_of(i2), valid_of(i2), row, a);
+      if (i + 1 < n) consume(p, qf, b, first + (i + 1) * NW, ctx, last_partial, row, st);
     }
   }
 
