@@ -553,14 +553,16 @@ void attn_mfma_append_kernel(AttnParams p) {
 }
 
 #ifndef PKV_MFMA_NW
-#define PKV_MFMA_NW 4
+#define PKV_MFMA_NW 4             // waves per workgroup: one pass and balanced slices
+#endif
+#ifndef PKV_MFMA_NW_PARTITIONS
+#define PKV_MFMA_NW_PARTITIONS 2  // waves per workgroup: fixed partitions
 #endif
 #ifndef PKV_MFMA_PIPE
 #define PKV_MFMA_PIPE 1
 #endif
-template <bool APPEND, class T, class KT, int D>
-static hipError_t launch_mfma(const AttnParams& p, hipStream_t stream) {
-  constexpr int NW = PKV_MFMA_NW;
+template <bool APPEND, class T, class KT, int D, int NW>
+static hipError_t launch_mfma_nw(const AttnParams& p, hipStream_t stream) {
   constexpr bool PIPE = PKV_MFMA_PIPE != 0;
   if constexpr (APPEND)
     hipLaunchKernelGGL((attn_mfma_append_kernel<T, KT, D, NW, PIPE>), dim3(p.total_wgs), dim3(NW * 64), 0, stream,
@@ -568,6 +570,18 @@ static hipError_t launch_mfma(const AttnParams& p, hipStream_t stream) {
   else
     hipLaunchKernelGGL((attn_mfma_kernel<T, KT, D, NW, PIPE>), dim3(p.total_wgs), dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
+}
+
+// Fixed partitions run with fewer waves per workgroup: a partition of a few
+// dozen blocks split over 4 waves leaves each wave a short walk whose fixed
+// costs (the head's prefix, the query fragments, the merge of the waves'
+// summaries through LDS) weigh more; 2 waves per partition measured faster on
+// 512-token partitions of long contexts, 4 faster for one pass and slices.
+template <bool APPEND, class T, class KT, int D>
+static hipError_t launch_mfma(const AttnParams& p, hipStream_t stream) {
+  if (p.num_slices == 0 && p.num_partitions > 1)
+    return launch_mfma_nw<APPEND, T, KT, D, PKV_MFMA_NW_PARTITIONS>(p, stream);
+  return launch_mfma_nw<APPEND, T, KT, D, PKV_MFMA_NW>(p, stream);
 }
 
 template <bool APPEND, class T, class KT>

@@ -120,9 +120,16 @@ void attn_shared_append_kernel(AttnParams p) {
   attn_shared_body<T, KT, D, NW, true>(p);
 }
 
+// Waves per workgroup.  The grid is one workgroup per (group, kv head), often
+// only a few per compute unit; with 2 waves each, every wave of such a grid is
+// resident from the start and walks twice the blocks, which measured faster
+// than 4 waves (some of which wait for a second round of residency).
+#ifndef PKV_SHARED_NW
+#define PKV_SHARED_NW 2
+#endif
 template <class T, class KT, int D>
 static hipError_t launch_shared(const AttnParams& p, bool append, hipStream_t stream) {
-  constexpr int NW = PKV_MFMA_NW;
+  constexpr int NW = PKV_SHARED_NW;
   if (append)
     hipLaunchKernelGGL((attn_shared_append_kernel<T, KT, D, NW>), dim3(p.total_wgs), dim3(NW * 64), 0, stream, p);
   else
