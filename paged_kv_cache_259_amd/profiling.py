@@ -15,6 +15,11 @@
         reduce when planned; for the shared-prefix workload the shared-block
         decode with append); the other decode kernels of the same run are
         listed but not counted.  For a prefill workload it is the prefill kernel.
+    python -m paged_kv_cache_259_amd.profiling sq DIR [DIR ...] --workload W
+        shader-sequencer counters of the timed call's kernels from one or more
+        ``--pmc`` runs of ``bench.py --workload W`` (counter sets PASS_A and
+        PASS_B below, one run each: a pass holds at most 8 SQ counters), averaged
+        per dispatch, with the ratios that say where the waves' time goes.
 """
 
 import argparse
@@ -118,6 +123,77 @@ def counters(fetch_dir, write_dir, workload, n_pairs, out=sys.stdout):
         fh.write("\n")
 
 
+# Counter sets of the two --pmc passes (8 SQ counters each, plus GRBM_GUI_ACTIVE).
+# MfmaUtil, OccupancyPercent, VALUBusy, LdsBankConflict and LdsUtil are rocprofv3's
+# derived metrics: MfmaUtil = 100 * sum(SQ_VALU_MFMA_BUSY_CYCLES) /
+# (max(GRBM_GUI_ACTIVE) * SIMDs); OccupancyPercent = 400 * sum(SQ_WAVE_CYCLES) /
+# max(GRBM_GUI_ACTIVE) / CUs / 32; VALUBusy = 100 * sum(SQ_ACTIVE_INST_VALU) / CUs /
+# max(GRBM_GUI_ACTIVE); LdsBankConflict = conflict cycles / (LDS indexed cycles -
+# conflict cycles); LdsUtil = 100 * sum(SQ_LDS_IDX_ACTIVE) / (max(GRBM_GUI_ACTIVE) * CUs).
+PASS_A = ("GRBM_GUI_ACTIVE MfmaUtil OccupancyPercent VALUBusy SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES "
+          "SQ_WAIT_INST_ANY SQ_WAIT_ANY SQ_ACTIVE_INST_VALU SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA")
+PASS_B = ("GRBM_GUI_ACTIVE LdsBankConflict LdsUtil SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_ACTIVE_INST_LDS "
+          "SQ_INSTS_LDS SQ_INSTS_VALU SQ_INSTS_VMEM_RD SQ_ACTIVE_INST_FLAT SQ_INSTS_SALU")
+
+
+def _all_counters(dirs):
+    """{(kernel, grid): {counter: mean value per dispatch}} over the runs in ``dirs``."""
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    for d in dirs:
+        for k, g, n, v in _db(d).execute("select kernel_name, grid_size, counter_name, value "
+                                         "from counters_collection").fetchall():
+            if "pkv" in k:
+                agg[(_short(k), g)][n].append(v)
+    return {key: {n: sum(v) / len(v) for n, v in cs.items()} for key, cs in agg.items()}
+
+
+def sq(dirs, workload, out=sys.stdout):
+    table = _all_counters(dirs)
+    keys = sorted(k for k in table if k[0].startswith(("attn_", "prefill_")) and _in_timed_call(k[0], workload))
+    if not keys:
+        raise SystemExit(f"no timed-call kernel of {workload} in {dirs}")
+
+    def ratio(c, a, b):
+        return c[a] / c[b] if a in c and b in c and c[b] else float("nan")
+
+    rows = []
+    for k in keys:
+        c = table[k]
+        waves = c.get("SQ_WAVES", float("nan"))
+        rows.append((f"{k[0][:52]} grid {k[1]}", [
+            ("GRBM_GUI_ACTIVE cycles", c.get("GRBM_GUI_ACTIVE")),
+            ("waves", waves),
+            ("MfmaUtil %", c.get("MfmaUtil")),
+            ("VALUBusy %", c.get("VALUBusy")),
+            ("OccupancyPercent %", c.get("OccupancyPercent")),
+            ("mean resident waves per CU", c["OccupancyPercent"] * 32 / 100 if "OccupancyPercent" in c else None),
+            ("SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES", ratio(c, "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES")),
+            ("SQ_WAIT_ANY / SQ_WAVE_CYCLES", ratio(c, "SQ_WAIT_ANY", "SQ_WAVE_CYCLES")),
+            ("SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES", ratio(c, "SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES")),
+            ("SQ_ACTIVE_INST_LDS / SQ_WAVE_CYCLES", ratio(c, "SQ_ACTIVE_INST_LDS", "SQ_WAVE_CYCLES")),
+            ("SQ_ACTIVE_INST_FLAT / SQ_WAVE_CYCLES", ratio(c, "SQ_ACTIVE_INST_FLAT", "SQ_WAVE_CYCLES")),
+            ("LdsBankConflict (conflict / conflict-free LDS cycles)", c.get("LdsBankConflict")),
+            ("LdsUtil %", c.get("LdsUtil")),
+            ("MFMA instructions per wave", c.get("SQ_INSTS_MFMA", float("nan")) / waves),
+            ("VALU instructions per wave", c.get("SQ_INSTS_VALU", float("nan")) / waves),
+            ("LDS instructions per wave", c.get("SQ_INSTS_LDS", float("nan")) / waves),
+            ("VMEM read instructions per wave", c.get("SQ_INSTS_VMEM_RD", float("nan")) / waves),
+            ("SALU instructions per wave", c.get("SQ_INSTS_SALU", float("nan")) / waves),
+        ]))
+    print(f"| {workload} | " + " | ".join(name for name, _ in rows) + " |", file=out)
+    print("|---|" + "---:|" * len(rows), file=out)
+    for i, (label, _) in enumerate(rows[0][1]):
+        cells = []
+        for _, vals in rows:
+            v = vals[i][1]
+            cells.append("n/a" if v is None or v != v else (f"{v:.0f}" if abs(v) >= 1000 else f"{v:.3g}"))
+        print(f"| {label} | " + " | ".join(cells) + " |", file=out)
+    print("\nraw means per dispatch (sums over shader engines / SIMDs, as rocprofv3 reports them):", file=out)
+    for k in keys:
+        print(f"  {k[0][:52]} grid {k[1]}: " + ", ".join(f"{n}={v:.0f}" for n, v in sorted(table[k].items())
+                                                         if n.startswith(("SQ_", "GRBM_"))), file=out)
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -128,9 +204,14 @@ def main():
     c.add_argument("write_dir")
     c.add_argument("--workload", required=True)
     c.add_argument("--calibrate-copy", type=int, required=True)
+    q = sub.add_parser("sq")
+    q.add_argument("dirs", nargs="+")
+    q.add_argument("--workload", required=True)
     a = ap.parse_args()
     if a.cmd == "trace":
         trace(a.dir)
+    elif a.cmd == "sq":
+        sq(a.dirs, a.workload)
     else:
         counters(a.fetch_dir, a.write_dir, a.workload, a.calibrate_copy)
 
