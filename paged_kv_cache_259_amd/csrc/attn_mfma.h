@@ -241,8 +241,7 @@ struct MfmaAttention {
     }
     float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));   // finite: every block has a real token
                                                                 // (-inf in a masked column, which never grows)
-    mx = fmaxf(mx, swz_xor16(mx));
-    mx = fmaxf(mx, xor32(mx));
+    mx = max_over_rows(mx);
     // The reference max st.m moves only when a head's block max exceeds it by
     // more than kLazyRescale (log2 domain): the weights stay below 2^kLazyRescale,
     // and the accumulators are rescaled on few blocks (a wave-uniform branch)
@@ -378,8 +377,7 @@ struct MfmaAttention {
   template <class Store>
   __device__ static void merge(State& st, Smem& sm, int ncols, int tid, int w, int c16, int g4, Store store) {
     float lsum = st.lsum;
-    lsum += swz_xor16(lsum);
-    lsum += xor32(lsum);
+    lsum = sum_over_rows(lsum);
     __syncthreads();                                    // every wave is done with its V tile (o shares it)
     if (c16 < ncols) {
 #pragma unroll

@@ -190,6 +190,39 @@ __device__ __forceinline__ float swz_xor16(float x) {  // lane ^ 16 within each 
 }
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
+// Reductions over the lane pairs (l, l ^ 32) and (l, l ^ 16) with gfx950's row
+// swaps, which move values between VGPRs without the LDS crossbar:
+// v_permlane32_swap_b32 exchanges the upper 32 lanes of its first operand with
+// the lower 32 of its second, v_permlane16_swap_b32 the odd 16-lane rows of the
+// first with the even rows of the second.  Given two copies of x, the two
+// results hold x of lanes l and l ^ 32 (l ^ 16) between them, so a commutative
+// op of the pair is the reduction (checked on hardware with lane ids).  The
+// instruction is written in asm because this toolchain's optimiser drops the
+// builtin's second result; the s_nops give it its VALU hazard wait states.
+__device__ __forceinline__ void row_swap32(float& a, float& b) {
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void row_swap16(float& a, float& b) {
+  asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+// max (sum) over the four lanes l, l ^ 16, l ^ 32, l ^ 48 of each column of 16
+__device__ __forceinline__ float max_over_rows(float x) {
+  float y = x;
+  row_swap32(x, y);
+  x = fmaxf(x, y);
+  y = x;
+  row_swap16(x, y);
+  return fmaxf(x, y);
+}
+__device__ __forceinline__ float sum_over_rows(float x) {
+  float y = x;
+  row_swap32(x, y);
+  x += y;
+  y = x;
+  row_swap16(x, y);
+  return x + y;
+}
+
 // Sum over each aligned group of N consecutive lanes (N = 1..64, power of two);
 // every lane of the group ends with the group's sum.
 template <int N>

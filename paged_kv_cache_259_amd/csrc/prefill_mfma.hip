@@ -241,21 +241,40 @@ void prefill_mfma_kernel(PrefillParams p) {
   // Load step i's K and V rows into LDS buffers kb, vb: instruction q of the
   // step (wave-uniform) fills rows q*RPI .. q*RPI+RPI-1; lane l fetches the
   // logical chunk that the swizzle puts at position l % CPR of row l / CPR.
+  // A wave's QPW instructions cover exactly one block of the step (block w),
+  // and the swizzles repeat within a block, so a lane's offset inside the
+  // block is the same on every step.  When every row of the wave's block is a
+  // key (all steps but the last) and its table entry lies in the pool, the
+  // loads take the block's base plus that offset; otherwise each lane checks
+  // its row and reads a zero chunk past the keys.
+  static_assert(P::QPW * P::RPI == BS && KT == P::NW, "each wave loads one block of each step");
+  static_assert(BS % (P::RPB * CPR) == 0, "the swizzles repeat within a block");
   const int dma_row = lane / CPR, dma_pos = lane % CPR;
   auto load_step = [&](int i, StepIds ids, uint16_t* kb, uint16_t* vb) {
+    int blk = ids.b[0];
 #pragma unroll
-    for (int j = 0; j < P::QPW; ++j) {
-      const int q = w * P::QPW + j;
-      const int r = q * P::RPI + dma_row;                  // token row of the step
-      int blk = ids.b[0];                                  // uniform: an instruction stays in one block
+    for (int kt = 1; kt < KT; ++kt) blk = w == kt ? ids.b[kt] : blk;   // the wave's block (uniform)
+    const bool in_pool = blk >= 0 && blk < p.num_blocks;
+    const size_t boff = (size_t)(in_pool ? blk : 0) * block_stride;
+    const uint16_t* kblk = kpool + boff;
+    const uint16_t* vblk = vpool + boff;
+    if (in_pool && i * STEP + (w + 1) * BS <= nkeys) {     // uniform
 #pragma unroll
-      for (int kt = 1; kt < KT; ++kt) blk = (q * P::RPI) / BS == kt ? ids.b[kt] : blk;   // no dynamic indexing
-      const bool ok = blk >= 0 && blk < p.num_blocks && i * STEP + r < nkeys;
-      const size_t row_off = (size_t)blk * block_stride + (size_t)(r % BS) * D;
-      const uint16_t* ks = ok ? kpool + row_off + (dma_pos ^ P::swz_k(r)) * 8 : kZeroChunk;
-      const uint16_t* vs = ok ? vpool + row_off + (dma_pos ^ P::swz_v(r)) * 8 : kZeroChunk;
-      load_lds16(ks, kb + q * 512);
-      load_lds16(vs, vb + q * 512);
+      for (int j = 0; j < P::QPW; ++j) {                   // uniform base + unsigned 32-bit lane offset
+        const int rb = j * P::RPI + dma_row;                // row inside the block
+        const uint32_t ko = (uint32_t)(rb * D + (dma_pos ^ P::swz_k(rb)) * 8) * 2u;
+        const uint32_t vo = (uint32_t)(rb * D + (dma_pos ^ P::swz_v(rb)) * 8) * 2u;
+        load_lds16(reinterpret_cast<const char*>(kblk) + ko, kb + (w * P::QPW + j) * 512);
+        load_lds16(reinterpret_cast<const char*>(vblk) + vo, vb + (w * P::QPW + j) * 512);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < P::QPW; ++j) {
+        const int rb = j * P::RPI + dma_row;
+        const bool ok = in_pool && i * STEP + w * BS + rb < nkeys;
+        load_lds16(ok ? kblk + rb * D + (dma_pos ^ P::swz_k(rb)) * 8 : kZeroChunk, kb + (w * P::QPW + j) * 512);
+        load_lds16(ok ? vblk + rb * D + (dma_pos ^ P::swz_v(rb)) * 8 : kZeroChunk, vb + (w * P::QPW + j) * 512);
+      }
     }
   };
   // Per-lane fragment addresses (elements) inside a buffer; the swizzles do not
@@ -320,8 +339,7 @@ void prefill_mfma_kernel(PrefillParams p) {
               mx = fmaxf(mx, s[kt][r]);
             }
         }
-        mx = fmaxf(mx, swz_xor16(mx));
-        mx = fmaxf(mx, xor32(mx));
+        mx = max_over_rows(mx);
         // The reference max only moves when a row's max grows by more than
         // kRescale (log2 domain): softmax does not depend on the reference, the
         // weights stay <= 2^kRescale, and the accumulators are rescaled on few
@@ -425,8 +443,7 @@ void prefill_mfma_kernel(PrefillParams p) {
 #pragma unroll
   for (int g = 0; g < RW; ++g) {
     float ls = lsum[g];
-    ls += swz_xor16(ls);
-    ls += xor32(ls);
+    ls = sum_over_rows(ls);
     if (qreal[g]) {
       const float inv = ls > 0.f ? 1.f / ls : 0.f;
       const size_t orow = ((size_t)(q0 + wrow0 + 16 * g + c16) * p.num_heads + h) * D;
