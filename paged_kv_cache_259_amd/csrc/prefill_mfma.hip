@@ -52,6 +52,7 @@ template <> struct PrefillOp<BF16> {
     const bf162_t h = {(__bf16)x, (__bf16)y};
     return __builtin_bit_cast(uint32_t, h);
   }
+  __device__ __forceinline__ static uint4 ones() { return make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u); }
 };
 template <> struct PrefillOp<F16> {
   __device__ __forceinline__ static f32x4_t mma(const uint4& a, const uint4& b, f32x4_t c) {
@@ -62,6 +63,7 @@ template <> struct PrefillOp<F16> {
     const half2_t h = {(_Float16)x, (_Float16)y};
     return __builtin_bit_cast(uint32_t, h);
   }
+  __device__ __forceinline__ static uint4 ones() { return make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u); }
 };
 
 constexpr float kRescale = 8.f;
@@ -204,12 +206,13 @@ void prefill_mfma_kernel(PrefillParams p) {
     }
   }
 
-  float m[RW], lsum[RW];
+  float m[RW];
+  f32x4_t lsum[RW];   // row sums of the rounded weights, from the PV MFMA with an all-ones A (every element equal)
   f32x4_t O[RW][ND];
 #pragma unroll
   for (int g = 0; g < RW; ++g) {
     m[g] = -__builtin_inff();
-    lsum[g] = 0.f;
+    lsum[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) O[g][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
@@ -355,14 +358,12 @@ void prefill_mfma_kernel(PrefillParams p) {
         }
         const float mref = m[g] == -__builtin_inff() ? 0.f : m[g];   // nothing visible yet: weights are 0
         float pr[KT][4];
-        float ps = 0.f;
         if constexpr (interior) {
 #pragma unroll
           for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               pr[kt][r] = exp2_fast(fmaf(s[kt][r], qs, -mref));
-              ps += pr[kt][r];
             }
         } else {
 #pragma unroll
@@ -370,10 +371,8 @@ void prefill_mfma_kernel(PrefillParams p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               pr[kt][r] = exp2_fast(s[kt][r] - mref);
-              ps += pr[kt][r];
             }
         }
-        lsum[g] += ps;
 #pragma unroll
         for (int ns = 0; ns < NS; ++ns)
           pk[g][ns] = make_uint4(Op::pack(pr[2 * ns][0], pr[2 * ns][1]), Op::pack(pr[2 * ns][2], pr[2 * ns][3]),
@@ -391,6 +390,10 @@ void prefill_mfma_kernel(PrefillParams p) {
 #pragma unroll
           for (int g = 0; g < RW; ++g) O[g][dt] = Op::mma(vf, pk[g][ns], O[g][dt]);
         }
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+        for (int g = 0; g < RW; ++g) lsum[g] = Op::mma(Op::ones(), pk[g][ns], lsum[g]);
     }
   };
   // Steps [0, n_open) are open to every row of the workgroup: every key is
@@ -442,8 +445,7 @@ void prefill_mfma_kernel(PrefillParams p) {
   // normalise and write: lane l holds out[row wrow0 + 16 g + c16][dims 16 dt + 4 g4 + r]
 #pragma unroll
   for (int g = 0; g < RW; ++g) {
-    float ls = lsum[g];
-    ls = sum_over_rows(ls);
+    const float ls = lsum[g][0];
     if (qreal[g]) {
       const float inv = ls > 0.f ? 1.f / ls : 0.f;
       const size_t orow = ((size_t)(q0 + wrow0 + 16 * g + c16) * p.num_heads + h) * D;
