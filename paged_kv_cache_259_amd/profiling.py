@@ -41,7 +41,7 @@ def _db(d):
 
 
 def _short(name):
-    s = name.split("(")[0]
+    s = name.replace("(anonymous namespace)::", "").split("(")[0]
     for p in ("void ", "pkv::"):
         s = s.replace(p, "")
     return s

@@ -74,3 +74,10 @@ def test_sq_without_timed_kernels_fails(tmp_path):
     _make_db(str(tmp_path / "a" / "run_results.db"), counters=[(OTHER, 64, "SQ_WAVES", 1)])
     with pytest.raises(SystemExit):
         profiling.sq([str(tmp_path / "a")], "gqa_bf16", io.StringIO())
+
+
+def test_short_names():
+    assert profiling._short("void (anonymous namespace)::stream_read_kernel(uint4 const*, unsigned long)") == \
+        "stream_read_kernel"
+    assert profiling._short("void pkv::attn_mfma_append_kernel<pkv::BF16, pkv::BF16, 128, 2, true>(pkv::AttnParams)") \
+        == "attn_mfma_append_kernel<BF16, BF16, 128, 2, true>"
