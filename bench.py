@@ -156,9 +156,11 @@ def timed_steps(fn, K, stream, flush=None):
     return np.array([a.elapsed_time(b) for a, b in ev])
 
 
-def hbm_probe(stream, reps=10):
+def hbm_probe(stream, reps=10, flush=None):
     """What HBM delivers to read-only kernels on this machine: a streaming read of 1 GiB (best of three grid
-    sizes) and reads of random 2/4/8 KiB tiles (0.75 GB per launch), GB/s from HIP events."""
+    sizes) and reads of scattered 2/4/8 KiB tiles (0.75 GB per launch, no tile read twice in a launch), GB/s
+    from HIP events around each launch; with ``flush`` (the decode steps' cache flush) the caches are cleared
+    before every launch, as before every timed decode step."""
     import torch
     from paged_kv_cache_259_amd import probe
     buf = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
@@ -167,28 +169,32 @@ def hbm_probe(stream, reps=10):
     def rate(fn, nbytes):
         for _ in range(3):
             fn()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        ms = timed_steps(fn, reps, stream, flush)
+        return nbytes / (float(np.mean(ms)) * 1e-3) / 1e9
 
     stream_rates = {}
     for wgs in (1024, 2048, 4096):
         stream_rates[wgs] = rate(lambda: probe.stream_read(buf, buf.numel(), wgs, sink, stream=stream), buf.numel())
     tiles = {}
     wgs = 2048
+    salt = [0]
+
+    def tile_launch(tb, per_wave):
+        salt[0] += 1                                    # another scattered order on every launch
+        probe.tile_read(buf, tb, wgs, per_wave, sink, salt=salt[0] * 7919, stream=stream)
+
     for tb in (2048, 4096, 8192):
         per_wave = (768 << 20) // (wgs * 4 * tb)
-        tiles[tb] = rate(lambda: probe.tile_read(buf, tb, wgs, per_wave, sink, stream=stream), wgs * 4 * per_wave * tb)
+        tiles[tb] = rate(lambda: tile_launch(tb, per_wave), wgs * 4 * per_wave * tb)
     del buf
     best = max(stream_rates, key=stream_rates.get)
     return {"stream_read_gbps": round(stream_rates[best], 1), "stream_read_workgroups": best,
             "stream_read_gbps_by_grid": {str(k): round(v, 1) for k, v in stream_rates.items()},
             "tile_read_gbps": {f"{k // 1024}KiB": round(v, 1) for k, v in tiles.items()},
-            "probe": "libpkv_probe.so: 16-byte loads, 1 GiB buffer; random tiles at hashed indices, two per wave in "
+            "flushed": flush is not None,
+            "probe": "libpkv_probe.so: 16-byte loads, 1 GiB buffer, mean of per-launch HIP-event times"
+                     + (", caches flushed before each launch" if flush is not None else "")
+                     + "; tiles in a scattered order that reads no tile twice per launch, two per wave in "
                      "flight, 2048 workgroups of 4 waves"}
 
 
@@ -897,7 +903,7 @@ def main_stream_probe(args):
     """What HBM delivers to read-only kernels on this machine (the decode roofline's achievable ceiling)."""
     import torch
     stream = torch.cuda.current_stream()
-    res = hbm_probe(stream, reps=max(args.steps // 10, 5))
+    res = hbm_probe(stream, reps=max(args.steps // 10, 5), flush=Flusher(stream))
     print(json.dumps({
         "metric": "HBM read GB/s of a streaming read kernel and of random-tile reads (% of 8 TB/s)",
         "value": res["stream_read_gbps"], "unit": "GB/s", "n_gpus": 1, "steps": max(args.steps // 10, 5),
@@ -1003,7 +1009,7 @@ def main_decode(args, w):
         calibration_copy(w, inp.k_cache.dtype, args.calibrate_copy, stream)
 
     # ---- what HBM delivers to a read-only kernel here, and the GQA step beside the headline workload
-    probe = None if args.calibrate_copy else hbm_probe(stream)
+    probe = None if args.calibrate_copy else hbm_probe(stream, flush=flusher)
     probe_gbps = probe["stream_read_gbps"] if probe else None
     gqa = None
     if args.workload == "llama13b_f16" and not args.calibrate_copy and not args.no_components:

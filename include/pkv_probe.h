@@ -41,8 +41,12 @@ int pkv_probe_stream_read(const void* buf, size_t bytes, int num_workgroups, uns
 /*
  * pkv_probe_tile_read -- each wave of `num_workgroups` workgroups of 4 waves
  * reads `tiles_per_wave` whole tiles of `tile_bytes` bytes (1024, 2048, 4096 or
- * 8192) at tile indices drawn by a hash of (wave, i, salt) over the
- * bytes / tile_bytes tiles of `buf`, two tiles in flight, 16-byte loads.
+ * 8192) of the T = bytes / tile_bytes tiles of `buf`, two tiles in flight,
+ * 16-byte loads.  Read number n (n = wave * tiles_per_wave + i) takes tile
+ * (n * P + salt) mod T for a fixed prime P that divides no such T: a
+ * scattered order that is a bijection, so a launch of at most T reads reads
+ * every tile at most once (none is served by the caches from an earlier read
+ * of the same launch; beyond T reads the order repeats).
  */
 int pkv_probe_tile_read(const void* buf, size_t bytes, int tile_bytes, int num_workgroups, int tiles_per_wave,
                         unsigned salt, unsigned* sink, void* stream);

@@ -41,7 +41,8 @@ def stream_read(buf, nbytes, workgroups, sink, salt=0x9E3779B9, stream=None):
 
 
 def tile_read(buf, tile_bytes, workgroups, tiles_per_wave, sink, salt=17, stream=None):
-    """Enqueue one random-tile read over the uint8 device tensor ``buf``."""
+    """Enqueue one scattered-tile read over the uint8 device tensor ``buf`` (no tile read twice per launch
+    while workgroups x 4 x tiles_per_wave stays within the buffer's tiles)."""
     if buf.device.type != "cuda" or sink.device != buf.device:
         raise ValueError("buf and sink must be device tensors")
     st = _lib.pkv_probe_tile_read(buf.data_ptr(), buf.numel(), tile_bytes, workgroups, tiles_per_wave, salt,

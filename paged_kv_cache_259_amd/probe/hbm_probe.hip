@@ -38,12 +38,15 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const uint4* __re
   if (acc == salt) sink[0] = acc;
 }
 
-__device__ __forceinline__ uint64_t tile_index(uint32_t wave, int i, uint32_t salt, uint64_t num_tiles) {
-  uint64_t x = (uint64_t)wave * 1000003ull + (uint64_t)i * 7919ull + salt;   // splitmix-style finaliser
-  x ^= x >> 33;
-  x *= 0xff51afd7ed558ccdull;
-  x ^= x >> 33;
-  return x % num_tiles;
+// Tile of read number lin = wave * per_wave + i: (lin * P + salt) mod num_tiles
+// with P a prime that divides no tile count a buffer can have (it exceeds any
+// tile count below 2^32), so the map is a bijection of [0, num_tiles): a launch
+// that reads at most num_tiles tiles reads every tile at most once, and no read
+// can be served by the caches from an earlier read of the same launch.
+constexpr uint64_t kTilePrime = 4294967291ull;   // the largest prime below 2^32
+__device__ __forceinline__ uint64_t tile_index(uint32_t wave, int i, int per_wave, uint32_t salt, uint64_t num_tiles) {
+  const uint64_t lin = (uint64_t)wave * (uint64_t)per_wave + (uint64_t)i;
+  return (lin % num_tiles * (kTilePrime % num_tiles) + salt) % num_tiles;
 }
 
 template <int TILE>
@@ -56,7 +59,7 @@ __global__ __launch_bounds__(kThreads) void tile_read_kernel(const uint4* __rest
   uint32_t acc = 0;
   uint4 a[LOADS], b[LOADS];
   auto issue = [&](int i, uint4* t) {
-    const uint4* p = buf + tile_index(wave, i, salt, num_tiles) * (TILE / 16) + lane;
+    const uint4* p = buf + tile_index(wave, i, per_wave, salt, num_tiles) * (TILE / 16) + lane;
 #pragma unroll
     for (int k = 0; k < LOADS; ++k) t[k] = p[k * 64];
   };
