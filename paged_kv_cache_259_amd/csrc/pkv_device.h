@@ -205,14 +205,20 @@ __device__ __forceinline__ void row_swap32(float& a, float& b) {
 __device__ __forceinline__ void row_swap16(float& a, float& b) {
   asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
 }
-// max (sum) over the four lanes l, l ^ 16, l ^ 32, l ^ 48 of each column of 16
+// max (sum) over the four lanes l, l ^ 16, l ^ 32, l ^ 48 of each column of 16.
+// The max is one asm block with its v_max_f32: an fmaxf of the asm outputs
+// would first quiet possible signalling NaNs (two more instructions per max);
+// the values here are never NaN (finite logits or -inf).
 __device__ __forceinline__ float max_over_rows(float x) {
-  float y = x;
-  row_swap32(x, y);
-  x = fmaxf(x, y);
-  y = x;
-  row_swap16(x, y);
-  return fmaxf(x, y);
+  float y;
+  asm("v_mov_b32 %1, %0\n\t"
+      "s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1\n\t"
+      "v_max_f32 %0, %0, %1\n\t"
+      "v_mov_b32 %1, %0\n\t"
+      "s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1\n\t"
+      "v_max_f32 %0, %0, %1"
+      : "+v"(x), "=&v"(y));
+  return x;
 }
 __device__ __forceinline__ float sum_over_rows(float x) {
   float y = x;

@@ -102,6 +102,18 @@ __device__ __forceinline__ void load_lds16(const void* src, void* dst) {
   __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 16, 0, 0);
 }
 
+// The same through a buffer resource: the 16 bytes at byte `off` (per lane) of
+// the `bytes`-byte range at `base` (wave-uniform, in scalar registers) go to
+// LDS bytes dst + 16 l .. +15.  The address is the resource's base plus the
+// 32-bit lane offset, so no 64-bit address is formed per lane.  Every offset
+// passed is inside the range.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint32_t off, void* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)dst, 16, off, 0, 0, 0);
+}
+
 // ds_read_b64_tr_b16 on an LDS address (8-byte aligned)
 __device__ __forceinline__ uint2 read_tr16(const uint16_t* lds) {
   const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(lds));
@@ -262,13 +274,12 @@ void prefill_mfma_kernel(PrefillParams p) {
     const uint16_t* kblk = kpool + boff;
     const uint16_t* vblk = vpool + boff;
     if (in_pool && i * STEP + (w + 1) * BS <= nkeys) {     // uniform
+      const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kblk, BS * D * 2), vr = buffer_rsrc(vblk, BS * D * 2);
 #pragma unroll
-      for (int j = 0; j < P::QPW; ++j) {                   // uniform base + unsigned 32-bit lane offset
+      for (int j = 0; j < P::QPW; ++j) {                   // the block's tile + a fixed 32-bit lane offset
         const int rb = j * P::RPI + dma_row;                // row inside the block
-        const uint32_t ko = (uint32_t)(rb * D + (dma_pos ^ P::swz_k(rb)) * 8) * 2u;
-        const uint32_t vo = (uint32_t)(rb * D + (dma_pos ^ P::swz_v(rb)) * 8) * 2u;
-        load_lds16(reinterpret_cast<const char*>(kblk) + ko, kb + (w * P::QPW + j) * 512);
-        load_lds16(reinterpret_cast<const char*>(vblk) + vo, vb + (w * P::QPW + j) * 512);
+        load_lds16(kr, (uint32_t)(rb * D + (dma_pos ^ P::swz_k(rb)) * 8) * 2u, kb + (w * P::QPW + j) * 512);
+        load_lds16(vr, (uint32_t)(rb * D + (dma_pos ^ P::swz_v(rb)) * 8) * 2u, vb + (w * P::QPW + j) * 512);
       }
     } else {
 #pragma unroll
@@ -290,6 +301,14 @@ void prefill_mfma_kernel(PrefillParams p) {
   const int kbase = c16 * D + (g4 ^ (P::swz_k(c16) & 3)) * 8, ksw = P::swz_k(c16) & ~3;
   const int vr = 4 * g4 + (c16 >> 2);
   const int vbase = vr * D + 8 * ((c16 & 3) >> 1) + 4 * (c16 & 1), vsw = P::swz_v(vr) / 2;
+  // The lane's fragment offsets, once: every read of a step is then one of
+  // these plus a compile-time offset (buffer, block, k-step), which the LDS
+  // instruction takes as its immediate.
+  int koff[NC], voff[ND];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) koff[c] = kbase + ((4 * c) ^ ksw) * 8;
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt) voff[dt] = vbase + (dt ^ vsw) * 16;
 
   // One step of the wave's rows.  `masked` (a compile-time tag) selects the
   // variant with the per-element causal / context / skipped-block mask; steps
@@ -311,7 +330,7 @@ void prefill_mfma_kernel(PrefillParams p) {
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          const uint4 kf = *reinterpret_cast<const uint4*>(kb + kt * 16 * D + kbase + ((4 * c) ^ ksw) * 8);
+          const uint4 kf = *reinterpret_cast<const uint4*>(kb + kt * 16 * D + koff[c]);
 #pragma unroll
           for (int g = 0; g < RW; ++g) S[g][kt] = Op::mma(kf, qf[g][c], S[g][kt]);
         }
@@ -383,7 +402,7 @@ void prefill_mfma_kernel(PrefillParams p) {
       for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt) {
-          const uint16_t* va = vb + 32 * ns * D + vbase + ((dt ^ vsw) * 16);
+          const uint16_t* va = vb + 32 * ns * D + voff[dt];
           const uint2 lo = read_tr16(va);                   // tokens 32 ns + 4 g4 + m
           const uint2 hi = read_tr16(va + 16 * D);          // tokens 32 ns + 16 + 4 g4 + m
           const uint4 vf = make_uint4(lo.x, lo.y, hi.x, hi.y);
