@@ -77,6 +77,9 @@ constexpr float kRescale = 8.f;
 #ifndef PKV_PREFILL_NW
 #define PKV_PREFILL_NW 4      // waves per workgroup
 #endif
+#ifndef PKV_PREFILL_RING
+#define PKV_PREFILL_RING 2    // stage buffers per tensor: loads run RING - 1 steps ahead
+#endif
 #ifndef PKV_PREFILL_WAVES_PER_EU
 #define PKV_PREFILL_WAVES_PER_EU 2   // occupancy the register allocation must allow
 #endif
@@ -155,9 +158,21 @@ void prefill_mfma_kernel(PrefillParams p) {
   constexpr int STEP = P::STEP, BS = P::BS, NC = P::NC, ND = P::ND, CPR = P::CPR, KT = P::KT,
                 NS = P::NS;
   struct StepIds { int b[KT]; };                            // block ids of one step (-1 past the keys)
-  // two buffers per tensor as separate objects: the compiler then sees that
-  // loads into one never alias reads of the other and adds no wait between them
+  // RING stage buffers per tensor as separate objects: the compiler then sees
+  // that loads into one never alias reads of another and adds no wait between them
+  constexpr int R = PKV_PREFILL_RING;
+  static_assert(R >= 2 && R <= 4, "2 to 4 stage buffers");
   __shared__ __align__(16) uint16_t sK0[P::TILE], sK1[P::TILE], sV0[P::TILE], sV1[P::TILE];
+  __shared__ __align__(16) uint16_t sK2[R > 2 ? P::TILE : 1], sV2[R > 2 ? P::TILE : 1];
+  __shared__ __align__(16) uint16_t sK3[R > 3 ? P::TILE : 1], sV3[R > 3 ? P::TILE : 1];
+  auto kbuf = [&](auto b) -> uint16_t* {
+    constexpr int k = decltype(b)::value;
+    if constexpr (k == 0) return sK0; else if constexpr (k == 1) return sK1; else if constexpr (k == 2) return sK2; else return sK3;
+  };
+  auto vbuf = [&](auto b) -> uint16_t* {
+    constexpr int k = decltype(b)::value;
+    if constexpr (k == 0) return sV0; else if constexpr (k == 1) return sV1; else if constexpr (k == 2) return sV2; else return sV3;
+  };
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -256,36 +271,39 @@ void prefill_mfma_kernel(PrefillParams p) {
   // Load step i's K and V rows into LDS buffers kb, vb: instruction q of the
   // step (wave-uniform) fills rows q*RPI .. q*RPI+RPI-1; lane l fetches the
   // logical chunk that the swizzle puts at position l % CPR of row l / CPR.
-  // A wave's QPW instructions cover exactly one block of the step (block w),
-  // and the swizzles repeat within a block, so a lane's offset inside the
-  // block is the same on every step.  When every row of the wave's block is a
-  // key (all steps but the last) and its table entry lies in the pool, the
-  // loads take the block's base plus that offset; otherwise each lane checks
-  // its row and reads a zero chunk past the keys.
-  static_assert(P::QPW * P::RPI == BS && KT == P::NW, "each wave loads one block of each step");
+  // A wave's QPW instructions cover QPW*RPI consecutive rows of one block of
+  // the step (block WR*w/BS, from row WR*w % BS, WR = QPW*RPI), and the
+  // swizzles repeat within a block, so a lane's offset inside the block is the
+  // same on every step.  When every one of those rows is a key (all steps but
+  // the last) and the block's table entry lies in the pool, the loads take the
+  // block's base plus that offset; otherwise each lane checks its row and
+  // reads a zero chunk past the keys.
+  constexpr int WR = P::QPW * P::RPI;                       // rows per wave and step
+  static_assert(BS % WR == 0 && KT * BS == P::NW * WR, "each wave loads part of one block of each step");
   static_assert(BS % (P::RPB * CPR) == 0, "the swizzles repeat within a block");
   const int dma_row = lane / CPR, dma_pos = lane % CPR;
+  const int wkt = WR * w / BS, wrb = WR * w % BS;           // the wave's block of the step and first row in it
   auto load_step = [&](int i, StepIds ids, uint16_t* kb, uint16_t* vb) {
     int blk = ids.b[0];
 #pragma unroll
-    for (int kt = 1; kt < KT; ++kt) blk = w == kt ? ids.b[kt] : blk;   // the wave's block (uniform)
+    for (int kt = 1; kt < KT; ++kt) blk = wkt == kt ? ids.b[kt] : blk;   // the wave's block (uniform)
     const bool in_pool = blk >= 0 && blk < p.num_blocks;
     const size_t boff = (size_t)(in_pool ? blk : 0) * block_stride;
     const uint16_t* kblk = kpool + boff;
     const uint16_t* vblk = vpool + boff;
-    if (in_pool && i * STEP + (w + 1) * BS <= nkeys) {     // uniform
+    if (in_pool && i * STEP + wkt * BS + wrb + WR <= nkeys) {   // uniform
       const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kblk, BS * D * 2), vr = buffer_rsrc(vblk, BS * D * 2);
 #pragma unroll
       for (int j = 0; j < P::QPW; ++j) {                   // the block's tile + a fixed 32-bit lane offset
-        const int rb = j * P::RPI + dma_row;                // row inside the block
+        const int rb = wrb + j * P::RPI + dma_row;          // row inside the block
         load_lds16(kr, (uint32_t)(rb * D + (dma_pos ^ P::swz_k(rb)) * 8) * 2u, kb + (w * P::QPW + j) * 512);
         load_lds16(vr, (uint32_t)(rb * D + (dma_pos ^ P::swz_v(rb)) * 8) * 2u, vb + (w * P::QPW + j) * 512);
       }
     } else {
 #pragma unroll
       for (int j = 0; j < P::QPW; ++j) {
-        const int rb = j * P::RPI + dma_row;
-        const bool ok = in_pool && i * STEP + w * BS + rb < nkeys;
+        const int rb = wrb + j * P::RPI + dma_row;
+        const bool ok = in_pool && i * STEP + wkt * BS + rb < nkeys;
         load_lds16(ok ? kblk + rb * D + (dma_pos ^ P::swz_k(rb)) * 8 : kZeroChunk, kb + (w * P::QPW + j) * 512);
         load_lds16(ok ? vblk + rb * D + (dma_pos ^ P::swz_v(rb)) * 8 : kZeroChunk, vb + (w * P::QPW + j) * 512);
       }
@@ -432,30 +450,53 @@ void prefill_mfma_kernel(PrefillParams p) {
     step_body(i, kb, vb, ids, std::true_type{});
   };
 
-  // Pipeline: step i+1's rows are loaded into the other buffer pair while step
-  // i is computed; block ids come two steps ahead.  Even steps use buffers 0,
-  // odd steps 1; the loops run in pairs of steps from an even step, so every
-  // access names its buffer statically (an odd open step, if any, runs with
-  // the mask: same result).
-  StepIds id0 = ids_of(0), id1 = ids_of(1);
-  if (nsteps > 0) load_step(0, id0, sK0, sV0);
-  wait_lds_loads();
-  __syncthreads();
-  auto one = [&](int i, auto open, uint16_t* kc, uint16_t* vc, uint16_t* kn, uint16_t* vn)
-      __attribute__((always_inline)) {
-    const StepIds id2 = ids_of(i + 2);
-    if (i + 1 < nsteps) load_step(i + 1, id1, kn, vn);
-    if constexpr (decltype(open)::value) compute_open(i, kc, vc, id0); else compute(i, kc, vc, id0);
+  // Pipeline: a ring of R buffer pairs; step j's rows live in pair j % R and
+  // are loaded R - 1 steps ahead, into the pair the previous step finished
+  // with (its readers passed the barrier that ended that step).  At the end of
+  // step i each wave waits until its loads of step i + 1 have landed (the
+  // loads of later steps may stay in flight: vmcnt counts them, the loads of
+  // one step are LPS instructions per wave), then meets the other waves at the
+  // barrier.  The loops run R steps per pass from a multiple of R, so every
+  // access names its buffers statically (open steps past the last multiple of
+  // R run with the mask: same result).  Block ids come R steps ahead.
+  constexpr int LPS = 2 * P::QPW;                           // load instructions per wave and step
+  auto wait_step_after = [&](int i) __attribute__((always_inline)) {   // step i + 1's loads have landed
+    const int later = (i + R - 1 < nsteps ? i + R - 1 : nsteps - 1) - (i + 1);   // later steps already issued
+    if constexpr (R >= 4) { if (later >= 2) { __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * LPS)); return; } }
+    if constexpr (R >= 3) { if (later >= 1) { __builtin_amdgcn_s_waitcnt(0x0F70 | LPS); return; } }
     wait_lds_loads();
-    __syncthreads();
-    id0 = id1;
-    id1 = id2;
   };
-  n_open &= ~1;
-  auto steps = [&](int i, int end, auto open) __attribute__((always_inline)) {   // steps [i, end) from an even i
-    for (; i < end; i += 2) {
-      one(i, open, sK0, sV0, sK1, sV1);
-      if (i + 1 < end) one(i + 1, open, sK1, sV1, sK0, sV0);
+  static_assert((R - 2) * LPS <= 15, "vmcnt immediate");
+  StepIds ids[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k) ids[k] = ids_of(k);
+  // steps 0 .. R-2 into pairs 0 .. R-2
+  if (0 < nsteps) load_step(0, ids[0], sK0, sV0);
+  if constexpr (R > 2) { if (1 < nsteps) load_step(1, ids[1], sK1, sV1); }
+  if constexpr (R > 3) { if (2 < nsteps) load_step(2, ids[2], sK2, sV2); }
+  wait_step_after(-1);
+  __syncthreads();
+  auto one = [&](int i, auto open, auto cur) __attribute__((always_inline)) {
+    constexpr int c = decltype(cur)::value, n = (c + R - 1) % R;
+    const StepIds idn = ids_of(i + R);
+    if (i + R - 1 < nsteps)
+      load_step(i + R - 1, ids[R - 1], kbuf(std::integral_constant<int, n>{}), vbuf(std::integral_constant<int, n>{}));
+    uint16_t* kc = kbuf(std::integral_constant<int, c>{});
+    uint16_t* vc = vbuf(std::integral_constant<int, c>{});
+    if constexpr (decltype(open)::value) compute_open(i, kc, vc, ids[0]); else compute(i, kc, vc, ids[0]);
+    wait_step_after(i);
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k + 1 < R; ++k) ids[k] = ids[k + 1];
+    ids[R - 1] = idn;
+  };
+  n_open -= n_open % R;
+  auto steps = [&](int i, int end, auto open) __attribute__((always_inline)) {   // steps [i, end) from a multiple of R
+    for (; i < end; i += R) {
+      one(i, open, std::integral_constant<int, 0>{});
+      if (i + 1 < end) one(i + 1, open, std::integral_constant<int, 1>{});
+      if constexpr (R > 2) { if (i + 2 < end) one(i + 2, open, std::integral_constant<int, 2>{}); }
+      if constexpr (R > 3) { if (i + 3 < end) one(i + 3, open, std::integral_constant<int, 3>{}); }
     }
   };
   steps(0, n_open, std::true_type{});
