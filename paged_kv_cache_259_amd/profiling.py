@@ -48,14 +48,20 @@ def _short(name):
 
 
 def trace(d, out=sys.stdout):
+    """Calls, mean, median, min and max duration per kernel (warm-up calls included, so the
+    median is the figure to set beside a bench line's steady-state mean)."""
     c = _db(d)
-    rows = c.execute("select name, count(*), avg(duration), min(duration), max(duration), sum(duration) "
-                     "from kernels group by name order by sum(duration) desc").fetchall()
-    tot = sum(r[5] for r in rows) or 1
-    print(f"{'kernel':64s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'total%':>7s}", file=out)
-    for name, n, avg, mn, mx, s in rows[:12]:
-        print(f"{_short(name)[:64]:64s} {n:6d} {avg / 1e3:9.2f} {mn / 1e3:9.2f} {mx / 1e3:9.2f} "
-              f"{100 * s / tot:7.2f}", file=out)
+    durs = collections.defaultdict(list)
+    for name, dur in c.execute("select name, duration from kernels").fetchall():
+        durs[name].append(dur)
+    tot = sum(sum(v) for v in durs.values()) or 1
+    print(f"{'kernel':64s} {'calls':>6s} {'avg_us':>9s} {'med_us':>9s} {'min_us':>9s} {'max_us':>9s} {'total%':>7s}",
+          file=out)
+    for name, v in sorted(durs.items(), key=lambda kv: -sum(kv[1]))[:12]:
+        v = sorted(v)
+        med = v[len(v) // 2] if len(v) % 2 else (v[len(v) // 2 - 1] + v[len(v) // 2]) / 2
+        print(f"{_short(name)[:64]:64s} {len(v):6d} {sum(v) / len(v) / 1e3:9.2f} {med / 1e3:9.2f} "
+              f"{v[0] / 1e3:9.2f} {v[-1] / 1e3:9.2f} {100 * sum(v) / tot:7.2f}", file=out)
 
 
 def _counter(d, counter):

@@ -32,7 +32,7 @@ def test_trace_groups_by_kernel(tmp_path):
     profiling.trace(str(tmp_path / "t"), out)
     lines = out.getvalue().splitlines()
     assert lines[1].startswith("attn_mfma_append_kernel")
-    assert lines[1].split()[-5:-2] == ["2", "2.00", "1.00"]     # calls, mean and min in microseconds
+    assert lines[1].split()[-6:-2] == ["2", "2.00", "2.00", "1.00"]     # calls, mean, median, min (microseconds)
 
 
 def test_sq_averages_per_dispatch_and_forms_ratios(tmp_path):
