@@ -776,8 +776,9 @@ def cpu_baseline_shared(w, q, kc, vc, ks, vs, tables, ctx, budget_s, gpu_out=Non
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the paged decode path has no "
-                                   "multi-GPU mode in this build (see the sharding notes in the design doc)",
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the paged decode path is a "
+                                   "single-GPU library (each GPU would hold its own share of the heads and "
+                                   "sequences); no multi-GPU mode exists",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
