@@ -69,6 +69,8 @@ extern "C" {
 #define PKV_ERR_MEMORY_KIND (-9)    /* a buffer is neither device memory nor pinned host     */
                                     /* memory the device can address                         */
 #define PKV_ERR_SCRATCH_LIMIT (-10) /* the call needs more than PKV_STATIC_SCRATCH_BYTES         */
+#define PKV_ERR_PRECONDITION (-11)  /* debug checks: a device-resident value breaks the call's
+                                       preconditions; nothing was launched (pkv_debug_report)  */
 
 /* Size of the static device scratch of pkv_paged_attention_decode_noalloc (one copy per GPU). */
 #define PKV_STATIC_SCRATCH_BYTES (48u << 20)
@@ -76,6 +78,70 @@ extern "C" {
 /* attention kernel families reported by pkv_attention_plan */
 #define PKV_PATH_VECTOR 0  /* per-query-head vector kernel (wave shuffles, no MFMA)  */
 #define PKV_PATH_MFMA 1    /* grouped-query kernel: one kv head's group on MFMA      */
+
+/*
+ * Debug checks of the device-resident values (pkv_set_debug_checks).
+ *
+ * The values a call reads from device memory -- block tables, context lengths,
+ * slots, block-copy pairs, the host order, the shared decode's groups, the
+ * prefill's query offsets -- cannot be checked on the host, and the kernels
+ * take them on trust: a value out of place is clamped or skipped (never an
+ * access outside the buffers) and gives wrong numbers.  With the checks on,
+ * each entry point, after its host checks, runs check kernels over those values
+ * on its stream, waits for them (the call then synchronises the stream), and
+ * returns PKV_ERR_PRECONDITION without launching anything else when a value
+ * breaks a rule below; pkv_debug_report then says which.  The rules restate
+ * what the pages fix: a sequence's table lists its blocks in order and position
+ * pos lives in block table[pos / bs] at offset pos % bs ("PagedAttention",
+ * Ultralytics glossary, section "Cách phân trang hoạt động"); a block two
+ * sequences share is copied to a fresh block before either writes into it
+ * ("KV cache paginado e batching contínuo para LLMs", section "Como funciona").
+ * Every value the kernels would clamp or skip counts as a violation here.
+ * Violation kinds, each counted once per offending value:
+ */
+#define PKV_CHECK_CONTEXT_LEN 1    /* context_lens[s] < 0, > max_context_len, or needing more than
+                                      max_blocks_per_seq blocks; index s                          */
+#define PKV_CHECK_BLOCK_ID 2       /* block_tables[s][j] outside [0, num_blocks) for one of the first
+                                      ceil(ctx_s / bs) entries; index s * max_blocks_per_seq + j  */
+#define PKV_CHECK_SLOT 3           /* a slot >= num_blocks * block_size (negative slots are
+                                      padding); index: the token                                   */
+#define PKV_CHECK_DUPLICATE_SLOT 4 /* a slot equal to an earlier token's; index: the later token  */
+#define PKV_CHECK_APPEND_SLOT 5    /* decode with append: slot_mapping[s] >= 0 is not the slot of
+                                      position context_lens[s] - 1; index s                       */
+#define PKV_CHECK_PAIR_ID 6        /* a copy / swap pair's src or dst outside its pool; index: pair */
+#define PKV_CHECK_DUPLICATE_DST 7  /* a pair's dst equal to an earlier pair's; index: the later pair */
+#define PKV_CHECK_DST_IS_SRC 8     /* copy_blocks: a pair's dst equal to some pair's src; index: pair */
+#define PKV_CHECK_SEQ_ORDER 9      /* seq_order not a permutation of 0..num_seqs-1: an entry out of
+                                      range or equal to an earlier one; index: the entry           */
+#define PKV_CHECK_GROUP 10         /* shared decode: group_offsets[0] != 0, decreasing, past
+                                      num_seqs, group_offsets[G] != num_seqs, a group larger than
+                                      max_group_size, or a negative shared count; index: group     */
+#define PKV_CHECK_GROUP_MEMBER 11  /* shared decode: a member outside [0, num_seqs) or listed twice;
+                                      index: position in group_members                             */
+#define PKV_CHECK_SHARED_BLOCK 12  /* shared decode: a member's table differs from the group's first
+                                      member on a block read as shared; index s * max_blocks_per_seq + j */
+#define PKV_CHECK_QUERY_START 13   /* prefill: query_start_loc[0] != 0, decreasing, outside
+                                      [0, num_tokens], [num_seqs] != num_tokens, or a chunk longer
+                                      than max_query_len; index: the entry                         */
+
+/*
+ * pkv_set_debug_checks -- turn the debug checks on (mode 1), off (0), or leave
+ * them to the PKV_DEBUG environment variable (-1, the default: on when it is set
+ * and not "0", read at each call).  Process-wide; returns the previous mode.
+ * Host-only.  With the checks on, calls serialise on one library-wide lock
+ * while their checks run, and every call waits for its stream, so they do not
+ * belong under HIP graph capture; results are unchanged.
+ */
+int pkv_set_debug_checks(int mode);
+
+/*
+ * pkv_debug_report -- the debug checks of the calling thread's most recent
+ * checked call: the number of violations (0 if it passed or no call was
+ * checked), and the kind (PKV_CHECK_*) and index of the first one in (kind,
+ * index) order (0 and -1 when there is none).  Any pointer may be NULL.
+ * Host-only; returns PKV_OK.
+ */
+int pkv_debug_report(int64_t* violations, int* kind, int64_t* index);
 
 /* Human-readable text of a status code (static string, never NULL). */
 const char* pkv_status_string(int status);

@@ -226,11 +226,18 @@ int pkv_reshape_and_cache(const void* key, const void* value, void* k_cache, voi
   if (num_tokens == 0) return PKV_OK;
   if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PKV_ERR_NULL_POINTER;
   if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_UNSUPPORTED;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (debug_checks_on()) {
+    DeviceChecks c(s);
+    c.slots(slot_mapping, num_tokens, (long long)num_blocks * block_size);
+    const int cst = c.finish();
+    if (cst != PKV_OK) return cst;
+  }
   (void)hipGetLastError();
   return launch_status(launch_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, num_tokens,
                                                      num_kv_heads, head_dim, block_size, num_blocks, src_dtype,
                                                      kv_dtype, k_scale, v_scale, fp8 ? k_scales : nullptr,
-                                                     fp8 ? v_scales : nullptr, reinterpret_cast<hipStream_t>(stream)));
+                                                     fp8 ? v_scales : nullptr, s));
 }
 
 int pkv_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, int num_pairs, int num_kv_heads,
@@ -246,10 +253,16 @@ int pkv_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, 
   if (num_pairs == 0) return PKV_OK;
   if (!k_cache || !v_cache || !block_mapping) return PKV_ERR_NULL_POINTER;
   if (!aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_UNSUPPORTED;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (debug_checks_on()) {
+    DeviceChecks c(s);
+    c.pairs(block_mapping, num_pairs, num_blocks, num_blocks, true);
+    const int cst = c.finish();
+    if (cst != PKV_OK) return cst;
+  }
   (void)hipGetLastError();
   return launch_status(launch_copy_blocks(k_cache, v_cache, num_blocks, k_cache, v_cache, num_blocks,
-                                               block_mapping, num_pairs, block_bytes,
-                                               reinterpret_cast<hipStream_t>(stream)));
+                                               block_mapping, num_pairs, block_bytes, s));
 }
 
 int pkv_swap_blocks(const void* src_k, const void* src_v, int src_num_blocks, void* dst_k, void* dst_v,
@@ -283,10 +296,16 @@ int pkv_swap_blocks(const void* src_k, const void* src_v, int src_num_blocks, vo
   }
   for (int i = 0; i < 4; ++i)
     if (!aligned16(a[i])) return PKV_ERR_UNSUPPORTED;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (debug_checks_on()) {
+    DeviceChecks c(s);
+    c.pairs(static_cast<const int64_t*>(a[4]), num_pairs, src_num_blocks, dst_num_blocks, false);
+    const int cst = c.finish();
+    if (cst != PKV_OK) return cst;
+  }
   (void)hipGetLastError();
   return launch_status(launch_copy_blocks(a[0], a[1], src_num_blocks, a[2], a[3], dst_num_blocks,
-                                               static_cast<const int64_t*>(a[4]), num_pairs, block_bytes,
-                                               reinterpret_cast<hipStream_t>(stream)));
+                                               static_cast<const int64_t*>(a[4]), num_pairs, block_bytes, s));
 }
 
 }  // extern "C"

@@ -1,7 +1,8 @@
 // pkv_api.hip -- the attention half of the C ABI declared in include/pkv.h:
 // host-side argument checks, the choice of kernel family and launch shape, and
 // launches; plus the status strings and version.
-// Nothing here allocates, frees or synchronises.
+// Nothing here allocates or frees; only the debug checks (checks.hip, off by
+// default) synchronise.
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
@@ -187,6 +188,9 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_SCRATCH_LIMIT:
       return "the call needs more split-context scratch than the library's static scratch holds "
              "(PKV_STATIC_SCRATCH_BYTES); call pkv_paged_attention_decode with a workspace instead";
+    case PKV_ERR_PRECONDITION:
+      return "debug checks: a device-resident value (block table, context length, slot, pair, order, group or "
+             "query offset) breaks the call's preconditions; nothing was launched (see pkv_debug_report)";
   }
   return "unknown status";
 }
@@ -306,6 +310,16 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   p.head_run_units = head_run_units_for(pl.mode, pl.units);
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (pkv::debug_checks_on()) {
+    pkv::DeviceChecks c(s);
+    c.tables(block_tables, max_blocks_per_seq, context_lens, num_seqs, block_size, num_blocks, max_context_len);
+    c.permutation(seq_order, num_seqs);
+    if (new_k)
+      c.append_slots(slot_mapping, block_tables, max_blocks_per_seq, context_lens, num_seqs, block_size,
+                     (long long)num_blocks * block_size);
+    const int cst = c.finish();
+    if (cst != PKV_OK) return cst;
+  }
   (void)hipGetLastError();  // start from a clean error state
   hipError_t e;
   if (pl.path == PKV_PATH_MFMA)
@@ -429,9 +443,20 @@ int pkv_paged_attention_decode_shared(void* out, const void* q, void* k_cache, v
   p.grp_mem = group_members;
   p.grp_shared = group_shared_blocks;
   p.grp_max = max_group_size;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (pkv::debug_checks_on()) {
+    pkv::DeviceChecks c(s);
+    c.tables(block_tables, max_blocks_per_seq, context_lens, num_seqs, block_size, num_blocks, max_context_len);
+    c.groups(group_offsets, group_members, group_shared_blocks, num_groups, max_group_size, block_tables,
+             max_blocks_per_seq, context_lens, num_seqs, block_size, p.ctx_cap);
+    if (key)
+      c.append_slots(slot_mapping, block_tables, max_blocks_per_seq, context_lens, num_seqs, block_size,
+                     (long long)num_blocks * block_size);
+    const int cst = c.finish();
+    if (cst != PKV_OK) return cst;
+  }
   (void)hipGetLastError();
-  return pkv::launch_status(pkv::launch_attention_shared(p, q_dtype, kv_dtype, head_dim, key != nullptr,
-                                                         reinterpret_cast<hipStream_t>(stream)));
+  return pkv::launch_status(pkv::launch_attention_shared(p, q_dtype, kv_dtype, head_dim, key != nullptr, s));
 }
 
 int pkv_paged_prefill_attention(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -482,8 +507,16 @@ int pkv_paged_prefill_attention(void* out, const void* q, const void* k_cache, c
   long long chunk = (long long)tiles * p.group;
   if (e && *e) chunk = atoi(e);
   p.xcd_chunk = (uint32_t)(chunk < 0 ? 0 : (chunk > 4096 ? 4096 : chunk));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (pkv::debug_checks_on()) {
+    pkv::DeviceChecks c(s);
+    c.tables(block_tables, max_blocks_per_seq, context_lens, num_seqs, block_size, num_blocks, max_context_len);
+    c.query_starts(query_start_loc, num_seqs, num_tokens, max_query_len);
+    const int cst = c.finish();
+    if (cst != PKV_OK) return cst;
+  }
   (void)hipGetLastError();
-  return pkv::launch_status(pkv::launch_prefill(p, q_dtype, head_dim, reinterpret_cast<hipStream_t>(stream)));
+  return pkv::launch_status(pkv::launch_prefill(p, q_dtype, head_dim, s));
 }
 
 }  // extern "C"

@@ -53,4 +53,36 @@ hipError_t launch_copy_blocks(const void* src_k, const void* src_v, int src_bloc
                               int dst_blocks, const int64_t* pairs, int num_pairs, int64_t block_bytes,
                               hipStream_t stream);
 
+// Debug checks of the device-resident values (checks.hip, pkv_set_debug_checks).
+// An entry point whose host checks passed builds one DeviceChecks on its
+// stream, adds the checks that fit its arguments, and calls finish(): PKV_OK,
+// PKV_ERR_PRECONDITION (launch nothing more) or PKV_ERR_LAUNCH.  The object
+// holds the library-wide check lock until it is destroyed.
+bool debug_checks_on();
+
+class DeviceChecks {
+ public:
+  explicit DeviceChecks(hipStream_t stream);
+  ~DeviceChecks();
+  DeviceChecks(const DeviceChecks&) = delete;
+  DeviceChecks& operator=(const DeviceChecks&) = delete;
+  void tables(const int32_t* tables, int max_blocks_per_seq, const int32_t* context_lens, int num_seqs,
+              int block_size, int num_blocks, int max_context_len);
+  void permutation(const int32_t* order, int n);
+  void slots(const int64_t* slots, int n, long long num_slots);
+  void append_slots(const int64_t* slots, const int32_t* tables, int max_blocks_per_seq, const int32_t* context_lens,
+                    int num_seqs, int block_size, long long num_slots);
+  void pairs(const int64_t* mapping, int n, int src_blocks, int dst_blocks, bool same_pool);
+  void groups(const int32_t* offsets, const int32_t* members, const int32_t* shared, int num_groups,
+              int max_group_size, const int32_t* tables, int max_blocks_per_seq, const int32_t* context_lens,
+              int num_seqs, int block_size, int ctx_cap);
+  void query_starts(const int32_t* query_start_loc, int num_seqs, int num_tokens, int max_query_len);
+  int finish();
+
+ private:
+  struct Impl;
+  Impl* impl_;
+  void note(hipError_t e);
+};
+
 }  // namespace pkv

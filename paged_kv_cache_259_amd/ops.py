@@ -67,13 +67,26 @@ _lib.pkv_paged_prefill_attention.restype = _c_int
 _lib.pkv_paged_prefill_attention.argtypes = [_vp] * 5 + [_c_int] + [_vp, _vp] + [_c_int] * 9 + [_c_float] + [_c_int] * 2 + [_vp]
 _lib.pkv_swap_blocks.restype = _c_int
 _lib.pkv_swap_blocks.argtypes = [_vp, _vp, _c_int, _vp, _vp, _c_int, _vp] + [_c_int] * 5 + [_vp]
+_lib.pkv_set_debug_checks.restype = _c_int
+_lib.pkv_set_debug_checks.argtypes = [_c_int]
+_lib.pkv_debug_report.restype = _c_int
+_lib.pkv_debug_report.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(_c_int),
+                                  ctypes.POINTER(ctypes.c_int64)]
 
 EXPORTED_SYMBOLS = (
     "pkv_status_string", "pkv_version", "pkv_attention_plan", "pkv_attention_workspace_bytes",
     "pkv_paged_attention_decode", "pkv_reshape_and_cache", "pkv_copy_blocks", "pkv_swap_blocks",
     "pkv_paged_prefill_attention", "pkv_paged_attention_decode_append", "pkv_paged_attention_decode_shared",
-    "pkv_paged_attention_decode_noalloc",
+    "pkv_paged_attention_decode_noalloc", "pkv_set_debug_checks", "pkv_debug_report",
 )
+
+ERR_PRECONDITION = -11              # PKV_ERR_PRECONDITION
+# PKV_CHECK_* violation kinds of the debug checks
+CHECK_KINDS = {
+    1: "context_len", 2: "block_id", 3: "slot", 4: "duplicate_slot", 5: "append_slot", 6: "pair_id",
+    7: "duplicate_dst", 8: "dst_is_src", 9: "seq_order", 10: "group", 11: "group_member", 12: "shared_block",
+    13: "query_start",
+}
 
 STATIC_SCRATCH_BYTES = 48 << 20     # PKV_STATIC_SCRATCH_BYTES
 
@@ -81,7 +94,24 @@ STATIC_SCRATCH_BYTES = 48 << 20     # PKV_STATIC_SCRATCH_BYTES
 class PkvError(RuntimeError):
     def __init__(self, status, call):
         self.status = status
-        super().__init__(f"{call}: {_lib.pkv_status_string(status).decode()} (status {status})")
+        self.report = debug_report() if status == ERR_PRECONDITION else None
+        msg = f"{call}: {_lib.pkv_status_string(status).decode()} (status {status})"
+        if self.report:
+            n, kind, index = self.report
+            msg += f"; {n} violation(s), first: {CHECK_KINDS.get(kind, kind)} at index {index}"
+        super().__init__(msg)
+
+
+def set_debug_checks(mode):
+    """Debug checks of the device-resident values: 1 on, 0 off, -1 follow PKV_DEBUG. Returns the previous mode."""
+    return _lib.pkv_set_debug_checks(int(mode))
+
+
+def debug_report():
+    """(violations, kind, index) of the calling thread's most recent checked call (kind 0 / index -1: none)."""
+    n, kind, index = ctypes.c_int64(0), ctypes.c_int(0), ctypes.c_int64(-1)
+    _check(_lib.pkv_debug_report(ctypes.byref(n), ctypes.byref(kind), ctypes.byref(index)), "pkv_debug_report")
+    return n.value, kind.value, index.value
 
 
 def _check(status, call):

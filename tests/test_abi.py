@@ -8,6 +8,7 @@ import os
 import re
 import subprocess
 import sys
+import threading
 
 import pytest
 
@@ -34,7 +35,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_symbols()
-    assert len(names) == 12
+    assert len(names) == 14
     for n in names:
         assert hasattr(lib, n), n
     nm = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
@@ -48,7 +49,7 @@ def test_binding_declares_the_same_symbols(lib):
 
 
 def test_status_strings(lib):
-    for st in range(0, -11, -1):
+    for st in range(0, -12, -1):
         s = lib.pkv_status_string(st)
         assert s and s != b"unknown status"
     assert lib.pkv_status_string(-99) == b"unknown status"
@@ -211,6 +212,37 @@ def test_shared_decode_host_checks(lib):
     assert call(out=None) == -1 and call(offs=None) == -1
     assert call(key=FAKE) == -1                                   # append needs value and slots too
     assert call(out=ctypes.c_void_p(0x10008)) == -4               # misaligned output
+
+
+def test_debug_check_switch_and_report(lib):
+    """The debug checks' switch and report are host-only; with the checks on, calls that fail a
+    host check (or have nothing to do) still return before any device call, so the usual codes hold."""
+    prev = lib.pkv_set_debug_checks(1)
+    try:
+        assert lib.pkv_set_debug_checks(1) == 1
+        assert _decode(lib, num_seqs=0) == 0 and _decode(lib, H=6, KVH=4) == -3 and _decode(lib, ptr=None) == -1
+        assert _noalloc(lib, max_ctx=2_000_000, part=16) == -10
+        f = ctypes.c_float
+        assert lib.pkv_reshape_and_cache(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 4, 128, 16, 8, 1, 1, f(1), f(1), None,
+                                         None, None) == 0
+        assert lib.pkv_copy_blocks(FAKE, FAKE, None, 3, 4, 128, 16, 8, 1, None) == -1
+        got = []
+
+        def report():                                                     # a thread with no checked call
+            n, kind, index = ctypes.c_int64(7), ctypes.c_int(7), ctypes.c_int64(7)
+            got.append(lib.pkv_debug_report(ctypes.byref(n), ctypes.byref(kind), ctypes.byref(index)))
+            got.append((n.value, kind.value, index.value))
+
+        t = threading.Thread(target=report)
+        t.start()
+        t.join()
+        assert got == [0, (0, 0, -1)]
+        assert lib.pkv_debug_report(None, None, None) == 0
+        assert lib.pkv_set_debug_checks(0) == 1 and lib.pkv_set_debug_checks(-5) == 0
+        assert lib.pkv_set_debug_checks(-1) == -1
+    finally:
+        lib.pkv_set_debug_checks(prev)
+    assert b"debug checks" in lib.pkv_status_string(-11)
 
 
 def test_missing_library_fails_loudly():
