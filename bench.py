@@ -2,7 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama13b_f16]
 
-With a prefill workload (prefill_llama13b_f16, prefill_gqa_bf16) the step is
+With a prefill workload (prefill_llama13b_f16, prefill_gqa_bf16, and
+prefill_gqa_fp8 over an E4M3 cache) the step is
 reshape_and_cache of the chunks' K/V followed by paged_prefill_attention, and
 the roofline is the dense MFMA peak instead of HBM.  prefix_cache_llama13b_f16
 times a prefill step of requests sharing a system prompt with the host prefix
@@ -354,12 +355,15 @@ def cpu_baseline_prefill(w, inp, tables, ctx, budget_s, gpu_out=None):
     import torch
     from threadpoolctl import threadpool_info
     qsl = inp.query_start_loc
+    decode = None
+    if w.kv8:                                         # E4M3 codes -> values, as the oracle reads them
+        decode = lambda c: oracle.dequant_e4m3(c, w.kv_scale)
     done, flops, spent, refs = 0, 0, 0.0, []
     for s in range(w.num_seqs):
         n, c = int(inp.chunk_lens[s]), int(ctx[s])
         blocks = tables[s, : -(-c // w.block_size)]
-        kp = _BlockSubset(inp.k_cache, blocks)
-        vp = _BlockSubset(inp.v_cache, blocks)
+        kp = _BlockSubset(inp.k_cache, blocks, decode)
+        vp = _BlockSubset(inp.v_cache, blocks, decode)
         q = inp.q[int(qsl[s]):int(qsl[s + 1])].cpu().to(torch.float64).numpy()
         t0 = time.perf_counter()
         refs.append(oracle.prefill_ref(q, kp, vp, tables[s:s + 1], ctx[s:s + 1], np.array([0, n]), w.softmax_scale,
@@ -406,12 +410,14 @@ def main_prefill(args, w):
     out = torch.empty_like(inp.q)
     stream = torch.cuda.current_stream()
 
+    sc = dict(k_scale=w.kv_scale, v_scale=w.kv_scale) if w.kv8 else {}
+
     def reshape():
-        ops.reshape_and_cache(inp.k_new, inp.v_new, inp.k_cache, inp.v_cache, slots, stream=stream)
+        ops.reshape_and_cache(inp.k_new, inp.v_new, inp.k_cache, inp.v_cache, slots, stream=stream, **sc)
 
     def attend():
         ops.paged_prefill_attention(out, inp.q, inp.k_cache, inp.v_cache, tables, ctx, qsl, w.softmax_scale, max_q,
-                                    max_ctx, stream=stream)
+                                    max_ctx, stream=stream, **sc)
 
     warm = warm_up(lambda: (reshape(), attend()), args.warmup)
     K = args.steps
@@ -441,7 +447,8 @@ def main_prefill(args, w):
         "value": round(flops / (step_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
         "warmup": warm, "ms_per_step": round(step_ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype,
-        "data": "synthetic (seeded N(0,1) q/K/V, uniform prior context lengths, shuffled block tables)",
+        "data": "synthetic (seeded N(0,1) q/K/V" + (", E4M3 pool codes" if w.kv8 else "")
+                + ", uniform prior context lengths, shuffled block tables)",
         "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_heads": w.num_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
                    "query_tokens": tokens, "sum_context": int(ctx_np.sum()), "max_context": max_ctx},

@@ -407,6 +407,9 @@ int pkv_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, 
  *   out[row][h][:] = sum_{t<=p} softmax_t(scale * <q[row][h], K_t>) V_t
  * in fp32 with an online softmax; the probabilities enter the PV product
  * rounded to the q dtype.  A row with p < 0 (more queries than context) is zero.
+ * Over an 8-bit cache ([PA/related] FP8 cache) K_t and V_t are the stored
+ * values, code * k_scale (resp. v_scale) or code * k_scales[g] with the
+ * per-head arrays, as for pkv_paged_attention_decode.
  *
  * out, q       [num_tokens][num_heads][head_dim], q_dtype.
  * query_start_loc  [num_seqs + 1] int32, non-decreasing, from 0 to num_tokens;
@@ -418,16 +421,21 @@ int pkv_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, 
  * max_query_len    host bound on every n_s (sizes the grid); rows past it are
  *              not written.  max_context_len: host bound on context_lens (larger
  *              values are clamped, giving wrong positions but no stray access).
- * Supported: q_dtype == kv_dtype in {PKV_F16, PKV_BF16}, head_dim 64 or 128,
- *   block_size 16.  Needs no workspace.  max_query_len, num_seqs or num_tokens
- *   == 0 is a no-op returning PKV_OK.
+ * k_scale, v_scale, k_scales, v_scales  the 8-bit cache's scales, as for
+ *              pkv_paged_attention_decode (checked the same way, PKV_ERR_SCALE);
+ *              ignored for a 16-bit cache.
+ * Supported: q_dtype in {PKV_F16, PKV_BF16} over a cache of q's type or either
+ *   8-bit format, head_dim 64 or 128, block_size 16.  Needs no workspace.
+ *   max_query_len, num_seqs or num_tokens == 0 is a no-op returning PKV_OK.
  */
 int pkv_paged_prefill_attention(void* out, const void* q, const void* k_cache, const void* v_cache,
                                 const int32_t* block_tables, int max_blocks_per_seq,
                                 const int32_t* context_lens, const int32_t* query_start_loc,
                                 int num_seqs, int num_tokens, int num_heads, int num_kv_heads, int head_dim,
                                 int block_size, int num_blocks, int max_query_len, int max_context_len,
-                                float scale, int q_dtype, int kv_dtype, void* stream);
+                                float scale, float k_scale, float v_scale,
+                                const float* k_scales, const float* v_scales,
+                                int q_dtype, int kv_dtype, void* stream);
 
 /*
  * pkv_swap_blocks -- whole-block copies between two pools, for preemption by

@@ -93,39 +93,6 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* lds) {
   return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(lds)));
 }
 
-// 8-bit K/V (E4M3 = FP8, E5M2 = BF8) as MFMA operands.  Both formats convert
-// exactly to f16 and bf16, so the products and sums are those of the 16-bit
-// path over the dequantised values; the scales are applied to the logits (k)
-// and to the output (v).
-// Two 8-bit codes (the low or high half of a word) -> two elements of the
-// 16-bit MFMA type T, through gfx950's scaled converts at scale 1 (exact:
-// checked on every code of both formats, both halves, NaN and infinity
-// classes included).
-template <class T, class KT> __device__ __forceinline__ uint32_t kv8x2_to_16(uint32_t u, bool hi);
-template <> __device__ __forceinline__ uint32_t kv8x2_to_16<BF16, FP8>(uint32_t u, bool hi) {
-  return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u, 1.0f, true)
-                                         : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u, 1.0f, false));
-}
-template <> __device__ __forceinline__ uint32_t kv8x2_to_16<BF16, BF8>(uint32_t u, bool hi) {
-  return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(u, 1.0f, true)
-                                         : __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(u, 1.0f, false));
-}
-template <> __device__ __forceinline__ uint32_t kv8x2_to_16<F16, FP8>(uint32_t u, bool hi) {
-  return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(u, 1.0f, true)
-                                         : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(u, 1.0f, false));
-}
-template <> __device__ __forceinline__ uint32_t kv8x2_to_16<F16, BF8>(uint32_t u, bool hi) {
-  return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(u, 1.0f, true)
-                                         : __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(u, 1.0f, false));
-}
-
-// Eight 8-bit codes (two words) -> eight elements of the 16-bit MFMA type T.
-template <class T, class KT>
-__device__ __forceinline__ uint4 kv8x8_to_16(uint32_t a, uint32_t b) {
-  return make_uint4(kv8x2_to_16<T, KT>(a, false), kv8x2_to_16<T, KT>(a, true), kv8x2_to_16<T, KT>(b, false),
-                    kv8x2_to_16<T, KT>(b, true));
-}
-
 // T: the q type and MFMA operand type (f16 / bf16); KT: the cache type, T itself
 // or one of the 8-bit formats.
 template <class T, class KT, int D, int NW, bool PIPE>

@@ -464,13 +464,17 @@ int pkv_paged_prefill_attention(void* out, const void* q, const void* k_cache, c
                                 const int32_t* query_start_loc, int num_seqs, int num_tokens, int num_heads,
                                 int num_kv_heads,
                                 int head_dim, int block_size, int num_blocks, int max_query_len,
-                                int max_context_len, float scale, int q_dtype, int kv_dtype, void* stream) {
+                                int max_context_len, float scale, float k_scale, float v_scale,
+                                const float* k_scales, const float* v_scales, int q_dtype, int kv_dtype,
+                                void* stream) {
   if (num_seqs < 0 || num_tokens < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
       max_query_len < 0 || max_context_len < 0 || max_blocks_per_seq <= 0 || num_blocks <= 0)
     return PKV_ERR_BAD_SIZE;
   if (num_heads % num_kv_heads != 0) return PKV_ERR_HEAD_GROUPING;
   if (!pkv::prefill_supported(q_dtype, kv_dtype, head_dim, block_size)) return PKV_ERR_UNSUPPORTED;
   if (!isfinite(scale)) return PKV_ERR_BAD_SIZE;
+  const bool fp8 = kv_dtype == PKV_FP8_E4M3 || kv_dtype == PKV_FP8_E5M2;
+  if (fp8 && !((k_scales || pkv::good_scale(k_scale)) && (v_scales || pkv::good_scale(v_scale)))) return PKV_ERR_SCALE;
   const int bm = pkv::prefill_tile_rows();
   const long long tiles = ((long long)max_query_len + bm - 1) / bm;
   const long long wgs = (long long)num_seqs * num_heads * tiles;
@@ -500,6 +504,10 @@ int pkv_paged_prefill_attention(void* out, const void* q, const void* k_cache, c
   const long long cap_table = (long long)max_blocks_per_seq * block_size;
   p.ctx_cap = (int)(max_context_len < cap_table ? max_context_len : cap_table);
   p.qk_scale = scale * kLog2e;
+  p.k_scale = fp8 ? k_scale : 1.f;
+  p.v_scale = fp8 ? v_scale : 1.f;
+  p.k_scales = fp8 ? k_scales : nullptr;
+  p.v_scales = fp8 ? v_scales : nullptr;
   p.longest_first = PKV_LONGEST_FIRST && num_seqs > 1 && num_seqs <= pkv::kMaxSliceSeqs;
   p.total_wgs = (uint32_t)wgs;
   // the query tiles and heads that read one kv head's K/V run on one XCD (shared L2)
@@ -516,7 +524,7 @@ int pkv_paged_prefill_attention(void* out, const void* q, const void* k_cache, c
     if (cst != PKV_OK) return cst;
   }
   (void)hipGetLastError();
-  return pkv::launch_status(pkv::launch_prefill(p, q_dtype, head_dim, s));
+  return pkv::launch_status(pkv::launch_prefill(p, q_dtype, kv_dtype, head_dim, s));
 }
 
 }  // extern "C"

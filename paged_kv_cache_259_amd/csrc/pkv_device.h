@@ -87,6 +87,39 @@ template <> struct Unpack<BF8> {
   }
 };
 
+// 8-bit K/V (E4M3 = FP8, E5M2 = BF8) as MFMA operands.  Both formats convert
+// exactly to f16 and bf16, so the products and sums are those of the 16-bit
+// path over the dequantised values; the scales are applied to the logits (k)
+// and to the output (v).
+// Two 8-bit codes (the low or high half of a word) -> two elements of the
+// 16-bit MFMA type T, through gfx950's scaled converts at scale 1 (exact:
+// checked on every code of both formats, both halves, NaN and infinity
+// classes included).
+template <class T, class KT> __device__ __forceinline__ uint32_t kv8x2_to_16(uint32_t u, bool hi);
+template <> __device__ __forceinline__ uint32_t kv8x2_to_16<BF16, FP8>(uint32_t u, bool hi) {
+  return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u, 1.0f, true)
+                                         : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u, 1.0f, false));
+}
+template <> __device__ __forceinline__ uint32_t kv8x2_to_16<BF16, BF8>(uint32_t u, bool hi) {
+  return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(u, 1.0f, true)
+                                         : __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(u, 1.0f, false));
+}
+template <> __device__ __forceinline__ uint32_t kv8x2_to_16<F16, FP8>(uint32_t u, bool hi) {
+  return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(u, 1.0f, true)
+                                         : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(u, 1.0f, false));
+}
+template <> __device__ __forceinline__ uint32_t kv8x2_to_16<F16, BF8>(uint32_t u, bool hi) {
+  return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(u, 1.0f, true)
+                                         : __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(u, 1.0f, false));
+}
+
+// Eight 8-bit codes (two words) -> eight elements of the 16-bit MFMA type T.
+template <class T, class KT>
+__device__ __forceinline__ uint4 kv8x8_to_16(uint32_t a, uint32_t b) {
+  return make_uint4(kv8x2_to_16<T, KT>(a, false), kv8x2_to_16<T, KT>(a, true), kv8x2_to_16<T, KT>(b, false),
+                    kv8x2_to_16<T, KT>(b, true));
+}
+
 // One scalar element of storage type T at p[i] -> fp32.
 template <class T> __device__ __forceinline__ float load_elem(const void* p, size_t i);
 template <> __device__ __forceinline__ float load_elem<F32>(const void* p, size_t i) {
@@ -598,6 +631,9 @@ struct PrefillParams {
   int ctx_cap;
   int longest_first;               // sequences dispatched in decreasing context length
   float qk_scale;                  // scale * log2(e)
+  float k_scale, v_scale;          // 8-bit cache: the pools' scales, or
+  const float* k_scales;           // per kv head ([num_kv_heads]) when given
+  const float* v_scales;
   uint32_t total_wgs;
   uint32_t xcd_chunk;
 };

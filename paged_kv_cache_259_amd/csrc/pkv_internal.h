@@ -42,7 +42,7 @@ hipError_t launch_attention_reduce(const ReduceParams& p, int out_dtype, int hea
 
 bool prefill_supported(int q_dtype, int kv_dtype, int head_dim, int block_size);
 int prefill_tile_rows();
-hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim, hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams& p, int dtype, int kv_dtype, int head_dim, hipStream_t stream);
 
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
                                     const int64_t* slot_mapping, int num_tokens, int num_kv_heads,

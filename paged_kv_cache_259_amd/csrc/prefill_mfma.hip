@@ -150,21 +150,29 @@ struct Prefill {
   __device__ __forceinline__ static int swz_v(int r) { return 2 * ((r / RPB) % (CPR / 2)); }
 };
 
-template <class T, int D, int RW>
+template <class T, class CT, int D, int RW>
 __global__ __launch_bounds__(PKV_PREFILL_NW * 64) __attribute__((amdgpu_waves_per_eu(PKV_PREFILL_WAVES_PER_EU)))
 void prefill_mfma_kernel(PrefillParams p) {
   using P = Prefill<T, D, RW>;
   using Op = PrefillOp<T>;
   constexpr int STEP = P::STEP, BS = P::BS, NC = P::NC, ND = P::ND, CPR = P::CPR, KT = P::KT,
                 NS = P::NS;
+  // CT, the cache type: T itself, or an 8-bit format (E4M3 / E5M2) whose
+  // codes are staged as bytes and converted, exactly, to T in LDS
+  constexpr bool kQuant = CT::bytes == 1;
+  static_assert(kQuant || CT::kId == T::kId, "a 16-bit cache has q's type");
   struct StepIds { int b[KT]; };                            // block ids of one step (-1 past the keys)
   // RING stage buffers per tensor as separate objects: the compiler then sees
   // that loads into one never alias reads of another and adds no wait between them
   constexpr int R = PKV_PREFILL_RING;
   static_assert(R >= 2 && R <= 4, "2 to 4 stage buffers");
-  __shared__ __align__(16) uint16_t sK0[P::TILE], sK1[P::TILE], sV0[P::TILE], sV1[P::TILE];
-  __shared__ __align__(16) uint16_t sK2[R > 2 ? P::TILE : 1], sV2[R > 2 ? P::TILE : 1];
-  __shared__ __align__(16) uint16_t sK3[R > 3 ? P::TILE : 1], sV3[R > 3 ? P::TILE : 1];
+  __shared__ __align__(16) uint16_t sK0[P::TILE], sV0[P::TILE];
+  __shared__ __align__(16) uint16_t sK1[kQuant ? 1 : P::TILE], sV1[kQuant ? 1 : P::TILE];
+  __shared__ __align__(16) uint16_t sK2[R > 2 && !kQuant ? P::TILE : 1], sV2[R > 2 && !kQuant ? P::TILE : 1];
+  __shared__ __align__(16) uint16_t sK3[R > 3 && !kQuant ? P::TILE : 1], sV3[R > 3 && !kQuant ? P::TILE : 1];
+  // 8-bit cache: two stage buffers of codes per tensor, converted into sK0 / sV0
+  constexpr int TILE8 = kQuant ? STEP * D : 16;
+  __shared__ __align__(16) uint8_t qK0[TILE8], qK1[TILE8], qV0[TILE8], qV1[TILE8];
   auto kbuf = [&](auto b) -> uint16_t* {
     constexpr int k = decltype(b)::value;
     if constexpr (k == 0) return sK0; else if constexpr (k == 1) return sK1; else if constexpr (k == 2) return sK2; else return sK3;
@@ -190,6 +198,14 @@ void prefill_mfma_kernel(PrefillParams p) {
     seq = seq_of_rank<P::NW * 64>(p.context_lens, p.num_seqs, p.ctx_cap, BS, seq, reinterpret_cast<int*>(sK0),
                                   reinterpret_cast<int*>(sK1));
   const int kvh = h / p.group;
+  // logit scale, and with an 8-bit cache the K scale folded into it (the
+  // converted codes are the cache's values divided by the scale) and the V
+  // scale applied to the output
+  float qk_scale = p.qk_scale, out_scale = 1.f;
+  if constexpr (kQuant) {
+    qk_scale *= p.k_scales ? p.k_scales[kvh] : p.k_scale;
+    out_scale = p.v_scales ? p.v_scales[kvh] : p.v_scale;
+  }
 
   // rows [q0, q1) of q / out; offsets are clamped to the num_tokens rows that exist
   int q0 = p.query_start_loc[seq];
@@ -214,8 +230,8 @@ void prefill_mfma_kernel(PrefillParams p) {
   // B operand of QK: Q^T, lane l holds query row wrow0 + 16 g + c16, dims 32c + 8 g4 .. +8.
   // With a negative scale Q enters negated (sign bits flipped, exact), so the
   // logit scale qs applied to the products is never negative.
-  const uint32_t qsign = p.qk_scale < 0.f ? 0x80008000u : 0u;
-  const float qs = fabsf(p.qk_scale);
+  const uint32_t qsign = qk_scale < 0.f ? 0x80008000u : 0u;
+  const float qs = fabsf(qk_scale);
   uint4 qf[RW][NC];
   int qpos[RW];
   bool qreal[RW];
@@ -307,6 +323,63 @@ void prefill_mfma_kernel(PrefillParams p) {
         load_lds16(ok ? kblk + rb * D + (dma_pos ^ P::swz_k(rb)) * 8 : kZeroChunk, kb + (w * P::QPW + j) * 512);
         load_lds16(ok ? vblk + rb * D + (dma_pos ^ P::swz_v(rb)) * 8 : kZeroChunk, vb + (w * P::QPW + j) * 512);
       }
+    }
+  };
+  // 8-bit cache: a step's codes go into a stage buffer as rows of D bytes, in
+  // order (row r of the step at byte r D).  One load instruction fills 1 KiB =
+  // RPI8 rows, so wave w loads block w of the step (QPW8 instructions per
+  // tensor), lane l the 16-byte chunk l % CPR8 of row l / CPR8 of its rows;
+  // the same fast and checked paths as the 16-bit staging.
+  constexpr int CPR8 = D / 16;                              // 16-byte chunks per row of codes
+  constexpr int RPI8 = 64 / CPR8;                           // rows per load instruction
+  constexpr int QPW8 = BS / RPI8;                           // load instructions per wave and tensor
+  static_assert(!kQuant || (KT == P::NW && BS % RPI8 == 0), "8-bit staging: one block per wave and step");
+  const int r8 = lane / CPR8, c8 = lane % CPR8;
+  auto load_step8 = [&](int i, StepIds ids, uint8_t* kb, uint8_t* vb) {
+    int blk = ids.b[0];
+#pragma unroll
+    for (int kt = 1; kt < KT; ++kt) blk = w == kt ? ids.b[kt] : blk;   // the wave's block (uniform)
+    const bool in_pool = blk >= 0 && blk < p.num_blocks;
+    const size_t boff = (size_t)(in_pool ? blk : 0) * block_stride + (size_t)kvh * BS * D;   // bytes
+    const uint8_t* kblk = reinterpret_cast<const uint8_t*>(p.k_cache) + boff;
+    const uint8_t* vblk = reinterpret_cast<const uint8_t*>(p.v_cache) + boff;
+    if (in_pool && i * STEP + w * BS + BS <= nkeys) {       // uniform: the whole block is keys
+      const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kblk, BS * D), vr = buffer_rsrc(vblk, BS * D);
+#pragma unroll
+      for (int j = 0; j < QPW8; ++j) {
+        const uint32_t off = (uint32_t)((j * RPI8 + r8) * D + c8 * 16);
+        load_lds16(kr, off, kb + (w * QPW8 + j) * 1024);
+        load_lds16(vr, off, vb + (w * QPW8 + j) * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < QPW8; ++j) {
+        const int rb = j * RPI8 + r8;                       // row inside the block
+        const bool ok = in_pool && i * STEP + w * BS + rb < nkeys;
+        load_lds16(ok ? kblk + rb * D + c8 * 16 : (const uint8_t*)kZeroChunk, kb + (w * QPW8 + j) * 1024);
+        load_lds16(ok ? vblk + rb * D + c8 * 16 : (const uint8_t*)kZeroChunk, vb + (w * QPW8 + j) * 1024);
+      }
+    }
+  };
+  // Codes of one step -> the 16-bit tiles sK0 / sV0 in the layout the
+  // fragment reads expect: the 16 codes of chunk c of row r are dims 16 c ..
+  // 16 c + 15, logical 16-bit chunks 2c and 2c + 1, stored at their swizzled
+  // positions.  Both formats convert exactly to f16 and bf16.
+  auto convert8 = [&](const uint8_t* kq, const uint8_t* vq) __attribute__((always_inline)) {
+    constexpr int CH = STEP * CPR8;                         // 16-byte chunks per tensor and step
+    static_assert(CH % (P::NW * 64) == 0, "whole passes");
+    if constexpr (kQuant) {
+#pragma unroll
+    for (int q = tid; q < CH; q += P::NW * 64) {
+      const int r = q / CPR8, c = q % CPR8;
+      const uint4 kx = *reinterpret_cast<const uint4*>(kq + q * 16);
+      const uint4 vx = *reinterpret_cast<const uint4*>(vq + q * 16);
+      const int sk = P::swz_k(r), sv = P::swz_v(r);
+      *reinterpret_cast<uint4*>(sK0 + r * D + ((2 * c) ^ sk) * 8) = kv8x8_to_16<T, CT>(kx.x, kx.y);
+      *reinterpret_cast<uint4*>(sK0 + r * D + ((2 * c + 1) ^ sk) * 8) = kv8x8_to_16<T, CT>(kx.z, kx.w);
+      *reinterpret_cast<uint4*>(sV0 + r * D + ((2 * c) ^ sv) * 8) = kv8x8_to_16<T, CT>(vx.x, vx.y);
+      *reinterpret_cast<uint4*>(sV0 + r * D + ((2 * c + 1) ^ sv) * 8) = kv8x8_to_16<T, CT>(vx.z, vx.w);
+    }
     }
   };
   // Per-lane fragment addresses (elements) inside a buffer; the swizzles do not
@@ -450,64 +523,100 @@ void prefill_mfma_kernel(PrefillParams p) {
     step_body(i, kb, vb, ids, std::true_type{});
   };
 
-  // Pipeline: a ring of R buffer pairs; step j's rows live in pair j % R and
-  // are loaded R - 1 steps ahead, into the pair the previous step finished
-  // with (its readers passed the barrier that ended that step).  At the end of
-  // step i each wave waits until its loads of step i + 1 have landed (the
-  // loads of later steps may stay in flight: vmcnt counts them, the loads of
-  // one step are LPS instructions per wave), then meets the other waves at the
-  // barrier.  The loops run R steps per pass from a multiple of R, so every
-  // access names its buffers statically (open steps past the last multiple of
-  // R run with the mask: same result).  Block ids come R steps ahead.
-  constexpr int LPS = 2 * P::QPW;                           // load instructions per wave and step
-  auto wait_step_after = [&](int i) __attribute__((always_inline)) {   // step i + 1's loads have landed
-    const int later = (i + R - 1 < nsteps ? i + R - 1 : nsteps - 1) - (i + 1);   // later steps already issued
-    if constexpr (R >= 4) { if (later >= 2) { __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * LPS)); return; } }
-    if constexpr (R >= 3) { if (later >= 1) { __builtin_amdgcn_s_waitcnt(0x0F70 | LPS); return; } }
-    wait_lds_loads();
-  };
-  static_assert((R - 2) * LPS <= 15, "vmcnt immediate");
-  StepIds ids[R];
-#pragma unroll
-  for (int k = 0; k < R; ++k) ids[k] = ids_of(k);
-  // steps 0 .. R-2 into pairs 0 .. R-2
-  if (0 < nsteps) load_step(0, ids[0], sK0, sV0);
-  if constexpr (R > 2) { if (1 < nsteps) load_step(1, ids[1], sK1, sV1); }
-  if constexpr (R > 3) { if (2 < nsteps) load_step(2, ids[2], sK2, sV2); }
-  wait_step_after(-1);
-  __syncthreads();
-  auto one = [&](int i, auto open, auto cur) __attribute__((always_inline)) {
-    constexpr int c = decltype(cur)::value, n = (c + R - 1) % R;
-    const StepIds idn = ids_of(i + R);
-    if (i + R - 1 < nsteps)
-      load_step(i + R - 1, ids[R - 1], kbuf(std::integral_constant<int, n>{}), vbuf(std::integral_constant<int, n>{}));
-    uint16_t* kc = kbuf(std::integral_constant<int, c>{});
-    uint16_t* vc = vbuf(std::integral_constant<int, c>{});
-    if constexpr (decltype(open)::value) compute_open(i, kc, vc, ids[0]); else compute(i, kc, vc, ids[0]);
-    wait_step_after(i);
+  if constexpr (!kQuant) {
+    // Pipeline: a ring of R buffer pairs; step j's rows live in pair j % R and
+    // are loaded R - 1 steps ahead, into the pair the previous step finished
+    // with (its readers passed the barrier that ended that step).  At the end of
+    // step i each wave waits until its loads of step i + 1 have landed (the
+    // loads of later steps may stay in flight: vmcnt counts them, the loads of
+    // one step are LPS instructions per wave), then meets the other waves at the
+    // barrier.  The loops run R steps per pass from a multiple of R, so every
+    // access names its buffers statically (open steps past the last multiple of
+    // R run with the mask: same result).  Block ids come R steps ahead.
+    constexpr int LPS = 2 * P::QPW;                           // load instructions per wave and step
+    auto wait_step_after = [&](int i) __attribute__((always_inline)) {   // step i + 1's loads have landed
+      const int later = (i + R - 1 < nsteps ? i + R - 1 : nsteps - 1) - (i + 1);   // later steps already issued
+      if constexpr (R >= 4) { if (later >= 2) { __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * LPS)); return; } }
+      if constexpr (R >= 3) { if (later >= 1) { __builtin_amdgcn_s_waitcnt(0x0F70 | LPS); return; } }
+      wait_lds_loads();
+    };
+    static_assert((R - 2) * LPS <= 15, "vmcnt immediate");
+    StepIds ids[R];
+  #pragma unroll
+    for (int k = 0; k < R; ++k) ids[k] = ids_of(k);
+    // steps 0 .. R-2 into pairs 0 .. R-2
+    if (0 < nsteps) load_step(0, ids[0], sK0, sV0);
+    if constexpr (R > 2) { if (1 < nsteps) load_step(1, ids[1], sK1, sV1); }
+    if constexpr (R > 3) { if (2 < nsteps) load_step(2, ids[2], sK2, sV2); }
+    wait_step_after(-1);
     __syncthreads();
-#pragma unroll
-    for (int k = 0; k + 1 < R; ++k) ids[k] = ids[k + 1];
-    ids[R - 1] = idn;
-  };
-  n_open -= n_open % R;
-  auto steps = [&](int i, int end, auto open) __attribute__((always_inline)) {   // steps [i, end) from a multiple of R
-    for (; i < end; i += R) {
-      one(i, open, std::integral_constant<int, 0>{});
-      if (i + 1 < end) one(i + 1, open, std::integral_constant<int, 1>{});
-      if constexpr (R > 2) { if (i + 2 < end) one(i + 2, open, std::integral_constant<int, 2>{}); }
-      if constexpr (R > 3) { if (i + 3 < end) one(i + 3, open, std::integral_constant<int, 3>{}); }
-    }
-  };
-  steps(0, n_open, std::true_type{});
-  steps(n_open, nsteps, std::false_type{});
+    auto one = [&](int i, auto open, auto cur) __attribute__((always_inline)) {
+      constexpr int c = decltype(cur)::value, n = (c + R - 1) % R;
+      const StepIds idn = ids_of(i + R);
+      if (i + R - 1 < nsteps)
+        load_step(i + R - 1, ids[R - 1], kbuf(std::integral_constant<int, n>{}), vbuf(std::integral_constant<int, n>{}));
+      uint16_t* kc = kbuf(std::integral_constant<int, c>{});
+      uint16_t* vc = vbuf(std::integral_constant<int, c>{});
+      if constexpr (decltype(open)::value) compute_open(i, kc, vc, ids[0]); else compute(i, kc, vc, ids[0]);
+      wait_step_after(i);
+      __syncthreads();
+  #pragma unroll
+      for (int k = 0; k + 1 < R; ++k) ids[k] = ids[k + 1];
+      ids[R - 1] = idn;
+    };
+    n_open -= n_open % R;
+    auto steps = [&](int i, int end, auto open) __attribute__((always_inline)) {   // steps [i, end) from a multiple of R
+      for (; i < end; i += R) {
+        one(i, open, std::integral_constant<int, 0>{});
+        if (i + 1 < end) one(i + 1, open, std::integral_constant<int, 1>{});
+        if constexpr (R > 2) { if (i + 2 < end) one(i + 2, open, std::integral_constant<int, 2>{}); }
+        if constexpr (R > 3) { if (i + 3 < end) one(i + 3, open, std::integral_constant<int, 3>{}); }
+      }
+    };
+    steps(0, n_open, std::true_type{});
+    steps(n_open, nsteps, std::false_type{});
+  } else {
+    // 8-bit cache, per step i (stage buffer i % 2 holds its codes, landed):
+    // issue the codes of step i + 1 into the other stage buffer (its codes
+    // were converted before the last barrier but one), convert step i into
+    // sK0 / sV0 (their readers passed the barrier that ended step i - 1),
+    // barrier, QK / softmax / PV, wait for this wave's loads of step i + 1,
+    // barrier.  Steps run in pairs from an even index, so each stage buffer is
+    // named statically.
+    StepIds idc = ids_of(0), idn = ids_of(1);
+    if (0 < nsteps) load_step8(0, idc, qK0, qV0);
+    wait_lds_loads();
+    __syncthreads();
+    auto one8 = [&](int i, auto open, auto cur) __attribute__((always_inline)) {
+      constexpr int c = decltype(cur)::value;
+      const StepIds idnn = ids_of(i + 2);
+      if (i + 1 < nsteps) load_step8(i + 1, idn, c ? qK0 : qK1, c ? qV0 : qV1);
+      convert8(c ? qK1 : qK0, c ? qV1 : qV0);
+      __syncthreads();
+      if constexpr (decltype(open)::value) compute_open(i, sK0, sV0, idc); else compute(i, sK0, sV0, idc);
+      wait_lds_loads();
+      __syncthreads();
+      idc = idn;
+      idn = idnn;
+    };
+    const int open_end = n_open - n_open % 2;
+    auto steps8 = [&](int i, int end, auto open) __attribute__((always_inline)) {   // steps [i, end) from an even index
+      for (; i < end; i += 2) {
+        one8(i, open, std::integral_constant<int, 0>{});
+        if (i + 1 < end) one8(i + 1, open, std::integral_constant<int, 1>{});
+      }
+    };
+    steps8(0, open_end, std::true_type{});
+    steps8(open_end, nsteps, std::false_type{});
+  }
 
   // normalise and write: lane l holds out[row wrow0 + 16 g + c16][dims 16 dt + 4 g4 + r]
 #pragma unroll
   for (int g = 0; g < RW; ++g) {
     const float ls = lsum[g][0];
     if (qreal[g]) {
-      const float inv = ls > 0.f ? 1.f / ls : 0.f;
+      float inv = ls > 0.f ? 1.f / ls : 0.f;
+      if constexpr (kQuant) inv = ls > 0.f ? out_scale / ls : 0.f;
       const size_t orow = ((size_t)(q0 + wrow0 + 16 * g + c16) * p.num_heads + h) * D;
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt) {
@@ -521,21 +630,36 @@ void prefill_mfma_kernel(PrefillParams p) {
 
 
 bool prefill_supported(int q_dtype, int kv_dtype, int head_dim, int block_size) {
-  return q_dtype == kv_dtype && (q_dtype == F16::kId || q_dtype == BF16::kId) && (head_dim == 64 || head_dim == 128) &&
+  return (q_dtype == F16::kId || q_dtype == BF16::kId) &&
+         (kv_dtype == q_dtype || kv_dtype == FP8::kId || kv_dtype == BF8::kId) && (head_dim == 64 || head_dim == 128) &&
          block_size == 16;
 }
 
 int prefill_tile_rows() { return Prefill<F16, 128, PKV_PREFILL_RW>::BM; }
 
-template <class T, int D>
+template <class T, class CT, int D>
 static hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((prefill_mfma_kernel<T, D, PKV_PREFILL_RW>), dim3(p.total_wgs), dim3(PKV_PREFILL_NW * 64), 0, stream, p);
+  hipLaunchKernelGGL((prefill_mfma_kernel<T, CT, D, PKV_PREFILL_RW>), dim3(p.total_wgs), dim3(PKV_PREFILL_NW * 64), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
-hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim, hipStream_t stream) {
-  if (dtype == F16::kId) return head_dim == 64 ? launch_prefill_t<F16, 64>(p, stream) : launch_prefill_t<F16, 128>(p, stream);
-  if (dtype == BF16::kId) return head_dim == 64 ? launch_prefill_t<BF16, 64>(p, stream) : launch_prefill_t<BF16, 128>(p, stream);
+template <class T, class CT>
+static hipError_t launch_prefill_d(const PrefillParams& p, int head_dim, hipStream_t stream) {
+  return head_dim == 64 ? launch_prefill_t<T, CT, 64>(p, stream) : launch_prefill_t<T, CT, 128>(p, stream);
+}
+
+template <class T>
+static hipError_t launch_prefill_kv(const PrefillParams& p, int kv_dtype, int head_dim, hipStream_t stream) {
+  if (kv_dtype == T::kId) return launch_prefill_d<T, T>(p, head_dim, stream);
+  if (kv_dtype == FP8::kId) return launch_prefill_d<T, FP8>(p, head_dim, stream);
+  if (kv_dtype == BF8::kId) return launch_prefill_d<T, BF8>(p, head_dim, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill(const PrefillParams& p, int dtype, int kv_dtype, int head_dim, hipStream_t stream) {
+  if (dtype == F16::kId) return launch_prefill_kv<F16>(p, kv_dtype, head_dim, stream);
+  if (dtype == BF16::kId) return launch_prefill_kv<BF16>(p, kv_dtype, head_dim, stream);
   return hipErrorInvalidValue;
 }
 

@@ -64,7 +64,8 @@ _lib.pkv_reshape_and_cache.argtypes = [_vp] * 5 + [_c_int] * 7 + [_c_float] * 2 
 _lib.pkv_copy_blocks.restype = _c_int
 _lib.pkv_copy_blocks.argtypes = [_vp, _vp, _vp] + [_c_int] * 6 + [_vp]
 _lib.pkv_paged_prefill_attention.restype = _c_int
-_lib.pkv_paged_prefill_attention.argtypes = [_vp] * 5 + [_c_int] + [_vp, _vp] + [_c_int] * 9 + [_c_float] + [_c_int] * 2 + [_vp]
+_lib.pkv_paged_prefill_attention.argtypes = ([_vp] * 5 + [_c_int] + [_vp, _vp] + [_c_int] * 9 + [_c_float] * 3
+                                              + [_vp, _vp] + [_c_int] * 2 + [_vp])
 _lib.pkv_swap_blocks.restype = _c_int
 _lib.pkv_swap_blocks.argtypes = [_vp, _vp, _c_int, _vp, _vp, _c_int, _vp] + [_c_int] * 5 + [_vp]
 _lib.pkv_set_debug_checks.restype = _c_int
@@ -262,12 +263,14 @@ def paged_attention_decode_noalloc(out, q, k_cache, v_cache, block_tables, conte
 
 
 def paged_prefill_attention(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale,
-                            max_query_len, max_context_len, num_blocks=None, stream=None):
+                            max_query_len, max_context_len, num_blocks=None, k_scale=1.0, v_scale=1.0,
+                            k_scales=None, v_scales=None, stream=None):
     """Chunked prefill: query row i of sequence s (rows query_start_loc[s]..) sits at
     position context_lens[s] - n_s + i and attends causally over the paged cache.
 
-    out, q: [num_tokens, H, d]; pools [NB, KVH, bs, d]; block_tables int32
-    [S, maxblk]; context_lens int32 [S]; query_start_loc int32 [S + 1].
+    out, q: [num_tokens, H, d]; pools [NB, KVH, bs, d] of q's type or an 8-bit
+    format (uint8 / float8_e4m3fn: E4M3, float8_e5m2: E5M2, values code * scale);
+    block_tables int32 [S, maxblk]; context_lens int32 [S]; query_start_loc int32 [S + 1].
     """
     T, H, d = q.shape
     NB, KVH, bs, d2 = k_cache.shape
@@ -283,12 +286,15 @@ def paged_prefill_attention(out, q, k_cache, v_cache, block_tables, context_lens
             raise ValueError("all tensors must be contiguous")
     if out.dtype != q.dtype:
         raise TypeError("out must have q's dtype")
+    if v_cache.dtype != k_cache.dtype:
+        raise TypeError("k_cache and v_cache differ in dtype")
     _on_device(k_cache.device, out, q, v_cache, block_tables, context_lens, query_start_loc)
     _check(_lib.pkv_paged_prefill_attention(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1],
         _ptr(context_lens), _ptr(query_start_loc), S, T, H, KVH, d, bs, NB if num_blocks is None else num_blocks,
-        int(max_query_len), int(max_context_len), float(scale), dtype_code(q.dtype), dtype_code(k_cache.dtype),
-        _stream(stream)), "pkv_paged_prefill_attention")
+        int(max_query_len), int(max_context_len), float(scale), float(k_scale), float(v_scale),
+        _ptr(_head_scales(k_scales, KVH, k_cache.device)), _ptr(_head_scales(v_scales, KVH, k_cache.device)),
+        dtype_code(q.dtype), dtype_code(k_cache.dtype), _stream(stream)), "pkv_paged_prefill_attention")
     return out
 
 

@@ -113,10 +113,17 @@ class PrefillWorkload:
     prior: tuple                 # length recipe of the context cached before the chunk
     max_blocks_per_seq: int
     pool_slack: float = 1.2
+    kv_dtype: str = ""           # "" -> the cache has ``dtype``; "fp8_e4m3": an 8-bit cache
+    kv_scale: float = 1.0        # 8-bit caches: the pool-wide k_scale and v_scale
+    code_max: int = 0x5F         # 8-bit caches: largest magnitude code drawn for the pools
 
     @property
     def softmax_scale(self):
         return 1.0 / math.sqrt(self.head_dim)
+
+    @property
+    def kv8(self):
+        return bool(self.kv_dtype) and DTYPES[self.kv_dtype] == torch.uint8
 
 
 # The five named workloads.
@@ -175,6 +182,15 @@ PREFILL_GQA_BF16 = PrefillWorkload(
     seed=25907, num_seqs=16, num_heads=64, num_kv_heads=8, head_dim=128, block_size=16, dtype="bf16",
     chunk=("fixed", (512,) * 16), prior=("uniform", 0, 7680), max_blocks_per_seq=512)
 
+# The GQA prefill over an E4M3 cache: the prior context's codes drawn like the
+# GQA E4M3 decode pool's, the chunk's K/V (bf16) encoded by reshape_and_cache.
+PREFILL_GQA_FP8 = PrefillWorkload(
+    name="chunked prefill, GQA layer over an E4M3 cache: 16 seqs x 512-token chunks over 0-7680 cached tokens, "
+         "64 q / 8 kv heads, d128, bf16 q, fp8 E4M3 K/V (scale 0.05), bs16",
+    seed=25910, num_seqs=16, num_heads=64, num_kv_heads=8, head_dim=128, block_size=16, dtype="bf16",
+    chunk=("fixed", (512,) * 16), prior=("uniform", 0, 7680), max_blocks_per_seq=512, kv_dtype="fp8_e4m3",
+    kv_scale=0.05)
+
 @dataclass(frozen=True)
 class PrefixCacheWorkload:
     """Requests that share a system prompt, prefilled with and without the prefix cache."""
@@ -210,6 +226,7 @@ WORKLOADS = {
     "shared_prefix_fp8": SHARED_PREFIX_FP8,
     "prefill_llama13b_f16": PREFILL_LLAMA13B_F16,
     "prefill_gqa_bf16": PREFILL_GQA_BF16,
+    "prefill_gqa_fp8": PREFILL_GQA_FP8,
     "prefix_cache_llama13b_f16": PREFIX_CACHE_LLAMA13B_F16,
 }
 
@@ -363,8 +380,12 @@ def make_prefill_inputs(w: PrefillWorkload, device="cpu", chunk=None, prior=None
     dt = DTYPES[w.dtype]
     H, KVH, d, bs = w.num_heads, w.num_kv_heads, w.head_dim, w.block_size
     q = randn(gen, (T, H, d), dt, device)
-    k_cache = randn(gen, (nb, KVH, bs, d), dt, device)
-    v_cache = randn(gen, (nb, KVH, bs, d), dt, device)
+    if w.kv8:
+        k_cache = codes8(gen, (nb, KVH, bs, d), w.code_max, device)
+        v_cache = codes8(gen, (nb, KVH, bs, d), w.code_max, device)
+    else:
+        k_cache = randn(gen, (nb, KVH, bs, d), dt, device)
+        v_cache = randn(gen, (nb, KVH, bs, d), dt, device)
     k_new = randn(gen, (T, KVH, d), dt, device)
     v_new = randn(gen, (T, KVH, d), dt, device)
     return PrefillInputs(w, n, ctx, qsl, free_list, nb, q, k_cache, v_cache, k_new, v_new)

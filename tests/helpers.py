@@ -148,3 +148,36 @@ def sample_pairs(rng, S, H, n, always=()):
     for s in always:
         picks.add((int(s), int(rng.integers(0, H))))
     return sorted(picks)
+
+
+def prefill_weight_spread(q, kc, vc, tables, ctx_lens, qsl, scale, bs, ref):
+    """sum_j w_j |v_j - o| per prefill output element, in fp64: w the softmax weights of
+    the row's visible keys, v_j their values, o the oracle's output.  The prefill's
+    weights are rounded to the input type (unit roundoff u) before the PV product,
+    which moves an output element by at most u / (1 - u) times this."""
+    H = q.shape[1]
+    G = H // kc.shape[1]
+    spread = np.zeros_like(ref)
+    for s in range(len(ctx_lens)):
+        q0, q1, ctx = int(qsl[s]), int(qsl[s + 1]), int(ctx_lens[s])
+        n = q1 - q0
+        if n == 0 or ctx == 0:
+            continue
+        blocks = tables[s, :-(-ctx // bs)]
+        pos = ctx - n + np.arange(n)                       # each row's position; < 0: no keys
+        for kvh in range(kc.shape[1]):
+            keys = oracle.gather_tokens(kc, blocks, ctx, bs, kvh)
+            vals = oracle.gather_tokens(vc, blocks, ctx, bs, kvh)
+            for h in range(kvh * G, (kvh + 1) * G):
+                for r0 in range(0, n, 32):
+                    rows = np.arange(r0, min(n, r0 + 32))
+                    lg = scale * (q[q0 + rows, h] @ keys.T)           # [rows, ctx]
+                    lg[np.arange(ctx)[None, :] > pos[rows][:, None]] = -np.inf
+                    live = pos[rows] >= 0
+                    lg[~live] = 0.0
+                    w = np.exp(lg - lg.max(axis=1, keepdims=True))
+                    w /= w.sum(axis=1, keepdims=True)
+                    w[~live] = 0.0
+                    o = ref[q0 + rows, h]                             # [rows, d]
+                    spread[q0 + rows, h] = np.einsum("rj,rjd->rd", w, np.abs(vals[None, :, :] - o[:, None, :]))
+    return spread

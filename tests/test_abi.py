@@ -179,14 +179,20 @@ def test_prefill_host_checks(lib):
     sc = ctypes.c_float(0.1)
 
     def call(S=2, T=100, H=4, KVH=4, d=128, bs=16, NB=8, mq=64, mc=128, qd=1, kvd=1, out=FAKE, tables=FAKE,
-             maxblk=8):
-        return f(out, FAKE, FAKE, FAKE, tables, maxblk, FAKE, FAKE, S, T, H, KVH, d, bs, NB, mq, mc, sc, qd, kvd, None)
+             maxblk=8, ks=1.0, vs=1.0, kss=None, vss=None):
+        return f(out, FAKE, FAKE, FAKE, tables, maxblk, FAKE, FAKE, S, T, H, KVH, d, bs, NB, mq, mc, sc,
+                 ctypes.c_float(ks), ctypes.c_float(vs), kss, vss, qd, kvd, None)
 
     assert call(S=0) == 0 and call(mq=0) == 0 and call(T=0) == 0   # nothing to do
     assert call(T=-1) == -2
     assert call(H=6, KVH=4) == -3
-    assert call(d=256) == -4 and call(bs=8) == -4 and call(qd=0, kvd=0) == -4 and call(kvd=3) == -4
-    assert call(qd=1, kvd=2) == -4
+    assert call(d=256) == -4 and call(bs=8) == -4 and call(qd=0, kvd=0) == -4
+    assert call(qd=1, kvd=2) == -4 and call(qd=3, kvd=3) == -4 and call(qd=1, kvd=5) == -4
+    # 8-bit caches: scales checked as for decode; per-head arrays replace the pool's
+    assert call(kvd=3, ks=0.0) == -8 and call(qd=2, kvd=4, vs=float("inf")) == -8
+    assert call(kvd=3, ks=0.0, vs=0.0, kss=FAKE, vss=FAKE, out=None) == -1
+    assert call(kvd=3, out=None) == -1 and call(qd=2, kvd=4, out=None) == -1
+    assert call(ks=0.0, out=None) == -1                           # 16-bit cache: scales ignored
     assert call(NB=0) == -2 and call(mq=-1) == -2 and call(maxblk=0) == -2
     assert call(out=None) == -1 and call(tables=None) == -1
     assert call(out=ctypes.c_void_p(0x10008)) == -4             # misaligned output

@@ -23,7 +23,7 @@ import pytest
 import torch
 
 import oracle
-from tests.helpers import TOL, as_f64, check_close
+from tests.helpers import TOL, as_f64, check_close, prefill_weight_spread
 from tests.test_gpu_prefill import DEV, PrefillCase, _w
 
 pytestmark = pytest.mark.gpu
@@ -50,37 +50,9 @@ def draw(rng):
 
 
 def _weight_spread(case, scale, ref):
-    """sum_j w_j |v_j - o| per output element: w the fp64 softmax weights of the row's
-    visible keys, v_j their values, o the oracle's output."""
-    q = as_f64(case.inp.q)
-    kc, vc = as_f64(case.k_cache), as_f64(case.v_cache)
-    H = q.shape[1]
-    G = H // kc.shape[1]
-    bs = case.w.block_size
-    spread = np.zeros_like(ref)
-    for s in range(len(case.ctx)):
-        q0, q1, ctx = int(case.qsl[s]), int(case.qsl[s + 1]), int(case.ctx[s])
-        n = q1 - q0
-        if n == 0 or ctx == 0:
-            continue
-        blocks = case.tables[s, :-(-ctx // bs)]
-        pos = ctx - n + np.arange(n)                       # each row's position; < 0: no keys
-        for kvh in range(kc.shape[1]):
-            keys = oracle.gather_tokens(kc, blocks, ctx, bs, kvh)
-            vals = oracle.gather_tokens(vc, blocks, ctx, bs, kvh)
-            for h in range(kvh * G, (kvh + 1) * G):
-                for r0 in range(0, n, 32):
-                    rows = np.arange(r0, min(n, r0 + 32))
-                    lg = scale * (q[q0 + rows, h] @ keys.T)           # [rows, ctx]
-                    lg[np.arange(ctx)[None, :] > pos[rows][:, None]] = -np.inf
-                    live = pos[rows] >= 0
-                    lg[~live] = 0.0
-                    w = np.exp(lg - lg.max(axis=1, keepdims=True))
-                    w /= w.sum(axis=1, keepdims=True)
-                    w[~live] = 0.0
-                    o = ref[q0 + rows, h]                             # [rows, d]
-                    spread[q0 + rows, h] = np.einsum("rj,rjd->rd", w, np.abs(vals[None, :, :] - o[:, None, :]))
-    return spread
+    """sum_j w_j |v_j - o| per output element (see prefill_weight_spread)."""
+    return prefill_weight_spread(as_f64(case.inp.q), as_f64(case.k_cache), as_f64(case.v_cache), case.tables,
+                                 case.ctx, case.qsl, scale, case.w.block_size, ref)
 
 
 @pytest.mark.timeout(600)
