@@ -123,6 +123,9 @@ extern "C" {
 #define PKV_CHECK_QUERY_START 13   /* prefill: query_start_loc[0] != 0, decreasing, outside
                                       [0, num_tokens], [num_seqs] != num_tokens, or a chunk longer
                                       than max_query_len; index: the entry                         */
+#define PKV_CHECK_SCALE 14         /* 8-bit cache: a per-kv-head scale (k_scales / v_scales) that is
+                                      not a positive finite number; index h for k_scales[h],
+                                      num_kv_heads + h for v_scales[h]                             */
 
 /*
  * pkv_set_debug_checks -- turn the debug checks on (mode 1), off (0), or leave

@@ -230,6 +230,7 @@ int pkv_reshape_and_cache(const void* key, const void* value, void* k_cache, voi
   if (debug_checks_on()) {
     DeviceChecks c(s);
     c.slots(slot_mapping, num_tokens, (long long)num_blocks * block_size);
+    if (fp8) c.scales(k_scales, v_scales, num_kv_heads);
     const int cst = c.finish();
     if (cst != PKV_OK) return cst;
   }

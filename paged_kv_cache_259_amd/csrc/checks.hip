@@ -1,6 +1,7 @@
 // checks.hip -- debug checks of the device-resident values each call takes on
 // trust: block tables and context lengths, slots, block-copy pairs, the host
-// order, the shared decode's groups and the prefill's query offsets.
+// order, the shared decode's groups, the prefill's query offsets and the
+// per-kv-head scales of an 8-bit cache.
 //
 // The pages fix what these values mean: a sequence's table names its blocks in
 // order and the token at position pos sits in block table[pos / bs] at offset
@@ -207,6 +208,17 @@ __global__ __launch_bounds__(256) void check_query_starts_kernel(const int32_t* 
   if (bad) flag(r, PKV_CHECK_QUERY_START, s);
 }
 
+// Per-kv-head scales of an 8-bit cache: positive and finite.  Entry i of
+// k_scales is flagged as index i, of v_scales as n + i.
+__global__ __launch_bounds__(256) void check_scales_kernel(const float* ks, const float* vs, int n, u64* r) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= 2 * n) return;
+  const float* a = i < n ? ks : vs;
+  if (!a) return;
+  const float x = a[i < n ? i : i - n];
+  if (!(x > 0.f && x <= 3.402823466e38f)) flag(r, PKV_CHECK_SCALE, i);
+}
+
 unsigned grid_of(long long n) { return (unsigned)((n + 255) / 256); }
 
 // 1 on, 0 off, -1: the PKV_DEBUG environment variable decides
@@ -340,6 +352,13 @@ void DeviceChecks::groups(const int32_t* offsets, const int32_t* members, const 
   hipLaunchKernelGGL(check_member_kernel<int32_t>, dim3(grid_of(num_seqs)), dim3(256), 0, impl_->stream, a,
                      (long long)num_seqs, a, (long long)num_seqs, offsets + num_groups, (long long)num_seqs, true,
                      (int)PKV_CHECK_GROUP_MEMBER, impl_->r);
+  note(hipGetLastError());
+}
+
+void DeviceChecks::scales(const float* k_scales, const float* v_scales, int num_kv_heads) {
+  if (impl_->failed || num_kv_heads <= 0 || (!k_scales && !v_scales)) return;
+  hipLaunchKernelGGL(check_scales_kernel, dim3(grid_of(2LL * num_kv_heads)), dim3(256), 0, impl_->stream, k_scales,
+                     v_scales, num_kv_heads, impl_->r);
   note(hipGetLastError());
 }
 

@@ -189,8 +189,9 @@ const char* pkv_status_string(int status) {
       return "the call needs more split-context scratch than the library's static scratch holds "
              "(PKV_STATIC_SCRATCH_BYTES); call pkv_paged_attention_decode with a workspace instead";
     case PKV_ERR_PRECONDITION:
-      return "debug checks: a device-resident value (block table, context length, slot, pair, order, group or "
-             "query offset) breaks the call's preconditions; nothing was launched (see pkv_debug_report)";
+      return "debug checks: a device-resident value (block table, context length, slot, pair, order, group, "
+             "query offset or per-head scale) breaks the call's preconditions; nothing was launched "
+             "(see pkv_debug_report)";
   }
   return "unknown status";
 }
@@ -314,6 +315,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
     pkv::DeviceChecks c(s);
     c.tables(block_tables, max_blocks_per_seq, context_lens, num_seqs, block_size, num_blocks, max_context_len);
     c.permutation(seq_order, num_seqs);
+    if (fp8) c.scales(k_scales, v_scales, num_kv_heads);
     if (new_k)
       c.append_slots(slot_mapping, block_tables, max_blocks_per_seq, context_lens, num_seqs, block_size,
                      (long long)num_blocks * block_size);
@@ -449,6 +451,7 @@ int pkv_paged_attention_decode_shared(void* out, const void* q, void* k_cache, v
     c.tables(block_tables, max_blocks_per_seq, context_lens, num_seqs, block_size, num_blocks, max_context_len);
     c.groups(group_offsets, group_members, group_shared_blocks, num_groups, max_group_size, block_tables,
              max_blocks_per_seq, context_lens, num_seqs, block_size, p.ctx_cap);
+    if (fp8) c.scales(k_scales, v_scales, num_kv_heads);
     if (key)
       c.append_slots(slot_mapping, block_tables, max_blocks_per_seq, context_lens, num_seqs, block_size,
                      (long long)num_blocks * block_size);
@@ -520,6 +523,7 @@ int pkv_paged_prefill_attention(void* out, const void* q, const void* k_cache, c
     pkv::DeviceChecks c(s);
     c.tables(block_tables, max_blocks_per_seq, context_lens, num_seqs, block_size, num_blocks, max_context_len);
     c.query_starts(query_start_loc, num_seqs, num_tokens, max_query_len);
+    if (fp8) c.scales(k_scales, v_scales, num_kv_heads);
     const int cst = c.finish();
     if (cst != PKV_OK) return cst;
   }

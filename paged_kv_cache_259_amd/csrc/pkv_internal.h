@@ -77,6 +77,7 @@ class DeviceChecks {
               int max_group_size, const int32_t* tables, int max_blocks_per_seq, const int32_t* context_lens,
               int num_seqs, int block_size, int ctx_cap);
   void query_starts(const int32_t* query_start_loc, int num_seqs, int num_tokens, int max_query_len);
+  void scales(const float* k_scales, const float* v_scales, int num_kv_heads);
   int finish();
 
  private:

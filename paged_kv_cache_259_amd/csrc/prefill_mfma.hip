@@ -35,6 +35,11 @@
 //            element j%4 of the 4 values at lane 4m + j/4's address, for
 //            m = 0..3; lane (c16, g4) points at token 4 g4 + c16/4, dims
 //            d0 + 4 (c16%4) .. +3, so it receives V[4 g4 + m][d0 + c16].
+// An 8-bit cache ("PagedAttention", Ultralytics glossary, section "Các kỹ thuật
+// liên quan": FP8 keys and values) is staged the same way as bytes, into two
+// stage buffers per tensor, and a convert pass turns each step's codes into the
+// 16-bit tiles above (exact for E4M3 and E5M2); its scales go to the logits
+// (K) and to the output (V).
 #include <type_traits>
 
 #include "pkv_device.h"

@@ -86,7 +86,7 @@ ERR_PRECONDITION = -11              # PKV_ERR_PRECONDITION
 CHECK_KINDS = {
     1: "context_len", 2: "block_id", 3: "slot", 4: "duplicate_slot", 5: "append_slot", 6: "pair_id",
     7: "duplicate_dst", 8: "dst_is_src", 9: "seq_order", 10: "group", 11: "group_member", 12: "shared_block",
-    13: "query_start",
+    13: "query_start", 14: "scale",
 }
 
 STATIC_SCRATCH_BYTES = 48 << 20     # PKV_STATIC_SCRATCH_BYTES

@@ -1,7 +1,7 @@
 """Debug checks of the device-resident values (pkv_set_debug_checks, PKV_DEBUG).
 
 With the checks on, every entry point scans the block tables, context lengths,
-slots, copy pairs, host order, groups or query offsets it was given on the GPU
+slots, copy pairs, host order, groups, query offsets or per-head scales it was given on the GPU
 before it launches anything, and returns PKV_ERR_PRECONDITION, launching
 nothing else, when a value breaks a rule of include/pkv.h.  Each case plants
 violations into valid inputs and compares the report (count, kind and index of
@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 (CONTEXT_LEN, BLOCK_ID, SLOT, DUPLICATE_SLOT, APPEND_SLOT, PAIR_ID, DUPLICATE_DST, DST_IS_SRC, SEQ_ORDER, GROUP,
- GROUP_MEMBER, SHARED_BLOCK, QUERY_START) = range(1, 14)
+ GROUP_MEMBER, SHARED_BLOCK, QUERY_START, SCALE) = range(1, 15)
 
 
 @pytest.fixture(scope="module")
@@ -532,3 +532,40 @@ def test_environment_switch(ops):
         else:
             os.environ["PKV_DEBUG"] = old
         ops.set_debug_checks(prev)
+
+
+@pytest.mark.parametrize("bad", [0.0, -0.5, float("inf"), float("nan")])
+def test_per_head_scales_planted(ops, checks, bad):
+    """8-bit caches: every per-kv-head scale must be a positive finite number (k_scales[h] is index h,
+    v_scales[h] index num_kv_heads + h), in decode, prefill and reshape_and_cache alike."""
+    rng = np.random.default_rng(700)
+    NB, KVH, bs, d, H = 24, 4, 16, 128, 8
+    codes = lambda: torch.from_numpy(rng.integers(0, 0x60, (NB, KVH, bs, d)).astype(np.uint8)).to(DEV)
+    kc, vc = codes(), codes()
+    ks = torch.full((KVH,), 0.05, device=DEV)
+    vs = torch.full((KVH,), 0.1, device=DEV)
+    vs[2] = bad
+    S = 3
+    tables = torch.from_numpy(rng.permutation(NB)[:S * 4].reshape(S, 4).astype(np.int32)).to(DEV)
+    ctx = torch.tensor([40, 64, 7], dtype=torch.int32, device=DEV)
+    q = randn(rng, (S, H, d), torch.bfloat16)
+    out = torch.full_like(q, 9.0)
+    want = (1, SCALE, KVH + 2)
+    with pytest.raises(ops.PkvError) as e:
+        ops.paged_attention_decode(out, q, kc, vc, tables, ctx, 0.09, 64, k_scales=ks, v_scales=vs)
+    assert e.value.report == want and bool((out == 9.0).all())
+    qsl = torch.tensor([0, 5, 9, 12], dtype=torch.int32, device=DEV)
+    qp = randn(rng, (12, H, d), torch.bfloat16)
+    outp = torch.full_like(qp, 9.0)
+    with pytest.raises(ops.PkvError) as e:
+        ops.paged_prefill_attention(outp, qp, kc, vc, tables, ctx, qsl, 0.09, 5, 64, k_scales=ks, v_scales=vs)
+    assert e.value.report == want and bool((outp == 9.0).all())
+    k0 = kc.clone()
+    kv = randn(rng, (2, KVH, d), torch.bfloat16)
+    ks[0] = bad
+    with pytest.raises(ops.PkvError) as e:
+        ops.reshape_and_cache(kv, kv, kc, vc, torch.tensor([3, 70], dtype=torch.int64, device=DEV),
+                              k_scales=ks, v_scales=vs)
+    assert e.value.report == (2, SCALE, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(kc, k0)
