@@ -95,7 +95,8 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* lds) {
 
 // T: the q type and MFMA operand type (f16 / bf16); KT: the cache type, T itself
 // or one of the 8-bit formats.
-template <class T, class KT, int D, int NW, bool PIPE>
+// NT: the K/V tiles are loaded with the non-temporal policy (see load_kv).
+template <class T, class KT, int D, int NW, bool PIPE, bool NT = PKV_KV_NT != 0>
 struct MfmaAttention {
   static constexpr int BS = 16;
   static constexpr int NC = D / 32;                 // QK steps of 32 dims
@@ -160,7 +161,7 @@ struct MfmaAttention {
     const int krow = c16 < valid ? c16 : valid - 1;     // valid >= 1: every block has a real token
     const char* kp = kbase + boff + (ptrdiff_t)(krow - c16) * (ptrdiff_t)ROW_BYTES;
 #pragma unroll
-    for (int c = 0; c < NK; ++c) t.k[c] = *reinterpret_cast<const uint4*>(kp + c * (KV8 ? 16 : 64));
+    for (int c = 0; c < NK; ++c) t.k[c] = load_kv<uint4, NT>(kp + c * (KV8 ? 16 : 64));
     const char* vp = vbase + boff;
 #pragma unroll
     for (int tg = 0; tg < 4; ++tg) {
@@ -168,7 +169,7 @@ struct MfmaAttention {
       const ptrdiff_t vrow = (ptrdiff_t)((row < valid ? row : valid - 1) - g4 * 4) * (ptrdiff_t)ROW_BYTES;
 #pragma unroll
       for (int hh = 0; hh < NH; ++hh)
-        t.v[tg][hh] = *reinterpret_cast<const VLoad*>(vp + vrow + hh * 128 * KT::bytes);
+        t.v[tg][hh] = load_kv<VLoad, NT>(vp + vrow + hh * 128 * KT::bytes);
     }
   }
 

@@ -136,8 +136,8 @@ struct VectorAttention {
     for (int i = 0; i < NI; ++i) {
       const int r = i * RPW + row;                            // valid >= 1: every block has a real token
       const ptrdiff_t off = (ptrdiff_t)((r < valid ? r : valid - 1) - row) * (ptrdiff_t)ROW_BYTES;
-      t.k[i] = *reinterpret_cast<const uint4*>(kp + off);
-      t.v[i] = *reinterpret_cast<const uint4*>(vp + off);
+      t.k[i] = load_kv<uint4, PKV_KV_NT != 0>(kp + off);
+      t.v[i] = load_kv<uint4, PKV_KV_NT != 0>(vp + off);
     }
   }
 

@@ -38,6 +38,32 @@ __device__ __forceinline__ void bf16x2_to_f32(uint32_t u, float& lo, float& hi) 
   hi = u32_as_f32(u & 0xffff0000u);
 }
 
+// K/V tile loads of the decode kernels.  A decode step reads each cached byte
+// once, so with NT they carry the non-temporal cache policy (the lines stream
+// through the caches instead of displacing others): on this GPU the read-only
+// probes read scattered tiles 9-11 % and a stream 7 % faster with it, and the
+// one-pass decodes ran 5-7 % faster.
+#ifndef PKV_KV_NT
+#define PKV_KV_NT 1
+#endif
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+template <class V, bool NT> __device__ __forceinline__ V load_kv(const void* p);
+template <> __device__ __forceinline__ uint4 load_kv<uint4, true>(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+template <> __device__ __forceinline__ uint2 load_kv<uint2, true>(const void* p) {
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(v.x, v.y);
+}
+template <> __device__ __forceinline__ uint4 load_kv<uint4, false>(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+template <> __device__ __forceinline__ uint2 load_kv<uint2, false>(const void* p) {
+  return *reinterpret_cast<const uint2*>(p);
+}
+
 // 16 bytes of storage -> 16/bytes fp32 values.
 template <class T> struct Unpack;
 template <> struct Unpack<F32> {
