@@ -193,7 +193,7 @@ def hbm_probe(stream, reps=10, flush=None):
             "stream_read_gbps_by_grid": {str(k): round(v, 1) for k, v in stream_rates.items()},
             "tile_read_gbps": {f"{k // 1024}KiB": round(v, 1) for k, v in tiles.items()},
             "flushed": flush is not None,
-            "probe": "libpkv_probe.so: 16-byte loads, 1 GiB buffer, mean of per-launch HIP-event times"
+            "probe": "libpkv_probe.so: 16-byte non-temporal loads, 1 GiB buffer, mean of per-launch HIP-event times"
                      + (", caches flushed before each launch" if flush is not None else "")
                      + "; tiles in a scattered order that reads no tile twice per launch, two per wave in "
                      "flight, 2048 workgroups of 4 waves"}

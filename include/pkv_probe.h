@@ -33,7 +33,8 @@ extern "C" {
  * `num_workgroups` workgroups of 4 waves reads whole 8 KiB chunks (eight 1 KiB
  * loads of consecutive bytes in flight), wave w taking chunks w, w + W, ...
  * (W waves), so the grid sweeps the buffer front to back.  `bytes` a positive
- * multiple of 16, `buf` 16-byte aligned.
+ * multiple of 16, `buf` 16-byte aligned.  Both probes load with the
+ * non-temporal cache policy, as the decode kernels' K/V loads do.
  */
 int pkv_probe_stream_read(const void* buf, size_t bytes, int num_workgroups, unsigned salt, unsigned* sink,
                           void* stream);

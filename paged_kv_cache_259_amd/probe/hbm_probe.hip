@@ -13,6 +13,15 @@ constexpr int kInFlight = 8;   // 16-byte loads per thread per round of the stre
 
 __device__ __forceinline__ uint32_t fold(const uint4& v) { return v.x ^ v.y ^ v.z ^ v.w; }
 
+// Every load carries the non-temporal cache policy, as the decode kernels' K/V
+// loads do: read once, the lines stream through the caches.  On this GPU plain
+// loads read 9-11 % slower (scattered tiles) and 7 % slower (the stream).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Each wave reads whole 8 KiB chunks (eight 1 KiB loads of consecutive bytes,
 // all in flight together); wave w takes chunks w, w + W, w + 2W, ... of the
 // buffer (W waves in the grid), so at any time the grid reads one contiguous
@@ -30,11 +39,11 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const uint4* __re
     const uint4* p = buf + c * kChunk16 + lane;
     uint4 v[kInFlight];
 #pragma unroll
-    for (int k = 0; k < kInFlight; ++k) v[k] = p[k * 64];
+    for (int k = 0; k < kInFlight; ++k) v[k] = load_nt(p + k * 64);
 #pragma unroll
     for (int k = 0; k < kInFlight; ++k) acc ^= fold(v[k]);
   }
-  for (uint64_t i = chunks * kChunk16 + wave * 64 + lane; i < n16; i += waves * 64) acc ^= fold(buf[i]);
+  for (uint64_t i = chunks * kChunk16 + wave * 64 + lane; i < n16; i += waves * 64) acc ^= fold(load_nt(buf + i));
   if (acc == salt) sink[0] = acc;
 }
 
@@ -61,7 +70,7 @@ __global__ __launch_bounds__(kThreads) void tile_read_kernel(const uint4* __rest
   auto issue = [&](int i, uint4* t) {
     const uint4* p = buf + tile_index(wave, i, per_wave, salt, num_tiles) * (TILE / 16) + lane;
 #pragma unroll
-    for (int k = 0; k < LOADS; ++k) t[k] = p[k * 64];
+    for (int k = 0; k < LOADS; ++k) t[k] = load_nt(p + k * 64);
   };
   auto use = [&](const uint4* t) {
 #pragma unroll
