@@ -122,9 +122,11 @@ class Flusher:
     """Clears L2 and the 256 MB Infinity Cache between timed steps, outside the timed events.
 
     Writes 512 MiB (torch fill) and then reads another 512 MiB (the probe's
-    streaming read): the write evicts whatever the caches held, and the read
-    leaves them holding clean lines of an unrelated buffer, so no write-back of
-    the flush's own dirty lines lands inside the next timed step.
+    streaming read, plain loads): the write evicts whatever the caches held, and
+    the read leaves them holding clean lines of an unrelated buffer, so no
+    write-back of the flush's own dirty lines lands inside the next timed step.
+    (A non-temporal read would not displace those dirty lines: their write-back
+    then lands in the timed step, which cost the decodes 2-8 %.)
     """
 
     def __init__(self, stream):
@@ -138,7 +140,7 @@ class Flusher:
     def __call__(self):
         self.n += 1
         self.buf[: self.half].fill_(self.n % 251)
-        self.probe.stream_read(self.buf[self.half:], self.half, 2048, self.sink, stream=self.stream)
+        self.probe.stream_read(self.buf[self.half:], self.half, 2048, self.sink, nontemporal=False, stream=self.stream)
 
 
 def timed_steps(fn, K, stream, flush=None):
@@ -176,24 +178,29 @@ def hbm_probe(stream, reps=10, flush=None):
     stream_rates = {}
     for wgs in (1024, 2048, 4096):
         stream_rates[wgs] = rate(lambda: probe.stream_read(buf, buf.numel(), wgs, sink, stream=stream), buf.numel())
-    tiles = {}
+    tiles, tiles_plain = {}, {}
     wgs = 2048
     salt = [0]
 
-    def tile_launch(tb, per_wave):
+    def tile_launch(tb, per_wave, nt=True):
         salt[0] += 1                                    # another scattered order on every launch
-        probe.tile_read(buf, tb, wgs, per_wave, sink, salt=salt[0] * 7919, stream=stream)
+        probe.tile_read(buf, tb, wgs, per_wave, sink, salt=salt[0] * 7919, nontemporal=nt, stream=stream)
 
     for tb in (2048, 4096, 8192):
         per_wave = (768 << 20) // (wgs * 4 * tb)
         tiles[tb] = rate(lambda: tile_launch(tb, per_wave), wgs * 4 * per_wave * tb)
-    del buf
+        tiles_plain[tb] = rate(lambda: tile_launch(tb, per_wave, False), wgs * 4 * per_wave * tb)
     best = max(stream_rates, key=stream_rates.get)
+    plain = rate(lambda: probe.stream_read(buf, buf.numel(), best, sink, nontemporal=False, stream=stream), buf.numel())
+    del buf
     return {"stream_read_gbps": round(stream_rates[best], 1), "stream_read_workgroups": best,
             "stream_read_gbps_by_grid": {str(k): round(v, 1) for k, v in stream_rates.items()},
             "tile_read_gbps": {f"{k // 1024}KiB": round(v, 1) for k, v in tiles.items()},
+            "plain_loads": {"stream_read_gbps": round(plain, 1),
+                            "tile_read_gbps": {f"{k // 1024}KiB": round(v, 1) for k, v in tiles_plain.items()}},
             "flushed": flush is not None,
-            "probe": "libpkv_probe.so: 16-byte non-temporal loads, 1 GiB buffer, mean of per-launch HIP-event times"
+            "probe": "libpkv_probe.so: 16-byte non-temporal loads (plain loads under plain_loads), 1 GiB buffer, "
+                     "mean of per-launch HIP-event times"
                      + (", caches flushed before each launch" if flush is not None else "")
                      + "; tiles in a scattered order that reads no tile twice per launch, two per wave in "
                      "flight, 2048 workgroups of 4 waves"}

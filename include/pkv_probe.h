@@ -33,11 +33,12 @@ extern "C" {
  * `num_workgroups` workgroups of 4 waves reads whole 8 KiB chunks (eight 1 KiB
  * loads of consecutive bytes in flight), wave w taking chunks w, w + W, ...
  * (W waves), so the grid sweeps the buffer front to back.  `bytes` a positive
- * multiple of 16, `buf` 16-byte aligned.  Both probes load with the
- * non-temporal cache policy, as the decode kernels' K/V loads do.
+ * multiple of 16, `buf` 16-byte aligned.  `nontemporal` != 0: the loads carry
+ * the non-temporal cache policy, as the decode kernels' K/V loads do; 0: plain
+ * loads, which displace what the caches hold (a cache flush needs them).
  */
 int pkv_probe_stream_read(const void* buf, size_t bytes, int num_workgroups, unsigned salt, unsigned* sink,
-                          void* stream);
+                          int nontemporal, void* stream);
 
 /*
  * pkv_probe_tile_read -- each wave of `num_workgroups` workgroups of 4 waves
@@ -47,10 +48,11 @@ int pkv_probe_stream_read(const void* buf, size_t bytes, int num_workgroups, uns
  * (n * P + salt) mod T for a fixed prime P that divides no such T: a
  * scattered order that is a bijection, so a launch of at most T reads reads
  * every tile at most once (none is served by the caches from an earlier read
- * of the same launch; beyond T reads the order repeats).
+ * of the same launch; beyond T reads the order repeats).  `nontemporal` as for
+ * pkv_probe_stream_read.
  */
 int pkv_probe_tile_read(const void* buf, size_t bytes, int tile_bytes, int num_workgroups, int tiles_per_wave,
-                        unsigned salt, unsigned* sink, void* stream);
+                        unsigned salt, unsigned* sink, int nontemporal, void* stream);
 
 #ifdef __cplusplus
 }

@@ -95,7 +95,7 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* lds) {
 
 // T: the q type and MFMA operand type (f16 / bf16); KT: the cache type, T itself
 // or one of the 8-bit formats.
-// NT: the K/V tiles are loaded with the non-temporal policy (see load_kv).
+// NT: the K/V tiles are loaded with the non-temporal policy (see load_tile).
 template <class T, class KT, int D, int NW, bool PIPE, bool NT = PKV_KV_NT != 0>
 struct MfmaAttention {
   static constexpr int BS = 16;
@@ -149,27 +149,32 @@ struct MfmaAttention {
 
   // Every lane loads unconditionally, so the compiler can count the loads in
   // flight and wait only for the tile being consumed (a load under a per-lane
-  // condition makes it wait for every load, the next tile's too).  A row at or
-  // past `valid` (the last block's tail) reads the block's last real row
-  // instead -- the same cache lines, no extra memory traffic -- and consume
-  // masks it; a table entry outside the pool reads block 0 and the block is
-  // skipped.
-  __device__ static void issue(const AttnParams& p, const char* kbase, const char* vbase, size_t block_stride,
-                               int blk, int valid, int c16, int g4, Tiles& t) {
+  // condition makes it wait for every load, the next tile's too).  kpool /
+  // vpool point at kv head kvh's tile of block 0 (wave-uniform); klane / vlane
+  // are the lane's byte offsets inside a tile.  A row at or past `valid` (the
+  // last block's tail) reads the block's last real row instead -- the same
+  // cache lines, no extra memory traffic -- and consume masks it.  A table
+  // entry outside the pool, or a block loaded only to keep the loads
+  // unconditional (!live), reads no memory (see load_tile); consume skips the
+  // former and never sees the latter.
+  __device__ static void issue(const AttnParams& p, const char* kpool, const char* vpool, size_t block_stride,
+                               uint32_t klane, uint32_t vlane, int blk, int valid, bool live, int c16, int g4,
+                               Tiles& t) {
     t.ok = blk >= 0 && blk < p.num_blocks;
     const size_t boff = (size_t)(t.ok ? blk : 0) * block_stride;
+    const int bytes = t.ok && live ? TILE_BYTES : 0;
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kpool + boff, bytes), vr = buffer_rsrc(vpool + boff, bytes);
     const int krow = c16 < valid ? c16 : valid - 1;     // valid >= 1: every block has a real token
-    const char* kp = kbase + boff + (ptrdiff_t)(krow - c16) * (ptrdiff_t)ROW_BYTES;
+    const uint32_t kof = klane + (uint32_t)((krow - c16) * ROW_BYTES);
 #pragma unroll
-    for (int c = 0; c < NK; ++c) t.k[c] = load_kv<uint4, NT>(kp + c * (KV8 ? 16 : 64));
-    const char* vp = vbase + boff;
+    for (int c = 0; c < NK; ++c) t.k[c] = load_tile<uint4, NT>(kr, kof + c * (KV8 ? 16 : 64));
 #pragma unroll
     for (int tg = 0; tg < 4; ++tg) {
       const int row = g4 * 4 + tg;
-      const ptrdiff_t vrow = (ptrdiff_t)((row < valid ? row : valid - 1) - g4 * 4) * (ptrdiff_t)ROW_BYTES;
+      const uint32_t vof = vlane + (uint32_t)(((row < valid ? row : valid - 1) - g4 * 4) * ROW_BYTES);
 #pragma unroll
       for (int hh = 0; hh < NH; ++hh)
-        t.v[tg][hh] = load_kv<VLoad, NT>(vp + vrow + hh * 128 * KT::bytes);
+        t.v[tg][hh] = load_tile<VLoad, NT>(vr, vof + hh * 128 * KT::bytes);
     }
   }
 
@@ -289,10 +294,10 @@ struct MfmaAttention {
     const int first = j0 + w;
     const int n = first < j1 ? (j1 - first + NW - 1) / NW : 0;
     if (n == 0) return;                                 // wave-uniform
-    const char* kbase = reinterpret_cast<const char*>(p.k_cache) + (size_t)kvh * TILE_BYTES + c16 * ROW_BYTES +
-                        (KV8 ? g4 * (D / 4) : g4 * 16);
-    const char* vbase =
-        reinterpret_cast<const char*>(p.v_cache) + (size_t)kvh * TILE_BYTES + (g4 * 4) * ROW_BYTES + c16 * 8 * KT::bytes;
+    const char* kpool = reinterpret_cast<const char*>(p.k_cache) + (size_t)kvh * TILE_BYTES;
+    const char* vpool = reinterpret_cast<const char*>(p.v_cache) + (size_t)kvh * TILE_BYTES;
+    const uint32_t klane = (uint32_t)(c16 * ROW_BYTES + (KV8 ? g4 * (D / 4) : g4 * 16));
+    const uint32_t vlane = (uint32_t)((g4 * 4) * ROW_BYTES + c16 * 8 * KT::bytes);
     const size_t block_stride = TILE_BYTES * (size_t)p.num_kv_heads;
     const int lane = threadIdx.x & 63;
     auto load_ids = [&](int chunk) -> int {
@@ -315,24 +320,24 @@ struct MfmaAttention {
       return r < BS ? r : BS;
     };
     Tiles a;
-    issue(p, kbase, vbase, block_stride, id_of(0), valid_of(0), c16, g4, a);
+    issue(p, kpool, vpool, block_stride, klane, vlane, id_of(0), valid_of(0), true, c16, g4, a);
     if constexpr (PIPE) {
       // Both tile sets are refilled on every pass, also past the wave's last
-      // block (which is then loaded again -- cached, never consumed): loads
-      // under a branch would make the compiler wait for all loads in flight
-      // before each consume instead of only the consumed tile's.
+      // block (issued for block n - 1 again but reading no memory, never
+      // consumed): loads under a branch would make the compiler wait for all
+      // loads in flight before each consume instead of only the consumed tile's.
       Tiles b;
       for (int i = 0; i < n; i += 2) {
         const int i1 = i + 1 < n ? i + 1 : n - 1;
         const int i2 = i + 2 < n ? i + 2 : n - 1;
-        issue(p, kbase, vbase, block_stride, id_of(i1), valid_of(i1), c16, g4, b);
+        issue(p, kpool, vpool, block_stride, klane, vlane, id_of(i1), valid_of(i1), i + 1 < n, c16, g4, b);
         consume<MASK>(p, qop, a, valid_of(i), c16, g4, vt, st, col_on);
-        issue(p, kbase, vbase, block_stride, id_of(i2), valid_of(i2), c16, g4, a);
+        issue(p, kpool, vpool, block_stride, klane, vlane, id_of(i2), valid_of(i2), i + 2 < n, c16, g4, a);
         if (i + 1 < n) consume<MASK>(p, qop, b, valid_of(i + 1), c16, g4, vt, st, col_on);
       }
     } else {
       for (int i = 0; i < n; ++i) {
-        if (i > 0) issue(p, kbase, vbase, block_stride, id_of(i), valid_of(i), c16, g4, a);
+        if (i > 0) issue(p, kpool, vpool, block_stride, klane, vlane, id_of(i), valid_of(i), true, c16, g4, a);
         consume<MASK>(p, qop, a, valid_of(i), c16, g4, vt, st, col_on);
       }
     }

@@ -121,23 +121,26 @@ struct VectorAttention {
 
   // Every lane loads unconditionally, so the compiler can count the loads in
   // flight and wait only for the tile being consumed (a load under a per-lane
-  // condition makes it wait for every load, the next tile's too).  A row at or
-  // past `valid` (the last block's tail) reads the block's last real row
-  // instead -- the same cache lines, no extra memory traffic -- and consume
-  // masks it; a table entry outside the pool reads block 0 and the block is
-  // skipped.
-  __device__ static void issue(const AttnParams& p, const char* kbase, const char* vbase, size_t block_stride,
-                               int blk, int valid, int row, Tiles& t) {
+  // condition makes it wait for every load, the next tile's too).  kpool /
+  // vpool point at kv head kvh's tile of block 0 (wave-uniform), lane_off is
+  // the lane's byte offset inside a tile.  A row at or past `valid` (the last
+  // block's tail) reads the block's last real row instead -- the same cache
+  // lines, no extra memory traffic -- and consume masks it.  A table entry
+  // outside the pool, or a block loaded only to keep the loads unconditional
+  // (!live), reads no memory (see load_tile); consume skips the former and
+  // never sees the latter.
+  __device__ static void issue(const AttnParams& p, const char* kpool, const char* vpool, size_t block_stride,
+                               uint32_t lane_off, int blk, int valid, int row, bool live, Tiles& t) {
     t.ok = blk >= 0 && blk < p.num_blocks;                  // out-of-pool entries are skipped
     const size_t boff = (size_t)(t.ok ? blk : 0) * block_stride;
-    const char* kp = kbase + boff;
-    const char* vp = vbase + boff;
+    const int bytes = t.ok && live ? TILE_BYTES : 0;
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kpool + boff, bytes), vr = buffer_rsrc(vpool + boff, bytes);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int r = i * RPW + row;                            // valid >= 1: every block has a real token
-      const ptrdiff_t off = (ptrdiff_t)((r < valid ? r : valid - 1) - row) * (ptrdiff_t)ROW_BYTES;
-      t.k[i] = load_kv<uint4, PKV_KV_NT != 0>(kp + off);
-      t.v[i] = load_kv<uint4, PKV_KV_NT != 0>(vp + off);
+      const uint32_t off = lane_off + (uint32_t)(((r < valid ? r : valid - 1) - row) * ROW_BYTES);
+      t.k[i] = load_tile<uint4, PKV_KV_NT != 0>(kr, off);
+      t.v[i] = load_tile<uint4, PKV_KV_NT != 0>(vr, off);
     }
   }
 
@@ -206,8 +209,9 @@ struct VectorAttention {
     QFrag<QT, KT, VEC> qf;
     qf.load(p.q, ((size_t)seq * p.num_heads + head) * D + (size_t)col * VEC);
     const int32_t* table = p.block_tables + (size_t)seq * p.max_blocks_per_seq;
-    const char* kbase = reinterpret_cast<const char*>(p.k_cache) + (size_t)kvh * TILE_BYTES + row * ROW_BYTES + col * 16;
-    const char* vbase = reinterpret_cast<const char*>(p.v_cache) + (size_t)kvh * TILE_BYTES + row * ROW_BYTES + col * 16;
+    const char* kpool = reinterpret_cast<const char*>(p.k_cache) + (size_t)kvh * TILE_BYTES;
+    const char* vpool = reinterpret_cast<const char*>(p.v_cache) + (size_t)kvh * TILE_BYTES;
+    const uint32_t lane_off = (uint32_t)(row * ROW_BYTES + col * 16);
     const size_t block_stride = TILE_BYTES * (size_t)p.num_kv_heads;
     const int last_partial = (ctx % BS) ? (ctx + BS - 1) / BS - 1 : -1;
     const int lane = threadIdx.x & 63;
@@ -231,17 +235,17 @@ struct VectorAttention {
       return r < BS ? r : BS;
     };
     // Both tile sets are refilled on every pass, also past the wave's last
-    // block (which is then loaded again -- cached, never consumed): loads under
-    // a branch would make the compiler wait for all loads in flight before
-    // each consume instead of only the consumed tile's.
+    // block (issued for block n - 1 again but reading no memory, never
+    // consumed): loads under a branch would make the compiler wait for all
+    // loads in flight before each consume instead of only the consumed tile's.
     Tiles a, b;
-    issue(p, kbase, vbase, block_stride, id_of(0), valid_of(0), row, a);
+    issue(p, kpool, vpool, block_stride, lane_off, id_of(0), valid_of(0), row, true, a);
     for (int i = 0; i < n; i += 2) {
       const int i1 = i + 1 < n ? i + 1 : n - 1;
       const int i2 = i + 2 < n ? i + 2 : n - 1;
-      issue(p, kbase, vbase, block_stride, id_of(i1), valid_of(i1), row, b);
+      issue(p, kpool, vpool, block_stride, lane_off, id_of(i1), valid_of(i1), row, i + 1 < n, b);
       consume(p, qf, a, first + i * NW, ctx, last_partial, row, st);
-      issue(p, kbase, vbase, block_stride, id_of(i2), valid_of(i2), row, a);
+      issue(p, kpool, vpool, block_stride, lane_off, id_of(i2), valid_of(i2), row, i + 2 < n, a);
       if (i + 1 < n) consume(p, qf, b, first + (i + 1) * NW, ctx, last_partial, row, st);
     }
   }

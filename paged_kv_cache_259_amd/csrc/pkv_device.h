@@ -38,30 +38,41 @@ __device__ __forceinline__ void bf16x2_to_f32(uint32_t u, float& lo, float& hi) 
   hi = u32_as_f32(u & 0xffff0000u);
 }
 
-// K/V tile loads of the decode kernels.  A decode step reads each cached byte
-// once, so with NT they carry the non-temporal cache policy (the lines stream
-// through the caches instead of displacing others): on this GPU the read-only
-// probes read scattered tiles 9-11 % and a stream 7 % faster with it, and the
-// one-pass decodes ran 5-7 % faster.
+// K/V tile loads of the decode kernels, through a buffer resource per tile.
+// A decode step reads each cached byte once, so with NT the loads carry the
+// non-temporal cache policy (the lines stream through the caches instead of
+// displacing others): on this GPU the read-only probes read scattered tiles
+// 9-11 % and a stream 7 % faster with it, and the one-pass decodes ran 5-7 %
+// faster.  A tile that need not be read (an entry outside the pool, or the
+// repeat of a wave's last block that keeps its loads unconditional) gets a
+// resource of 0 bytes: a buffer load past the resource's end returns zeros and
+// reads no memory.
 #ifndef PKV_KV_NT
 #define PKV_KV_NT 1
 #endif
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-template <class V, bool NT> __device__ __forceinline__ V load_kv(const void* p);
-template <> __device__ __forceinline__ uint4 load_kv<uint4, true>(const void* p) {
-  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+// A raw buffer resource over the `bytes`-byte range at `base` (wave-uniform:
+// it lives in scalar registers); loads address it with 32-bit byte offsets.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+template <class V, bool NT> __device__ __forceinline__ V load_tile(__amdgpu_buffer_rsrc_t r, uint32_t off);
+template <> __device__ __forceinline__ uint4 load_tile<uint4, true>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);     // cache policy: nt
   return make_uint4(v.x, v.y, v.z, v.w);
 }
-template <> __device__ __forceinline__ uint2 load_kv<uint2, true>(const void* p) {
-  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+template <> __device__ __forceinline__ uint4 load_tile<uint4, false>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+template <> __device__ __forceinline__ uint2 load_tile<uint2, true>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 2);
   return make_uint2(v.x, v.y);
 }
-template <> __device__ __forceinline__ uint4 load_kv<uint4, false>(const void* p) {
-  return *reinterpret_cast<const uint4*>(p);
-}
-template <> __device__ __forceinline__ uint2 load_kv<uint2, false>(const void* p) {
-  return *reinterpret_cast<const uint2*>(p);
+template <> __device__ __forceinline__ uint2 load_tile<uint2, false>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  return make_uint2(v.x, v.y);
 }
 
 // 16 bytes of storage -> 16/bytes fp32 values.

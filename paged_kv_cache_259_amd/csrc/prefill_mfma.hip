@@ -110,14 +110,10 @@ __device__ __forceinline__ void load_lds16(const void* src, void* dst) {
   __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 16, 0, 0);
 }
 
-// The same through a buffer resource: the 16 bytes at byte `off` (per lane) of
-// the `bytes`-byte range at `base` (wave-uniform, in scalar registers) go to
-// LDS bytes dst + 16 l .. +15.  The address is the resource's base plus the
-// 32-bit lane offset, so no 64-bit address is formed per lane.  Every offset
-// passed is inside the range.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
-}
+// The same through a buffer resource (buffer_rsrc): the 16 bytes at byte `off`
+// (per lane) of the resource's range go to LDS bytes dst + 16 l .. +15.  The
+// address is the resource's base plus the 32-bit lane offset, so no 64-bit
+// address is formed per lane.  Every offset passed is inside the range.
 __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint32_t off, void* dst) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)dst, 16, off, 0, 0, 0);
 }

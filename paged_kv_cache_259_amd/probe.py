@@ -20,9 +20,9 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 _vp, _sz, _i, _u = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_uint
 _lib.pkv_probe_stream_read.restype = _i
-_lib.pkv_probe_stream_read.argtypes = [_vp, _sz, _i, _u, _vp, _vp]
+_lib.pkv_probe_stream_read.argtypes = [_vp, _sz, _i, _u, _vp, _i, _vp]
 _lib.pkv_probe_tile_read.restype = _i
-_lib.pkv_probe_tile_read.argtypes = [_vp, _sz, _i, _i, _i, _u, _vp, _vp]
+_lib.pkv_probe_tile_read.argtypes = [_vp, _sz, _i, _i, _i, _u, _vp, _i, _vp]
 
 EXPORTED_SYMBOLS = ("pkv_probe_stream_read", "pkv_probe_tile_read")
 
@@ -31,22 +31,24 @@ def _stream(stream):
     return ctypes.c_void_p((stream or torch.cuda.current_stream()).cuda_stream)
 
 
-def stream_read(buf, nbytes, workgroups, sink, salt=0x9E3779B9, stream=None):
-    """Enqueue one read of the first ``nbytes`` bytes of the uint8 device tensor ``buf``."""
+def stream_read(buf, nbytes, workgroups, sink, salt=0x9E3779B9, nontemporal=True, stream=None):
+    """Enqueue one read of the first ``nbytes`` bytes of the uint8 device tensor ``buf`` (non-temporal
+    loads, or plain ones that displace what the caches hold)."""
     if buf.device.type != "cuda" or sink.device != buf.device or nbytes > buf.numel():
         raise ValueError("buf and sink must be device tensors and nbytes within buf")
-    st = _lib.pkv_probe_stream_read(buf.data_ptr(), nbytes, workgroups, salt, sink.data_ptr(), _stream(stream))
+    st = _lib.pkv_probe_stream_read(buf.data_ptr(), nbytes, workgroups, salt, sink.data_ptr(), int(bool(nontemporal)),
+                                    _stream(stream))
     if st != 0:
         raise RuntimeError(f"pkv_probe_stream_read: status {st}")
 
 
-def tile_read(buf, tile_bytes, workgroups, tiles_per_wave, sink, salt=17, stream=None):
+def tile_read(buf, tile_bytes, workgroups, tiles_per_wave, sink, salt=17, nontemporal=True, stream=None):
     """Enqueue one scattered-tile read over the uint8 device tensor ``buf`` (no tile read twice per launch
     while workgroups x 4 x tiles_per_wave stays within the buffer's tiles)."""
     if buf.device.type != "cuda" or sink.device != buf.device:
         raise ValueError("buf and sink must be device tensors")
     st = _lib.pkv_probe_tile_read(buf.data_ptr(), buf.numel(), tile_bytes, workgroups, tiles_per_wave, salt,
-                                  sink.data_ptr(), _stream(stream))
+                                  sink.data_ptr(), int(bool(nontemporal)), _stream(stream))
     if st != 0:
         raise RuntimeError(f"pkv_probe_tile_read: status {st}")
 

@@ -298,9 +298,9 @@ def test_probe_library_exports_and_host_checks():
     nm = subprocess.run(["nm", "-D", "--defined-only", build.PROBE_LIB], capture_output=True, text=True).stdout
     assert set(names) <= set(re.findall(r"\bT (pkv_probe_\w+)", nm))
     lib = probe.raw_lib()
-    assert lib.pkv_probe_stream_read(None, 1024, 8, 0, FAKE, None) == -1
-    assert lib.pkv_probe_stream_read(FAKE, 1000, 8, 0, FAKE, None) == -2          # not a multiple of 16
-    assert lib.pkv_probe_stream_read(FAKE, 1024, 0, 0, FAKE, None) == -2
-    assert lib.pkv_probe_tile_read(FAKE, 1 << 20, 3000, 8, 4, 0, FAKE, None) == -2  # tile size not built
-    assert lib.pkv_probe_tile_read(FAKE, 1024, 4096, 8, 4, 0, FAKE, None) == -2     # no whole tile
-    assert lib.pkv_probe_tile_read(FAKE, 1 << 20, 4096, 8, 0, 0, FAKE, None) == -2
+    assert lib.pkv_probe_stream_read(None, 1024, 8, 0, FAKE, 1, None) == -1
+    assert lib.pkv_probe_stream_read(FAKE, 1000, 8, 0, FAKE, 0, None) == -2          # not a multiple of 16
+    assert lib.pkv_probe_stream_read(FAKE, 1024, 0, 0, FAKE, 1, None) == -2
+    assert lib.pkv_probe_tile_read(FAKE, 1 << 20, 3000, 8, 4, 0, FAKE, 1, None) == -2  # tile size not built
+    assert lib.pkv_probe_tile_read(FAKE, 1024, 4096, 8, 4, 0, FAKE, 0, None) == -2     # no whole tile
+    assert lib.pkv_probe_tile_read(FAKE, 1 << 20, 4096, 8, 0, 0, FAKE, 1, None) == -2
