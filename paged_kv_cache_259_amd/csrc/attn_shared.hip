@@ -24,7 +24,7 @@ namespace pkv {
 
 template <class T, class KT, int D, int NW, bool APPEND>
 __device__ __forceinline__ void attn_shared_body(AttnParams p) {
-  using A = MfmaAttention<T, KT, D, NW, true>;
+  using A = MfmaAttention<T, KT, D, NW, true, true>;   // non-temporal loads: the group reads each block once
   constexpr int BS = A::BS;
   __shared__ typename A::Smem sm;
   __shared__ int s_seq[16];                                 // member of each group of G columns, -1 if none

@@ -83,7 +83,8 @@ struct QFrag<BF16, BF16, 8> {
   }
 };
 
-template <class QT, class KT, int D, int BS, int NW, int UNROLL>
+// NT: the K/V tiles are loaded with the non-temporal policy (see load_tile).
+template <class QT, class KT, int D, int BS, int NW, int UNROLL, bool NT>
 struct VectorAttention {
   static constexpr int ELT = KT::bytes;
   static constexpr int VEC = 16 / ELT;        // elements per 16-byte load
@@ -139,8 +140,8 @@ struct VectorAttention {
     for (int i = 0; i < NI; ++i) {
       const int r = i * RPW + row;                            // valid >= 1: every block has a real token
       const uint32_t off = lane_off + (uint32_t)(((r < valid ? r : valid - 1) - row) * ROW_BYTES);
-      t.k[i] = load_tile<uint4, PKV_KV_NT != 0>(kr, off);
-      t.v[i] = load_tile<uint4, PKV_KV_NT != 0>(vr, off);
+      t.k[i] = load_tile<uint4, NT>(kr, off);
+      t.v[i] = load_tile<uint4, NT>(vr, off);
     }
   }
 
@@ -319,9 +320,9 @@ constexpr int vector_waves_per_eu() {
 #ifndef PKV_VEC_WAVES_PER_EU
 #define PKV_VEC_WAVES_PER_EU 0   // 0: from the tile size
 #endif
-template <class QT, class KT, int D, int BS, int NW, int UNROLL, bool APPEND>
+template <class QT, class KT, int D, int BS, int NW, int UNROLL, bool NT, bool APPEND>
 __device__ __forceinline__ void attn_vector_body(AttnParams p) {
-  using A = VectorAttention<QT, KT, D, BS, NW, UNROLL>;
+  using A = VectorAttention<QT, KT, D, BS, NW, UNROLL, NT>;
   __shared__ typename A::Smem sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -406,18 +407,18 @@ __device__ __forceinline__ void attn_vector_body(AttnParams p) {
   A::finish(p, st, sm, seq, head, prow, tid, w, row, col);
 }
 
-template <class QT, class KT, int D, int BS, int NW, int UNROLL>
+template <class QT, class KT, int D, int BS, int NW, int UNROLL, bool NT>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(PKV_VEC_WAVES_PER_EU ? PKV_VEC_WAVES_PER_EU : vector_waves_per_eu<KT, D, BS>())))
 void attn_vector_kernel(AttnParams p) {
-  attn_vector_body<QT, KT, D, BS, NW, UNROLL, false>(p);
+  attn_vector_body<QT, KT, D, BS, NW, UNROLL, NT, false>(p);
 }
 
-template <class QT, class KT, int D, int BS, int NW, int UNROLL>
+template <class QT, class KT, int D, int BS, int NW, int UNROLL, bool NT>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(PKV_VEC_WAVES_PER_EU ? PKV_VEC_WAVES_PER_EU : vector_waves_per_eu<KT, D, BS>())))
 void attn_vector_append_kernel(AttnParams p) {
-  attn_vector_body<QT, KT, D, BS, NW, UNROLL, true>(p);
+  attn_vector_body<QT, KT, D, BS, NW, UNROLL, NT, true>(p);
 }
 
 // ---------------------------------------------------------------------------
@@ -429,17 +430,24 @@ void attn_vector_append_kernel(AttnParams p) {
 #ifndef PKV_VEC_UNROLL
 #define PKV_VEC_UNROLL 2
 #endif
-template <bool APPEND, class QT, class KT, int D, int BS>
-static hipError_t launch_vec(const AttnParams& p, hipStream_t stream) {
+template <bool APPEND, class QT, class KT, int D, int BS, bool NT>
+static hipError_t launch_vec_nt(const AttnParams& p, hipStream_t stream) {
   constexpr int NW = PKV_VEC_NW;
   constexpr int NI = BS / (64 / (D * KT::bytes / 16));
   constexpr int UNROLL = NI <= 4 ? PKV_VEC_UNROLL : 1;   // keep small tiles in flight per wave
   if constexpr (APPEND)
-    hipLaunchKernelGGL((attn_vector_append_kernel<QT, KT, D, BS, NW, UNROLL>), dim3(p.total_wgs), dim3(NW * 64), 0,
-                       stream, p);
+    hipLaunchKernelGGL((attn_vector_append_kernel<QT, KT, D, BS, NW, UNROLL, NT>), dim3(p.total_wgs), dim3(NW * 64),
+                       0, stream, p);
   else
-    hipLaunchKernelGGL((attn_vector_kernel<QT, KT, D, BS, NW, UNROLL>), dim3(p.total_wgs), dim3(NW * 64), 0, stream, p);
+    hipLaunchKernelGGL((attn_vector_kernel<QT, KT, D, BS, NW, UNROLL, NT>), dim3(p.total_wgs), dim3(NW * 64), 0,
+                       stream, p);
   return hipGetLastError();
+}
+
+template <bool APPEND, class QT, class KT, int D, int BS>
+static hipError_t launch_vec(const AttnParams& p, hipStream_t stream) {
+  return p.kv_cached ? launch_vec_nt<APPEND, QT, KT, D, BS, false>(p, stream)
+                     : launch_vec_nt<APPEND, QT, KT, D, BS, true>(p, stream);
 }
 
 template <bool APPEND, class QT, class KT, int D>

@@ -224,6 +224,9 @@ size_t pkv_attention_workspace_bytes(int num_seqs, int num_heads, int num_kv_hea
 
 namespace {
 
+// The calling thread's K/V load policy (pkv_set_kv_load_policy).
+thread_local int t_kv_load_policy = PKV_KV_LOADS_STREAM;
+
 // Decode, optionally writing each sequence's new token first (new_k != NULL).
 int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache, const void* new_k,
                 const void* new_v, const int64_t* slot_mapping, const int32_t* block_tables, int max_blocks_per_seq,
@@ -309,6 +312,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
     if (xcd_chunk_env() < 0) p.xcd_chunk = 0;
   }
   p.head_run_units = head_run_units_for(pl.mode, pl.units);
+  p.kv_cached = t_kv_load_policy == PKV_KV_LOADS_CACHED ? 1 : 0;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (pkv::debug_checks_on()) {
@@ -353,6 +357,13 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
 }  // namespace
 
 extern "C" {
+
+int pkv_set_kv_load_policy(int policy) {
+  if (policy != PKV_KV_LOADS_STREAM && policy != PKV_KV_LOADS_CACHED) return PKV_ERR_BAD_SIZE;
+  const int prev = t_kv_load_policy;
+  t_kv_load_policy = policy;
+  return prev;
+}
 
 int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                                const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,

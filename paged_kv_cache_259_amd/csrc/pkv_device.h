@@ -39,17 +39,16 @@ __device__ __forceinline__ void bf16x2_to_f32(uint32_t u, float& lo, float& hi) 
 }
 
 // K/V tile loads of the decode kernels, through a buffer resource per tile.
-// A decode step reads each cached byte once, so with NT the loads carry the
-// non-temporal cache policy (the lines stream through the caches instead of
-// displacing others): on this GPU the read-only probes read scattered tiles
-// 9-11 % and a stream 7 % faster with it, and the one-pass decodes ran 5-7 %
-// faster.  A tile that need not be read (an entry outside the pool, or the
-// repeat of a wave's last block that keeps its loads unconditional) gets a
-// resource of 0 bytes: a buffer load past the resource's end returns zeros and
-// reads no memory.
-#ifndef PKV_KV_NT
-#define PKV_KV_NT 1
-#endif
+// When a launch reads each cached byte once (distinct contexts), NT gives the
+// loads the non-temporal cache policy: the lines stream through the caches
+// instead of displacing others.  On this GPU the read-only probes read
+// scattered tiles 9-11 % and a stream 7 % faster with it, and the one-pass
+// decodes ran 5-7 % faster.  Blocks that several sequences of one launch share
+// are read again by the later sequences, and those re-reads hit L2 or the
+// Infinity Cache only with the default policy (NT false).  A tile that need not
+// be read (an entry outside the pool, or the repeat of a wave's last block
+// that keeps its loads unconditional) gets a resource of 0 bytes: a buffer load
+// past the resource's end returns zeros and reads no memory.
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 // A raw buffer resource over the `bytes`-byte range at `base` (wave-uniform:
@@ -561,6 +560,7 @@ struct AttnParams {
   uint32_t total_wgs;
   uint32_t xcd_chunk;       // see xcd_remap
   uint32_t head_run_units;  // > 0: one pass, workgroup -> work id through head_runs (xcd_chunk unused)
+  int kv_cached;            // K/V loads with the default cache policy (else non-temporal; see load_tile)
   // shared-block decode only (attn_shared.hip): group g's members are
   // grp_mem[grp_off[g] .. grp_off[g+1]) (at most grp_max of them); the first
   // grp_shared[g] blocks of their tables are the same physical blocks.

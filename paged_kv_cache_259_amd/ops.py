@@ -7,6 +7,7 @@ kernels; there is no CPU fallback -- importing this module raises ImportError
 when the library has not been built.
 """
 
+import contextlib
 import ctypes
 import os
 
@@ -73,12 +74,14 @@ _lib.pkv_set_debug_checks.argtypes = [_c_int]
 _lib.pkv_debug_report.restype = _c_int
 _lib.pkv_debug_report.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(_c_int),
                                   ctypes.POINTER(ctypes.c_int64)]
+_lib.pkv_set_kv_load_policy.restype = _c_int
+_lib.pkv_set_kv_load_policy.argtypes = [_c_int]
 
 EXPORTED_SYMBOLS = (
     "pkv_status_string", "pkv_version", "pkv_attention_plan", "pkv_attention_workspace_bytes",
     "pkv_paged_attention_decode", "pkv_reshape_and_cache", "pkv_copy_blocks", "pkv_swap_blocks",
     "pkv_paged_prefill_attention", "pkv_paged_attention_decode_append", "pkv_paged_attention_decode_shared",
-    "pkv_paged_attention_decode_noalloc", "pkv_set_debug_checks", "pkv_debug_report",
+    "pkv_paged_attention_decode_noalloc", "pkv_set_debug_checks", "pkv_debug_report", "pkv_set_kv_load_policy",
 )
 
 ERR_PRECONDITION = -11              # PKV_ERR_PRECONDITION
@@ -90,6 +93,7 @@ CHECK_KINDS = {
 }
 
 STATIC_SCRATCH_BYTES = 48 << 20     # PKV_STATIC_SCRATCH_BYTES
+KV_LOAD_POLICIES = {"stream": 0, "cached": 1}   # PKV_KV_LOADS_STREAM, PKV_KV_LOADS_CACHED
 
 
 class PkvError(RuntimeError):
@@ -106,6 +110,25 @@ class PkvError(RuntimeError):
 def set_debug_checks(mode):
     """Debug checks of the device-resident values: 1 on, 0 off, -1 follow PKV_DEBUG. Returns the previous mode."""
     return _lib.pkv_set_debug_checks(int(mode))
+
+
+def set_kv_load_policy(policy):
+    """K/V load policy of this thread's later decode calls: "stream" (non-temporal, the default: each block
+    read once per launch) or "cached" (shared blocks stay in the caches between their readers).  Returns the
+    previous policy's name."""
+    prev = _lib.pkv_set_kv_load_policy(KV_LOAD_POLICIES[policy])
+    _check(prev if prev < 0 else 0, "pkv_set_kv_load_policy")
+    return {v: k for k, v in KV_LOAD_POLICIES.items()}[prev]
+
+
+@contextlib.contextmanager
+def kv_load_policy(policy):
+    """Run the enclosed decode calls of this thread under `policy` (see set_kv_load_policy)."""
+    prev = set_kv_load_policy(policy)
+    try:
+        yield
+    finally:
+        set_kv_load_policy(prev)
 
 
 def debug_report():

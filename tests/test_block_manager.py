@@ -382,3 +382,20 @@ def test_shared_groups_cover_each_sequence_once_and_share_only_common_blocks():
     assert sorted(len(m) for m in a_groups) == [2, 4]     # six samples in chunks of four
     with pytest.raises(ValueError):
         bm.shared_groups(seqs, 0)
+
+
+def test_kv_load_policy_counts_repeated_block_reads():
+    """A launch whose sequences read distinct blocks streams; forks that share their prompt's blocks
+    (a repeat for every fork after the first) ask for the cached policy; the threshold is a share of
+    the launch's block reads, and only the blocks a context covers count."""
+    bm = BlockManager(64, 16)
+    bm.add_sequence(0, 100)                 # 7 blocks
+    bm.add_sequence(1, 33)                  # 3 blocks
+    assert bm.kv_load_policy([0, 1]) == "stream" and bm.kv_load_policy([]) == "stream"
+    bm.fork(0, 2)
+    bm.append_slot(2)                       # copy-on-write of the partial last block: 6 blocks shared
+    assert bm.kv_load_policy([0, 1, 2]) == "cached"                       # 6 repeats in 17 reads
+    assert bm.kv_load_policy([0, 1, 2], repeat_share=0.5) == "stream"
+    assert bm.kv_load_policy([1, 2]) == "stream"                          # the sharer is not in the launch
+    bm.tables[1].append(bm.tables[0][0])    # an entry past sequence 1's context is never read
+    assert bm.kv_load_policy([0, 1]) == "stream"

@@ -3,7 +3,7 @@
 Both paths start from the same pools, in which every sequence's newest position
 is not yet written (NaN there).  The outputs and the whole pools must come out
 bit-identical, in every launch shape (one pass, fixed partitions, balanced
-slices), both kernel families and all cache formats.
+slices), both kernel families, all cache formats and both K/V load policies.
 """
 
 import numpy as np
@@ -45,8 +45,14 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("policy", ["stream", "cached"])
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-def test_append_equals_write_then_decode(ops, case):
+def test_append_equals_write_then_decode(ops, case, policy):
+    with ops.kv_load_policy(policy):              # the K/V loads' cache policy changes no bit
+        _append_equals_write_then_decode(ops, case)
+
+
+def _append_equals_write_then_decode(ops, case):
     name, qdt, fmt, H, KVH, d, bs, lens, part = case
     rng = np.random.default_rng(sum(ord(c) for c in name))
     S = len(lens)
