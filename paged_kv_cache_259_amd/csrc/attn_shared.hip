@@ -121,11 +121,13 @@ void attn_shared_append_kernel(AttnParams p) {
 }
 
 // Waves per workgroup.  The grid is one workgroup per (group, kv head), often
-// only a few per compute unit; with 2 waves each, every wave of such a grid is
-// resident from the start and walks twice the blocks, which measured faster
-// than 4 waves (some of which wait for a second round of residency).
+// only a few per compute unit.  With plain K/V loads 2 waves measured faster
+// (every wave of such a grid resident from the start, walking twice the
+// blocks); with the non-temporal loads 4 waves are 1 % faster (shared-prefix
+// E4M3 workload: 129.8-130.1 -> 128.7-129.1 us), although some wait for a
+// second round of residency.
 #ifndef PKV_SHARED_NW
-#define PKV_SHARED_NW 2
+#define PKV_SHARED_NW 4
 #endif
 template <class T, class KT, int D>
 static hipError_t launch_shared(const AttnParams& p, bool append, hipStream_t stream) {
