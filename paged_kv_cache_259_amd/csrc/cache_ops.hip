@@ -151,32 +151,67 @@ struct CopyParams {
   int wgs_per_block;
 };
 
-// Whole blocks, K and V, 16 bytes per thread.  Serves copy_blocks (one pool) and
-// swap_blocks (a device pool and a pinned host pool, either way round).
+// Whole blocks, K and V.  Serves copy_blocks (one pool) and swap_blocks (a
+// device pool and a pinned host pool, either way round).  A workgroup copies
+// 256 * U 16-byte chunks of one pair's block in each tensor: thread t takes
+// chunks t + 256 u (u < U) and issues all 2U loads before the first store, so
+// each thread keeps 2U loads in flight.  NT: both ends are device memory, and
+// the copy reads each source byte once and writes each destination byte once,
+// so loads and stores carry the non-temporal cache policy; copies to or from
+// the host pool keep the default.
+template <int U, bool NT>
 __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyParams p) {
   const int pair = blockIdx.x / p.wgs_per_block;
-  const int64_t chunk = (int64_t)(blockIdx.x - pair * p.wgs_per_block) * 256 + threadIdx.x;
-  if (chunk * 16 >= p.block_bytes) return;
+  const int64_t c0 = (int64_t)(blockIdx.x - pair * p.wgs_per_block) * (256 * U) + threadIdx.x;
+  const int64_t chunks = p.block_bytes / 16;
   const int64_t src = p.pairs[2 * pair];
   const int64_t dst = p.pairs[2 * pair + 1];
   if (src < 0 || src >= p.src_blocks || dst < 0 || dst >= p.dst_blocks) return;
-  const int64_t so = src * p.block_bytes + chunk * 16;
-  const int64_t dof = dst * p.block_bytes + chunk * 16;
-  const uint4 k = *reinterpret_cast<const uint4*>(p.src_k + so);
-  const uint4 v = *reinterpret_cast<const uint4*>(p.src_v + so);
-  *reinterpret_cast<uint4*>(p.dst_k + dof) = k;
-  *reinterpret_cast<uint4*>(p.dst_v + dof) = v;
+  const u32x4_t* sk = reinterpret_cast<const u32x4_t*>(p.src_k + src * p.block_bytes);
+  const u32x4_t* sv = reinterpret_cast<const u32x4_t*>(p.src_v + src * p.block_bytes);
+  u32x4_t* dk = reinterpret_cast<u32x4_t*>(p.dst_k + dst * p.block_bytes);
+  u32x4_t* dv = reinterpret_cast<u32x4_t*>(p.dst_v + dst * p.block_bytes);
+  u32x4_t k[U], v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t c = c0 + 256 * u;
+    if (c < chunks) {
+      if constexpr (NT) {
+        k[u] = __builtin_nontemporal_load(sk + c);
+        v[u] = __builtin_nontemporal_load(sv + c);
+      } else {
+        k[u] = sk[c];
+        v[u] = sv[c];
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t c = c0 + 256 * u;
+    if (c < chunks) {
+      if constexpr (NT) {
+        __builtin_nontemporal_store(k[u], dk + c);
+        __builtin_nontemporal_store(v[u], dv + c);
+      } else {
+        dk[c] = k[u];
+        dv[c] = v[u];
+      }
+    }
+  }
 }
 
 hipError_t launch_copy_blocks(const void* src_k, const void* src_v, int src_blocks, void* dst_k, void* dst_v,
                               int dst_blocks, const int64_t* pairs, int num_pairs, int64_t block_bytes,
-                              hipStream_t stream) {
+                              bool device_only, hipStream_t stream) {
+  constexpr int U = kCopyChunksPerWg / 256;
   const int64_t chunks = block_bytes / 16;
-  const int wgs = (int)((chunks + 255) / 256);
+  const int wgs = (int)((chunks + kCopyChunksPerWg - 1) / kCopyChunksPerWg);
   CopyParams p{reinterpret_cast<const char*>(src_k), reinterpret_cast<const char*>(src_v),
                reinterpret_cast<char*>(dst_k), reinterpret_cast<char*>(dst_v), pairs, block_bytes,
                src_blocks, dst_blocks, wgs};
-  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)((int64_t)num_pairs * wgs)), dim3(256), 0, stream, p);
+  const dim3 grid((unsigned)((int64_t)num_pairs * wgs));
+  if (device_only) hipLaunchKernelGGL((copy_blocks_kernel<U, true>), grid, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL((copy_blocks_kernel<U, false>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -249,7 +284,7 @@ int pkv_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, 
   if (eb == 0) return PKV_ERR_UNSUPPORTED;
   const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * eb;
   if (block_bytes % 16 != 0) return PKV_ERR_UNSUPPORTED;
-  const int64_t wgs = (block_bytes / 16 + 255) / 256;
+  const int64_t wgs = (block_bytes / 16 + kCopyChunksPerWg - 1) / kCopyChunksPerWg;
   if ((double)num_pairs * wgs > 2147483647.0) return PKV_ERR_BAD_SIZE;
   if (num_pairs == 0) return PKV_OK;
   if (!k_cache || !v_cache || !block_mapping) return PKV_ERR_NULL_POINTER;
@@ -263,7 +298,7 @@ int pkv_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, 
   }
   (void)hipGetLastError();
   return launch_status(launch_copy_blocks(k_cache, v_cache, num_blocks, k_cache, v_cache, num_blocks,
-                                               block_mapping, num_pairs, block_bytes, s));
+                                               block_mapping, num_pairs, block_bytes, true, s));
 }
 
 int pkv_swap_blocks(const void* src_k, const void* src_v, int src_num_blocks, void* dst_k, void* dst_v,
@@ -276,7 +311,7 @@ int pkv_swap_blocks(const void* src_k, const void* src_v, int src_num_blocks, vo
   if (eb == 0) return PKV_ERR_UNSUPPORTED;
   const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * eb;
   if (block_bytes % 16 != 0) return PKV_ERR_UNSUPPORTED;
-  const int64_t wgs = (block_bytes / 16 + 255) / 256;
+  const int64_t wgs = (block_bytes / 16 + kCopyChunksPerWg - 1) / kCopyChunksPerWg;
   if ((double)num_pairs * wgs > 2147483647.0) return PKV_ERR_BAD_SIZE;
   if (num_pairs == 0) return PKV_OK;
   if (!src_k || !src_v || !dst_k || !dst_v || !block_mapping) return PKV_ERR_NULL_POINTER;
@@ -306,7 +341,7 @@ int pkv_swap_blocks(const void* src_k, const void* src_v, int src_num_blocks, vo
   }
   (void)hipGetLastError();
   return launch_status(launch_copy_blocks(a[0], a[1], src_num_blocks, a[2], a[3], dst_num_blocks,
-                                               static_cast<const int64_t*>(a[4]), num_pairs, block_bytes, s));
+                                               static_cast<const int64_t*>(a[4]), num_pairs, block_bytes, false, s));
 }
 
 }  // extern "C"

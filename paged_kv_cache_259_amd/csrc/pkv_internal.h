@@ -49,9 +49,14 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
                                     int head_dim, int block_size, int num_blocks, int src_dtype, int kv_dtype,
                                     float k_scale, float v_scale, const float* k_scales, const float* v_scales,
                                     hipStream_t stream);
+// 16-byte chunks of each tensor one copy_blocks workgroup moves (256 threads x 4)
+#ifndef PKV_COPY_CHUNKS_PER_WG
+#define PKV_COPY_CHUNKS_PER_WG 1024
+#endif
+constexpr int kCopyChunksPerWg = PKV_COPY_CHUNKS_PER_WG;
 hipError_t launch_copy_blocks(const void* src_k, const void* src_v, int src_blocks, void* dst_k, void* dst_v,
                               int dst_blocks, const int64_t* pairs, int num_pairs, int64_t block_bytes,
-                              hipStream_t stream);
+                              bool device_only, hipStream_t stream);
 
 // Debug checks of the device-resident values (checks.hip, pkv_set_debug_checks).
 // An entry point whose host checks passed builds one DeviceChecks on its

@@ -84,6 +84,9 @@ def _in_timed_call(kernel, workload):
     return "_append_" in kernel or kernel.startswith(("attn_reduce", "attn_slice_finish"))
 
 
+COPY_CHUNKS_PER_WG = 1024   # kCopyChunksPerWg: 16-byte chunks per copy_blocks workgroup and tensor
+
+
 def counters(fetch_dir, write_dir, workload, n_pairs, out=sys.stdout):
     sys.path.insert(0, ROOT)
     import bench
@@ -93,11 +96,12 @@ def counters(fetch_dir, write_dir, workload, n_pairs, out=sys.stdout):
     block_bytes = w.num_kv_heads * w.block_size * w.head_dim * elt
     f = _counter(fetch_dir, "FETCH_SIZE")
     wr = _counter(write_dir, "WRITE_SIZE")
-    # the calibration copy is the copy_blocks dispatch whose grid is n_pairs x (workgroups per block);
-    # other copy_blocks dispatches (copy-on-write pairs, swaps) have other grids
-    grid = n_pairs * ((block_bytes // 16 + 255) // 256) * 256
-    cal = ("copy_blocks_kernel", grid)
-    if cal not in f or cal not in wr:
+    # the calibration copy is the device-to-device copy_blocks dispatch whose grid is n_pairs x
+    # (workgroups per block, COPY_CHUNKS_PER_WG 16-byte chunks each); other copy_blocks dispatches
+    # (copy-on-write pairs, swaps) have other grids
+    grid = n_pairs * ((block_bytes // 16 + COPY_CHUNKS_PER_WG - 1) // COPY_CHUNKS_PER_WG) * 256
+    cal = next((k for k in f if k[0].startswith("copy_blocks_kernel") and k[1] == grid and k in wr), None)
+    if cal is None:
         raise SystemExit(f"no copy_blocks dispatch with grid {grid} (the calibration copy) in the counter runs")
     copy_bytes = 2 * n_pairs * block_bytes          # K and V pools, each read once and written once
     fs, ws = copy_bytes / (f[cal] * 1024), copy_bytes / (wr[cal] * 1024)

@@ -81,3 +81,28 @@ def test_short_names():
         "stream_read_kernel"
     assert profiling._short("void pkv::attn_mfma_append_kernel<pkv::BF16, pkv::BF16, 128, 2, true>(pkv::AttnParams)") \
         == "attn_mfma_append_kernel<BF16, BF16, 128, 2, true>"
+
+
+def test_counters_calibrate_on_the_device_copy(tmp_path, monkeypatch):
+    """The calibration copy is the copy_blocks dispatch with n_pairs x (workgroups per block) x 256
+    threads; FETCH_SIZE / WRITE_SIZE of the attention kernel are scaled by what the counters read on
+    it against its known bytes.  The grid formula follows the library's chunks per workgroup."""
+    import re
+    hdr = open(os.path.join(profiling.ROOT, "paged_kv_cache_259_amd", "csrc", "pkv_internal.h")).read()
+    assert int(re.search(r"#define PKV_COPY_CHUNKS_PER_WG (\d+)", hdr).group(1)) == profiling.COPY_CHUNKS_PER_WG
+    monkeypatch.setattr(profiling, "ROOT", str(tmp_path))         # the traffic table goes under tmp_path
+    os.makedirs(tmp_path / "profiles")
+    n = 64
+    block_bytes = 8 * 16 * 128 * 2                                 # the GQA bf16 pool's block
+    grid = n * (block_bytes // 16 // profiling.COPY_CHUNKS_PER_WG) * 256
+    copy = "void pkv::copy_blocks_kernel<4, true>(pkv::CopyParams)"
+    kib = 2 * n * block_bytes / 1024
+    _make_db(str(tmp_path / "f" / "run_results.db"),
+             counters=[(copy, grid, "FETCH_SIZE", kib / 2), (copy, 999, "FETCH_SIZE", 1.0), (APPEND, 4096, "FETCH_SIZE", 100.0)])
+    _make_db(str(tmp_path / "w" / "run_results.db"),
+             counters=[(copy, grid, "WRITE_SIZE", kib), (APPEND, 4096, "WRITE_SIZE", 10.0)])
+    out = io.StringIO()
+    profiling.counters(str(tmp_path / "f"), str(tmp_path / "w"), "gqa_bf16", n, out)
+    text = out.getvalue()
+    assert "scale 2.0000" in text and "scale 1.0000" in text
+    assert "timed call total: 0.20 MB read + 0.01 MB written" in text
