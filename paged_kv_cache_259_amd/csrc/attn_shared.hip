@@ -123,11 +123,11 @@ void attn_shared_append_kernel(AttnParams p) {
 // Waves per workgroup.  The grid is one workgroup per (group, kv head), often
 // only a few per compute unit.  With plain K/V loads 2 waves measured faster
 // (every wave of such a grid resident from the start, walking twice the
-// blocks); with the non-temporal loads 4 waves are 1 % faster (shared-prefix
-// E4M3 workload: 129.8-130.1 -> 128.7-129.1 us), although some wait for a
-// second round of residency.
+// blocks).  With the non-temporal loads, on the shared-prefix E4M3 workload
+// (1280 workgroups): 2 waves 129.8-130.1 us, 4 waves 128.7-129.6 us, 3 waves
+// 127.9-128.0 us, 8 waves 129.6-129.9 us.
 #ifndef PKV_SHARED_NW
-#define PKV_SHARED_NW 4
+#define PKV_SHARED_NW 3
 #endif
 template <class T, class KT, int D>
 static hipError_t launch_shared(const AttnParams& p, bool append, hipStream_t stream) {
