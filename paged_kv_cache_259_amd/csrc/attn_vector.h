@@ -84,7 +84,7 @@ struct QFrag<BF16, BF16, 8> {
 };
 
 // NT: the K/V tiles are loaded with the non-temporal policy (see load_tile).
-template <class QT, class KT, int D, int BS, int NW, int UNROLL, bool NT>
+template <class QT, class KT, int D, int BS, int NW, bool NT>
 struct VectorAttention {
   static constexpr int ELT = KT::bytes;
   static constexpr int VEC = 16 / ELT;        // elements per 16-byte load
@@ -320,9 +320,9 @@ constexpr int vector_waves_per_eu() {
 #ifndef PKV_VEC_WAVES_PER_EU
 #define PKV_VEC_WAVES_PER_EU 0   // 0: from the tile size
 #endif
-template <class QT, class KT, int D, int BS, int NW, int UNROLL, bool NT, bool APPEND>
+template <class QT, class KT, int D, int BS, int NW, bool NT, bool APPEND>
 __device__ __forceinline__ void attn_vector_body(AttnParams p) {
-  using A = VectorAttention<QT, KT, D, BS, NW, UNROLL, NT>;
+  using A = VectorAttention<QT, KT, D, BS, NW, NT>;
   __shared__ typename A::Smem sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -407,18 +407,18 @@ __device__ __forceinline__ void attn_vector_body(AttnParams p) {
   A::finish(p, st, sm, seq, head, prow, tid, w, row, col);
 }
 
-template <class QT, class KT, int D, int BS, int NW, int UNROLL, bool NT>
+template <class QT, class KT, int D, int BS, int NW, bool NT>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(PKV_VEC_WAVES_PER_EU ? PKV_VEC_WAVES_PER_EU : vector_waves_per_eu<KT, D, BS>())))
 void attn_vector_kernel(AttnParams p) {
-  attn_vector_body<QT, KT, D, BS, NW, UNROLL, NT, false>(p);
+  attn_vector_body<QT, KT, D, BS, NW, NT, false>(p);
 }
 
-template <class QT, class KT, int D, int BS, int NW, int UNROLL, bool NT>
+template <class QT, class KT, int D, int BS, int NW, bool NT>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(PKV_VEC_WAVES_PER_EU ? PKV_VEC_WAVES_PER_EU : vector_waves_per_eu<KT, D, BS>())))
 void attn_vector_append_kernel(AttnParams p) {
-  attn_vector_body<QT, KT, D, BS, NW, UNROLL, NT, true>(p);
+  attn_vector_body<QT, KT, D, BS, NW, NT, true>(p);
 }
 
 // ---------------------------------------------------------------------------
@@ -427,20 +427,14 @@ void attn_vector_append_kernel(AttnParams p) {
 #ifndef PKV_VEC_NW
 #define PKV_VEC_NW 4
 #endif
-#ifndef PKV_VEC_UNROLL
-#define PKV_VEC_UNROLL 2
-#endif
 template <bool APPEND, class QT, class KT, int D, int BS, bool NT>
 static hipError_t launch_vec_nt(const AttnParams& p, hipStream_t stream) {
   constexpr int NW = PKV_VEC_NW;
-  constexpr int NI = BS / (64 / (D * KT::bytes / 16));
-  constexpr int UNROLL = NI <= 4 ? PKV_VEC_UNROLL : 1;   // keep small tiles in flight per wave
   if constexpr (APPEND)
-    hipLaunchKernelGGL((attn_vector_append_kernel<QT, KT, D, BS, NW, UNROLL, NT>), dim3(p.total_wgs), dim3(NW * 64),
-                       0, stream, p);
-  else
-    hipLaunchKernelGGL((attn_vector_kernel<QT, KT, D, BS, NW, UNROLL, NT>), dim3(p.total_wgs), dim3(NW * 64), 0,
+    hipLaunchKernelGGL((attn_vector_append_kernel<QT, KT, D, BS, NW, NT>), dim3(p.total_wgs), dim3(NW * 64), 0,
                        stream, p);
+  else
+    hipLaunchKernelGGL((attn_vector_kernel<QT, KT, D, BS, NW, NT>), dim3(p.total_wgs), dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
